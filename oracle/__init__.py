@@ -1,0 +1,44 @@
+"""CPU oracle for group-wise symmetric INT4 (RTN) quantization and the W4A16 linear.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code, tables or helpers with the HIP
+library under ``bit_group_quantized_w4_amd/``; the only thing both sides see is
+the seeded synthetic input from ``workloads/``.
+
+What it computes (sources are the public pages this project is built from):
+
+* ``rtn_quantize_ref`` -- the group quantizer of the Qwen3.5-4B quantization
+  study (parksieon.github.io/qwen35-4b-quantization-study), section 1 "what was
+  compressed": the equation q = clip(round(w/d) + z, qmin, qmax), w_hat = d(q - z)
+  with its symbol table, groups of 128 consecutive inputs along each row, and
+  section 2's settings table (RTN, symmetric, min/max range, group 128, no
+  clipping search).  Done in fp32, as the kernel does.
+* ``w4_linear_ref`` -- y = W_hat x from the same section 1 (the 2560x9216 FFN
+  example) with 4-bit weights and BF16 inputs (section 2 settings table), in
+  fp64.
+* ``pack_canonical`` / ``unpack_canonical`` -- the canonical two-codes-per-byte
+  byte order used to compare codes bit for bit.
+
+Every function here is pinned by ``tests/test_oracle.py`` against exact
+rational arithmetic, brute force on small inputs, closed forms and hand-derived
+fixtures in ``tests/golden/``; none is "parity unpinned".
+"""
+
+from .bf16 import bf16_bits_to_f64
+from .linear import dequantize_ref, w4_linear_ref
+from .packing import pack_canonical, unpack_canonical
+from .rtn import GROUP, NAN_BITS, QMAX, QMIN, rtn_quantize_ref
+
+__all__ = [
+    "GROUP",
+    "NAN_BITS",
+    "QMAX",
+    "QMIN",
+    "bf16_bits_to_f64",
+    "dequantize_ref",
+    "pack_canonical",
+    "rtn_quantize_ref",
+    "unpack_canonical",
+    "w4_linear_ref",
+]

@@ -1,0 +1,329 @@
+"""Independent checks ("pins") for the CPU oracle.
+
+Each check takes the function under test as an argument so that the same
+check can be run against the oracle (it must pass) and against deliberately
+broken copies of it (it must fail): see test_oracle.py.  The expectations come
+from exact rational arithmetic (fractions.Fraction), brute force over the 16
+code levels, closed forms and the hand-derived fixtures in tests/golden/ --
+never from the oracle itself and never from the HIP library.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+class PinFailure(AssertionError):
+    pass
+
+
+def _check(cond, msg):
+    if not cond:
+        raise PinFailure(msg)
+
+
+# ----------------------------------------------------------------------------
+# exact fp32 helpers (independent of numpy's float32 division)
+# ----------------------------------------------------------------------------
+
+def f32_bits(v):
+    return int(np.asarray(v, dtype=np.float32).view(np.uint32))
+
+
+def bits_f32(b):
+    return np.array([b], dtype=np.uint32).view(np.float32)[0]
+
+
+def f32_nearest(fr):
+    """fp32 value nearest to the rational `fr`, ties to even (exact search)."""
+    c = np.float32(float(fr))  # within one fp32 ulp of the answer
+    cands = []
+    for v in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        if np.isfinite(v):
+            cands.append(v)
+    best = None
+    for v in cands:
+        dist = abs(Fraction(float(v)) - fr)
+        key = (dist, f32_bits(v) & 1)  # ties: even significand first
+        if best is None or key < best[0]:
+            best = (key, v)
+    return np.float32(best[1])
+
+
+def nearest_level(t):
+    """Brute force: the code in [-8, 7] nearest to t (a Fraction), ties away from 0."""
+    best = None
+    for q in range(-8, 8):
+        key = (abs(t - q), -abs(q))
+        if best is None or key < best[0]:
+            best = (key, q)
+    return best[1]
+
+
+# ----------------------------------------------------------------------------
+# golden fixtures
+# ----------------------------------------------------------------------------
+
+def load_groups(name):
+    """Parse a tests/golden/*.txt group fixture -> list of (name, d_bits, w[128], q[128])."""
+    groups = []
+    cur = None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "group":
+                cur = {"name": tok[1], "d": None,
+                       "w": np.zeros(128, dtype=np.uint32), "q": np.zeros(128, dtype=np.int64)}
+            elif tok[0] == "d":
+                cur["d"] = int(tok[1], 16)
+            elif tok[0] == "w":
+                i = int(tok[1])
+                cur["w"][i] = int(tok[2], 16)
+                cur["q"][i] = int(tok[3])
+            elif tok[0] == "end":
+                groups.append((cur["name"], cur["d"], cur["w"].view(np.float32), cur["q"]))
+                cur = None
+    return groups
+
+
+def check_golden(quantize, fixture):
+    """Each fixture group, quantized as one 1x128 row, gives exactly the listed d and codes."""
+    for name, d_bits, w, q_exp in load_groups(fixture):
+        q, d = quantize(w.reshape(1, 128).copy())
+        _check(f32_bits(d[0, 0]) == d_bits,
+               f"{fixture}:{name}: d bits {f32_bits(d[0, 0]):#010x} != {d_bits:#010x}")
+        bad = np.nonzero(np.asarray(q[0], dtype=np.int64) != q_exp)[0]
+        _check(bad.size == 0, f"{fixture}:{name}: codes differ at {bad[:8].tolist()}")
+
+
+# ----------------------------------------------------------------------------
+# exact-rational pins of the quantizer
+# ----------------------------------------------------------------------------
+
+def toy_weights(seed, N=4, K=256):
+    """Small fp32 matrices with mixed magnitudes: normal, tiny, subnormal, large groups."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    G = K // 128
+    for n in range(N):
+        for g in range(G):
+            kind = (n * G + g) % 6
+            sl = slice(128 * g, 128 * g + 128)
+            if kind == 1:
+                W[n, sl] *= np.float32(1e-30)
+            elif kind == 2:  # subnormal group
+                W[n, sl] = (rng.integers(-4000, 4000, 128) * 2.0 ** -149).astype(np.float32)
+            elif kind == 3:  # large group
+                W[n, sl] *= np.float32(1e36)
+            elif kind == 4:  # values on a coarse grid: many exact ties after division
+                W[n, sl] = (rng.integers(-14, 15, 128) * 0.25).astype(np.float32)
+    return W
+
+
+def check_scale_exact(quantize, W):
+    """d is the fp32 nearest to max|w| / 7 (exact rationals), and codes are zero when d is."""
+    q, d = quantize(W)
+    N, K = W.shape
+    for n in range(N):
+        for g in range(K // 128):
+            grp = W[n, 128 * g:128 * g + 128]
+            a = max(abs(Fraction(float(v))) for v in grp)
+            exp = f32_nearest(a / 7)
+            _check(f32_bits(d[n, g]) == f32_bits(exp),
+                   f"scale ({n},{g}): got {d[n, g]!r}, nearest fp32 to a/7 is {exp!r}")
+
+
+def check_codes_bruteforce(quantize, W):
+    """Each code is the level in [-8, 7] nearest to fl32(w / d) (ties away from 0)."""
+    q, d = quantize(W)
+    N, K = W.shape
+    for n in range(N):
+        for k in range(K):
+            dv = d[n, k // 128]
+            if dv == 0:
+                _check(q[n, k] == 0, f"code ({n},{k}) must be 0 when d == 0")
+                continue
+            t = f32_nearest(Fraction(float(W[n, k])) / Fraction(float(dv)))
+            exp = nearest_level(Fraction(float(t)))
+            _check(int(q[n, k]) == exp, f"code ({n},{k}): got {int(q[n, k])}, expected {exp}")
+
+
+def check_round_trip(quantize, W):
+    """|w - d q| <= d (1/2 + 2^-21) for every weight of a group with a normal scale."""
+    q, d = quantize(W)
+    N, K = W.shape
+    dd = np.repeat(d.astype(np.float64), 128, axis=1)
+    err = np.abs(W.astype(np.float64) - dd * q.astype(np.float64))
+    normal = dd >= float(np.finfo(np.float32).tiny)
+    bound = dd * (0.5 + 2.0 ** -21)
+    _check(np.all(err[normal] <= bound[normal]), "round-trip bound |w - d q| <= d/2 violated")
+
+
+def check_invariants(quantize, W):
+    """Largest magnitude gets |q| = 7; codes in [-7, 7]; sign(q) in {sign(w), 0} (normal d)."""
+    q, d = quantize(W)
+    N, K = W.shape
+    G = K // 128
+    qg = q.reshape(N, G, 128).astype(np.int64)
+    Wg = W.reshape(N, G, 128)
+    normal = d >= np.finfo(np.float32).tiny
+    amax = np.abs(Wg).argmax(axis=2)
+    top = np.take_along_axis(qg, amax[:, :, None], axis=2)[:, :, 0]
+    _check(np.all(np.abs(top[normal]) == 7), "largest weight of a group must get |q| = 7")
+    _check(np.all(np.abs(qg[normal]) <= 7), "codes must lie in [-7, 7] for normal scales")
+    s = np.sign(Wg).astype(np.int64)
+    ok = (np.sign(qg) == s) | (qg == 0)
+    _check(np.all(ok[normal]), "sign(q) must equal sign(w) or be 0")
+
+
+def check_scale_equivariance(quantize, W, e):
+    """quant(2^e W) = same codes and 2^e d, bit for bit (no under/overflow)."""
+    q0, d0 = quantize(W)
+    W1 = (W.astype(np.float64) * 2.0 ** e).astype(np.float32)
+    q1, d1 = quantize(W1)
+    _check(np.array_equal(q0, q1), "codes must not change under power-of-two scaling")
+    _check(np.array_equal((d0.astype(np.float64) * 2.0 ** e).astype(np.float32).view(np.uint32),
+                          d1.view(np.uint32)), "scales must scale exactly")
+
+
+def check_group_permutation(quantize, W, seed=0):
+    """Permuting weights inside a group permutes their codes and keeps the scale."""
+    rng = np.random.default_rng(seed)
+    q0, d0 = quantize(W)
+    N, K = W.shape
+    perm = np.concatenate([128 * g + rng.permutation(128) for g in range(K // 128)])
+    q1, d1 = quantize(np.ascontiguousarray(W[:, perm]))
+    _check(np.array_equal(q1, q0[:, perm]), "codes must follow a within-group permutation")
+    _check(np.array_equal(d1.view(np.uint32), d0.view(np.uint32)), "scales must not change")
+
+
+def check_group_count(quantize):
+    """Group 128 along the input direction: a 9216-wide row has 72 groups (study, section 1)."""
+    W = np.ones((2, 9216), dtype=np.float32)
+    q, d = quantize(W)
+    _check(d.shape == (2, 72), f"expected 72 groups per row, got {d.shape}")
+    _check(q.shape == (2, 9216), "codes must keep the weight shape")
+
+
+# ----------------------------------------------------------------------------
+# pins of the linear
+# ----------------------------------------------------------------------------
+
+def bf16_values(x_bits):
+    return [[float(np.array([int(b) << 16], dtype=np.uint32).view(np.float32)[0]) for b in row]
+            for row in np.asarray(x_bits, dtype=np.uint16)]
+
+
+def check_linear_exact(linear, x_bits, q, d):
+    """fp64 y against the exact rational sum of x * d * q (4 x 128-class toys)."""
+    y, absdot = linear(x_bits, q, d)
+    xv = bf16_values(x_bits)
+    N, K = q.shape
+    for m in range(len(xv)):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                if q[n, k]:
+                    acc += Fraction(xv[m][k]) * Fraction(float(d[n, k // 128])) * int(q[n, k])
+            tol = 2.0 ** -50 * float(absdot[m, n]) + 1e-300
+            _check(abs(Fraction(float(y[m, n])) - acc) <= Fraction(tol),
+                   f"y[{m},{n}] = {y[m, n]!r} differs from exact {float(acc)!r}")
+
+
+def check_linear_closed_forms(linear):
+    """All-ones codes with d = 1 give row sums of x; one-hot codes pick columns of x times d."""
+    rng = np.random.default_rng(7)
+    K, M = 256, 3
+    xf = rng.integers(-64, 64, (M, K)).astype(np.float32) * np.float32(0.125)
+    x_bits = (xf.view(np.uint32) >> 16).astype(np.uint16)  # exact: few significant bits
+    q = np.ones((2, K), dtype=np.int8)
+    d = np.ones((2, K // 128), dtype=np.float32)
+    y, _ = linear(x_bits, q, d)
+    rows = xf.astype(np.float64).sum(axis=1)
+    _check(np.array_equal(y[:, 0], rows) and np.array_equal(y[:, 1], rows), "row sums")
+    # one-hot codes: row n has q = 1 at column pi(n) (in group pi(n)//128), scale 2^-n
+    N = 5
+    pi = rng.permutation(K)[:N]
+    q = np.zeros((N, K), dtype=np.int8)
+    d = np.zeros((N, K // 128), dtype=np.float32)
+    for n in range(N):
+        q[n, pi[n]] = 1 if n % 2 == 0 else -1
+        d[n, pi[n] // 128] = np.float32(2.0 ** -n)
+    y, _ = linear(x_bits, q, d)
+    for n in range(N):
+        sign = 1.0 if n % 2 == 0 else -1.0
+        exp = xf[:, pi[n]].astype(np.float64) * 2.0 ** -n * sign
+        _check(np.array_equal(y[:, n], exp), f"one-hot column {n}")
+    # codes 7 / -8 alternating, d = 0.25, x = 1: y = 0.25 * 64 * (7 - 8) = -16 per 128 group
+    q = np.tile(np.array([7, -8], dtype=np.int8), (1, 64))
+    d = np.array([[0.25]], dtype=np.float32)
+    one = np.full((1, 128), 0x3F80, dtype=np.uint16)
+    y, absdot = linear(one, q, d)
+    _check(y[0, 0] == -16.0 and absdot[0, 0] == 0.25 * 64 * 15, "alternating 7/-8 closed form")
+
+
+def check_channel_scaling(quantize, linear, W, x_bits):
+    """Channel scaling identity (study, section 2: W'_ij = W_ij s_j, x'_j = x_j / s_j, W'x' = Wx).
+
+    (a) unquantized, general s: fp64 products agree to rounding;
+    (b) with s a power of two constant on each 128-group, quantized codes are
+        unchanged, scales scale exactly and y is bit-identical.
+    """
+    rng = np.random.default_rng(11)
+    N, K = W.shape
+    xv = np.array(bf16_values(x_bits))
+    s = rng.uniform(0.25, 4.0, K)
+    lhs = xv / s @ (W.astype(np.float64) * s).T
+    rhs = xv @ W.astype(np.float64).T
+    scale = np.abs(xv) @ np.abs(W.astype(np.float64)).T
+    _check(np.all(np.abs(lhs - rhs) <= 1e-14 * scale), "W' x' must equal W x")
+
+    e = rng.integers(-3, 4, K // 128)
+    s2 = np.repeat(2.0 ** e, 128)
+    q0, d0 = quantize(W)
+    q1, d1 = quantize((W.astype(np.float64) * s2).astype(np.float32))
+    _check(np.array_equal(q0, q1), "codes must not change under per-group power-of-two scaling")
+    _check(np.array_equal((d0.astype(np.float64) * 2.0 ** e).astype(np.float32).view(np.uint32),
+                          d1.view(np.uint32)), "per-group scales must scale exactly")
+    xs = (xv / s2).astype(np.float32)
+    xs_bits = (xs.view(np.uint32) >> 16).astype(np.uint16)
+    _check(np.array_equal(((xs_bits.astype(np.uint32) << 16).view(np.float32)).astype(np.float64),
+                          xv / s2), "x / s must stay exact in bf16")
+    y0, _ = linear(x_bits, q0, d0)
+    y1, _ = linear(xs_bits, q1, d1)
+    _check(np.array_equal(y0, y1), "y must be bit-identical under paired power-of-two scaling")
+
+
+# ----------------------------------------------------------------------------
+# pins of the canonical packing
+# ----------------------------------------------------------------------------
+
+def check_packing(pack, unpack):
+    """Byte k/2 holds code k (low nibble) and code k+1 (high nibble), offset by 8."""
+    rng = np.random.default_rng(3)
+    q = rng.integers(-8, 8, (3, 256)).astype(np.int8)
+    b = pack(q)
+    _check(b.shape == (3, 128) and b.dtype == np.uint8, "packed shape")
+    for n in range(3):
+        for j in range(128):
+            lo, hi = int(q[n, 2 * j]) + 8, int(q[n, 2 * j + 1]) + 8
+            _check(int(b[n, j]) == lo + 16 * hi, f"byte ({n},{j})")
+    _check(np.array_equal(unpack(b), q), "unpack(pack(q)) == q")
+    every = np.arange(256, dtype=np.uint16).astype(np.uint8).reshape(1, 256)
+    _check(np.array_equal(pack(unpack(every)), every), "pack(unpack(b)) == b for all 256 bytes")
+
+
+def nan_mask_equal(a, b):
+    return np.array_equal(np.isnan(a), np.isnan(b))
+
+
+def is_close_f32(a, b):
+    return math.isclose(float(a), float(b), rel_tol=0, abs_tol=0)

@@ -1,0 +1,239 @@
+"""Pins of the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: exact rationals,
+brute force over the 16 code levels, closed forms, the channel-scaling
+identity the study states, and hand-derived fixtures.  The second half of the
+file runs the same checks against deliberately broken copies of the oracle
+(one plausible mistake each) and requires every copy to be caught.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rtn as rtn_mod
+from tests import pins
+
+Q = oracle.rtn_quantize_ref
+L = oracle.w4_linear_ref
+
+
+def _x_bits(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 pattern will do
+
+
+# ----------------------------------------------------------------------------
+# the oracle passes every pin
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fixture", ["rtn_ties.txt", "rtn_special.txt"])
+def test_golden_fixtures(fixture):
+    pins.check_golden(Q, fixture)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_scale_exact_rational(seed):
+    pins.check_scale_exact(Q, pins.toy_weights(seed))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_codes_bruteforce(seed):
+    pins.check_codes_bruteforce(Q, pins.toy_weights(seed))
+
+
+def test_round_trip_bound():
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    pins.check_round_trip(Q, W)
+    pins.check_round_trip(Q, pins.toy_weights(9, N=16, K=768))
+
+
+def test_invariants():
+    rng = np.random.default_rng(6)
+    W = (rng.standard_t(4, size=(64, 1024)) * 0.01).astype(np.float32)
+    pins.check_invariants(Q, W)
+
+
+def test_scale_equivariance():
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    for e in (-10, -1, 1, 7):
+        pins.check_scale_equivariance(Q, W, e)
+
+
+def test_group_permutation():
+    rng = np.random.default_rng(12)
+    W = (rng.standard_normal((8, 384)) * 0.02).astype(np.float32)
+    pins.check_group_permutation(Q, W)
+
+
+def test_group_count_matches_study():
+    pins.check_group_count(Q)
+
+
+def test_linear_exact_rational():
+    W = pins.toy_weights(21, N=4, K=256)
+    W[W == 0] = 0  # keep
+    q, d = Q(W)
+    pins.check_linear_exact(L, _x_bits(3, 256, 4), q, d)
+
+
+def test_linear_closed_forms():
+    pins.check_linear_closed_forms(L)
+
+
+def test_channel_scaling_identity():
+    rng = np.random.default_rng(13)
+    W = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    pins.check_channel_scaling(Q, L, W, _x_bits(2, 512, 14))
+
+
+def test_packing():
+    pins.check_packing(oracle.pack_canonical, oracle.unpack_canonical)
+
+
+def test_nan_scale_poisons_outputs():
+    W = np.zeros((2, 256), dtype=np.float32)
+    W[0, 3] = np.nan
+    W[1, :] = 0.01
+    q, d = Q(W)
+    y, _ = L(_x_bits(1, 256, 0), q, d)
+    assert np.isnan(y[0, 0]) and np.isfinite(y[0, 1])
+
+
+def test_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        Q(np.zeros((2, 100), dtype=np.float32))
+    with pytest.raises(TypeError):
+        Q(np.zeros((2, 128), dtype=np.float64))
+
+
+# ----------------------------------------------------------------------------
+# plausible mistakes are caught (mistakes are planted in copies of the oracle)
+# ----------------------------------------------------------------------------
+
+def _mutant_quantize(*, rounding="away", divisor=7.0, recip=False, clamp=True, poison=True,
+                     zero_codes=True, abs_max=True):
+    nan = rtn_mod._nan_f32()
+
+    def quantize(W):
+        N, K = W.shape
+        Wg = W.reshape(N, K // 128, 128)
+        finite = np.isfinite(Wg).all(axis=2)
+        with np.errstate(all="ignore"):
+            a = (np.abs(Wg) if abs_max else Wg).max(axis=2).astype(np.float32)
+            d = (a / np.float32(divisor)).astype(np.float32)
+        if poison:
+            d[~finite] = nan
+        usable = finite & (d != 0) if zero_codes else np.ones_like(finite)
+        safe = np.where(usable, d, np.float32(1)).astype(np.float32)
+        with np.errstate(all="ignore"):
+            if recip:
+                t = (Wg * (np.float32(1) / safe)[:, :, None]).astype(np.float32)
+            else:
+                t = (Wg / safe[:, :, None]).astype(np.float32)
+        if rounding == "even":
+            r = np.round(t.astype(np.float64))
+        elif rounding == "f32floor":
+            r = np.sign(t) * np.floor((np.abs(t) + np.float32(0.5)).astype(np.float32))
+        elif rounding == "trunc":
+            r = np.trunc(t.astype(np.float64))
+        else:
+            r = rtn_mod._round_half_away(t)
+        if clamp:
+            r = np.clip(r, -8, 7)
+        r = np.nan_to_num(r, nan=0.0, posinf=127, neginf=-127)
+        if zero_codes:
+            r[~usable] = 0
+        return r.reshape(N, K).astype(np.int8), d
+
+    return quantize
+
+
+def _all_quantizer_pins(quantize):
+    pins.check_golden(quantize, "rtn_ties.txt")
+    pins.check_golden(quantize, "rtn_special.txt")
+    for seed in (0, 1):
+        W = pins.toy_weights(seed)
+        pins.check_scale_exact(quantize, W)
+        pins.check_codes_bruteforce(quantize, W)
+        pins.check_round_trip(quantize, W)
+    rng = np.random.default_rng(6)
+    pins.check_invariants(quantize, (rng.standard_t(4, size=(32, 512)) * 0.01).astype(np.float32))
+
+
+@pytest.mark.parametrize("mutation", [
+    dict(rounding="even"),       # numpy round: ties to even
+    dict(rounding="f32floor"),   # float32 floor(|t| + 0.5)
+    dict(rounding="trunc"),      # truncation instead of rounding
+    dict(divisor=8.0),           # wrong range mapping
+    dict(divisor=7.5),
+    dict(recip=True),            # multiply by 1/d instead of dividing by d
+    dict(clamp=False),           # no clip to [-8, 7]
+    dict(poison=False),          # non-finite groups not flagged
+    dict(zero_codes=False),      # codes of zero-scale groups not forced to 0
+    dict(abs_max=False),         # max instead of max of magnitudes
+])
+def test_quantizer_mutants_are_caught(mutation):
+    assert pins.check_golden  # the checks exist
+    _all_quantizer_pins(Q)  # the oracle itself passes
+    with pytest.raises(pins.PinFailure):
+        _all_quantizer_pins(_mutant_quantize(**mutation))
+
+
+def _mutant_linear(kind):
+    def linear(x_bits, q, d):
+        x = oracle.bf16_bits_to_f64(x_bits)
+        N, K = q.shape
+        if kind == "group_index":
+            dd = d.astype(np.float64)[:, np.arange(K) % d.shape[1]]
+        elif kind == "transposed_scale":
+            dd = np.repeat(d.astype(np.float64), 128, axis=1)[::-1]
+        else:
+            dd = np.repeat(d.astype(np.float64), 128, axis=1)
+        w = dd * q.astype(np.float64)
+        if kind == "zero_point":
+            w = dd * (q.astype(np.float64) + 8)
+        if kind == "sign":
+            w = -w
+        if kind == "f32":
+            y = (x.astype(np.float32) @ w.astype(np.float32).T).astype(np.float64)
+        elif kind == "drop_last_group":
+            y = x[:, :-128] @ w[:, :-128].T
+        else:
+            y = x @ w.T
+        return y, np.abs(x) @ np.abs(w).T
+
+    return linear
+
+
+def _all_linear_pins(linear):
+    W = pins.toy_weights(21, N=4, K=256)
+    q, d = Q(W)
+    pins.check_linear_exact(linear, _x_bits(3, 256, 4), q, d)
+    pins.check_linear_closed_forms(linear)
+    rng = np.random.default_rng(13)
+    Wc = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    pins.check_channel_scaling(Q, linear, Wc, _x_bits(2, 512, 14))
+
+
+@pytest.mark.parametrize("kind", ["group_index", "transposed_scale", "zero_point", "sign",
+                                  "f32", "drop_last_group"])
+def test_linear_mutants_are_caught(kind):
+    _all_linear_pins(L)
+    with pytest.raises(pins.PinFailure):
+        _all_linear_pins(_mutant_linear(kind))
+
+
+@pytest.mark.parametrize("kind", ["swap", "nooffset"])
+def test_packing_mutants_are_caught(kind):
+    def pack(q):
+        u = (q.astype(np.int16) + (8 if kind == "swap" else 0)).astype(np.uint8) & 0x0F
+        if kind == "swap":
+            return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
+        return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+    with pytest.raises(pins.PinFailure):
+        pins.check_packing(pack, oracle.unpack_canonical)
