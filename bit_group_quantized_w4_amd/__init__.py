@@ -1,0 +1,168 @@
+"""Python binding of libw4.so: group-wise INT4 (RTN) quantization and the W4A16
+linear layer on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of quantization and of the linear runs
+in the HIP kernels behind the C ABI declared in include/w4.h.  PyTorch provides
+device memory and the current stream; nothing here computes on the CPU and
+there is no fallback.  Importing this module fails loudly when libw4.so has not
+been built (build it with ``python -m bit_group_quantized_w4_amd._build``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4.so")
+
+W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_HIP, W4_ERR_ARG = range(6)
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+GROUP = 128
+
+# (name, restype, argtypes) of every symbol include/w4.h declares
+_VP, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "w4_status_str": (ctypes.c_char_p, [_INT]),
+    "w4_last_hip_error": (_INT, []),
+    "w4_group_size": (_INT, []),
+    "w4_packed_bytes": (_SZ, [_I64, _I64]),
+    "w4_scale_count": (_SZ, [_I64, _I64]),
+    "w4_quantize_rtn": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_linear": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP]),
+    "w4_linear_ex": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
+    "w4_pack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_unpack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+}
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.w4_status_str(status).decode()
+        if status == W4_ERR_HIP:
+            msg += f" (hipError_t {_lib.w4_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: the HIP library must be built first "
+            "(python -m bit_group_quantized_w4_amd._build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes handle of libw4.so."""
+    return _lib
+
+
+def _check(status, where):
+    if status != W4_OK:
+        raise W4Error(status, where)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def packed_bytes(N, K):
+    return int(_lib.w4_packed_bytes(N, K))
+
+
+def scale_count(N, K):
+    return int(_lib.w4_scale_count(N, K))
+
+
+def _empty_packed(N, K, device):
+    nb, ns = packed_bytes(N, K), scale_count(N, K)
+    if nb == 0:
+        _check(W4_ERR_SHAPE, "packed buffers")
+    return (torch.empty(nb, dtype=torch.uint8, device=device),
+            torch.empty(ns, dtype=torch.float32, device=device))
+
+
+def quantize_rtn(W, out=None):
+    """fp32 weight [N, K] on the GPU -> (codes uint8 [packed_bytes], scales fp32 [scale_count]),
+    both in the library's native layout."""
+    N, K = W.shape
+    q, d = out if out is not None else _empty_packed(N, K, W.device)
+    _check(_lib.w4_quantize_rtn(_dev(W, torch.float32, "W"), N, K, _dev(q, torch.uint8, "q"),
+                                _dev(d, torch.float32, "d"), _stream(W)), "w4_quantize_rtn")
+    return q, d
+
+
+def linear(x, q, d, N, path="auto", out=None):
+    """y [M, N] bf16 = x [M, K] bf16 times the dequantized weight (native q, d)."""
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if y.shape != (M, N):
+        raise ValueError("out must be [M, N]")
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    _check(_lib.w4_linear_ex(_dev(x, torch.bfloat16, "x"), M, K, _dev(q, torch.uint8, "q"),
+                             _dev(d, torch.float32, "d"), N, _dev(y, torch.bfloat16, "y"),
+                             PATHS[path], _stream(x)), "w4_linear")
+    return y
+
+
+def pack(q_canon, d_canon, out=None):
+    """Canonical codes int8 [N, K] and scales fp32 [N, K/128] -> native (q, d)."""
+    N, K = q_canon.shape
+    q, d = out if out is not None else _empty_packed(N, K, q_canon.device)
+    _check(_lib.w4_pack(_dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, torch.float32, "d_canon"),
+                        N, K, _dev(q, torch.uint8, "q"), _dev(d, torch.float32, "d"),
+                        _stream(q_canon)), "w4_pack")
+    return q, d
+
+
+def unpack(q, d, N, K):
+    """Native (q, d) -> canonical codes int8 [N, K] and scales fp32 [N, K/128]."""
+    qc = torch.empty((N, K), dtype=torch.int8, device=q.device)
+    dc = torch.empty((N, K // GROUP), dtype=torch.float32, device=q.device)
+    _check(_lib.w4_unpack(_dev(q, torch.uint8, "q"), _dev(d, torch.float32, "d"), N, K,
+                          _dev(qc, torch.int8, "q_canon"), _dev(dc, torch.float32, "d_canon"),
+                          _stream(q)), "w4_unpack")
+    return qc, dc
+
+
+class W4Linear:
+    """A quantized weight held in native layout, callable on bf16 activations."""
+
+    def __init__(self, q, d, N, K):
+        self.q, self.d, self.N, self.K = q, d, N, K
+
+    @classmethod
+    def from_float(cls, W):
+        q, d = quantize_rtn(W)
+        return cls(q, d, W.shape[0], W.shape[1])
+
+    def __call__(self, x, path="auto", out=None):
+        return linear(x, self.q, self.d, self.N, path=path, out=out)
+
+
+__all__ = [
+    "GROUP", "LIB_PATH", "PATHS", "SIGNATURES", "W4Error", "W4Linear", "library", "linear",
+    "pack", "packed_bytes", "quantize_rtn", "scale_count", "unpack",
+]

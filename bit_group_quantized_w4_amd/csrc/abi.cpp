@@ -1,0 +1,141 @@
+// C ABI of libw4.so (declared in include/w4.h): argument checks on the host,
+// then one asynchronous launch on the caller's stream.  No allocation, no
+// host synchronisation, no state beyond the thread-local last HIP error.
+#include "w4.h"
+#include "w4_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMaxK = int64_t(1) << 24;       // keeps every in-kernel index in range
+constexpr int64_t kMaxN = (int64_t(1) << 31) - 16;
+constexpr int64_t kMaxM = 65535 * 4;              // grid rows of 4-row slabs
+
+bool k_ok(int64_t K) { return K > 0 && K % kGroup == 0 && K <= kMaxK; }
+bool n_ok(int64_t N) { return N >= 0 && N <= kMaxN; }
+int64_t padded_rows(int64_t N) { return (N + 15) / 16 * 16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Kernel used by w4_linear for a shape.  The MFMA kernel needs fewer VALU
+// instructions per weight than the dot2 kernel at every M (one 16x16x32 MFMA
+// replaces 16 dot2 per row of x), so it is the default everywhere.
+int auto_path(int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N; (void)K;
+  return W4_PATH_MFMA;
+}
+
+w4_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return W4_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return W4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_str(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK: success";
+    case W4_ERR_NULL: return "W4_ERR_NULL: a required pointer is NULL";
+    case W4_ERR_SHAPE: return "W4_ERR_SHAPE: invalid shape (K must be a positive multiple of 128; M, N >= 0; size limits)";
+    case W4_ERR_ALIGN: return "W4_ERR_ALIGN: a pointer is not aligned as required";
+    case W4_ERR_HIP: return "W4_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case W4_ERR_ARG: return "W4_ERR_ARG: invalid argument";
+    default: return "unknown w4 status";
+  }
+}
+
+int w4_last_hip_error(void) { return g_last_hip_error; }
+
+int w4_group_size(void) { return (int)kGroup; }
+
+size_t w4_packed_bytes(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return 0;
+  return (size_t)padded_rows(N) * (size_t)K / 2;
+}
+
+size_t w4_scale_count(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return 0;
+  return (size_t)padded_rows(N) * (size_t)(K / kGroup);
+}
+
+w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed, float* d_packed,
+                          hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!W || !q_packed || !d_packed) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16)) return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K), wb = 4 * (size_t)N * K;
+  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, W, wb) || overlaps(d_packed, db, W, wb))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_quantize_rtn(W, N, K, q_packed, d_packed, stream));
+}
+
+w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                       const float* d_packed, int64_t N, uint16_t* y, int path, hipStream_t stream) {
+  if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
+  if (M < 0 || M > kMaxM || !n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!x || !q_packed || !d_packed || !y) return W4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16) || !aligned(y, 2))
+    return W4_ERR_ALIGN;
+  const size_t yb = 2 * (size_t)M * N;
+  if (overlaps(y, yb, x, 2 * (size_t)M * K) || overlaps(y, yb, q_packed, w4_packed_bytes(N, K)) ||
+      overlaps(y, yb, d_packed, 4 * w4_scale_count(N, K)))
+    return W4_ERR_ARG;
+  if (path == W4_PATH_AUTO) path = auto_path(M, N, K);
+  const hipError_t e = path == W4_PATH_GEMV
+                           ? w4::launch_linear_gemv(x, M, K, q_packed, d_packed, N, y, stream)
+                           : w4::launch_linear_mfma(x, M, K, q_packed, d_packed, N, y, stream);
+  return hip_status(e);
+}
+
+w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                    const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream) {
+  return w4_linear_ex(x, M, K, q_packed, d_packed, N, y, W4_PATH_AUTO, stream);
+}
+
+w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
+                  uint8_t* q_packed, float* d_packed, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
+  if (!aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
+    return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K);
+  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, q_canon, (size_t)N * K) ||
+      overlaps(q_packed, qb, d_canon, 4 * (size_t)N * (K / kGroup)) ||
+      overlaps(d_packed, db, q_canon, (size_t)N * K) ||
+      overlaps(d_packed, db, d_canon, 4 * (size_t)N * (K / kGroup)))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_pack(q_canon, d_canon, N, K, q_packed, d_packed, stream));
+}
+
+w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
+                    int8_t* q_canon, float* d_canon, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
+  if (!aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
+    return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K);
+  const size_t qcb = (size_t)N * K, dcb = 4 * (size_t)N * (K / kGroup);
+  if (overlaps(q_canon, qcb, d_canon, dcb) || overlaps(q_canon, qcb, q_packed, qb) ||
+      overlaps(q_canon, qcb, d_packed, db) || overlaps(d_canon, dcb, q_packed, qb) ||
+      overlaps(d_canon, dcb, d_packed, db))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_unpack(q_packed, d_packed, N, K, q_canon, d_canon, stream));
+}
+
+}  // extern "C"

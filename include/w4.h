@@ -1,0 +1,158 @@
+/*
+ * w4.h -- group-wise symmetric INT4 weight quantization and the W4A16 linear
+ * layer for AMD Instinct MI355X (gfx950).  C ABI, C99-compatible.
+ *
+ * The method (Qwen3.5-4B quantization study, parksieon.github.io/
+ * qwen35-4b-quantization-study):
+ *   - section 1, group-quantization equation and its symbol table:
+ *       q = clip(round(w/d) + z, qmin, qmax),   w_hat = d (q - z),
+ *     with one restore scale d per group of 128 consecutive inputs of a row
+ *     (72 groups per row of the 2560x9216 FFN example), 16 codes per 4-bit
+ *     slot, and zero point z = 0 for the symmetric scheme;
+ *   - section 2 settings table: RTN, group 128, min/max symmetric range, no
+ *     clipping search, 4-bit weights with BF16 inputs;
+ *   - section 1, y = W x with W stored N x K (N outputs, K inputs).
+ * The linear layer is what memory-bound decode runs once per generated token
+ * (M = 1), and what verifying K drafted tokens runs once with M = K + 1 rows
+ * (27B quantization-and-drafter ladder, thakicloud.com, stage 1 "why 4-bit is
+ * faster" and stage 2 "drafter").
+ *
+ * Conventions of this library:
+ *   d        = fl32(max|w| / 7) per group (IEEE divide, no flush to zero);
+ *   code     q = clamp(round_half_away_from_zero(fl32(w / d)), -8, 7);
+ *   degenerate groups: a NaN or infinity in the group gives d = NaN (bits
+ *   0x7FC00000) and codes 0; d == 0 gives codes 0;
+ *   y[m][n]  = bf16_rne( sum_g d[n][g] * sum_{k in g} q[n][k] x[m][k] ),
+ *            accumulated in fp32 per 128-group.
+ *
+ * All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
+ * caller owns every buffer; the library allocates nothing and keeps no state
+ * besides a per-thread copy of the last HIP error.  Every call is enqueued
+ * asynchronously on `stream` (0 = the null stream) and performs no host
+ * synchronisation.  Argument errors are detected on the host before anything
+ * is enqueued and leave outputs untouched.  A launch failure returns
+ * W4_ERR_HIP (w4_last_hip_error() gives the hipError_t); faults during
+ * execution surface at the caller's next synchronisation, as in HIP.
+ * Results are bitwise reproducible run to run (no floating-point atomics).
+ *
+ * NATIVE LAYOUT (what w4_quantize_rtn writes and w4_linear reads)
+ *   Let Np = N rounded up to a multiple of 16, G = K / 128.  The matrix is
+ *   cut into tiles of 16 rows x 128 inputs (one group); tile (r, g) covers
+ *   rows 16r .. 16r+15 and group g.
+ *   Codes: tile (r, g) is 1024 contiguous bytes at byte offset (r*G + g)*1024.
+ *     Its 16-byte lane L (0..63) holds row n = 16r + (L % 16), and its four
+ *     little-endian 32-bit words w_i (i = 0..3) hold inputs
+ *     k = 128g + 32i + 8(L / 16) + j, j = 0..7, as offset-binary nibbles
+ *     u_j = q_j + 8:  w_i = rotl32(v, 3) where
+ *     v = sum_{p=0..3} u_{2p} << 4p  +  sum_{p=0..3} u_{2p+1} << (16 + 4p).
+ *   Scales: tile (r, g) owns 16 consecutive floats at index (r*G + g)*16,
+ *     entry (n % 16) for row n.
+ *   Rows N .. Np-1 are padding: codes 0 (u = 8) and d = 0.
+ *   Total sizes: w4_packed_bytes(N, K) = Np*K/2 bytes of codes and
+ *   w4_scale_count(N, K) = Np*K/128 floats of scales.
+ *
+ * CANONICAL LAYOUT (for exchange and bit-exact comparison)
+ *   codes int8 [N][K] row-major, each in [-8, 7];
+ *   scales float32 [N][K/128] row-major.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_NULL = 1,   /* a required pointer is NULL                           */
+  W4_ERR_SHAPE = 2,  /* N, M < 0; K not a positive multiple of 128; too large */
+  W4_ERR_ALIGN = 3,  /* a pointer is not aligned as documented                */
+  W4_ERR_HIP = 4,    /* a HIP runtime call or launch failed                   */
+  W4_ERR_ARG = 5     /* another invalid argument (unknown path, aliasing ...) */
+} w4_status;
+
+/* Which linear kernel w4_linear_ex runs. */
+typedef enum {
+  W4_PATH_AUTO = 0,  /* the library's choice by M, N, K (what w4_linear does)  */
+  W4_PATH_GEMV = 1,  /* VALU dot-product streaming kernel, any M (slabs of 4)   */
+  W4_PATH_MFMA = 2   /* bf16 MFMA streaming kernel, any M (slabs of 16)        */
+} w4_path;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* w4_status_str(int status);
+
+/* The hipError_t of the last W4_ERR_HIP returned on this thread (0 if none). */
+int w4_last_hip_error(void);
+
+/* Group size along K: 128 (study, section 1). */
+int w4_group_size(void);
+
+/* Bytes of native codes for an N x K matrix: roundup(N, 16) * K / 2.
+ * Returns 0 when N < 0, K <= 0 or K % 128 != 0. */
+size_t w4_packed_bytes(int64_t N, int64_t K);
+
+/* Number of native fp32 scales: roundup(N, 16) * K / 128 (0 on bad shape). */
+size_t w4_scale_count(int64_t N, int64_t K);
+
+/*
+ * w4_quantize_rtn -- RTN INT4 group quantization (study, section 1 equation;
+ * section 2 settings: group 128, symmetric min/max, no calibration input).
+ *   W        [in]  fp32 row-major [N][K] weights; 16-byte aligned.
+ *   N        [in]  rows (outputs), N >= 0 (N == 0: nothing is done).
+ *   K        [in]  columns (inputs), positive multiple of 128.
+ *   q_packed [out] w4_packed_bytes(N, K) bytes, native layout; 16-byte aligned.
+ *   d_packed [out] w4_scale_count(N, K) floats, native layout; 16-byte aligned.
+ * Codes and scales are bit-exact with respect to the conventions above.
+ */
+w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
+                          float* d_packed, hipStream_t stream);
+
+/*
+ * w4_linear -- y = W_hat x (study, section 1: y = W x; section 2: 4-bit
+ * weights, BF16 inputs), the memory-bound decode / draft-verify layer.
+ *   x        [in]  bf16 bit patterns, row-major [M][K]; 16-byte aligned.
+ *   M        [in]  activation rows, 0 <= M <= 262140 (M == 0: nothing is
+ *                  done).  Tuned for M <= 16; larger M runs in row slabs.
+ *   K        [in]  inputs, positive multiple of 128.
+ *   q_packed [in]  native codes of the N x K matrix; 16-byte aligned.
+ *   d_packed [in]  native scales; 16-byte aligned.
+ *   N        [in]  outputs, N >= 0 (N == 0: nothing is done).
+ *   y        [out] bf16 bit patterns, row-major [M][N]; 2-byte aligned; must
+ *                  not overlap any input (W4_ERR_ARG).  Rounded to nearest
+ *                  even from fp32.
+ */
+w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                    const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream);
+
+/* w4_linear with an explicit kernel choice (same contract; W4_ERR_ARG for an
+ * unknown path). */
+w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                       const float* d_packed, int64_t N, uint16_t* y, int path,
+                       hipStream_t stream);
+
+/*
+ * w4_pack -- canonical codes and scales -> native layout (for codes computed
+ * elsewhere).  q_canon int8 [N][K] (values must lie in [-8, 7]; others are
+ * reduced modulo 16), d_canon fp32 [N][K/128].  Outputs as w4_quantize_rtn.
+ * q_canon and d_canon need 16- and 4-byte alignment.
+ */
+w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
+                  uint8_t* q_packed, float* d_packed, hipStream_t stream);
+
+/*
+ * w4_unpack -- native layout -> canonical codes int8 [N][K] and scales fp32
+ * [N][K/128] (padding rows are dropped).  Bit-exact inverse of w4_pack.
+ */
+w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
+                    int8_t* q_canon, float* d_canon, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,129 @@
+"""C-ABI contract tests that need no GPU.
+
+They load libw4.so, check that every function include/w4.h declares is
+exported, and exercise argument validation: each call here is rejected on the
+host before any HIP call is made, so nothing is launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "w4.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_ARG = range(6)
+FAKE = 0x10000000  # a 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("w4_quantize_rtn", "w4_linear", "w4_linear_ex", "w4_pack", "w4_unpack"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(w4):
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in w4.SIGNATURES, f"binding lacks {name}"
+    assert set(w4.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(w4):
+    lib = w4.library()
+    for s in range(6):
+        assert lib.w4_status_str(s).decode().startswith("W4_")
+    assert b"unknown" in lib.w4_status_str(99)
+    assert lib.w4_last_hip_error() == 0
+
+
+def test_size_helpers(w4):
+    lib = w4.library()
+    assert lib.w4_group_size() == 128
+    assert lib.w4_packed_bytes(2560, 9216) == 2560 * 9216 // 2
+    assert lib.w4_scale_count(2560, 9216) == 2560 * 72
+    assert lib.w4_packed_bytes(37, 384) == 48 * 384 // 2  # rows padded to 16
+    assert lib.w4_scale_count(37, 384) == 48 * 3
+    assert lib.w4_packed_bytes(0, 128) == 0
+    for N, K in ((16, 100), (16, 0), (16, -128), (-1, 128)):
+        assert lib.w4_packed_bytes(N, K) == 0 and lib.w4_scale_count(N, K) == 0
+
+
+def _linear(lib, x=FAKE, M=1, K=128, q=FAKE + 0x100000, d=FAKE + 0x200000, N=16,
+            y=FAKE + 0x300000, path=0):
+    return lib.w4_linear_ex(x, M, K, q, d, N, y, path, None)
+
+
+def test_linear_validation(w4):
+    lib = w4.library()
+    assert _linear(lib, K=100) == ERR_SHAPE
+    assert _linear(lib, K=0) == ERR_SHAPE
+    assert _linear(lib, M=-1) == ERR_SHAPE
+    assert _linear(lib, N=-3) == ERR_SHAPE
+    assert _linear(lib, M=262141) == ERR_SHAPE
+    assert _linear(lib, x=None) == ERR_NULL
+    assert _linear(lib, q=None) == ERR_NULL
+    assert _linear(lib, d=None) == ERR_NULL
+    assert _linear(lib, y=None) == ERR_NULL
+    assert _linear(lib, x=FAKE + 8) == ERR_ALIGN
+    assert _linear(lib, q=FAKE + 0x100004) == ERR_ALIGN
+    assert _linear(lib, d=FAKE + 0x200004) == ERR_ALIGN
+    assert _linear(lib, y=FAKE + 0x300001) == ERR_ALIGN
+    assert _linear(lib, y=FAKE) == ERR_ARG  # output aliases x
+    assert _linear(lib, y=FAKE + 0x100000 + 64) == ERR_ARG  # output inside the codes
+    assert _linear(lib, path=7) == ERR_ARG
+    # empty problems are valid no-ops that launch nothing, even with NULL buffers
+    assert _linear(lib, M=0, x=None, y=None) == OK
+    assert _linear(lib, N=0, q=None, d=None, y=None) == OK
+    assert lib.w4_linear(None, 0, 128, None, None, 16, None, None) == OK
+
+
+def test_quantize_pack_unpack_validation(w4):
+    lib = w4.library()
+    q, d, src = FAKE, FAKE + 0x100000, FAKE + 0x200000
+    assert lib.w4_quantize_rtn(src, 16, 100, q, d, None) == ERR_SHAPE
+    assert lib.w4_quantize_rtn(None, 16, 128, q, d, None) == ERR_NULL
+    assert lib.w4_quantize_rtn(src + 4, 16, 128, q, d, None) == ERR_ALIGN
+    assert lib.w4_quantize_rtn(src, 16, 128, q, q + 512, None) == ERR_ARG  # codes/scales overlap
+    assert lib.w4_quantize_rtn(src, 0, 128, None, None, None) == OK
+    assert lib.w4_pack(src, d + 0x40000, 16, 256, None, d, None) == ERR_NULL
+    assert lib.w4_pack(src + 8, d + 0x40000, 16, 256, q, d, None) == ERR_ALIGN
+    assert lib.w4_pack(src, d + 0x40000, 16, 127, q, d, None) == ERR_SHAPE
+    assert lib.w4_unpack(q, d, 16, 256, None, src, None) == ERR_NULL
+    assert lib.w4_unpack(q, d, 16, 256, src, src + 64, None) == ERR_ARG
+    assert lib.w4_unpack(q, d, -2, 256, src, src + 0x40000, None) == ERR_SHAPE
+
+
+def test_python_binding_rejects_cpu_tensors(w4):
+    import torch
+
+    with pytest.raises(ValueError):
+        w4.quantize_rtn(torch.zeros(16, 128))
+    with pytest.raises(ValueError):
+        w4.linear(torch.zeros(1, 128, dtype=torch.bfloat16), torch.zeros(1024, dtype=torch.uint8),
+                  torch.zeros(16), 16)
+
+
+# ----------------------------------------------------------------------------
+# byte accounting used by the roofline (hand-computed figures)
+# ----------------------------------------------------------------------------
+
+def test_algorithmic_bytes():
+    # N*K/2 codes + 4*N*K/128 scales + 2*M*K x + 2*M*N y
+    assert workloads.algorithmic_bytes(1, 2560, 9216) == 12_557_312
+    assert workloads.algorithmic_bytes(8, 2560, 9216) == 12_722_176
+    assert workloads.algorithmic_bytes(1, 9216, 2560) == 11_796_480 + 737_280 + 5_120 + 18_432
+    assert round(workloads.stack_bytes("stack_4b", 1) / 1e9, 3) == 1.859
+    assert round(workloads.stack_bytes("stack_27b", 1) / 1e9, 3) == 11.600
+    assert round(workloads.stack_bytes("stack_70b", 1) / 1e9, 3) == 36.391
+    assert workloads.stack_weights("stack_70b") == 80 * (2 * 8192 * 8192 + 2 * 1024 * 8192 + 3 * 28672 * 8192)

@@ -1,0 +1,267 @@
+"""Parity of the HIP path against the CPU oracle, on an MI355X.
+
+Every call goes through the C ABI (via the ctypes binding).  Codes and scales
+must match the oracle bit for bit (compared in canonical form after
+w4_unpack); outputs must satisfy, element by element,
+
+    |y_gpu - y_ref| <= 2e-3 * sum_k |w_hat[n,k] x[m,k]| + 1e-6,
+
+with y_ref and the sum computed in fp64 by the oracle, and NaN exactly where
+the oracle has NaN.  Inputs come from workloads/ (seeded); the oracle always
+sees a host copy of the very tensor the kernel consumed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pins
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+ABS_TOL = 1e-6
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _bits(x_bf16):
+    return x_bf16.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_y(y_gpu, y_ref, absdot, what):
+    y = oracle.bf16_bits_to_f64(_bits(y_gpu))
+    nan_ref = np.isnan(y_ref)
+    assert np.array_equal(np.isnan(y), nan_ref), f"{what}: NaN positions differ"
+    ok = ~nan_ref
+    err = np.abs(y[ok] - y_ref[ok])
+    tol = REL_TOL * absdot[ok] + ABS_TOL
+    worst = float(np.max(err / tol)) if err.size else 0.0
+    assert np.all(err <= tol), f"{what}: {int(np.sum(err > tol))} outputs out of tolerance (worst {worst:.3f})"
+    return worst
+
+
+def quantize_and_compare(w4, W_dev, what, rows=None):
+    """Quantize on the GPU, unpack, compare with the oracle (all rows or a row sample)."""
+    N, K = W_dev.shape
+    q, d = w4.quantize_rtn(W_dev)
+    qc, dc = w4.unpack(q, d, N, K)
+    torch.cuda.synchronize()
+    if rows is None:
+        W_h = W_dev.cpu().numpy()
+        qg, dg = qc.cpu().numpy(), dc.cpu().numpy()
+    else:
+        idx = torch.as_tensor(rows, device=W_dev.device)
+        W_h = W_dev.index_select(0, idx).cpu().numpy()
+        qg, dg = qc.index_select(0, idx).cpu().numpy(), dc.index_select(0, idx).cpu().numpy()
+    q_ref, d_ref = oracle.rtn_quantize_ref(W_h)
+    assert np.array_equal(dg.view(np.uint32), d_ref.view(np.uint32)), f"{what}: scales differ"
+    bad = np.argwhere(qg != q_ref)
+    assert bad.size == 0, f"{what}: {len(bad)} codes differ, first {bad[:4].tolist()}"
+    return q, d, q_ref, d_ref
+
+
+# ----------------------------------------------------------------------------
+# quantization: bit-exact codes and scales
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fixture", ["rtn_ties.txt", "rtn_special.txt"])
+def test_quantize_golden(w4, gpu, fixture):
+    groups = pins.load_groups(fixture)
+    _say(f"quantize golden {fixture} ({len(groups)} groups)")
+    W = np.stack([g[2] for g in groups]).astype(np.float32)
+    W_dev = torch.from_numpy(W).to(gpu)
+    q, d = w4.quantize_rtn(W_dev)
+    qc, dc = w4.unpack(q, d, W.shape[0], 128)
+    qc, dc = qc.cpu().numpy(), dc.cpu().numpy()
+    for i, (name, d_bits, _, q_exp) in enumerate(groups):
+        assert int(dc[i, 0:1].view(np.uint32)[0]) == d_bits, f"{name}: scale"
+        assert np.array_equal(qc[i].astype(np.int64), q_exp), f"{name}: codes"
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_quantize_toys(w4, gpu, seed):
+    _say(f"quantize toys seed={seed}")
+    W = pins.toy_weights(seed, N=37, K=768)
+    quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"toys{seed}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 128), (37, 384), (100, 1152), (64, 9216), (257, 2560)])
+def test_quantize_shapes(w4, gpu, N, K):
+    _say(f"quantize N={N} K={K}")
+    W = workloads.random_weight(N, K, std=0.02, seed=N + K)
+    quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"{N}x{K}")
+
+
+@pytest.mark.parametrize("workload", ["ffn_2560x9216", "ffn_pair_outliers"])
+def test_quantize_single_matrix_workloads(w4, gpu, workload):
+    for m in workloads.WORKLOADS[workload].matrices:
+        _say(f"quantize {workload}/{m.name} {m.N}x{m.K}")
+        W = workloads.weight(workload, 0, m.name, "cpu")
+        quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"{workload}/{m.name}")
+
+
+@pytest.mark.parametrize("workload", ["stack_4b", "stack_27b", "stack_70b"])
+def test_quantize_stack_matrices_sampled(w4, gpu, workload):
+    """Full-size matrices drawn on the GPU; 96 sampled rows checked bit for bit."""
+    wl = workloads.WORKLOADS[workload]
+    for layer in (0, wl.layers - 1):
+        for m in wl.matrices:
+            _say(f"quantize {workload} layer {layer} {m.name} {m.N}x{m.K}")
+            W = workloads.weight(workload, layer, m.name, gpu)
+            rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(layer).choice(m.N, 94)]))
+            quantize_and_compare(w4, W, f"{workload}/{layer}/{m.name}", rows=rows)
+            del W
+            torch.cuda.empty_cache()
+
+
+def test_pack_unpack_roundtrip(w4, gpu):
+    _say("pack/unpack round trip N=45 K=640")
+    rng = np.random.default_rng(0)
+    qc = torch.from_numpy(rng.integers(-8, 8, (45, 640)).astype(np.int8)).to(gpu)
+    dc = torch.from_numpy(rng.standard_normal((45, 5)).astype(np.float32)).to(gpu)
+    q, d = w4.pack(qc, dc)
+    qc2, dc2 = w4.unpack(q, d, 45, 640)
+    assert torch.equal(qc2, qc) and torch.equal(dc2.view(torch.int32), dc.view(torch.int32))
+    # padding rows of the native layout are code 0 / scale 0
+    dn = d.view(-1, 5, 16)[2]  # row block 2 holds rows 32..47
+    assert torch.all(dn[:, 13:] == 0)
+    # quantize output re-packed from its canonical form is identical
+    W = torch.from_numpy(workloads.random_weight(45, 640, seed=3)).to(gpu)
+    q1, d1 = w4.quantize_rtn(W)
+    q2, d2 = w4.pack(*w4.unpack(q1, d1, 45, 640))
+    assert torch.equal(q1, q2) and torch.equal(d1.view(torch.int32), d2.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------
+# linear: tolerance against the fp64 oracle
+# ----------------------------------------------------------------------------
+
+def linear_case(w4, gpu, M, N, K, path, seed=0, std=0.02, x_scale=1.0):
+    W = torch.from_numpy(workloads.random_weight(N, K, std=std, seed=seed)).to(gpu)
+    x = workloads.random_activations(M, K, seed=seed, scale=x_scale, device=gpu)
+    q, d = w4.quantize_rtn(W)
+    y = w4.linear(x, q, d, N, path=path)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W.cpu().numpy())
+    y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+    return check_y(y, y_ref, absdot, f"M={M} N={N} K={K} {path}")
+
+
+SHAPES = [(1, 16, 128), (1, 37, 384), (2, 50, 1152), (3, 64, 256), (4, 100, 640),
+          (5, 48, 2560), (7, 33, 1024), (8, 200, 1408), (13, 17, 512), (16, 160, 896),
+          (17, 40, 384), (33, 24, 256), (1, 1040, 4096)]
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv", "auto"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_linear_shapes(w4, gpu, M, N, K, path):
+    _say(f"linear M={M} N={N} K={K} path={path}")
+    linear_case(w4, gpu, M, N, K, path, seed=M * 7 + N)
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_linear_single_matrix_workloads(w4, gpu, path):
+    for workload in ("ffn_2560x9216", "ffn_pair_outliers"):
+        wl = workloads.WORKLOADS[workload]
+        for m in wl.matrices:
+            W = torch.from_numpy(workloads.weight(workload, 0, m.name, "cpu")).to(gpu)
+            q, d = w4.quantize_rtn(W)
+            q_ref, d_ref = oracle.rtn_quantize_ref(W.cpu().numpy())
+            for M in wl.ms:
+                _say(f"linear {workload}/{m.name} {m.N}x{m.K} M={M} path={path}")
+                x = workloads.activations(workload, 0, m.name, M, gpu)
+                y = w4.linear(x, q, d, m.N, path=path)
+                y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+                check_y(y, y_ref, absdot, f"{workload}/{m.name} M={M}")
+
+
+@pytest.mark.parametrize("workload", ["stack_4b", "stack_27b", "stack_70b"])
+def test_linear_stack_matrices_sampled(w4, gpu, workload):
+    """Full-size layers (first, middle, last) at every listed M; 128 sampled output rows."""
+    wl = workloads.WORKLOADS[workload]
+    for layer in (0, wl.layers // 2, wl.layers - 1):
+        for m in wl.matrices:
+            W = workloads.weight(workload, layer, m.name, gpu)
+            q, d = w4.quantize_rtn(W)
+            rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(layer + 1).choice(m.N, 126)]))
+            idx = torch.as_tensor(rows, device=gpu)
+            q_ref, d_ref = oracle.rtn_quantize_ref(W.index_select(0, idx).cpu().numpy())
+            del W
+            for M in wl.ms:
+                _say(f"linear {workload} layer {layer} {m.name} {m.N}x{m.K} M={M}")
+                x = workloads.activations(workload, layer, m.name, M, gpu)
+                y = w4.linear(x, q, d, m.N)
+                y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+                check_y(y.index_select(1, idx), y_ref, absdot, f"{workload}/{layer}/{m.name} M={M}")
+            del q, d
+            torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# properties that hold at any size
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_linear_deterministic(w4, gpu, path):
+    _say(f"determinism path={path}")
+    W = torch.from_numpy(workloads.random_weight(2048, 4096, seed=5)).to(gpu)
+    x = workloads.random_activations(8, 4096, seed=5, device=gpu)
+    q, d = w4.quantize_rtn(W)
+    y1 = w4.linear(x, q, d, 2048, path=path)
+    y2 = w4.linear(x, q, d, 2048, path=path)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_linear_channel_scaling_bit_identical(w4, gpu, path):
+    """Per-group power-of-two channel scaling (study, section 2 identity W'x' = Wx):
+    codes unchanged, scales scaled exactly, outputs bit-identical."""
+    _say(f"channel scaling path={path}")
+    N, K, M = 96, 1024, 5
+    W = workloads.random_weight(N, K, seed=17)
+    x = workloads.random_activations(M, K, seed=17)
+    e = np.random.default_rng(17).integers(-3, 4, K // 128)
+    s = np.repeat(2.0 ** e, 128)
+    W2 = (W.astype(np.float64) * s).astype(np.float32)
+    x2 = (x.float().numpy().astype(np.float64) / s).astype(np.float32)
+    x2 = torch.from_numpy(x2).to(torch.bfloat16)
+    assert np.array_equal(x2.float().numpy().astype(np.float64), x.float().numpy() / s)
+    q1, d1 = w4.quantize_rtn(torch.from_numpy(W).to(gpu))
+    q2, d2 = w4.quantize_rtn(torch.from_numpy(W2).to(gpu))
+    assert torch.equal(q1, q2)
+    y1 = w4.linear(x.to(gpu), q1, d1, N, path=path)
+    y2 = w4.linear(x2.to(gpu), q2, d2, N, path=path)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_linear_degenerate_groups(w4, gpu, path):
+    """NaN scales poison exactly their rows; zero groups contribute nothing."""
+    _say(f"degenerate groups path={path}")
+    N, K, M = 48, 512, 3
+    W = workloads.random_weight(N, K, seed=23)
+    W[5, 130] = np.nan
+    W[9, 0:128] = 0.0
+    W[17, 300] = np.inf
+    x = workloads.random_activations(M, K, seed=23)
+    W_dev = torch.from_numpy(W).to(gpu)
+    q, d = w4.quantize_rtn(W_dev)
+    y = w4.linear(x.to(gpu), q, d, N, path=path)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W)
+    y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+    check_y(y, y_ref, absdot, "degenerate")
+    assert np.isnan(y_ref[:, 5]).all() and np.isnan(y_ref[:, 17]).all()
+
+
+def test_linear_empty_is_noop(w4, gpu):
+    _say("empty problems")
+    q = torch.zeros(w4.packed_bytes(16, 128), dtype=torch.uint8, device=gpu)
+    d = torch.zeros(w4.scale_count(16, 128), dtype=torch.float32, device=gpu)
+    y = w4.linear(torch.zeros((0, 128), dtype=torch.bfloat16, device=gpu), q, d, 16)
+    assert y.shape == (0, 16)
+    y = w4.linear(torch.zeros((2, 128), dtype=torch.bfloat16, device=gpu), q, d, 0)
+    assert y.shape == (2, 0)
