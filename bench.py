@@ -1,0 +1,320 @@
+"""Benchmark of the W4A16 decode linear on one MI355X.
+
+Headline (the JSON line's `value`): achieved algorithmic HBM bandwidth of
+w4_linear at M = 1 on the 2560x9216 / 9216x2560 FFN pair with 0.5% outliers
+(workload ffn_pair_outliers).  One step is one decode-style pass: every one of
+the 2 x C weight copies is multiplied once at M = 1 (C copies, > 2x the 256 MB
+Infinity Cache, so every step streams from HBM).  Steps are replayed from one
+HIP graph; the timed region is bracketed by synchronisations and measured with
+events on the replay stream.  Also reported in the same line: the same pass at
+M = 8 (verifying 7 drafted tokens + 1), quantization throughput, 27B- and
+70B-class layer stacks as equivalent decode tokens/s, the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 27b,70b|none] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "w4_linear achieved HBM GB/s (% of peak) at M=1 and M=8; equiv decode tok/s"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E nameplate
+HEADLINE = "ffn_pair_outliers"
+KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_mfma_ffn_pair_outliers_m1_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# GPU timing helpers
+# ----------------------------------------------------------------------------
+
+def capture(torch, fn):
+    """Capture fn() (a sequence of library launches) into a HIP graph."""
+    fn()  # eager run first: nothing lazy happens inside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+# ----------------------------------------------------------------------------
+# headline: single-matrix pair, weight copies rotated through HBM
+# ----------------------------------------------------------------------------
+
+def bench_pair(torch, w4, workloads, steps, warmup, copies):
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[HEADLINE]
+    mats = []
+    for m in wl.matrices:
+        W = torch.from_numpy(workloads.weight(HEADLINE, 0, m.name, "cpu")).to(dev)
+        q0, d0 = w4.quantize_rtn(W)
+        qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+        ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+        mats.append((m, W, qs, ds))
+    torch.cuda.synchronize()
+    out = {}
+    for M in wl.ms:
+        xs = [workloads.activations(HEADLINE, 0, m.name, M, dev) for (m, _, _, _) in mats]
+        ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
+
+        def step():
+            for c in range(copies):
+                for i, (m, _, qs, ds) in enumerate(mats):
+                    w4.linear(xs[i], qs[c], ds[c], m.N, out=ys[i])
+
+        g = capture(torch, step)
+        t = time_graph(torch, g, steps, warmup)
+        launches = steps * copies * len(mats)
+        step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats)
+        gbs = steps * step_bytes / t / 1e9
+        out[M] = {
+            "GBps": round(gbs, 1),
+            "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "us_per_call": round(t / launches * 1e6, 3),
+            "ms_per_step": round(t / steps * 1e3, 4),
+            "bytes_per_call": {m.name: workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats},
+            "launches_per_step": copies * len(mats),
+        }
+        log(f"[bench] {HEADLINE} M={M}: {gbs:.0f} GB/s, {t / launches * 1e6:.2f} us/call")
+        del g
+    # quantization throughput (rows a1-a4), same matrices, rotated over 4 fp32 copies
+    qout = {}
+    for (m, W, qs, ds) in mats:
+        Ws = [W] + [W.clone() for _ in range(3)]
+
+        def qstep():
+            for c in range(4):
+                w4.quantize_rtn(Ws[c], out=(qs[c], ds[c]))
+
+        g = capture(torch, qstep)
+        t = time_graph(torch, g, max(3, steps // 4), 2)
+        n = max(3, steps // 4) * 4
+        qb = workloads.quantize_bytes(m.N, m.K)
+        qout[m.name] = {"GBps": round(n * qb / t / 1e9, 1), "us_per_call": round(t / n * 1e6, 2),
+                        "bytes_per_call": qb}
+        log(f"[bench] quantize {m.name} {m.N}x{m.K}: {n * qb / t / 1e9:.0f} GB/s")
+        del g, Ws
+    del mats
+    torch.cuda.empty_cache()
+    return out, qout
+
+
+# ----------------------------------------------------------------------------
+# layer stacks: one graph = one decode (or verify) pass over every linear
+# ----------------------------------------------------------------------------
+
+def bench_stack(torch, w4, workloads, name, steps, warmup):
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[name]
+    t0 = time.time()
+    layers = []
+    for layer in range(wl.layers):
+        mats = []
+        for m in wl.matrices:
+            W = workloads.weight(name, layer, m.name, dev)
+            q, d = w4.quantize_rtn(W)
+            del W
+            mats.append((m, q, d))
+        layers.append(mats)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[bench] stack {name}: {wl.layers} layers quantized in {time.time() - t0:.1f}s")
+    res = {}
+    for M in wl.ms:
+        xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
+        ys = {m.N: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+
+        def step():
+            for mats in layers:
+                for (m, q, d) in mats:
+                    w4.linear(xs[m.K], q, d, m.N, out=ys[m.N])
+
+        g = capture(torch, step)
+        t = time_graph(torch, g, steps, warmup)
+        per = t / steps
+        nbytes = workloads.stack_bytes(name, M)
+        gbs = nbytes / per / 1e9
+        res[M] = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1),
+                  "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                  "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(M / per, 1),
+                  "bytes_per_pass": nbytes, "launches_per_pass": len(layers) * len(wl.matrices)}
+        log(f"[bench] stack {name} M={M}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s")
+        del g
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample, rank 0, after the GPU phase)
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(workloads, budget_s=12.0):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    wl = workloads.WORKLOADS[HEADLINE]
+    data = []
+    for m in wl.matrices:
+        W = workloads.weight(HEADLINE, 0, m.name, "cpu")
+        q, d = oracle.rtn_quantize_ref(W)
+        x = workloads.activations(HEADLINE, 0, m.name, 1, "cpu")
+        xb = x.view(torch.int16).numpy().view(np.uint16)
+        data.append((m, q, d, xb))
+    passes = 0
+    nbytes = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for (m, q, d, xb) in data:
+                oracle.w4_linear_ref(xb, q, d)
+                nbytes += workloads.algorithmic_bytes(1, m.N, m.K)
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        t = time.perf_counter() - t0
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full M=1 passes over both {HEADLINE} matrices "
+                      f"(2560x9216 and 9216x2560, fp64 oracle.w4_linear_ref), {t:.1f} s, "
+                      "one BLAS/NumPy thread",
+            "seconds": round(t, 2)}
+
+
+# ----------------------------------------------------------------------------
+
+def roofline(pair_m1, copies, steps):
+    """Dominant kernel: the MFMA linear at M = 1 on the headline pair."""
+    achieved = pair_m1["GBps"]
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            traffic = c.get("hbm_bytes_per_call")
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "linear_mfma_kernel (M=1)",
+            "algorithmic_bytes_per_call": pair_m1["bytes_per_call"],
+            "avg_launch_us": pair_m1["us_per_call"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=32)
+    ap.add_argument("--stacks", default="27b,70b")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run the plain copy kernel on this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_group_quantized_w4_amd as w4
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+
+    pair, quant = bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies)
+
+    stacks = {}
+    for s in [s for s in args.stacks.split(",") if s and s != "none"]:
+        stacks["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
+                                           max(2, args.warmup))
+
+    if args.calibrate_copy_mb:
+        import ctypes
+
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(w4.__file__), "libw4_bench.so"))
+        nb = args.calibrate_copy_mb << 20
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(3):
+            assert lib.w4bench_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                    ctypes.c_int64(nb), 2048, s) == 0
+        torch.cuda.synchronize()
+        log(f"[bench] copy kernel: 3 x {args.calibrate_copy_mb} MiB")
+
+    torch.cuda.synchronize()
+    cpu = None if args.no_cpu else cpu_baseline(workloads)
+
+    m1 = pair[1]
+    line = {
+        "metric": METRIC,
+        "value": m1["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m1["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "matrices": ["2560x9216", "9216x2560"], "M": 1,
+                   "weight_copies": args.copies, "group": 128, "weights": "int4 codes + fp32 scales",
+                   "x": "bf16", "timing": "hip graph replay, events on the replay stream"},
+        "pct_of_peak": m1["pct_of_peak"],
+        "us_per_call": m1["us_per_call"],
+        "m8": pair.get(8),
+        "quantize": quant,
+        "stacks": stacks,
+        "roofline": roofline(m1, args.copies, args.steps),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,6 +45,9 @@ def common_flags():
         "-fno-fast-math",
         "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: the per-group scaling reads them with
+        # plain VALU instead of v_accvgpr_read copies.
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE,
         "-I", CSRC,
     ]

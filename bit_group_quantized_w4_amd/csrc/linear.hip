@@ -34,9 +34,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return bitcast<bf16x8>(v); }
 
-__device__ __forceinline__ bf16x8 unpack_step(uint32_t w) {
+__device__ __forceinline__ bf16x8 unpack_step(uint32_t w, const UnpackConsts& uc) {
   uint32_t b[4];
-  unpack_word(w, b);
+  unpack_word(w, b, uc);
   return bitcast<bf16x8>(u32x4{b[0], b[1], b[2], b[3]});
 }
 
@@ -72,8 +72,8 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
     for (int r = 0; r < R; ++r) {
       if (r < rvalid) {
         const int64_t t = (int64_t)(rb0 + r) * G + g;
-        bq[s][r] = qp[t * kTileLanes + lane];
-        bd[s][r] = dp[t * kTileRows + nl];
+        bq[s][r] = load_stream(qp + t * kTileLanes + lane);
+        bd[s][r] = load_stream(dp + t * kTileRows + nl);
       }
     }
   };
@@ -88,6 +88,7 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
   uint4 xa[4], xn[4];
   if (g0 < g1) load_x(g0, xa);
 
+  const UnpackConsts uc = unpack_consts();
   const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
   const bf16x8 kneg = bitcast<bf16x8>(u32x4{kneg2, kneg2, kneg2, kneg2});
 
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
             const uint32_t wv[4] = {bq[s][r].x, bq[s][r].y, bq[s][r].z, bq[s][r].w};
             f32x4 c = off;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c = mfma16x16x32(a[i], unpack_step(wv[i]), c);
+            for (int i = 0; i < 4; ++i) c = mfma16x16x32(a[i], unpack_step(wv[i], uc), c);
             const float dv = bd[s][r];
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[r][j] += dv * c[j];
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
     for (int r = 0; r < R; ++r) {
       if (r < rvalid) {
         const int64_t t = (int64_t)(rb0 + r) * G + g;
-        bq[s][r] = qp[t * kTileLanes + lane];
-        bd[s][r] = dp[t * kTileRows + nl];
+        bq[s][r] = load_stream(qp + t * kTileLanes + lane);
+        bd[s][r] = load_stream(dp + t * kTileRows + nl);
       }
     }
   };
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
   for (int s = 0; s < PF; ++s)
     if (g0 + s < g1) issue(s, g0 + s);
 
+  const UnpackConsts uc = unpack_consts();
   const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
 
   float acc[R][MT];
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
             const uint32_t wv[4] = {bq[s][r].x, bq[s][r].y, bq[s][r].z, bq[s][r].w};
             uint32_t b[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unpack_word(wv[i], &b[4 * i]);
+            for (int i = 0; i < 4; ++i) unpack_word(wv[i], &b[4 * i], uc);
             const float dv = bd[s][r];
 #pragma unroll
             for (int mm = 0; mm < MT; ++mm) {

@@ -37,16 +37,42 @@ __device__ __forceinline__ int nibble_shift(int j) {
   return (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1);
 }
 
+// Constants of the nibble widening, held in registers: gfx9 VOP3 encodings
+// take no 32-bit literal, so with immediate masks the compiler would split
+// every (w & mask) | magic into two instructions instead of one v_and_or_b32.
+struct UnpackConsts {
+  uint32_t mask;   // mantissa bits 3..6 of both bf16 halves (SGPR)
+  uint32_t magic;  // bf16 1.0 in both halves (VGPR)
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts c{0x00780078u, 0x3F803F80u};
+  asm volatile("" : "+s"(c.mask));
+  asm volatile("" : "+v"(c.magic));
+  return c;
+}
+
 // Native word -> four bf16 pairs (inputs 2p, 2p+1 for p = 0..3).
 // Each nibble u lands in mantissa bits 3..6 of bf16 1.0, giving 1 + u/16
 // = 1.5 + q/16 exactly; the kernels remove the 1.5 through their accumulator
-// start value and scale the result by 16 at the end.
-__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4]) {
-  out[0] = (w & 0x00780078u) | 0x3F803F80u;
-  out[1] = (rotr32(w, 4) & 0x00780078u) | 0x3F803F80u;
-  out[2] = (rotr32(w, 8) & 0x00780078u) | 0x3F803F80u;
-  out[3] = (rotr32(w, 12) & 0x00780078u) | 0x3F803F80u;
+// start value and scale the result by 16 at the end.  Seven VALU
+// instructions per word: three rotates and four v_and_or_b32.
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4], const UnpackConsts& c) {
+  out[0] = (w & c.mask) | c.magic;
+  out[1] = (rotr32(w, 4) & c.mask) | c.magic;
+  out[2] = (rotr32(w, 8) & c.mask) | c.magic;
+  out[3] = (rotr32(w, 12) & c.mask) | c.magic;
 }
+
+// Streaming 16-byte load that does not keep the line in the caches (the
+// packed weights are read exactly once per call).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float load_stream(const float* p) { return __builtin_nontemporal_load(p); }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
