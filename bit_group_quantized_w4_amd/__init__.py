@@ -20,8 +20,18 @@ W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_HIP, W4_ERR_ARG = range(6
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 GROUP = 128
 
-# (name, restype, argtypes) of every symbol include/w4.h declares
 _VP, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+MAX_BATCH = 64
+
+
+class LinearDesc(ctypes.Structure):
+    """ctypes mirror of w4_linear_desc."""
+
+    _fields_ = [("x", _VP), ("M", _I64), ("K", _I64), ("q_packed", _VP), ("d_packed", _VP),
+                ("N", _I64), ("y", _VP)]
+
+
+# (name, restype, argtypes) of every symbol include/w4.h declares
 SIGNATURES = {
     "w4_status_str": (ctypes.c_char_p, [_INT]),
     "w4_last_hip_error": (_INT, []),
@@ -31,6 +41,7 @@ SIGNATURES = {
     "w4_quantize_rtn": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_linear": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP]),
     "w4_linear_ex": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
+    "w4_linear_batched": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
     "w4_pack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_unpack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
 }
@@ -127,6 +138,28 @@ def linear(x, q, d, N, path="auto", out=None):
     return y
 
 
+def linear_batched(items, path="auto"):
+    """Several independent linears in one launch.
+
+    items: sequence of (x [M, K] bf16, q, d, N, y [M, N] bf16) with every y
+    preallocated; at most MAX_BATCH items.  Returns the list of y.
+    """
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    items = list(items)
+    descs = (LinearDesc * max(1, len(items)))()
+    stream = None
+    for i, (x, q, d, N, y) in enumerate(items):
+        M, K = x.shape
+        if y.shape != (M, N):
+            raise ValueError(f"item {i}: y must be [M, N]")
+        descs[i] = LinearDesc(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
+                              _dev(d, torch.float32, "d").value, N, _dev(y, torch.bfloat16, "y").value)
+        stream = stream or _stream(x)
+    _check(_lib.w4_linear_batched(descs, len(items), PATHS[path], stream), "w4_linear_batched")
+    return [it[4] for it in items]
+
+
 def pack(q_canon, d_canon, out=None):
     """Canonical codes int8 [N, K] and scales fp32 [N, K/128] -> native (q, d)."""
     N, K = q_canon.shape
@@ -163,6 +196,7 @@ class W4Linear:
 
 
 __all__ = [
-    "GROUP", "LIB_PATH", "PATHS", "SIGNATURES", "W4Error", "W4Linear", "library", "linear",
+    "GROUP", "LIB_PATH", "MAX_BATCH", "PATHS", "SIGNATURES", "LinearDesc", "W4Error", "W4Linear",
+    "library", "linear", "linear_batched",
     "pack", "packed_bytes", "quantize_rtn", "scale_count", "unpack",
 ]

@@ -13,7 +13,7 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMaxK = int64_t(1) << 24;       // keeps every in-kernel index in range
 constexpr int64_t kMaxN = (int64_t(1) << 31) - 16;
-constexpr int64_t kMaxM = 65535 * 4;              // grid rows of 4-row slabs
+constexpr int64_t kMaxM = 65535 * 4;              // kept within 32-bit block indices
 
 bool k_ok(int64_t K) { return K > 0 && K % kGroup == 0 && K <= kMaxK; }
 bool n_ok(int64_t N) { return N >= 0 && N <= kMaxN; }
@@ -29,8 +29,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Kernel used by w4_linear for a shape.  The MFMA kernel needs fewer VALU
 // instructions per weight than the dot2 kernel at every M (one 16x16x32 MFMA
 // replaces 16 dot2 per row of x), so it is the default everywhere.
-int auto_path(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
+int auto_path(int64_t M, int64_t K) {
+  (void)M; (void)K;
   return W4_PATH_MFMA;
 }
 
@@ -38,6 +38,52 @@ w4_status hip_status(hipError_t e) {
   if (e == hipSuccess) return W4_OK;
   g_last_hip_error = static_cast<int>(e);
   return W4_ERR_HIP;
+}
+
+// Checks one linear of a call; on success appends it to the batch.
+w4_status check_linear(const w4_linear_desc& l, w4::BatchArgs& a) {
+  if (l.M < 0 || l.M > kMaxM || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
+  if (l.M == 0 || l.N == 0) return W4_OK;  // empty: nothing to launch
+  if (!l.x || !l.q_packed || !l.d_packed || !l.y) return W4_ERR_NULL;
+  if (!aligned(l.x, 16) || !aligned(l.q_packed, 16) || !aligned(l.d_packed, 16) || !aligned(l.y, 2))
+    return W4_ERR_ALIGN;
+  w4::LinearDesc& d = a.desc[a.count++];
+  d.x = l.x;
+  d.q = l.q_packed;
+  d.d = l.d_packed;
+  d.y = l.y;
+  d.M = (int)l.M;
+  d.K = (int)l.K;
+  d.N = (int)l.N;
+  d.pad = 0;
+  return W4_OK;
+}
+
+// Every output must be disjoint from every input and every other output of the call.
+w4_status check_aliasing(const w4_linear_desc* l, int count) {
+  for (int i = 0; i < count; ++i) {
+    if (l[i].M <= 0 || l[i].N <= 0) continue;
+    const size_t yb = 2 * (size_t)l[i].M * l[i].N;
+    for (int j = 0; j < count; ++j) {
+      if (l[j].M <= 0 || l[j].N <= 0) continue;
+      if (overlaps(l[i].y, yb, l[j].x, 2 * (size_t)l[j].M * l[j].K) ||
+          overlaps(l[i].y, yb, l[j].q_packed, w4_packed_bytes(l[j].N, l[j].K)) ||
+          overlaps(l[i].y, yb, l[j].d_packed, 4 * w4_scale_count(l[j].N, l[j].K)))
+        return W4_ERR_ARG;
+      if (j != i && overlaps(l[i].y, yb, l[j].y, 2 * (size_t)l[j].M * l[j].N)) return W4_ERR_ARG;
+    }
+  }
+  return W4_OK;
+}
+
+w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, hipStream_t stream) {
+  if (a.count == 0) return W4_OK;
+  if (path == W4_PATH_AUTO) path = auto_path(max_m, max_k);
+  if (path == W4_PATH_GEMV) {
+    if (2 * max_k > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
+    return hip_status(w4::launch_linear_gemv(a, w4::gemv_rows_per_slab(max_m, max_k), stream));
+  }
+  return hip_status(w4::launch_linear_mfma(a, stream));
 }
 
 }  // namespace
@@ -67,7 +113,7 @@ size_t w4_packed_bytes(int64_t N, int64_t K) {
 
 size_t w4_scale_count(int64_t N, int64_t K) {
   if (!n_ok(N) || !k_ok(K)) return 0;
-  return (size_t)padded_rows(N) * (size_t)(K / kGroup);
+  return (size_t)padded_rows(N) * (size_t)((K / kGroup + 3) / 4 * 4);
 }
 
 w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed, float* d_packed,
@@ -82,23 +128,31 @@ w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packe
   return hip_status(w4::launch_quantize_rtn(W, N, K, q_packed, d_packed, stream));
 }
 
+w4_status w4_linear_batched(const w4_linear_desc* linears, int count, int path, hipStream_t stream) {
+  if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
+  if (count < 0 || count > W4_MAX_BATCH) return W4_ERR_ARG;
+  if (count == 0) return W4_OK;
+  if (!linears) return W4_ERR_NULL;
+  w4::BatchArgs a;
+  a.count = 0;
+  int64_t max_m = 0, max_k = 0;
+  for (int i = 0; i < count; ++i) {
+    const w4_status st = check_linear(linears[i], a);
+    if (st != W4_OK) return st;
+    if (linears[i].M > 0 && linears[i].N > 0) {
+      max_m = linears[i].M > max_m ? linears[i].M : max_m;
+      max_k = linears[i].K > max_k ? linears[i].K : max_k;
+    }
+  }
+  const w4_status al = check_aliasing(linears, count);
+  if (al != W4_OK) return al;
+  return run_batch(a, path, max_m, max_k, stream);
+}
+
 w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
                        const float* d_packed, int64_t N, uint16_t* y, int path, hipStream_t stream) {
-  if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
-  if (M < 0 || M > kMaxM || !n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
-  if (M == 0 || N == 0) return W4_OK;
-  if (!x || !q_packed || !d_packed || !y) return W4_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16) || !aligned(y, 2))
-    return W4_ERR_ALIGN;
-  const size_t yb = 2 * (size_t)M * N;
-  if (overlaps(y, yb, x, 2 * (size_t)M * K) || overlaps(y, yb, q_packed, w4_packed_bytes(N, K)) ||
-      overlaps(y, yb, d_packed, 4 * w4_scale_count(N, K)))
-    return W4_ERR_ARG;
-  if (path == W4_PATH_AUTO) path = auto_path(M, N, K);
-  const hipError_t e = path == W4_PATH_GEMV
-                           ? w4::launch_linear_gemv(x, M, K, q_packed, d_packed, N, y, stream)
-                           : w4::launch_linear_mfma(x, M, K, q_packed, d_packed, N, y, stream);
-  return hip_status(e);
+  const w4_linear_desc l = {x, M, K, q_packed, d_packed, N, y};
+  return w4_linear_batched(&l, 1, path, stream);
 }
 
 w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,

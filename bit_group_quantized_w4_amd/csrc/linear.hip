@@ -4,12 +4,18 @@
 // draft verification at M = K + 1 (27B quantization-and-drafter ladder,
 // stage 2), so it is bound by streaming the packed weights from HBM.
 //
-// Both kernels read the same native layout (one 1 KiB tile = 16 rows x one
-// 128-input group, 16 bytes per lane) and the same decomposition:
-//   * a workgroup owns R consecutive 16-row blocks and all K;
-//   * its NW wavefronts split the groups of K into contiguous ranges;
-//   * each wavefront keeps PF groups of weight tiles in flight (a register
-//     ring), so the loads of later groups overlap the math of earlier ones;
+// One launch serves a batch of up to kMaxBatch independent linears (a single
+// w4_linear call is a batch of one).  Work decomposition, per linear:
+//   * a workgroup owns R consecutive 16-row blocks, all K, and one slab of
+//     x rows (16 for the MFMA kernel, MT for the dot2 kernel);
+//   * its NW wavefronts split K into contiguous ranges of whole scale quads
+//     (4 groups of 128 inputs);
+//   * each wavefront walks its range one group at a time with a 4-deep
+//     register ring of loads, issued in exactly the order they are consumed,
+//     so waiting for group g never waits for loads issued after it; the
+//     16-byte scale quad of each row is loaded once per 4 groups into a
+//     double buffer;
+//   * weight tiles and scales use non-temporal loads (each byte is read once);
 //   * partial sums of the wavefronts are combined in LDS in a fixed order,
 //     so results are bitwise reproducible (no atomics).
 // Nibbles are widened in registers to bf16 1 + u/16 = 1.5 + q/16 (see
@@ -21,18 +27,16 @@
 
 #include <stdio.h>
 #include <stdlib.h>
-#include <string.h>
 
 namespace w4 {
 namespace {
 
 constexpr uint16_t kBf16NegOneHalf = 0xBFC0;  // bf16 -1.5
+constexpr int kRing = 4;                      // groups in flight per wavefront = one scale quad
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return bitcast<bf16x8>(v); }
 
 __device__ __forceinline__ bf16x8 unpack_step(uint32_t w, const UnpackConsts& uc) {
   uint32_t b[4];
@@ -44,49 +48,81 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(a), bitcast<bf16x2>(b), c, false);
 }
 
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float quad_elem(const uint4& v, int s) { return __uint_as_float(word(v, s)); }
+
+// Which linear of the batch, and which (row panel, x slab) of it, a block runs.
+struct Work {
+  int di, rb0, m0;
+};
+
+__device__ __forceinline__ Work locate(const BatchArgs& a, int R, int MT) {
+  const int b = blockIdx.x;
+  int di = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i)
+    if (i < a.count && b >= a.block0[i]) di = i;
+  const LinearDesc& d = a.desc[di];
+  const int nb = (d.N + kTileRows - 1) / kTileRows;
+  const int panels = (nb + R - 1) / R;
+  const int local = b - a.block0[di];
+  const int slab = local / panels;
+  return Work{di, (local - slab * panels) * R, slab * MT};
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel.  One v_mfma_f32_16x16x32_bf16 per 32-input step: A = 16 rows
-// of x (rows >= M are zero), B = the tile's 16 rows of W^T.  Lane l holds
-// A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16] and D[4(l/16)+j][l%16], j = 0..3.
-// The -1.5*sum(x) start value is itself one MFMA chain with B = -1.5.
+// of x, B = the tile's 16 rows of W^T.  Lane l holds A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16] and D[4(l/16)+j][l%16], j = 0..3.  Rows of A at or
+// beyond M repeat row M-1 (their outputs are computed and discarded), so every
+// lane loads valid memory with no branches.  The -1.5*sum(x) start value is
+// itself one MFMA chain with B = -1.5.
 // ---------------------------------------------------------------------------
-template <int R, int NW, int PF>
-__global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int G, const uint4* __restrict__ qp,
-    const float* __restrict__ dp, int N, int Nb, uint16_t* __restrict__ y) {
+template <int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
-  const int rb0 = blockIdx.x * R;
-  const int m0 = blockIdx.y * 16;
-  const int g0 = (int)(((int64_t)G * wave) / NW);
-  const int g1 = (int)(((int64_t)G * (wave + 1)) / NW);
-  const int rvalid = min(R, Nb - rb0);
+  const Work wk = locate(args, R, 16);
+  const LinearDesc& D = args.desc[wk.di];
+  const int M = D.M, K = D.K, N = D.N;
+  const int G = K / kGroup;
+  const int Q = (G + 3) >> 2;
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  const int rvalid = min(R, nb - wk.rb0);
+  const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
 
-  const bool xok = (m0 + nl) < M;
-  const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)(xok ? m0 + nl : 0) * K) + kb;
-
-  uint4 bq[PF][R];
-  float bd[PF][R];
-  auto issue = [&](int s, int g) {
+  const int xrow = min(wk.m0 + nl, M - 1);
+  const uint4* xs = reinterpret_cast<const uint4*>(D.x + (int64_t)xrow * K) + kb;
+  const uint4* qp = reinterpret_cast<const uint4*>(D.q);
+  const uint4* dq = reinterpret_cast<const uint4*>(D.d);
+  // Row blocks past the end of the matrix re-read the last one (never stored);
+  // padding groups of the last quad re-read group G-1 and carry scale 0.
+  int64_t rowq[R], rows[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < rvalid) {
-        const int64_t t = (int64_t)(rb0 + r) * G + g;
-        bq[s][r] = load_stream(qp + t * kTileLanes + lane);
-        bd[s][r] = load_stream(dp + t * kTileRows + nl);
-      }
-    }
+  for (int r = 0; r < R; ++r) {
+    const int rb = min(wk.rb0 + r, nb - 1);
+    rowq[r] = (int64_t)rb * G * kTileLanes + lane;
+    rows[r] = (int64_t)rb * Q * kTileRows + nl;
+  }
+
+  uint4 bx[kRing][4];
+  uint4 bw[kRing][R];
+  uint4 sc[R], sn[R];  // scale quads: current and next
+
+  auto issue_group = [&](int s, int g) {
+    const int gc = min(g, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bx[s][i] = xs[gc * 16 + i * 4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qp + rowq[r] + (int64_t)gc * kTileLanes);
   };
-  auto load_x = [&](int g, uint4 (&xa)[4]) {
+  auto issue_scales = [&](uint4 (&dst)[R], int j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = xok ? xs[g * 16 + i * 4] : make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < R; ++r) dst[r] = load_stream(dq + rows[r] + (int64_t)j * kTileRows);
   };
-
-#pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (g0 + s < g1) issue(s, g0 + s);
-  uint4 xa[4], xn[4];
-  if (g0 < g1) load_x(g0, xa);
 
   const UnpackConsts uc = unpack_consts();
   const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
@@ -96,44 +132,54 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int gb = g0; gb < g1; gb += PF) {
+  auto compute = [&](int s) {
+    bf16x8 a[4];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      const int g = gb + s;
-      if (g < g1) {
-        if (g + 1 < g1) load_x(g + 1, xn);
-        bf16x8 a[4];
+    for (int i = 0; i < 4; ++i) a[i] = bitcast<bf16x8>(bx[s][i]);
+    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(xa[i]);
-        f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) off = mfma16x16x32(a[i], kneg, off);
+    f32x4 c[R];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) off = mfma16x16x32(a[i], kneg, off);
+    for (int r = 0; r < R; ++r) c[r] = off;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r < rvalid) {
-            const uint32_t wv[4] = {bq[s][r].x, bq[s][r].y, bq[s][r].z, bq[s][r].w};
-            f32x4 c = off;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c = mfma16x16x32(a[i], unpack_step(wv[i], uc), c);
-            const float dv = bd[s][r];
+      for (int r = 0; r < R; ++r) c[r] = mfma16x16x32(a[i], unpack_step(word(bw[s][r], i), uc), c[r]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[r][j] += dv * c[j];
-          }
-        }
-        if (g + PF < g1) issue(s, g + PF);
+    for (int r = 0; r < R; ++r) {
+      const float dv = quad_elem(sc[r], s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = xn[i];
-      }
+      for (int e = 0; e < 4; ++e) acc[r][e] += dv * c[r][e];
     }
+  };
+
+  if (j0 < j1) {
+    issue_scales(sc, j0);
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) issue_group(s, 4 * j0 + s);
+    // steady state: every load unconditional, issued in consumption order
+    for (int j = j0; j < j1 - 1; ++j) {
+      issue_scales(sn, j + 1);
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        compute(s);
+        issue_group(s, 4 * (j + 1) + s);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[r] = sn[r];
+    }
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) compute(s);
   }
 
   auto store = [&](int r, const f32x4& v) {
-    const int64_t n = (int64_t)(rb0 + r) * kTileRows + nl;
+    const int n = (wk.rb0 + r) * kTileRows + nl;
     if (n >= N) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + 4 * kb + j;
-      if (m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v[j]);
+    for (int e = 0; e < 4; ++e) {
+      const int m = wk.m0 + 4 * kb + e;
+      if (m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v[e]);
     }
   };
 
@@ -152,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
       for (int w = 1; w < NW; ++w) {
         const f32x4 o = red[w][r][lane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] += o[j];
+        for (int e = 0; e < 4; ++e) v[e] += o[e];
       }
       store(r, v);
     }
@@ -161,44 +207,58 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(
 
 // ---------------------------------------------------------------------------
 // VALU kernel (v_dot2_f32_bf16).  Lane (row l%16, quarter l/16) multiplies its
-// 32 weights of a group by the matching 32 inputs of each of MT x rows; the
-// four quarters of a row are summed with cross-lane shuffles at the end.
+// 32 weights of a group by the matching 32 inputs of each of the MT x rows of
+// its slab; x is staged once per block in LDS (MT * K bf16).  The four
+// quarters of a row are summed with cross-lane shuffles at the end.
 // ---------------------------------------------------------------------------
-template <int MT, int R, int NW, int PF>
-__global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int G, const uint4* __restrict__ qp,
-    const float* __restrict__ dp, int N, int Nb, uint16_t* __restrict__ y) {
+template <int MT, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
+  extern __shared__ uint4 xlds[];  // [MT][K/8] uint4
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
-  const int rb0 = blockIdx.x * R;
-  const int m0 = blockIdx.y * MT;
-  const int g0 = (int)(((int64_t)G * wave) / NW);
-  const int g1 = (int)(((int64_t)G * (wave + 1)) / NW);
-  const int rvalid = min(R, Nb - rb0);
-
-  const uint4* xs[MT];
-  bool xok[MT];
+  const Work wk = locate(args, R, MT);
+  const LinearDesc& D = args.desc[wk.di];
+  const int M = D.M, K = D.K, N = D.N;
+  const int G = K / kGroup;
+  const int Q = (G + 3) >> 2;
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  const int rvalid = min(R, nb - wk.rb0);
+  const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
+  const uint4* qp = reinterpret_cast<const uint4*>(D.q);
+  const uint4* dq = reinterpret_cast<const uint4*>(D.d);
+  int64_t rowq[R], rows[R];
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    xok[mm] = (m0 + mm) < M;
-    xs[mm] = reinterpret_cast<const uint4*>(x + (int64_t)(xok[mm] ? m0 + mm : 0) * K) + kb;
+  for (int r = 0; r < R; ++r) {
+    const int rb = min(wk.rb0 + r, nb - 1);
+    rowq[r] = (int64_t)rb * G * kTileLanes + lane;
+    rows[r] = (int64_t)rb * Q * kTileRows + nl;
   }
 
-  uint4 bq[PF][R];
-  float bd[PF][R];
-  auto issue = [&](int s, int g) {
+  uint4 bw[kRing][R];
+  uint4 sc[R], sn[R];
+  auto issue_group = [&](int s, int g) {
+    const int gc = min(g, G - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < rvalid) {
-        const int64_t t = (int64_t)(rb0 + r) * G + g;
-        bq[s][r] = load_stream(qp + t * kTileLanes + lane);
-        bd[s][r] = load_stream(dp + t * kTileRows + nl);
-      }
-    }
+    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qp + rowq[r] + (int64_t)gc * kTileLanes);
   };
+  auto issue_scales = [&](uint4 (&dst)[R], int j) {
 #pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (g0 + s < g1) issue(s, g0 + s);
+    for (int r = 0; r < R; ++r) dst[r] = load_stream(dq + rows[r] + (int64_t)j * kTileRows);
+  };
+  if (j0 < j1) {
+    issue_scales(sc, j0);
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) issue_group(s, 4 * j0 + s);
+  }
+
+  // stage this slab's x rows (rows beyond M repeat row M-1; their outputs are dropped)
+  const int kq = K / 8;  // uint4 per row
+  for (int e = threadIdx.x; e < MT * kq; e += NW * 64) {
+    const int mm = e / kq;
+    const int row = min(wk.m0 + mm, M - 1);
+    xlds[e] = reinterpret_cast<const uint4*>(D.x + (int64_t)row * K)[e - mm * kq];
+  }
+  __syncthreads();
 
   const UnpackConsts uc = unpack_consts();
   const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
@@ -209,49 +269,54 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.f;
 
-  for (int gb = g0; gb < g1; gb += PF) {
+  auto compute = [&](int s, int g) {
+    const int gc = min(g, G - 1);  // padding groups: any valid x, scale 0
+    uint32_t xv[MT][16];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      const int g = gb + s;
-      if (g < g1) {
-        uint32_t xv[MT][16];
+    for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
+      for (int i = 0; i < 4; ++i) {
+        const uint4 t = xlds[mm * kq + gc * 16 + i * 4 + kb];
+        xv[mm][4 * i + 0] = t.x; xv[mm][4 * i + 1] = t.y;
+        xv[mm][4 * i + 2] = t.z; xv[mm][4 * i + 3] = t.w;
+      }
+    float c0[MT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 t = xok[mm] ? xs[mm][g * 16 + i * 4] : make_uint4(0, 0, 0, 0);
-            xv[mm][4 * i + 0] = t.x; xv[mm][4 * i + 1] = t.y;
-            xv[mm][4 * i + 2] = t.z; xv[mm][4 * i + 3] = t.w;
-          }
-        }
-        float c0[MT];
+    for (int mm = 0; mm < MT; ++mm) {
+      float c = 0.f;
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
-          float c = 0.f;
+      for (int e = 0; e < 16; ++e) c = dot2(xv[mm][e], kneg2, c);
+      c0[mm] = c;
+    }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) c = dot2(xv[mm][e], kneg2, c);
-          c0[mm] = c;
-        }
+    for (int r = 0; r < R; ++r) {
+      uint32_t b[16];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r < rvalid) {
-            const uint32_t wv[4] = {bq[s][r].x, bq[s][r].y, bq[s][r].z, bq[s][r].w};
-            uint32_t b[16];
+      for (int i = 0; i < 4; ++i) unpack_word(word(bw[s][r], i), &b[4 * i], uc);
+      const float dv = quad_elem(sc[r], s);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unpack_word(wv[i], &b[4 * i], uc);
-            const float dv = bd[s][r];
+      for (int mm = 0; mm < MT; ++mm) {
+        float c = c0[mm];
 #pragma unroll
-            for (int mm = 0; mm < MT; ++mm) {
-              float c = c0[mm];
-#pragma unroll
-              for (int e = 0; e < 16; ++e) c = dot2(b[e], xv[mm][e], c);
-              acc[r][mm] += dv * c;
-            }
-          }
-        }
-        if (g + PF < g1) issue(s, g + PF);
+        for (int e = 0; e < 16; ++e) c = dot2(b[e], xv[mm][e], c);
+        acc[r][mm] += dv * c;
       }
     }
+  };
+
+  if (j0 < j1) {
+    for (int j = j0; j < j1 - 1; ++j) {
+      issue_scales(sn, j + 1);
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        compute(s, 4 * j + s);
+        issue_group(s, 4 * (j + 1) + s);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[r] = sn[r];
+    }
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) compute(s, 4 * (j1 - 1) + s);
   }
 
   // Sum the four quarters of each row: lanes l, l^16, l^32, l^48.
@@ -265,42 +330,25 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
       acc[r][mm] = v;
     }
 
-  auto store = [&](int r, int mm, float v) {
-    const int64_t n = (int64_t)(rb0 + r) * kTileRows + nl;
-    const int m = m0 + mm;
-    if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v);
-  };
-
-  if constexpr (NW == 1) {
-    if (kb == 0) {
+  __shared__ float red[NW][R][MT][16];
+  if (kb == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (r < rvalid)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int mm = 0; mm < MT; ++mm) store(r, mm, acc[r][mm]);
-    }
-  } else {
-    __shared__ float red[NW][R][MT][16];
-    if (kb == 0) {
+      for (int mm = 0; mm < MT; ++mm) red[wave][r][mm][nl] = acc[r][mm];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < R * MT * 16; e += NW * 64) {
+    const int row = e & 15;
+    const int mm = (e >> 4) % MT;
+    const int r = (e >> 4) / MT;
+    if (r < rvalid) {
+      float v = red[0][r][mm][row];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm) red[wave][r][mm][nl] = acc[r][mm];
-    }
-    __syncthreads();
-    // thread t of the block finalizes (r, mm, row) = t / 16 ..., fixed order over waves
-    for (int e = threadIdx.x; e < R * MT * 16; e += NW * 64) {
-      const int row = e & 15;
-      const int mm = (e >> 4) % MT;
-      const int r = (e >> 4) / MT;
-      if (r < rvalid) {
-        float v = red[0][r][mm][row];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][r][mm][row];
-        const int64_t n = (int64_t)(rb0 + r) * kTileRows + row;
-        const int m = m0 + mm;
-        if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v);
-      }
+      for (int w = 1; w < NW; ++w) v += red[w][r][mm][row];
+      const int n = (wk.rb0 + r) * kTileRows + row;
+      const int m = wk.m0 + mm;
+      if (n < N && m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v);
     }
   }
 }
@@ -309,77 +357,71 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(
 // launch configuration
 // ---------------------------------------------------------------------------
 struct Cfg {
-  int R, NW, PF;
+  int R, NW;
 };
 
-// Every (R, NW, PF) compiled for each kernel.  W4_MFMA_CFG / W4_GEMV_CFG
-// ("R,NW,PF") may pick one of them for measurement; anything else falls back
-// to the built-in choice.
-constexpr Cfg kCfgs[] = {{1, 4, 4}, {1, 8, 4}, {2, 4, 4}, {2, 8, 4}, {1, 8, 8}, {1, 16, 4}, {4, 4, 2}, {2, 4, 8}};
+// Every (R, NW) compiled for each kernel.  W4_MFMA_CFG / W4_GEMV_CFG ("R,NW")
+// may pick one of them for measurement; anything else falls back to the
+// built-in choice.
+constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {2, 4}, {2, 8}, {1, 16}, {4, 4}, {4, 8}, {1, 2}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 int cfg_from_env(const char* name) {
   const char* s = getenv(name);
   if (!s) return -1;
-  int R = 0, NW = 0, PF = 0;
-  if (sscanf(s, "%d,%d,%d", &R, &NW, &PF) != 3) return -1;
+  int R = 0, NW = 0;
+  if (sscanf(s, "%d,%d", &R, &NW) != 2) return -1;
   for (int i = 0; i < kNumCfgs; ++i)
-    if (kCfgs[i].R == R && kCfgs[i].NW == NW && kCfgs[i].PF == PF) return i;
+    if (kCfgs[i].R == R && kCfgs[i].NW == NW) return i;
   return -1;
 }
 
-// Built-in choice: enough wavefronts in flight for the weight stream.  The
-// bytes in flight are (N/16) * NW * PF KiB whatever R is, so small N gets more
-// wavefronts per block; large N keeps R = 1..2 so that there are enough blocks.
-int choose_cfg(int64_t N, int64_t K) {
-  (void)K;
-  const int64_t Nb = (N + kTileRows - 1) / kTileRows;
-  if (Nb >= 1024) return 2;  // {2, 4, 4}
-  if (Nb >= 256) return 1;   // {1, 8, 4}
-  return 5;                  // {1, 16, 4}
+int find_cfg(int R, int NW) {
+  for (int i = 0; i < kNumCfgs; ++i)
+    if (kCfgs[i].R == R && kCfgs[i].NW == NW) return i;
+  return 0;
 }
 
-template <int R, int NW, int PF>
-void run_mfma(dim3 grid, hipStream_t st, const uint16_t* x, int M, int K, int G, const uint4* q,
-              const float* d, int N, int Nb, uint16_t* y) {
-  linear_mfma_kernel<R, NW, PF><<<grid, NW * 64, 0, st>>>(x, M, K, G, q, d, N, Nb, y);
-}
-
-template <int MT, int R, int NW, int PF>
-void run_gemv(dim3 grid, hipStream_t st, const uint16_t* x, int M, int K, int G, const uint4* q,
-              const float* d, int N, int Nb, uint16_t* y) {
-  linear_gemv_kernel<MT, R, NW, PF><<<grid, NW * 64, 0, st>>>(x, M, K, G, q, d, N, Nb, y);
-}
-
-template <int MT>
-void dispatch_gemv(int ci, dim3 grid, hipStream_t st, const uint16_t* x, int M, int K, int G,
-                   const uint4* q, const float* d, int N, int Nb, uint16_t* y) {
-  switch (ci) {
-#define W4_CASE(i)                                                                          \
-  case i:                                                                                   \
-    run_gemv<MT, kCfgs[i].R, kCfgs[i].NW, kCfgs[i].PF>(grid, st, x, M, K, G, q, d, N, Nb, y); \
-    break;
-    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
-#undef W4_CASE
+// Built-in choice from the batch's total row blocks and largest K: enough
+// wavefronts in flight on all 256 CUs, whole scale quads per wavefront.
+int choose_cfg(const BatchArgs& a) {
+  int64_t rows = 0;
+  int kmax = 0;
+  for (int i = 0; i < a.count; ++i) {
+    rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
+    kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   }
+  const int quads = (kmax / kGroup + 3) / 4;
+  if (rows >= 2048) return find_cfg(2, quads >= 32 ? 8 : 4);
+  if (rows >= 512) return find_cfg(1, quads >= 16 ? 8 : 4);
+  return find_cfg(1, quads >= 32 ? 16 : 8);
+}
+
+int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
+  int64_t total = 0;
+  for (int i = 0; i < a.count; ++i) {
+    a.block0[i] = (int)total;
+    const int nb = (a.desc[i].N + kTileRows - 1) / kTileRows;
+    const int panels = (nb + R - 1) / R;
+    const int slabs = (a.desc[i].M + slab_rows - 1) / slab_rows;
+    total += (int64_t)panels * slabs;
+  }
+  return total;
 }
 
 }  // namespace
 
-hipError_t launch_linear_mfma(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
-                              const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream) {
+hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
   const int env = cfg_from_env("W4_MFMA_CFG");
-  const int ci = env >= 0 ? env : choose_cfg(N, K);
-  const int Nb = (int)((N + kTileRows - 1) / kTileRows);
-  const int G = (int)(K / kGroup);
+  const int ci = env >= 0 ? env : choose_cfg(a);
   const Cfg c = kCfgs[ci];
-  const dim3 grid((unsigned)((Nb + c.R - 1) / c.R), (unsigned)((M + 15) / 16));
-  const uint4* q = reinterpret_cast<const uint4*>(q_packed);
+  const int64_t blocks = fill_blocks(a, c.R, 16);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   switch (ci) {
-#define W4_CASE(i)                                                                                   \
-  case i:                                                                                            \
-    run_mfma<kCfgs[i].R, kCfgs[i].NW, kCfgs[i].PF>(grid, stream, x, (int)M, (int)K, G, q, d_packed, \
-                                                   (int)N, Nb, y);                                   \
+#define W4_CASE(i)                                                                               \
+  case i:                                                                                        \
+    linear_mfma_kernel<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(a); \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
@@ -387,22 +429,46 @@ hipError_t launch_linear_mfma(const uint16_t* x, int64_t M, int64_t K, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_linear_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
-                              const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream) {
+int gemv_rows_per_slab(int64_t M, int64_t K) {
+  // x of one slab lives in LDS: MT * K * 2 bytes, at most kGemvLdsBytes.
+  for (int mt = 4; mt > 1; mt >>= 1)
+    if (M >= mt && (int64_t)mt * K * 2 <= kGemvLdsBytes) return mt;
+  return 1;
+}
+
+hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
   const int env = cfg_from_env("W4_GEMV_CFG");
-  const int ci = env >= 0 ? env : choose_cfg(N, K);
-  const int Nb = (int)((N + kTileRows - 1) / kTileRows);
-  const int G = (int)(K / kGroup);
+  int ci = env >= 0 ? env : choose_cfg(a);
+  if (MT == 4 && kCfgs[ci].NW == 16) ci = find_cfg(1, 8);  // 16 wavefronts x 4 rows exceeds 128 VGPRs
   const Cfg c = kCfgs[ci];
-  const uint4* q = reinterpret_cast<const uint4*>(q_packed);
-  const int MT = M >= 4 ? 4 : (int)M;
-  const dim3 grid((unsigned)((Nb + c.R - 1) / c.R), (unsigned)((M + MT - 1) / MT));
-  switch (MT) {
-    case 1: dispatch_gemv<1>(ci, grid, stream, x, (int)M, (int)K, G, q, d_packed, (int)N, Nb, y); break;
-    case 2: dispatch_gemv<2>(ci, grid, stream, x, (int)M, (int)K, G, q, d_packed, (int)N, Nb, y); break;
-    case 3: dispatch_gemv<3>(ci, grid, stream, x, (int)M, (int)K, G, q, d_packed, (int)N, Nb, y); break;
-    default: dispatch_gemv<4>(ci, grid, stream, x, (int)M, (int)K, G, q, d_packed, (int)N, Nb, y); break;
+  const int64_t blocks = fill_blocks(a, c.R, MT);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  int kmax = 0;
+  for (int i = 0; i < a.count; ++i) kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
+  const size_t lds = (size_t)MT * kmax * 2;
+#define W4_LAUNCH(mt, i)                                                                          \
+  linear_gemv_kernel<mt, kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, lds, stream>>>(a)
+#define W4_CASES(mt)                                 \
+  switch (ci) {                                      \
+    case 0: W4_LAUNCH(mt, 0); break;                 \
+    case 1: W4_LAUNCH(mt, 1); break;                 \
+    case 2: W4_LAUNCH(mt, 2); break;                 \
+    case 3: W4_LAUNCH(mt, 3); break;                 \
+    case 4: W4_LAUNCH(mt, 4); break;                 \
+    case 5: W4_LAUNCH(mt, 5); break;                 \
+    case 6: W4_LAUNCH(mt, 6); break;                 \
+    default: W4_LAUNCH(mt, 7); break;                \
   }
+  if (MT == 4) {
+    W4_CASES(4)
+  } else if (MT == 2) {
+    W4_CASES(2)
+  } else {
+    W4_CASES(1)
+  }
+#undef W4_CASES
+#undef W4_LAUNCH
   return hipGetLastError();
 }
 

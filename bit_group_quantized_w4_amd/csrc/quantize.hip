@@ -13,7 +13,7 @@
 // it will own in the native layout (its row, 8 inputs in each of the four
 // 32-input steps), the group max is finished across the four lanes that share
 // a row, and the lane writes its 16 bytes of codes; the 16 scales of the tile
-// are written by the lanes of the first quarter.
+// are written by the lanes of the first quarter into their rows' scale quads.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -23,6 +23,20 @@ namespace w4 {
 namespace {
 
 constexpr int kTilesPerBlock = 4;  // one tile per wavefront, 4 wavefronts per block
+
+// Native scale layout: the scales of row n for the four consecutive groups
+// 4j .. 4j+3 are one 16-byte quad, quad (r, j) of row block r holding rows
+// 16r .. 16r+15 in order; the group count is padded to a multiple of 4 with
+// zero scales.
+__device__ __forceinline__ int64_t scale_index(int64_t r, int Q, int g, int nl) {
+  return ((r * Q + (g >> 2)) * kTileRows + nl) * 4 + (g & 3);
+}
+
+// Zero scales of the padding groups G .. 4Q-1 (written by the last group's tile).
+__device__ __forceinline__ void zero_scale_padding(float* dp, int64_t r, int Q, int G, int g, int nl) {
+  if (g == G - 1)
+    for (int gp = G; gp < 4 * Q; ++gp) dp[scale_index(r, Q, gp, nl)] = 0.0f;
+}
 
 __device__ __forceinline__ uint32_t native_word(const int u[8]) {
   uint32_t v = 0;
@@ -97,7 +111,11 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     words[i] = native_word(u);
   }
   qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (kb == 0) dp[tile * kTileRows + nl] = d;
+  if (kb == 0) {
+    const int Q = (G + 3) >> 2;
+    dp[scale_index(r, Q, g, nl)] = d;
+    zero_scale_padding(dp, r, Q, G, g, nl);
+  }
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc,
@@ -131,7 +149,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc
     words[i] = native_word(u);
   }
   qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (kb == 0) dp[tile * kTileRows + nl] = n < N ? dc[n * G + g] : 0.0f;
+  if (kb == 0) {
+    const int Q = (G + 3) >> 2;
+    dp[scale_index(r, Q, g, nl)] = n < N ? dc[n * G + g] : 0.0f;
+    zero_scale_padding(dp, r, Q, G, g, nl);
+  }
 }
 
 __global__ __launch_bounds__(256) void unpack_kernel(const uint4* __restrict__ qp,
@@ -161,7 +183,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4* __restrict__ q
     }
     *reinterpret_cast<uint2*>(qc + n * K + (int64_t)g * kGroup + 32 * i + 8 * kb) = make_uint2(lo, hi);
   }
-  if (kb == 0) dc[n * G + g] = dp[tile * kTileRows + nl];
+  if (kb == 0) dc[n * G + g] = dp[scale_index(r, (G + 3) >> 2, g, nl)];
 }
 
 inline int64_t tiles_of(int64_t N, int64_t K) { return ((N + kTileRows - 1) / kTileRows) * (K / kGroup); }

@@ -8,6 +8,25 @@
 
 namespace w4 {
 
+constexpr int kMaxBatch = 64;                // linears per launch (kernel arguments < 4 KiB)
+constexpr int kGemvLdsBytes = 64 * 1024;     // x slab staged in LDS by the dot2 kernel
+
+// One linear of a batch, as the kernels see it (validated by the ABI layer).
+struct LinearDesc {
+  const uint16_t* x;  // bf16 [M][K]
+  const uint8_t* q;   // native codes
+  const float* d;     // native scale quads
+  uint16_t* y;        // bf16 [M][N]
+  int M, K, N, pad;
+};
+
+// Kernel argument block: block0[i] is the first workgroup of linear i.
+struct BatchArgs {
+  int count;
+  int block0[kMaxBatch];
+  LinearDesc desc[kMaxBatch];
+};
+
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
                                float* d_packed, hipStream_t stream);
 hipError_t launch_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
@@ -15,11 +34,12 @@ hipError_t launch_pack(const int8_t* q_canon, const float* d_canon, int64_t N, i
 hipError_t launch_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
                          int8_t* q_canon, float* d_canon, hipStream_t stream);
 
-// MFMA streaming kernel: any M (16-row slabs of x per grid row).
-hipError_t launch_linear_mfma(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
-                              const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream);
-// VALU dot2 streaming kernel: any M (4-row slabs of x per grid row).
-hipError_t launch_linear_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
-                              const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream);
+// MFMA streaming kernel over a batch (16-row slabs of x).
+hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream);
+// dot2 streaming kernel over a batch (MT-row slabs of x staged in LDS; every
+// K must satisfy MT * K * 2 <= kGemvLdsBytes).
+hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream);
+// Largest slab (4, 2 or 1 rows) the dot2 kernel can stage for M rows of K.
+int gemv_rows_per_slab(int64_t M, int64_t K);
 
 }  // namespace w4

@@ -45,11 +45,12 @@
  *     k = 128g + 32i + 8(L / 16) + j, j = 0..7, as offset-binary nibbles
  *     u_j = q_j + 8:  w_i = rotl32(v, 3) where
  *     v = sum_{p=0..3} u_{2p} << 4p  +  sum_{p=0..3} u_{2p+1} << (16 + 4p).
- *   Scales: tile (r, g) owns 16 consecutive floats at index (r*G + g)*16,
- *     entry (n % 16) for row n.
- *   Rows N .. Np-1 are padding: codes 0 (u = 8) and d = 0.
+ *   Scales: let Q = ceil(G / 4).  The scales of row n for the four groups
+ *     4j .. 4j+3 form one 16-byte quad at float index ((r*Q + j)*16 + n%16)*4
+ *     (r = n / 16), group 4j+t at offset t; groups G .. 4Q-1 are padding.
+ *   Rows N .. Np-1 and padding groups hold codes 0 (u = 8) and scales 0.
  *   Total sizes: w4_packed_bytes(N, K) = Np*K/2 bytes of codes and
- *   w4_scale_count(N, K) = Np*K/128 floats of scales.
+ *   w4_scale_count(N, K) = Np*4Q floats of scales.
  *
  * CANONICAL LAYOUT (for exchange and bit-exact comparison)
  *   codes int8 [N][K] row-major, each in [-8, 7];
@@ -76,12 +77,28 @@ typedef enum {
   W4_ERR_ARG = 5     /* another invalid argument (unknown path, aliasing ...) */
 } w4_status;
 
-/* Which linear kernel w4_linear_ex runs. */
+/* Which linear kernel w4_linear_ex / w4_linear_batched run. */
 typedef enum {
-  W4_PATH_AUTO = 0,  /* the library's choice by M, N, K (what w4_linear does)  */
-  W4_PATH_GEMV = 1,  /* VALU dot-product streaming kernel, any M (slabs of 4)   */
-  W4_PATH_MFMA = 2   /* bf16 MFMA streaming kernel, any M (slabs of 16)        */
+  W4_PATH_AUTO = 0,  /* the library's choice by M and K (what w4_linear does)   */
+  W4_PATH_GEMV = 1,  /* VALU dot-product kernel, x staged in LDS in slabs of up
+                        to 4 rows; needs K <= 32768 (else W4_ERR_SHAPE)          */
+  W4_PATH_MFMA = 2   /* bf16 MFMA kernel, any M (slabs of 16 rows)             */
 } w4_path;
+
+/* Most linears one w4_linear_batched call accepts. */
+#define W4_MAX_BATCH 64
+
+/* One linear y = W_hat x of a batch (same meaning and requirements as the
+ * arguments of w4_linear). */
+typedef struct w4_linear_desc {
+  const uint16_t* x;       /* bf16 [M][K]                  */
+  int64_t M;
+  int64_t K;
+  const uint8_t* q_packed; /* native codes of the N x K W  */
+  const float* d_packed;   /* native scales                */
+  int64_t N;
+  uint16_t* y;             /* bf16 [M][N]                  */
+} w4_linear_desc;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* w4_status_str(int status);
@@ -96,7 +113,8 @@ int w4_group_size(void);
  * Returns 0 when N < 0, K <= 0 or K % 128 != 0. */
 size_t w4_packed_bytes(int64_t N, int64_t K);
 
-/* Number of native fp32 scales: roundup(N, 16) * K / 128 (0 on bad shape). */
+/* Number of native fp32 scales: roundup(N, 16) * 4 * ceil(K / 512)
+ * (0 on bad shape). */
 size_t w4_scale_count(int64_t N, int64_t K);
 
 /*
@@ -134,6 +152,21 @@ w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_pa
 w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
                        const float* d_packed, int64_t N, uint16_t* y, int path,
                        hipStream_t stream);
+
+/*
+ * w4_linear_batched -- up to W4_MAX_BATCH independent linears in ONE launch
+ * (the projections of a decode layer that read the same input -- q/k/v,
+ * gate/up -- or any set of linears with no data dependence between them).
+ * Each element obeys the w4_linear contract; inputs may be shared between
+ * elements, but no output may overlap any input or any other output
+ * (W4_ERR_ARG).  `linears` is host memory and is read before the call
+ * returns.  count == 0 does nothing.  All elements run the same kernel
+ * (`path`, W4_ERR_ARG if unknown; W4_PATH_AUTO decides from the largest M
+ * and K).  Results are bitwise identical to one w4_linear_ex call per element
+ * with the same kernel configuration.
+ */
+w4_status w4_linear_batched(const w4_linear_desc* linears, int count, int path,
+                            hipStream_t stream);
 
 /*
  * w4_pack -- canonical codes and scales -> native layout (for codes computed

@@ -53,7 +53,8 @@ def test_size_helpers(w4):
     assert lib.w4_packed_bytes(2560, 9216) == 2560 * 9216 // 2
     assert lib.w4_scale_count(2560, 9216) == 2560 * 72
     assert lib.w4_packed_bytes(37, 384) == 48 * 384 // 2  # rows padded to 16
-    assert lib.w4_scale_count(37, 384) == 48 * 3
+    assert lib.w4_scale_count(37, 384) == 48 * 4  # groups padded to whole quads of 4
+    assert lib.w4_scale_count(16, 2560) == 16 * 20
     assert lib.w4_packed_bytes(0, 128) == 0
     for N, K in ((16, 100), (16, 0), (16, -128), (-1, 128)):
         assert lib.w4_packed_bytes(N, K) == 0 and lib.w4_scale_count(N, K) == 0
@@ -86,6 +87,33 @@ def test_linear_validation(w4):
     assert _linear(lib, M=0, x=None, y=None) == OK
     assert _linear(lib, N=0, q=None, d=None, y=None) == OK
     assert lib.w4_linear(None, 0, 128, None, None, 16, None, None) == OK
+
+
+def test_batched_validation(w4):
+    lib = w4.library()
+    D = w4.LinearDesc
+    good = dict(x=FAKE, M=1, K=128, q_packed=FAKE + 0x100000, d_packed=FAKE + 0x200000, N=16,
+                y=FAKE + 0x300000)
+    arr = (D * 65)(*[D(**good) for _ in range(65)])
+    assert lib.w4_linear_batched(arr, 65, 0, None) == ERR_ARG  # more than W4_MAX_BATCH
+    assert lib.w4_linear_batched(arr, -1, 0, None) == ERR_ARG
+    assert lib.w4_linear_batched(arr, 2, 9, None) == ERR_ARG  # unknown path
+    assert lib.w4_linear_batched(None, 2, 0, None) == ERR_NULL
+    assert lib.w4_linear_batched(None, 0, 0, None) == OK
+    # two outputs that overlap each other
+    a = (D * 2)(D(**good), D(**dict(good, y=FAKE + 0x300010)))
+    assert lib.w4_linear_batched(a, 2, 0, None) == ERR_ARG
+    # an output that overlaps another element's input
+    a = (D * 2)(D(**good), D(**dict(good, x=FAKE + 0x400000, y=FAKE)))
+    assert lib.w4_linear_batched(a, 2, 0, None) == ERR_ARG
+    # the first bad element's status is returned, nothing is launched
+    a = (D * 2)(D(**good), D(**dict(good, K=100)))
+    assert lib.w4_linear_batched(a, 2, 0, None) == ERR_SHAPE
+    a = (D * 2)(D(**dict(good, M=0)), D(**dict(good, q_packed=None)))
+    assert lib.w4_linear_batched(a, 2, 0, None) == ERR_NULL
+    # the dot2 kernel stages x in 64 KiB of LDS: K above 32768 is refused for it
+    big = (D * 1)(D(**dict(good, K=32896)))
+    assert lib.w4_linear_batched(big, 1, 1, None) == ERR_SHAPE
 
 
 def test_quantize_pack_unpack_validation(w4):

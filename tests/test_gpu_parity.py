@@ -127,9 +127,10 @@ def test_pack_unpack_roundtrip(w4, gpu):
     q, d = w4.pack(qc, dc)
     qc2, dc2 = w4.unpack(q, d, 45, 640)
     assert torch.equal(qc2, qc) and torch.equal(dc2.view(torch.int32), dc.view(torch.int32))
-    # padding rows of the native layout are code 0 / scale 0
-    dn = d.view(-1, 5, 16)[2]  # row block 2 holds rows 32..47
-    assert torch.all(dn[:, 13:] == 0)
+    # padding rows (45..47) and padding groups (5..7) of the native layout hold scale 0
+    dn = d.view(3, 2, 16, 4)  # [row block][scale quad][row in block][group in quad]
+    assert torch.all(dn[2, :, 13:, :] == 0)
+    assert torch.all(dn[:, 1, :, 1:] == 0)
     # quantize output re-packed from its canonical form is identical
     W = torch.from_numpy(workloads.random_weight(45, 640, seed=3)).to(gpu)
     q1, d1 = w4.quantize_rtn(W)
@@ -265,3 +266,57 @@ def test_linear_empty_is_noop(w4, gpu):
     assert y.shape == (0, 16)
     y = w4.linear(torch.zeros((2, 128), dtype=torch.bfloat16, device=gpu), q, d, 0)
     assert y.shape == (2, 0)
+
+
+# ----------------------------------------------------------------------------
+# batched launches
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_linear_batched_matches_single_calls(w4, gpu, path, monkeypatch):
+    """A decode layer's seven projections in one launch: bitwise equal to one call each
+    (same kernel configuration), and within tolerance of the oracle."""
+    monkeypatch.setenv("W4_MFMA_CFG", "1,8")
+    monkeypatch.setenv("W4_GEMV_CFG", "1,8")
+    shapes = [("q", 320, 512), ("k", 64, 512), ("v", 64, 512), ("o", 512, 320 + 64),
+              ("gate", 700, 512), ("up", 700, 512), ("down", 512, 1408)]
+    for M in (1, 3, 8):
+        _say(f"batched layer M={M} path={path}")
+        items, refs = [], []
+        x_attn = workloads.random_activations(M, 512, seed=M, device=gpu)
+        for i, (name, N, K) in enumerate(shapes):
+            W = torch.from_numpy(workloads.random_weight(N, K, seed=100 + i)).to(gpu)
+            q, d = w4.quantize_rtn(W)
+            x = x_attn if K == 512 else workloads.random_activations(M, K, seed=M + i, device=gpu)
+            items.append((x, q, d, N, torch.empty((M, N), dtype=torch.bfloat16, device=gpu)))
+            refs.append(W.cpu().numpy())
+        ys = w4.linear_batched(items, path=path)
+        for (x, q, d, N, _), y, Wh, (name, _, _) in zip(items, ys, refs, shapes):
+            y1 = w4.linear(x, q, d, N, path=path)
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"{name}: batched != single"
+            q_ref, d_ref = oracle.rtn_quantize_ref(Wh)
+            y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+            check_y(y, y_ref, absdot, f"batched {name} M={M}")
+
+
+def test_linear_batched_full_size_layer(w4, gpu):
+    """One 70B-class layer (seven full-size matrices) in one launch at M = 1 and 16."""
+    wl = workloads.WORKLOADS["stack_70b"]
+    mats = []
+    for m in wl.matrices:
+        W = workloads.weight("stack_70b", 3, m.name, gpu)
+        q, d = w4.quantize_rtn(W)
+        rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(7).choice(m.N, 62)]))
+        idx = torch.as_tensor(rows, device=gpu)
+        mats.append((m, q, d, idx, oracle.rtn_quantize_ref(W.index_select(0, idx).cpu().numpy())))
+        del W
+    for M in (1, 16):
+        _say(f"batched 70b layer M={M}")
+        items = []
+        for (m, q, d, idx, _) in mats:
+            x = workloads.activations("stack_70b", 3, m.name, M, gpu)
+            items.append((x, q, d, m.N, torch.empty((M, m.N), dtype=torch.bfloat16, device=gpu)))
+        ys = w4.linear_batched(items)
+        for (m, q, d, idx, (q_ref, d_ref)), (x, *_), y in zip(mats, items, ys):
+            y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+            check_y(y.index_select(1, idx), y_ref, absdot, f"70b batched {m.name} M={M}")
