@@ -92,27 +92,42 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
     for M in wl.ms:
         xs = [workloads.activations(HEADLINE, 0, m.name, M, dev) for (m, _, _, _) in mats]
         ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
+        # batched mode: every linear of a step writes its own output
+        ysb = [[torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
+               for _ in range(copies)]
 
         def step():
             for c in range(copies):
                 for i, (m, _, qs, ds) in enumerate(mats):
                     w4.linear(xs[i], qs[c], ds[c], m.N, out=ys[i])
 
-        g = capture(torch, step)
-        t = time_graph(torch, g, steps, warmup)
-        launches = steps * copies * len(mats)
+        def step_batched():
+            items = [(xs[i], qs[c], ds[c], m.N, ysb[c][i])
+                     for c in range(copies) for i, (m, _, qs, ds) in enumerate(mats)]
+            for b in range(0, len(items), w4.MAX_BATCH):
+                w4.linear_batched(items[b:b + w4.MAX_BATCH])
+
         step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats)
-        gbs = steps * step_bytes / t / 1e9
-        out[M] = {
-            "GBps": round(gbs, 1),
-            "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-            "us_per_call": round(t / launches * 1e6, 3),
-            "ms_per_step": round(t / steps * 1e3, 4),
-            "bytes_per_call": {m.name: workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats},
-            "launches_per_step": copies * len(mats),
-        }
-        log(f"[bench] {HEADLINE} M={M}: {gbs:.0f} GB/s, {t / launches * 1e6:.2f} us/call")
-        del g
+        res = {}
+        for mode, fn in (("per_call", step), ("batched", step_batched)):
+            g = capture(torch, fn)
+            t = time_graph(torch, g, steps, warmup)
+            launches = steps * (copies * len(mats) if mode == "per_call"
+                                else -(-copies * len(mats) // w4.MAX_BATCH))
+            gbs = steps * step_bytes / t / 1e9
+            res[mode] = {
+                "GBps": round(gbs, 1),
+                "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                "us_per_launch": round(t / launches * 1e6, 3),
+                "us_per_linear": round(t / (steps * copies * len(mats)) * 1e6, 3),
+                "ms_per_step": round(t / steps * 1e3, 4),
+                "launches_per_step": launches // steps,
+            }
+            log(f"[bench] {HEADLINE} M={M} {mode}: {gbs:.0f} GB/s, "
+                f"{t / (steps * copies * len(mats)) * 1e6:.2f} us per linear")
+            del g
+        res["bytes_per_call"] = {m.name: workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats}
+        out[M] = res
     # quantization throughput (rows a1-a4), same matrices, rotated over 4 fp32 copies
     qout = {}
     for (m, W, qs, ds) in mats:
@@ -139,6 +154,18 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
 # layer stacks: one graph = one decode (or verify) pass over every linear
 # ----------------------------------------------------------------------------
 
+def _shared_input_groups(wl):
+    """Matrices of one layer grouped by the input they read (q|k|v, o, gate|up, down)."""
+    order, by_tag = [], {}
+    for i, m in enumerate(wl.matrices):
+        tag = wl.input_groups.get(m.name, m.name)
+        if tag not in by_tag:
+            by_tag[tag] = []
+            order.append(tag)
+        by_tag[tag].append(i)
+    return [by_tag[t] for t in order]
+
+
 def bench_stack(torch, w4, workloads, name, steps, warmup):
     dev = torch.device("cuda:0")
     wl = workloads.WORKLOADS[name]
@@ -156,26 +183,37 @@ def bench_stack(torch, w4, workloads, name, steps, warmup):
     torch.cuda.empty_cache()
     log(f"[bench] stack {name}: {wl.layers} layers quantized in {time.time() - t0:.1f}s")
     res = {}
+    groups = {"per_call": [[i] for i in range(len(wl.matrices))],
+              "fused_shared_input": _shared_input_groups(wl),
+              "layer_batched": [list(range(len(wl.matrices)))]}
     for M in wl.ms:
         xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
-        ys = {m.N: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+        ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices]
+        res[M] = {}
+        for mode, grp in groups.items():
+            def step():
+                for mats in layers:
+                    for gi in grp:
+                        if len(gi) == 1:
+                            m, q, d = mats[gi[0]]
+                            w4.linear(xs[m.K], q, d, m.N, out=ys[gi[0]])
+                        else:
+                            w4.linear_batched([(xs[mats[i][0].K], mats[i][1], mats[i][2], mats[i][0].N, ys[i])
+                                               for i in gi])
 
-        def step():
-            for mats in layers:
-                for (m, q, d) in mats:
-                    w4.linear(xs[m.K], q, d, m.N, out=ys[m.N])
-
-        g = capture(torch, step)
-        t = time_graph(torch, g, steps, warmup)
-        per = t / steps
-        nbytes = workloads.stack_bytes(name, M)
-        gbs = nbytes / per / 1e9
-        res[M] = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1),
-                  "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-                  "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(M / per, 1),
-                  "bytes_per_pass": nbytes, "launches_per_pass": len(layers) * len(wl.matrices)}
-        log(f"[bench] stack {name} M={M}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s")
-        del g
+            g = capture(torch, step)
+            t = time_graph(torch, g, steps, warmup)
+            per = t / steps
+            nbytes = workloads.stack_bytes(name, M)
+            gbs = nbytes / per / 1e9
+            res[M][mode] = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1),
+                            "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                            "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(M / per, 1),
+                            "launches_per_pass": len(layers) * len(grp)}
+            log(f"[bench] stack {name} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
+                f"{1 / per:.1f} passes/s")
+            del g
+        res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M)
     del layers
     torch.cuda.empty_cache()
     return res
@@ -221,8 +259,8 @@ def cpu_baseline(workloads, budget_s=12.0):
 
 # ----------------------------------------------------------------------------
 
-def roofline(pair_m1, copies, steps):
-    """Dominant kernel: the MFMA linear at M = 1 on the headline pair."""
+def roofline(pair_m1, bytes_per_call):
+    """Dominant kernel: the M = 1 linear on the headline pair, one launch per call."""
     achieved = pair_m1["GBps"]
     traffic = None
     if os.path.exists(COUNTERS_FILE):
@@ -232,9 +270,47 @@ def roofline(pair_m1, copies, steps):
             traffic = c.get("hbm_bytes_per_call")
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "linear_mfma_kernel (M=1)",
-            "algorithmic_bytes_per_call": pair_m1["bytes_per_call"],
-            "avg_launch_us": pair_m1["us_per_call"]}
+            "kernel": "linear_gemv_kernel<1,1,4> (M=1, dot2, x in LDS)",
+            "algorithmic_bytes_per_call": bytes_per_call,
+            "avg_launch_us": pair_m1["us_per_launch"]}
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 output summaries (used to write the text files under profiles/)
+# ----------------------------------------------------------------------------
+
+def summarize_trace(path):
+    """Per (kernel, grid, block) duration statistics from a rocprofv3 kernel_trace.csv."""
+    import csv
+    import statistics
+
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].replace("w4::(anonymous namespace)::", "")
+        key = (name[:70], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])), int(r["Grid_Size_Y"]),
+               int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| kernel | blocks | grid y | block | calls | avg us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {key[0]} | {key[1]} | {key[2]} | {key[3]} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
+              f"{statistics.median(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+
+
+def summarize_counters(path):
+    """Mean of each counter per (kernel, grid) from a rocprofv3 counter_collection.csv."""
+    import csv
+    import statistics
+
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].replace("w4::(anonymous namespace)::", "")[:70]
+        grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)))
+        groups.setdefault((name, grid, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    print("| kernel | grid (threads) | counter | dispatches | mean per dispatch |")
+    print("|---|---|---|---|---|")
+    for (name, grid, cn), v in sorted(groups.items()):
+        print(f"| {name} | {grid} | {cn} | {len(v)} | {statistics.mean(v):.1f} |")
 
 
 def main():
@@ -247,7 +323,18 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run the plain copy kernel on this many MiB (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print a duration summary of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--counter-summary", metavar="COUNTER_COLLECTION_CSV",
+                    help="print a summary of a rocprofv3 counter collection and exit")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        summarize_trace(args.trace_summary)
+        return
+    if args.counter_summary:
+        summarize_counters(args.counter_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -288,7 +375,7 @@ def main():
     torch.cuda.synchronize()
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
-    m1 = pair[1]
+    m1 = pair[1]["per_call"]
     line = {
         "metric": METRIC,
         "value": m1["GBps"],
@@ -306,11 +393,11 @@ def main():
                    "weight_copies": args.copies, "group": 128, "weights": "int4 codes + fp32 scales",
                    "x": "bf16", "timing": "hip graph replay, events on the replay stream"},
         "pct_of_peak": m1["pct_of_peak"],
-        "us_per_call": m1["us_per_call"],
-        "m8": pair.get(8),
+        "us_per_call": m1["us_per_linear"],
+        "pair": pair,
         "quantize": quant,
         "stacks": stacks,
-        "roofline": roofline(m1, args.copies, args.steps),
+        "roofline": roofline(m1, pair[1]["bytes_per_call"]),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -26,11 +26,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Kernel used by w4_linear for a shape.  The MFMA kernel needs fewer VALU
-// instructions per weight than the dot2 kernel at every M (one 16x16x32 MFMA
-// replaces 16 dot2 per row of x), so it is the default everywhere.
+// Kernel used by w4_linear for a shape.  At M = 1 the dot2 kernel, which
+// stages x in LDS and so issues no x loads through the vector memory
+// pipeline, measured faster on every projection shape; from M = 2 on, the
+// dot products grow with M while one MFMA serves 16 rows of x.
 int auto_path(int64_t M, int64_t K) {
-  (void)M; (void)K;
+  if (M == 1 && w4::gemv_lds_bytes(1, K) <= w4::kGemvLdsBytes) return W4_PATH_GEMV;
   return W4_PATH_MFMA;
 }
 
@@ -80,7 +81,7 @@ w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, hi
   if (a.count == 0) return W4_OK;
   if (path == W4_PATH_AUTO) path = auto_path(max_m, max_k);
   if (path == W4_PATH_GEMV) {
-    if (2 * max_k > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
+    if (w4::gemv_lds_bytes(1, max_k) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
     return hip_status(w4::launch_linear_gemv(a, w4::gemv_rows_per_slab(max_m, max_k), stream));
   }
   return hip_status(w4::launch_linear_mfma(a, stream));
@@ -108,7 +109,7 @@ int w4_group_size(void) { return (int)kGroup; }
 
 size_t w4_packed_bytes(int64_t N, int64_t K) {
   if (!n_ok(N) || !k_ok(K)) return 0;
-  return (size_t)padded_rows(N) * (size_t)K / 2;
+  return (size_t)padded_rows(N) * (size_t)((K + 511) / 512 * 512) / 2;
 }
 
 size_t w4_scale_count(int64_t N, int64_t K) {

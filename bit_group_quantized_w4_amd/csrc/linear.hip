@@ -89,23 +89,21 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
   const LinearDesc& D = args.desc[wk.di];
   const int M = D.M, K = D.K, N = D.N;
   const int G = K / kGroup;
-  const int Q = (G + 3) >> 2;
+  const int Q = (G + 3) >> 2;  // scale quads; the native layout pads G to 4Q groups
   const int nb = (N + kTileRows - 1) / kTileRows;
   const int rvalid = min(R, nb - wk.rb0);
   const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
 
   const int xrow = min(wk.m0 + nl, M - 1);
   const uint4* xs = reinterpret_cast<const uint4*>(D.x + (int64_t)xrow * K) + kb;
-  const uint4* qp = reinterpret_cast<const uint4*>(D.q);
-  const uint4* dq = reinterpret_cast<const uint4*>(D.d);
-  // Row blocks past the end of the matrix re-read the last one (never stored);
-  // padding groups of the last quad re-read group G-1 and carry scale 0.
-  int64_t rowq[R], rows[R];
+  // Row blocks past the end of the matrix re-read the last one (never stored).
+  const uint4* qrow[R];
+  const uint4* srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int rb = min(wk.rb0 + r, nb - 1);
-    rowq[r] = (int64_t)rb * G * kTileLanes + lane;
-    rows[r] = (int64_t)rb * Q * kTileRows + nl;
+    const int64_t rb = min(wk.rb0 + r, nb - 1);
+    qrow[r] = reinterpret_cast<const uint4*>(D.q) + rb * (4 * Q) * kTileLanes + lane;
+    srow[r] = reinterpret_cast<const uint4*>(D.d) + rb * Q * kTileRows + nl;
   }
 
   uint4 bx[kRing][4];
@@ -113,15 +111,15 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
   uint4 sc[R], sn[R];  // scale quads: current and next
 
   auto issue_group = [&](int s, int g) {
-    const int gc = min(g, G - 1);
+    const int gx = min(g, G - 1);  // padding groups: any valid x (their scale is 0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bx[s][i] = xs[gc * 16 + i * 4];
+    for (int i = 0; i < 4; ++i) bx[s][i] = xs[gx * 16 + i * 4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qp + rowq[r] + (int64_t)gc * kTileLanes);
+    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qrow[r] + g * kTileLanes);
   };
   auto issue_scales = [&](uint4 (&dst)[R], int j) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = load_stream(dq + rows[r] + (int64_t)j * kTileRows);
+    for (int r = 0; r < R; ++r) dst[r] = load_stream(srow[r] + j * kTileRows);
   };
 
   const UnpackConsts uc = unpack_consts();
@@ -213,7 +211,9 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
 // ---------------------------------------------------------------------------
 template <int MT, int R, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
-  extern __shared__ uint4 xlds[];  // [MT][K/8] uint4
+  // LDS: x of the slab, [MT][4Q * 16] uint4 (zero past K), then the start
+  // values -1.5 * sum(x) of every (row, group, quarter), [MT][4Q][4] floats.
+  extern __shared__ uint4 xlds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
   const Work wk = locate(args, R, MT);
@@ -221,29 +221,28 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
   const int M = D.M, K = D.K, N = D.N;
   const int G = K / kGroup;
   const int Q = (G + 3) >> 2;
+  const int GP = 4 * Q;
   const int nb = (N + kTileRows - 1) / kTileRows;
   const int rvalid = min(R, nb - wk.rb0);
   const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
-  const uint4* qp = reinterpret_cast<const uint4*>(D.q);
-  const uint4* dq = reinterpret_cast<const uint4*>(D.d);
-  int64_t rowq[R], rows[R];
+  const uint4* qrow[R];
+  const uint4* srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int rb = min(wk.rb0 + r, nb - 1);
-    rowq[r] = (int64_t)rb * G * kTileLanes + lane;
-    rows[r] = (int64_t)rb * Q * kTileRows + nl;
+    const int64_t rb = min(wk.rb0 + r, nb - 1);
+    qrow[r] = reinterpret_cast<const uint4*>(D.q) + rb * GP * kTileLanes + lane;
+    srow[r] = reinterpret_cast<const uint4*>(D.d) + rb * Q * kTileRows + nl;
   }
 
   uint4 bw[kRing][R];
   uint4 sc[R], sn[R];
   auto issue_group = [&](int s, int g) {
-    const int gc = min(g, G - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qp + rowq[r] + (int64_t)gc * kTileLanes);
+    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qrow[r] + g * kTileLanes);
   };
   auto issue_scales = [&](uint4 (&dst)[R], int j) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = load_stream(dq + rows[r] + (int64_t)j * kTileRows);
+    for (int r = 0; r < R; ++r) dst[r] = load_stream(srow[r] + j * kTileRows);
   };
   if (j0 < j1) {
     issue_scales(sc, j0);
@@ -251,17 +250,38 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
     for (int s = 0; s < kRing; ++s) issue_group(s, 4 * j0 + s);
   }
 
-  // stage this slab's x rows (rows beyond M repeat row M-1; their outputs are dropped)
-  const int kq = K / 8;  // uint4 per row
-  for (int e = threadIdx.x; e < MT * kq; e += NW * 64) {
-    const int mm = e / kq;
-    const int row = min(wk.m0 + mm, M - 1);
-    xlds[e] = reinterpret_cast<const uint4*>(D.x + (int64_t)row * K)[e - mm * kq];
+  const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
+
+  // Stage the slab's x rows (rows beyond M repeat row M-1; their outputs are
+  // dropped) together with the start value of every (row, group, quarter).
+  float* offs = reinterpret_cast<float*>(xlds + MT * GP * 16);
+  for (int e = threadIdx.x; e < MT * GP * 4; e += NW * 64) {
+    const int mm = e / (GP * 4);
+    const int rem = e - mm * GP * 4;
+    const int g = rem >> 2, q4 = rem & 3;
+    uint4 v[4];
+    if (g < G) {
+      const uint4* src = reinterpret_cast<const uint4*>(D.x + (int64_t)min(wk.m0 + mm, M - 1) * K) + g * 16 + q4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = src[i * 4];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    }
+    float c = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c = dot2(v[i].x, kneg2, c);
+      c = dot2(v[i].y, kneg2, c);
+      c = dot2(v[i].z, kneg2, c);
+      c = dot2(v[i].w, kneg2, c);
+      xlds[(mm * GP + g) * 16 + i * 4 + q4] = v[i];
+    }
+    offs[(mm * GP + g) * 4 + q4] = c;
   }
   __syncthreads();
 
   const UnpackConsts uc = unpack_consts();
-  const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
 
   float acc[R][MT];
 #pragma unroll
@@ -270,23 +290,17 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
     for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.f;
 
   auto compute = [&](int s, int g) {
-    const int gc = min(g, G - 1);  // padding groups: any valid x, scale 0
     uint32_t xv[MT][16];
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 t = xlds[mm * kq + gc * 16 + i * 4 + kb];
-        xv[mm][4 * i + 0] = t.x; xv[mm][4 * i + 1] = t.y;
-        xv[mm][4 * i + 2] = t.z; xv[mm][4 * i + 3] = t.w;
-      }
     float c0[MT];
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
-      float c = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) c = dot2(xv[mm][e], kneg2, c);
-      c0[mm] = c;
+      for (int i = 0; i < 4; ++i) {
+        const uint4 t = xlds[(mm * GP + g) * 16 + i * 4 + kb];
+        xv[mm][4 * i + 0] = t.x; xv[mm][4 * i + 1] = t.y;
+        xv[mm][4 * i + 2] = t.z; xv[mm][4 * i + 3] = t.w;
+      }
+      c0[mm] = offs[(mm * GP + g) * 4 + kb];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -382,19 +396,25 @@ int find_cfg(int R, int NW) {
   return 0;
 }
 
-// Built-in choice from the batch's total row blocks and largest K: enough
-// wavefronts in flight on all 256 CUs, whole scale quads per wavefront.
-int choose_cfg(const BatchArgs& a) {
+// Built-in choices, from graph-replayed sweeps of every (R, NW) on MI355X over
+// the 4B/27B/70B-class projection shapes: enough wavefronts in flight on all
+// 256 CUs for the batch's total row blocks, more wavefronts per block when K
+// is long.
+int choose_cfg_mfma(const BatchArgs& a) {
+  int64_t rows = 0;
+  for (int i = 0; i < a.count; ++i) rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
+  return rows >= 384 ? find_cfg(2, 4) : find_cfg(1, 4);
+}
+
+int choose_cfg_gemv(const BatchArgs& a) {
   int64_t rows = 0;
   int kmax = 0;
   for (int i = 0; i < a.count; ++i) {
     rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
     kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   }
-  const int quads = (kmax / kGroup + 3) / 4;
-  if (rows >= 2048) return find_cfg(2, quads >= 32 ? 8 : 4);
-  if (rows >= 512) return find_cfg(1, quads >= 16 ? 8 : 4);
-  return find_cfg(1, quads >= 32 ? 16 : 8);
+  if (rows < 256) return find_cfg(1, 8);
+  return find_cfg(1, kmax >= 16384 ? 8 : 4);
 }
 
 int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
@@ -413,7 +433,7 @@ int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
 
 hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
   const int env = cfg_from_env("W4_MFMA_CFG");
-  const int ci = env >= 0 ? env : choose_cfg(a);
+  const int ci = env >= 0 ? env : choose_cfg_mfma(a);
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, 16);
   if (blocks <= 0) return hipSuccess;
@@ -430,15 +450,14 @@ hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
 }
 
 int gemv_rows_per_slab(int64_t M, int64_t K) {
-  // x of one slab lives in LDS: MT * K * 2 bytes, at most kGemvLdsBytes.
   for (int mt = 4; mt > 1; mt >>= 1)
-    if (M >= mt && (int64_t)mt * K * 2 <= kGemvLdsBytes) return mt;
+    if (M >= mt && gemv_lds_bytes(mt, K) <= kGemvLdsBytes) return mt;
   return 1;
 }
 
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
   const int env = cfg_from_env("W4_GEMV_CFG");
-  int ci = env >= 0 ? env : choose_cfg(a);
+  int ci = env >= 0 ? env : choose_cfg_gemv(a);
   if (MT == 4 && kCfgs[ci].NW == 16) ci = find_cfg(1, 8);  // 16 wavefronts x 4 rows exceeds 128 VGPRs
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, MT);
@@ -446,7 +465,7 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   int kmax = 0;
   for (int i = 0; i < a.count; ++i) kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
-  const size_t lds = (size_t)MT * kmax * 2;
+  const size_t lds = (size_t)gemv_lds_bytes(MT, kmax);
 #define W4_LAUNCH(mt, i)                                                                          \
   linear_gemv_kernel<mt, kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, lds, stream>>>(a)
 #define W4_CASES(mt)                                 \

@@ -14,6 +14,8 @@
 // 32-input steps), the group max is finished across the four lanes that share
 // a row, and the lane writes its 16 bytes of codes; the 16 scales of the tile
 // are written by the lanes of the first quarter into their rows' scale quads.
+// Tiles of the padding rows (N .. Np-1) and padding groups (G .. 4Q-1) are
+// written as code 0 with scale 0.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -24,18 +26,29 @@ namespace {
 
 constexpr int kTilesPerBlock = 4;  // one tile per wavefront, 4 wavefronts per block
 
-// Native scale layout: the scales of row n for the four consecutive groups
-// 4j .. 4j+3 are one 16-byte quad, quad (r, j) of row block r holding rows
-// 16r .. 16r+15 in order; the group count is padded to a multiple of 4 with
-// zero scales.
-__device__ __forceinline__ int64_t scale_index(int64_t r, int Q, int g, int nl) {
-  return ((r * Q + (g >> 2)) * kTileRows + nl) * 4 + (g & 3);
+// Tile (r, g) of the native layout, g < GP = 4 * ceil(G / 4).
+struct TileAt {
+  int64_t tile, r;
+  int g, nl, kb, lane;
+  int64_t n;
+};
+
+__device__ __forceinline__ bool tile_at(int64_t ntiles, int GP, TileAt& t) {
+  t.tile = (int64_t)blockIdx.x * kTilesPerBlock + (threadIdx.x >> 6);
+  if (t.tile >= ntiles) return false;
+  t.lane = threadIdx.x & 63;
+  t.nl = t.lane & 15;
+  t.kb = t.lane >> 4;
+  t.r = t.tile / GP;
+  t.g = (int)(t.tile - t.r * GP);
+  t.n = t.r * kTileRows + t.nl;
+  return true;
 }
 
-// Zero scales of the padding groups G .. 4Q-1 (written by the last group's tile).
-__device__ __forceinline__ void zero_scale_padding(float* dp, int64_t r, int Q, int G, int g, int nl) {
-  if (g == G - 1)
-    for (int gp = G; gp < 4 * Q; ++gp) dp[scale_index(r, Q, gp, nl)] = 0.0f;
+// Scales of row n for groups 4j .. 4j+3 form one 16-byte quad; quad (r, j)
+// of row block r holds rows 16r .. 16r+15 in order.
+__device__ __forceinline__ int64_t scale_index(int64_t r, int GP, int g, int nl) {
+  return ((r * (GP >> 2) + (g >> 2)) * kTileRows + nl) * 4 + (g & 3);
 }
 
 __device__ __forceinline__ uint32_t native_word(const int u[8]) {
@@ -45,22 +58,30 @@ __device__ __forceinline__ uint32_t native_word(const int u[8]) {
   return rotl32(v, 3);
 }
 
+__device__ __forceinline__ uint4 zero_code_lane() {
+  int u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = 8;
+  const uint32_t w = native_word(u);
+  return make_uint4(w, w, w, w);
+}
+
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restrict__ W, int N,
-                                                           int K, int G, int64_t ntiles,
+                                                           int K, int G, int GP, int64_t ntiles,
                                                            uint4* __restrict__ qp,
                                                            float* __restrict__ dp) {
 #pragma clang fp contract(off)
-  const int64_t tile = (int64_t)blockIdx.x * kTilesPerBlock + (threadIdx.x >> 6);
-  if (tile >= ntiles) return;
-  const int lane = threadIdx.x & 63;
-  const int nl = lane & 15, kb = lane >> 4;
-  const int64_t r = tile / G;
-  const int g = (int)(tile - r * G);
-  const int64_t n = r * kTileRows + nl;
+  TileAt t;
+  if (!tile_at(ntiles, GP, t)) return;
+  if (t.g >= G) {  // padding group
+    qp[t.tile * kTileLanes + t.lane] = zero_code_lane();
+    if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = 0.0f;
+    return;
+  }
 
   float v[32];
-  if (n < N) {
-    const float4* src = reinterpret_cast<const float4*>(W + n * K + (int64_t)g * kGroup + 8 * kb);
+  if (t.n < N) {
+    const float4* src = reinterpret_cast<const float4*>(W + t.n * K + (int64_t)t.g * kGroup + 8 * t.kb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 a = src[8 * i];
@@ -100,9 +121,9 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     for (int j = 0; j < 8; ++j) {
       int code = 0;
       if (usable) {
-        const float t = v[8 * i + j] / d;  // IEEE fp32 quotient by the stored scale
-        float rr = truncf(t);
-        if (fabsf(t - rr) >= 0.5f) rr += copysignf(1.0f, t);  // ties away from zero
+        const float q = v[8 * i + j] / d;  // IEEE fp32 quotient by the stored scale
+        float rr = truncf(q);
+        if (fabsf(q - rr) >= 0.5f) rr += copysignf(1.0f, q);  // ties away from zero
         rr = fminf(fmaxf(rr, -8.0f), 7.0f);
         code = (int)rr;
       }
@@ -110,32 +131,23 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     }
     words[i] = native_word(u);
   }
-  qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (kb == 0) {
-    const int Q = (G + 3) >> 2;
-    dp[scale_index(r, Q, g, nl)] = d;
-    zero_scale_padding(dp, r, Q, G, g, nl);
-  }
+  qp[t.tile * kTileLanes + t.lane] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = d;
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc,
                                                    const float* __restrict__ dc, int N, int K,
-                                                   int G, int64_t ntiles, uint4* __restrict__ qp,
-                                                   float* __restrict__ dp) {
-  const int64_t tile = (int64_t)blockIdx.x * kTilesPerBlock + (threadIdx.x >> 6);
-  if (tile >= ntiles) return;
-  const int lane = threadIdx.x & 63;
-  const int nl = lane & 15, kb = lane >> 4;
-  const int64_t r = tile / G;
-  const int g = (int)(tile - r * G);
-  const int64_t n = r * kTileRows + nl;
-
+                                                   int G, int GP, int64_t ntiles,
+                                                   uint4* __restrict__ qp, float* __restrict__ dp) {
+  TileAt t;
+  if (!tile_at(ntiles, GP, t)) return;
+  const bool real = t.n < N && t.g < G;
   uint32_t words[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int u[8];
-    if (n < N) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(qc + n * K + (int64_t)g * kGroup + 32 * i + 8 * kb);
+    if (real) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(qc + t.n * K + (int64_t)t.g * kGroup + 32 * i + 8 * t.kb);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t wv = j < 4 ? raw.x : raw.y;
@@ -148,28 +160,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc
     }
     words[i] = native_word(u);
   }
-  qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (kb == 0) {
-    const int Q = (G + 3) >> 2;
-    dp[scale_index(r, Q, g, nl)] = n < N ? dc[n * G + g] : 0.0f;
-    zero_scale_padding(dp, r, Q, G, g, nl);
-  }
+  qp[t.tile * kTileLanes + t.lane] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = real ? dc[t.n * G + t.g] : 0.0f;
 }
 
 __global__ __launch_bounds__(256) void unpack_kernel(const uint4* __restrict__ qp,
                                                      const float* __restrict__ dp, int N, int K,
-                                                     int G, int64_t ntiles, int8_t* __restrict__ qc,
-                                                     float* __restrict__ dc) {
-  const int64_t tile = (int64_t)blockIdx.x * kTilesPerBlock + (threadIdx.x >> 6);
-  if (tile >= ntiles) return;
-  const int lane = threadIdx.x & 63;
-  const int nl = lane & 15, kb = lane >> 4;
-  const int64_t r = tile / G;
-  const int g = (int)(tile - r * G);
-  const int64_t n = r * kTileRows + nl;
-  if (n >= N) return;
-
-  const uint4 wq = qp[tile * kTileLanes + lane];
+                                                     int G, int GP, int64_t ntiles,
+                                                     int8_t* __restrict__ qc, float* __restrict__ dc) {
+  TileAt t;
+  if (!tile_at(ntiles, GP, t)) return;
+  if (t.n >= N || t.g >= G) return;
+  const uint4 wq = qp[t.tile * kTileLanes + t.lane];
   const uint32_t w4v[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -181,39 +183,49 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4* __restrict__ q
       if (j < 4) lo |= code << (8 * j);
       else hi |= code << (8 * (j - 4));
     }
-    *reinterpret_cast<uint2*>(qc + n * K + (int64_t)g * kGroup + 32 * i + 8 * kb) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(qc + t.n * K + (int64_t)t.g * kGroup + 32 * i + 8 * t.kb) = make_uint2(lo, hi);
   }
-  if (kb == 0) dc[n * G + g] = dp[scale_index(r, (G + 3) >> 2, g, nl)];
+  if (t.kb == 0) dc[t.n * G + t.g] = dp[scale_index(t.r, GP, t.g, t.nl)];
 }
 
-inline int64_t tiles_of(int64_t N, int64_t K) { return ((N + kTileRows - 1) / kTileRows) * (K / kGroup); }
-inline unsigned blocks_of(int64_t ntiles) { return (unsigned)((ntiles + kTilesPerBlock - 1) / kTilesPerBlock); }
+struct Grid {
+  int G, GP;
+  int64_t ntiles;
+  unsigned blocks;
+};
+
+inline Grid grid_of(int64_t N, int64_t K) {
+  Grid g;
+  g.G = (int)(K / kGroup);
+  g.GP = (g.G + 3) / 4 * 4;
+  g.ntiles = ((N + kTileRows - 1) / kTileRows) * g.GP;
+  g.blocks = (unsigned)((g.ntiles + kTilesPerBlock - 1) / kTilesPerBlock);
+  return g;
+}
 
 }  // namespace
 
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
                                float* d_packed, hipStream_t stream) {
-  const int64_t nt = tiles_of(N, K);
-  quantize_rtn_kernel<<<blocks_of(nt), 256, 0, stream>>>(
-      W, (int)N, (int)K, (int)(K / kGroup), nt, reinterpret_cast<uint4*>(q_packed), d_packed);
+  const Grid g = grid_of(N, K);
+  quantize_rtn_kernel<<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles,
+                                                     reinterpret_cast<uint4*>(q_packed), d_packed);
   return hipGetLastError();
 }
 
 hipError_t launch_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
                        uint8_t* q_packed, float* d_packed, hipStream_t stream) {
-  const int64_t nt = tiles_of(N, K);
-  pack_kernel<<<blocks_of(nt), 256, 0, stream>>>(q_canon, d_canon, (int)N, (int)K,
-                                                 (int)(K / kGroup), nt,
-                                                 reinterpret_cast<uint4*>(q_packed), d_packed);
+  const Grid g = grid_of(N, K);
+  pack_kernel<<<g.blocks, 256, 0, stream>>>(q_canon, d_canon, (int)N, (int)K, g.G, g.GP, g.ntiles,
+                                            reinterpret_cast<uint4*>(q_packed), d_packed);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
                          int8_t* q_canon, float* d_canon, hipStream_t stream) {
-  const int64_t nt = tiles_of(N, K);
-  unpack_kernel<<<blocks_of(nt), 256, 0, stream>>>(reinterpret_cast<const uint4*>(q_packed),
-                                                   d_packed, (int)N, (int)K, (int)(K / kGroup),
-                                                   nt, q_canon, d_canon);
+  const Grid g = grid_of(N, K);
+  unpack_kernel<<<g.blocks, 256, 0, stream>>>(reinterpret_cast<const uint4*>(q_packed), d_packed,
+                                              (int)N, (int)K, g.G, g.GP, g.ntiles, q_canon, d_canon);
   return hipGetLastError();
 }
 

@@ -11,6 +11,14 @@ namespace w4 {
 constexpr int kMaxBatch = 64;                // linears per launch (kernel arguments < 4 KiB)
 constexpr int kGemvLdsBytes = 64 * 1024;     // x slab staged in LDS by the dot2 kernel
 
+// LDS the dot2 kernel needs for an MT-row slab of x with K inputs: the x rows
+// padded to whole scale quads (512 inputs) plus one float per (row, group,
+// quarter of a group).
+inline int64_t gemv_lds_bytes(int64_t MT, int64_t K) {
+  const int64_t gp = (K / 128 + 3) / 4 * 4;
+  return MT * gp * (128 * 2 + 4 * 4);
+}
+
 // One linear of a batch, as the kernels see it (validated by the ABI layer).
 struct LinearDesc {
   const uint16_t* x;  // bf16 [M][K]
@@ -37,7 +45,7 @@ hipError_t launch_unpack(const uint8_t* q_packed, const float* d_packed, int64_t
 // MFMA streaming kernel over a batch (16-row slabs of x).
 hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream);
 // dot2 streaming kernel over a batch (MT-row slabs of x staged in LDS; every
-// K must satisfy MT * K * 2 <= kGemvLdsBytes).
+// K must satisfy gemv_lds_bytes(MT, K) <= kGemvLdsBytes).
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream);
 // Largest slab (4, 2 or 1 rows) the dot2 kernel can stage for M rows of K.
 int gemv_rows_per_slab(int64_t M, int64_t K);

@@ -36,21 +36,22 @@
  * Results are bitwise reproducible run to run (no floating-point atomics).
  *
  * NATIVE LAYOUT (what w4_quantize_rtn writes and w4_linear reads)
- *   Let Np = N rounded up to a multiple of 16, G = K / 128.  The matrix is
+ *   Let Np = N rounded up to a multiple of 16, G = K / 128, Q = ceil(G / 4)
+ *   and GP = 4Q (the group count padded to whole scale quads).  The matrix is
  *   cut into tiles of 16 rows x 128 inputs (one group); tile (r, g) covers
- *   rows 16r .. 16r+15 and group g.
- *   Codes: tile (r, g) is 1024 contiguous bytes at byte offset (r*G + g)*1024.
+ *   rows 16r .. 16r+15 and group g, for g < GP.
+ *   Codes: tile (r, g) is 1024 contiguous bytes at byte offset (r*GP + g)*1024.
  *     Its 16-byte lane L (0..63) holds row n = 16r + (L % 16), and its four
  *     little-endian 32-bit words w_i (i = 0..3) hold inputs
  *     k = 128g + 32i + 8(L / 16) + j, j = 0..7, as offset-binary nibbles
  *     u_j = q_j + 8:  w_i = rotl32(v, 3) where
  *     v = sum_{p=0..3} u_{2p} << 4p  +  sum_{p=0..3} u_{2p+1} << (16 + 4p).
- *   Scales: let Q = ceil(G / 4).  The scales of row n for the four groups
- *     4j .. 4j+3 form one 16-byte quad at float index ((r*Q + j)*16 + n%16)*4
- *     (r = n / 16), group 4j+t at offset t; groups G .. 4Q-1 are padding.
- *   Rows N .. Np-1 and padding groups hold codes 0 (u = 8) and scales 0.
- *   Total sizes: w4_packed_bytes(N, K) = Np*K/2 bytes of codes and
- *   w4_scale_count(N, K) = Np*4Q floats of scales.
+ *   Scales: the scales of row n for the four groups 4j .. 4j+3 form one
+ *     16-byte quad at float index ((r*Q + j)*16 + n%16)*4 (r = n / 16),
+ *     group 4j+t at offset t.
+ *   Rows N .. Np-1 and groups G .. GP-1 are padding: codes 0 (u = 8), scales 0.
+ *   Total sizes: w4_packed_bytes(N, K) = Np*GP*64 bytes of codes and
+ *   w4_scale_count(N, K) = Np*GP floats of scales.
  *
  * CANONICAL LAYOUT (for exchange and bit-exact comparison)
  *   codes int8 [N][K] row-major, each in [-8, 7];
@@ -81,7 +82,7 @@ typedef enum {
 typedef enum {
   W4_PATH_AUTO = 0,  /* the library's choice by M and K (what w4_linear does)   */
   W4_PATH_GEMV = 1,  /* VALU dot-product kernel, x staged in LDS in slabs of up
-                        to 4 rows; needs K <= 32768 (else W4_ERR_SHAPE)          */
+                        to 4 rows; needs K <= 30720 (else W4_ERR_SHAPE)          */
   W4_PATH_MFMA = 2   /* bf16 MFMA kernel, any M (slabs of 16 rows)             */
 } w4_path;
 
@@ -109,7 +110,7 @@ int w4_last_hip_error(void);
 /* Group size along K: 128 (study, section 1). */
 int w4_group_size(void);
 
-/* Bytes of native codes for an N x K matrix: roundup(N, 16) * K / 2.
+/* Bytes of native codes for an N x K matrix: roundup(N, 16) * roundup(K, 512) / 2.
  * Returns 0 when N < 0, K <= 0 or K % 128 != 0. */
 size_t w4_packed_bytes(int64_t N, int64_t K);
 

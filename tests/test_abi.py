@@ -52,7 +52,7 @@ def test_size_helpers(w4):
     assert lib.w4_group_size() == 128
     assert lib.w4_packed_bytes(2560, 9216) == 2560 * 9216 // 2
     assert lib.w4_scale_count(2560, 9216) == 2560 * 72
-    assert lib.w4_packed_bytes(37, 384) == 48 * 384 // 2  # rows padded to 16
+    assert lib.w4_packed_bytes(37, 384) == 48 * 512 // 2  # rows padded to 16, K to 512
     assert lib.w4_scale_count(37, 384) == 48 * 4  # groups padded to whole quads of 4
     assert lib.w4_scale_count(16, 2560) == 16 * 20
     assert lib.w4_packed_bytes(0, 128) == 0
@@ -112,7 +112,7 @@ def test_batched_validation(w4):
     a = (D * 2)(D(**dict(good, M=0)), D(**dict(good, q_packed=None)))
     assert lib.w4_linear_batched(a, 2, 0, None) == ERR_NULL
     # the dot2 kernel stages x in 64 KiB of LDS: K above 32768 is refused for it
-    big = (D * 1)(D(**dict(good, K=32896)))
+    big = (D * 1)(D(**dict(good, K=30720 + 512)))
     assert lib.w4_linear_batched(big, 1, 1, None) == ERR_SHAPE
 
 
