@@ -29,7 +29,9 @@ METRIC = "w4_linear achieved HBM GB/s (% of peak) at M=1 and M=8; equiv decode t
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E nameplate
 HEADLINE = "ffn_pair_outliers"
 KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_mfma_ffn_pair_outliers_m1_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_gemv_ffn_pair_outliers_m1_batched_counters.json")
+HEADLINE_KERNEL = "linear_gemv_kernel<1, 1, 4>"  # dot2 kernel, x in LDS: the batched M = 1 step
+HEADLINE_GRID = 32 * (160 + 576) * 256           # threads of one 64-linear launch (R = 1, 4 waves)
 
 
 def log(msg):
@@ -48,25 +50,35 @@ def kernel_source_hash():
 # GPU timing helpers
 # ----------------------------------------------------------------------------
 
-def capture(torch, fn):
-    """Capture fn() (a sequence of library launches) into a HIP graph."""
+def capture(torch, fn, reps=1):
+    """Capture `reps` back-to-back calls of fn() (library launches) into one HIP graph."""
     fn()  # eager run first: nothing lazy happens inside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
+        for _ in range(reps):
+            fn()
     torch.cuda.synchronize()
     return g
 
 
-def time_graph(torch, g, steps, warmup):
+def graph_steps(steps):
+    """Steps per graph replay: the largest of 8, 4, 2, 1 dividing `steps`, so
+    that exactly `steps` steps are timed while replay overhead is amortized."""
+    for r in (8, 4, 2, 1):
+        if steps % r == 0:
+            return r
+    return 1
+
+
+def time_graph(torch, g, replays, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
+    for _ in range(replays):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
@@ -110,8 +122,9 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
         step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats)
         res = {}
         for mode, fn in (("per_call", step), ("batched", step_batched)):
-            g = capture(torch, fn)
-            t = time_graph(torch, g, steps, warmup)
+            gs = graph_steps(steps)
+            g = capture(torch, fn, gs)
+            t = time_graph(torch, g, steps // gs, max(1, warmup // gs))
             launches = steps * (copies * len(mats) if mode == "per_call"
                                 else -(-copies * len(mats) // w4.MAX_BATCH))
             gbs = steps * step_bytes / t / 1e9
@@ -259,20 +272,22 @@ def cpu_baseline(workloads, budget_s=12.0):
 
 # ----------------------------------------------------------------------------
 
-def roofline(pair_m1, bytes_per_call):
-    """Dominant kernel: the M = 1 linear on the headline pair, one launch per call."""
+def roofline(pair_m1, bytes_per_call, copies):
+    """Dominant kernel: the M = 1 dot2 linear on the headline pair, one launch per step."""
     achieved = pair_m1["GBps"]
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
         if c.get("kernel_source_hash") == kernel_source_hash():
-            traffic = c.get("hbm_bytes_per_call")
+            traffic = c.get("hbm_bytes_per_launch")
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "linear_gemv_kernel<1,1,4> (M=1, dot2, x in LDS)",
-            "algorithmic_bytes_per_call": bytes_per_call,
-            "avg_launch_us": pair_m1["us_per_launch"]}
+            "kernel": "linear_gemv_kernel<1, 1, 4> (dot2, x in LDS), 64 linears per launch",
+            "algorithmic_bytes_per_launch": copies * sum(bytes_per_call.values()),
+            "avg_launch_us": pair_m1["us_per_launch"],
+            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this launch, copy-kernel calibrated"
+                              if traffic else None}
 
 
 # ----------------------------------------------------------------------------
@@ -313,11 +328,53 @@ def summarize_counters(path):
         print(f"| {name} | {grid} | {cn} | {len(v)} | {statistics.mean(v):.1f} |")
 
 
+def write_counters(fetch_csv, write_csv, copy_mb, out_path):
+    """Traffic of the headline kernel from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the same counter reads for the plain copy
+    kernel of known size."""
+    import csv
+    import statistics
+
+    import workloads
+
+    def per_dispatch(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return out
+
+    copy_bytes = copy_mb << 20
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = per_dispatch(path, counter)
+        copy = [v for (k, g), v in d.items() if "copy_kernel" in k]
+        factor = statistics.mean(copy[0]) * 1024 / copy_bytes  # counter bytes per real byte
+        # the headline launch: 64 linears (32 copies of 2560x9216 and of 9216x2560) at M = 1
+        grid = HEADLINE_GRID
+        vals = [v for (k, g), v in d.items() if HEADLINE_KERNEL.replace(" ", "") in k.replace(" ", "") and g == grid]
+        if not vals:
+            raise SystemExit(f"no {HEADLINE_KERNEL} dispatch with grid {grid} in {path}")
+        kib = statistics.mean(vals[0])
+        res[counter] = {"kib_per_dispatch": kib, "copy_calibration_factor": round(factor, 4),
+                        "bytes_per_dispatch": round(kib * 1024 / factor)}
+    traffic = res["FETCH_SIZE"]["bytes_per_dispatch"] + res["WRITE_SIZE"]["bytes_per_dispatch"]
+    out = {"kernel": HEADLINE_KERNEL, "launch": "64 linears: 32 x (2560x9216 + 9216x2560), M = 1",
+           "kernel_source_hash": kernel_source_hash(), "counters": res,
+           "hbm_bytes_per_launch": traffic,
+           "algorithmic_bytes_per_launch": 32 * (workloads.algorithmic_bytes(1, 2560, 9216)
+                                                 + workloads.algorithmic_bytes(1, 9216, 2560))}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--copies", type=int, default=32)
     ap.add_argument("--stacks", default="27b,70b")
     ap.add_argument("--no-cpu", action="store_true")
@@ -327,8 +384,14 @@ def main():
                     help="print a duration summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--counter-summary", metavar="COUNTER_COLLECTION_CSV",
                     help="print a summary of a rocprofv3 counter collection and exit")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files into the traffic file and exit")
     args = ap.parse_args()
 
+    if args.write_counters:
+        write_counters(args.write_counters[0], args.write_counters[1], args.calibrate_copy_mb or 256,
+                       COUNTERS_FILE)
+        return
     if args.trace_summary:
         summarize_trace(args.trace_summary)
         return
@@ -375,7 +438,7 @@ def main():
     torch.cuda.synchronize()
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
-    m1 = pair[1]["per_call"]
+    m1 = pair[1]["batched"]
     line = {
         "metric": METRIC,
         "value": m1["GBps"],
@@ -390,14 +453,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": HEADLINE, "matrices": ["2560x9216", "9216x2560"], "M": 1,
-                   "weight_copies": args.copies, "group": 128, "weights": "int4 codes + fp32 scales",
-                   "x": "bf16", "timing": "hip graph replay, events on the replay stream"},
+                   "weight_copies": args.copies, "linears_per_step": 2 * args.copies,
+                   "launch": "w4_linear_batched, 64 independent linears per launch",
+                   "group": 128, "weights": "int4 codes + fp32 scales", "x": "bf16",
+                   "timing": "hip graph replay, events on the replay stream"},
         "pct_of_peak": m1["pct_of_peak"],
-        "us_per_call": m1["us_per_linear"],
+        "us_per_linear": m1["us_per_linear"],
+        "per_call_m1": pair[1]["per_call"],
         "pair": pair,
         "quantize": quant,
         "stacks": stacks,
-        "roofline": roofline(m1, pair[1]["bytes_per_call"]),
+        "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
