@@ -45,6 +45,8 @@ w4_status hip_status(hipError_t e) {
 w4_status check_linear(const w4_linear_desc& l, w4::BatchArgs& a) {
   if (l.M < 0 || l.M > kMaxM || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
   if (l.M == 0 || l.N == 0) return W4_OK;  // empty: nothing to launch
+  // The kernels address codes with 32-bit offsets below 2 GiB and x below 1 GiB.
+  if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31 || 2 * (size_t)l.M * l.K > (size_t)1 << 30) return W4_ERR_SHAPE;
   if (!l.x || !l.q_packed || !l.d_packed || !l.y) return W4_ERR_NULL;
   if (!aligned(l.x, 16) || !aligned(l.q_packed, 16) || !aligned(l.d_packed, 16) || !aligned(l.y, 2))
     return W4_ERR_ALIGN;

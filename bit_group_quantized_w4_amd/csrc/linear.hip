@@ -10,12 +10,14 @@
 //     x rows (16 for the MFMA kernel, MT for the dot2 kernel);
 //   * its NW wavefronts split K into contiguous ranges of whole scale quads
 //     (4 groups of 128 inputs);
-//   * each wavefront walks its range one group at a time with a 4-deep
-//     register ring of loads, issued in exactly the order they are consumed,
-//     so waiting for group g never waits for loads issued after it; the
-//     16-byte scale quad of each row is loaded once per 4 groups into a
-//     double buffer;
-//   * weight tiles and scales use non-temporal loads (each byte is read once);
+//   * each wavefront walks its range quad by quad with a ring of loads in
+//     flight, issued in exactly the order they are consumed;
+//   * weight, scale and x loads are raw buffer loads: a quad beyond the
+//     wavefront's range, or an x row beyond M, gets an offset past the end of
+//     its buffer and reads zeros without touching memory, so every load in
+//     the loop is unconditional (exact vmcnt waits, no branches) and the ring
+//     needs no peeled tail (a zero scale cancels whatever zero codes give);
+//   * weights and scales use non-temporal loads (each byte is read once);
 //   * partial sums of the wavefronts are combined in LDS in a fixed order,
 //     so results are bitwise reproducible (no atomics).
 // Nibbles are widened in registers to bf16 1 + u/16 = 1.5 + q/16 (see
@@ -32,11 +34,35 @@ namespace w4 {
 namespace {
 
 constexpr uint16_t kBf16NegOneHalf = 0xBFC0;  // bf16 -1.5
-constexpr int kRing = 4;                      // groups in flight per wavefront = one scale quad
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
+constexpr int kNonTemporal = 2;               // buffer-load cache policy: non-temporal
+// Offsets at or past these read zeros.  Codes and scales of one matrix stay
+// below 2 GiB and x below 1 GiB (the C ABI refuses larger operands), so an
+// in-range offset plus kOobW or kOobX never wraps around 2^32.
+constexpr uint32_t kOobW = 0x80000000u;
+constexpr uint32_t kOobX = 0x40000000u;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float quad_elem(const uint4& v, int s) { return __uint_as_float(word(v, s)); }
 
 __device__ __forceinline__ bf16x8 unpack_step(uint32_t w, const UnpackConsts& uc) {
   uint32_t b[4];
@@ -47,12 +73,6 @@ __device__ __forceinline__ bf16x8 unpack_step(uint32_t w, const UnpackConsts& uc
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(a), bitcast<bf16x2>(b), c, false);
 }
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ float quad_elem(const uint4& v, int s) { return __uint_as_float(word(v, s)); }
 
 // Which linear of the batch, and which (row panel, x slab) of it, a block runs.
 struct Work {
@@ -73,13 +93,43 @@ __device__ __forceinline__ Work locate(const BatchArgs& a, int R, int MT) {
   return Work{di, (local - slab * panels) * R, slab * MT};
 }
 
+// Geometry of one linear and the weight-side buffers of one wavefront.
+template <int R>
+struct Weights {
+  int G, Q, GP, nb, rvalid, j0, j1;
+  __amdgpu_buffer_rsrc_t rq, rd;
+  uint32_t qo[R], so[R];  // byte offsets of this lane's 16 bytes at group 0 / quad 0, per row block
+
+  __device__ __forceinline__ Weights(const LinearDesc& D, const Work& wk, int lane, int wave, int nw) {
+    G = D.K / kGroup;
+    Q = (G + 3) >> 2;
+    GP = 4 * Q;
+    nb = (D.N + kTileRows - 1) / kTileRows;
+    rvalid = min(R, nb - wk.rb0);
+    j0 = (int)(((int64_t)Q * wave) / nw);
+    j1 = (int)(((int64_t)Q * (wave + 1)) / nw);
+    rq = make_rsrc(D.q, (uint32_t)nb * GP * 1024u);
+    rd = make_rsrc(D.d, (uint32_t)nb * GP * 64u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // row blocks past the end re-read the last one; they are never stored
+      const uint32_t rb = (uint32_t)min(wk.rb0 + r, nb - 1);
+      qo[r] = (rb * GP * kTileLanes + lane) * 16u;
+      so[r] = (rb * Q * kTileRows + (lane & 15)) * 16u;
+    }
+  }
+  // base added to qo / so: the group's (quad's) offset, or past the end
+  __device__ __forceinline__ uint32_t qbase(int j, int g) const { return j < j1 ? (uint32_t)g * 1024u : kOobW; }
+  __device__ __forceinline__ uint32_t sbase(int j) const { return j < j1 ? (uint32_t)j * 256u : kOobW; }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA kernel.  One v_mfma_f32_16x16x32_bf16 per 32-input step: A = 16 rows
 // of x, B = the tile's 16 rows of W^T.  Lane l holds A[l%16][8(l/16)..+7],
 // B[8(l/16)..+7][l%16] and D[4(l/16)+j][l%16], j = 0..3.  Rows of A at or
-// beyond M repeat row M-1 (their outputs are computed and discarded), so every
-// lane loads valid memory with no branches.  The -1.5*sum(x) start value is
-// itself one MFMA chain with B = -1.5.
+// beyond M read zeros (their outputs are discarded).  The -1.5*sum(x) start
+// value is itself one MFMA chain with B = -1.5.  One quad is in flight: the x
+// operands of a quad alone take 64 VGPRs.
 // ---------------------------------------------------------------------------
 template <int R, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
@@ -88,38 +138,30 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
   const Work wk = locate(args, R, 16);
   const LinearDesc& D = args.desc[wk.di];
   const int M = D.M, K = D.K, N = D.N;
-  const int G = K / kGroup;
-  const int Q = (G + 3) >> 2;  // scale quads; the native layout pads G to 4Q groups
-  const int nb = (N + kTileRows - 1) / kTileRows;
-  const int rvalid = min(R, nb - wk.rb0);
-  const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
+  const Weights<R> w(D, wk, lane, wave, NW);
 
-  const int xrow = min(wk.m0 + nl, M - 1);
-  const uint4* xs = reinterpret_cast<const uint4*>(D.x + (int64_t)xrow * K) + kb;
-  // Row blocks past the end of the matrix re-read the last one (never stored).
-  const uint4* qrow[R];
-  const uint4* srow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t rb = min(wk.rb0 + r, nb - 1);
-    qrow[r] = reinterpret_cast<const uint4*>(D.q) + rb * (4 * Q) * kTileLanes + lane;
-    srow[r] = reinterpret_cast<const uint4*>(D.d) + rb * Q * kTileRows + nl;
-  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
+  const int xrow = wk.m0 + nl;
+  const uint32_t xo = xrow < M ? ((uint32_t)xrow * K + 8u * kb) * 2u : kOobX;
+  const int j1 = w.j1;
+  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
 
-  uint4 bx[kRing][4];
-  uint4 bw[kRing][R];
+  uint4 bx[4][4];
+  uint4 bw[4][R];
   uint4 sc[R], sn[R];  // scale quads: current and next
 
-  auto issue_group = [&](int s, int g) {
-    const int gx = min(g, G - 1);  // padding groups: any valid x (their scale is 0)
+  auto issue_group = [&](int s, int j) {
+    const int g = 4 * j + s;
+    const uint32_t xb = xbase(j, g), qb = w.qbase(j, g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bx[s][i] = xs[gx * 16 + i * 4];
+    for (int i = 0; i < 4; ++i) bx[s][i] = bload<0>(rx, xo + xb + 64u * i);
 #pragma unroll
-    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qrow[r] + g * kTileLanes);
+    for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
   auto issue_scales = [&](uint4 (&dst)[R], int j) {
+    const uint32_t sb = w.sbase(j);
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = load_stream(srow[r] + j * kTileRows);
+    for (int r = 0; r < R; ++r) dst[r] = bload<kNonTemporal>(w.rd, w.so[r] + sb);
   };
 
   const UnpackConsts uc = unpack_consts();
@@ -152,23 +194,25 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
     }
   };
 
-  if (j0 < j1) {
-    issue_scales(sc, j0);
+  // The prologue issues in the loop's order (scales, then groups 0..3), so that
+  // the wait for each group at the loop head is the same on entry and on the
+  // back edge.  A wavefront with no quads (j0 == j1) reads zeros here.
+  issue_scales(sc, w.j0);
 #pragma unroll
-    for (int s = 0; s < kRing; ++s) issue_group(s, 4 * j0 + s);
-    // steady state: every load unconditional, issued in consumption order
-    for (int j = j0; j < j1 - 1; ++j) {
-      issue_scales(sn, j + 1);
+  for (int s = 0; s < 4; ++s) {
+    issue_group(s, w.j0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int j = w.j0; j < j1; ++j) {
+    issue_scales(sn, j + 1);  // past the range: zeros, no memory access
 #pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        compute(s);
-        issue_group(s, 4 * (j + 1) + s);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) sc[r] = sn[r];
+    for (int s = 0; s < 4; ++s) {
+      compute(s);
+      issue_group(s, j + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the refill here, not sunk to the loop end
     }
 #pragma unroll
-    for (int s = 0; s < kRing; ++s) compute(s);
+    for (int r = 0; r < R; ++r) sc[r] = sn[r];
   }
 
   auto store = [&](int r, const f32x4& v) {
@@ -184,17 +228,17 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
   if constexpr (NW == 1) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < rvalid) store(r, acc[r]);
+      if (r < w.rvalid) store(r, acc[r]);
   } else {
     __shared__ f32x4 red[NW][R][64];
 #pragma unroll
     for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
-    for (int r = wave; r < rvalid; r += NW) {
+    for (int r = wave; r < w.rvalid; r += NW) {
       f32x4 v = red[0][r][lane];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        const f32x4 o = red[w][r][lane];
+      for (int ww = 1; ww < NW; ++ww) {
+        const f32x4 o = red[ww][r][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += o[e];
       }
@@ -206,68 +250,61 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
 // ---------------------------------------------------------------------------
 // VALU kernel (v_dot2_f32_bf16).  Lane (row l%16, quarter l/16) multiplies its
 // 32 weights of a group by the matching 32 inputs of each of the MT x rows of
-// its slab; x is staged once per block in LDS (MT * K bf16).  The four
-// quarters of a row are summed with cross-lane shuffles at the end.
+// its slab; x is staged once per block in LDS (MT * K bf16) together with the
+// start value of every (row, group, quarter).  One quad of weights is in
+// flight per wavefront, refilled group by group as each is consumed: with
+// few VGPRs many wavefronts stay resident, which hides more latency than a
+// deeper ring per wavefront.  The four quarters of a row are summed with
+// cross-lane shuffles at the end.
 // ---------------------------------------------------------------------------
 template <int MT, int R, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
-  // LDS: x of the slab, [MT][4Q * 16] uint4 (zero past K), then the start
-  // values -1.5 * sum(x) of every (row, group, quarter), [MT][4Q][4] floats.
+  // LDS: x of the slab, [MT][GP * 16] uint4 (zero past K), then the start
+  // values -1.5 * sum(x) of every (row, group, quarter), [MT][GP][4] floats.
   extern __shared__ uint4 xlds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
   const Work wk = locate(args, R, MT);
   const LinearDesc& D = args.desc[wk.di];
   const int M = D.M, K = D.K, N = D.N;
-  const int G = K / kGroup;
-  const int Q = (G + 3) >> 2;
-  const int GP = 4 * Q;
-  const int nb = (N + kTileRows - 1) / kTileRows;
-  const int rvalid = min(R, nb - wk.rb0);
-  const int j0 = (int)(((int64_t)Q * wave) / NW), j1 = (int)(((int64_t)Q * (wave + 1)) / NW);
-  const uint4* qrow[R];
-  const uint4* srow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t rb = min(wk.rb0 + r, nb - 1);
-    qrow[r] = reinterpret_cast<const uint4*>(D.q) + rb * GP * kTileLanes + lane;
-    srow[r] = reinterpret_cast<const uint4*>(D.d) + rb * Q * kTileRows + nl;
-  }
+  const Weights<R> w(D, wk, lane, wave, NW);
+  const int GP = w.GP;
 
-  uint4 bw[kRing][R];
-  uint4 sc[R], sn[R];
-  auto issue_group = [&](int s, int g) {
+  uint4 bw[4][R];
+  uint4 sc[R], sn[R];  // scale quads: current and next
+  auto issue_group = [&](int s, int j) {
+    const uint32_t qb = w.qbase(j, 4 * j + s);
 #pragma unroll
-    for (int r = 0; r < R; ++r) bw[s][r] = load_stream(qrow[r] + g * kTileLanes);
+    for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
   auto issue_scales = [&](uint4 (&dst)[R], int j) {
+    const uint32_t sb = w.sbase(j);
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = load_stream(srow[r] + j * kTileRows);
+    for (int r = 0; r < R; ++r) dst[r] = bload<kNonTemporal>(w.rd, w.so[r] + sb);
   };
-  if (j0 < j1) {
-    issue_scales(sc, j0);
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) issue_group(s, 4 * j0 + s);
-  }
-
-  const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
 
   // Stage the slab's x rows (rows beyond M repeat row M-1; their outputs are
   // dropped) together with the start value of every (row, group, quarter).
-  float* offs = reinterpret_cast<float*>(xlds + MT * GP * 16);
-  for (int e = threadIdx.x; e < MT * GP * 4; e += NW * 64) {
+  // Element e = (row, group, quarter) covers 4 x 16 bytes; groups past K read
+  // zeros.  The first element of every thread is loaded before the weight
+  // prologue: loads retire in issue order, so x queued behind the weights
+  // would wait for their HBM round trip.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
+  const int total = MT * GP * 4;
+  auto x_off = [&](int e) -> uint32_t {
     const int mm = e / (GP * 4);
     const int rem = e - mm * GP * 4;
     const int g = rem >> 2, q4 = rem & 3;
-    uint4 v[4];
-    if (g < G) {
-      const uint4* src = reinterpret_cast<const uint4*>(D.x + (int64_t)min(wk.m0 + mm, M - 1) * K) + g * 16 + q4;
+    if (e >= total || g >= w.G) return kOobX;
+    return ((uint32_t)min(wk.m0 + mm, M - 1) * K + (uint32_t)g * kGroup + 8u * q4) * 2u;
+  };
+  auto load_x = [&](uint32_t o, uint4 (&v)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = src[i * 4];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) v[i] = bload<0>(rx, o + 64u * i);
+  };
+  const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
+  float* offs = reinterpret_cast<float*>(xlds + MT * GP * 16);
+  auto store_x = [&](int e, const uint4 (&v)[4]) {
     float c = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -275,9 +312,33 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
       c = dot2(v[i].y, kneg2, c);
       c = dot2(v[i].z, kneg2, c);
       c = dot2(v[i].w, kneg2, c);
-      xlds[(mm * GP + g) * 16 + i * 4 + q4] = v[i];
+      xlds[(e >> 2) * 16 + i * 4 + (e & 3)] = v[i];
     }
-    offs[(mm * GP + g) * 4 + q4] = c;
+    offs[e] = c;
+  };
+
+  {
+    uint4 v[4];
+    load_x(x_off(threadIdx.x), v);
+    __builtin_amdgcn_sched_barrier(0);
+    // Weight prologue in the loop's order (scales, then groups 0..3); a
+    // wavefront with no quads (j0 == j1) reads zeros here.
+    issue_scales(sc, w.j0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      issue_group(s, w.j0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Consume x here, before the branch, so the loads are not sunk into it
+    // (behind the weights).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+    if ((int)threadIdx.x < total) store_x(threadIdx.x, v);
+  }
+  for (int e = threadIdx.x + NW * 64; e < total; e += NW * 64) {
+    uint4 v[4];
+    load_x(x_off(e), v);
+    store_x(e, v);
   }
   __syncthreads();
 
@@ -304,33 +365,30 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      uint32_t b[16];
+      uint32_t bb[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) unpack_word(word(bw[s][r], i), &b[4 * i], uc);
+      for (int i = 0; i < 4; ++i) unpack_word(word(bw[s][r], i), &bb[4 * i], uc);
       const float dv = quad_elem(sc[r], s);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
         float c = c0[mm];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c = dot2(b[e], xv[mm][e], c);
+        for (int e = 0; e < 16; ++e) c = dot2(bb[e], xv[mm][e], c);
         acc[r][mm] += dv * c;
       }
     }
   };
 
-  if (j0 < j1) {
-    for (int j = j0; j < j1 - 1; ++j) {
-      issue_scales(sn, j + 1);
+  for (int j = w.j0; j < w.j1; ++j) {
+    issue_scales(sn, j + 1);  // past the range: zeros, no memory access
 #pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        compute(s, 4 * j + s);
-        issue_group(s, 4 * (j + 1) + s);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) sc[r] = sn[r];
+    for (int s = 0; s < 4; ++s) {
+      compute(s, 4 * j + s);
+      issue_group(s, j + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the refill here, not sunk to the loop end
     }
 #pragma unroll
-    for (int s = 0; s < kRing; ++s) compute(s, 4 * (j1 - 1) + s);
+    for (int r = 0; r < R; ++r) sc[r] = sn[r];
   }
 
   // Sum the four quarters of each row: lanes l, l^16, l^32, l^48.
@@ -356,10 +414,10 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
     const int row = e & 15;
     const int mm = (e >> 4) % MT;
     const int r = (e >> 4) / MT;
-    if (r < rvalid) {
+    if (r < w.rvalid) {
       float v = red[0][r][mm][row];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v += red[w][r][mm][row];
+      for (int ww = 1; ww < NW; ++ww) v += red[ww][r][mm][row];
       const int n = (wk.rb0 + r) * kTileRows + row;
       const int m = wk.m0 + mm;
       if (n < N && m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v);
@@ -429,6 +487,18 @@ int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
   return total;
 }
 
+template <int MT>
+void launch_gemv_cfg(int ci, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
+  switch (ci) {
+#define W4_CASE(i)                                                                              \
+  case i:                                                                                       \
+    linear_gemv_kernel<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(a); \
+    break;
+    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
+#undef W4_CASE
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
@@ -466,28 +536,9 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
   int kmax = 0;
   for (int i = 0; i < a.count; ++i) kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   const size_t lds = (size_t)gemv_lds_bytes(MT, kmax);
-#define W4_LAUNCH(mt, i)                                                                          \
-  linear_gemv_kernel<mt, kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, lds, stream>>>(a)
-#define W4_CASES(mt)                                 \
-  switch (ci) {                                      \
-    case 0: W4_LAUNCH(mt, 0); break;                 \
-    case 1: W4_LAUNCH(mt, 1); break;                 \
-    case 2: W4_LAUNCH(mt, 2); break;                 \
-    case 3: W4_LAUNCH(mt, 3); break;                 \
-    case 4: W4_LAUNCH(mt, 4); break;                 \
-    case 5: W4_LAUNCH(mt, 5); break;                 \
-    case 6: W4_LAUNCH(mt, 6); break;                 \
-    default: W4_LAUNCH(mt, 7); break;                \
-  }
-  if (MT == 4) {
-    W4_CASES(4)
-  } else if (MT == 2) {
-    W4_CASES(2)
-  } else {
-    W4_CASES(1)
-  }
-#undef W4_CASES
-#undef W4_LAUNCH
+  if (MT == 4) launch_gemv_cfg<4>(ci, (unsigned)blocks, lds, stream, a);
+  else if (MT == 2) launch_gemv_cfg<2>(ci, (unsigned)blocks, lds, stream, a);
+  else launch_gemv_cfg<1>(ci, (unsigned)blocks, lds, stream, a);
   return hipGetLastError();
 }
 

@@ -144,6 +144,8 @@ w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packe
  *   y        [out] bf16 bit patterns, row-major [M][N]; 2-byte aligned; must
  *                  not overlap any input (W4_ERR_ARG).  Rounded to nearest
  *                  even from fp32.
+ * Size limits (W4_ERR_SHAPE beyond them): w4_packed_bytes(N, K) < 2 GiB and
+ * 2*M*K <= 1 GiB, so that every operand is addressed with 32-bit offsets.
  */
 w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
                     const float* d_packed, int64_t N, uint16_t* y, hipStream_t stream);

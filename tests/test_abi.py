@@ -83,6 +83,11 @@ def test_linear_validation(w4):
     assert _linear(lib, y=FAKE) == ERR_ARG  # output aliases x
     assert _linear(lib, y=FAKE + 0x100000 + 64) == ERR_ARG  # output inside the codes
     assert _linear(lib, path=7) == ERR_ARG
+    # operands addressed with 32-bit offsets: codes below 2 GiB, x at most 1 GiB
+    assert _linear(lib, N=1 << 17, K=1 << 15, x=None) == ERR_SHAPE  # codes exactly 2 GiB
+    assert _linear(lib, N=(1 << 17) - 16, K=1 << 15, x=None) == ERR_NULL  # just below
+    assert _linear(lib, M=(1 << 14) + 1, K=1 << 15, x=None) == ERR_SHAPE  # x above 1 GiB
+    assert _linear(lib, M=1 << 14, K=1 << 15, x=None) == ERR_NULL  # x exactly 1 GiB
     # empty problems are valid no-ops that launch nothing, even with NULL buffers
     assert _linear(lib, M=0, x=None, y=None) == OK
     assert _linear(lib, N=0, q=None, d=None, y=None) == OK
