@@ -48,6 +48,10 @@ def common_flags():
         # MFMA accumulators in VGPRs: the per-group scaling reads them with
         # plain VALU instead of v_accvgpr_read copies.
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # the first 16 dwords of scalar kernel arguments arrive preloaded in
+        # SGPRs, so single-linear and quantize kernels start issuing loads
+        # without a kernel-argument fetch.
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", INCLUDE,
         "-I", CSRC,
     ]

@@ -93,6 +93,15 @@ __device__ __forceinline__ Work locate(const BatchArgs& a, int R, int MT) {
   return Work{di, (local - slab * panels) * R, slab * MT};
 }
 
+// The same for a launch of one linear.
+__device__ __forceinline__ Work locate_one(int N, int R, int MT) {
+  const int b = blockIdx.x;
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  const int panels = (nb + R - 1) / R;
+  const int slab = b / panels;
+  return Work{0, (b - slab * panels) * R, slab * MT};
+}
+
 // Geometry of one linear and the weight-side buffers of one wavefront.
 template <int R>
 struct Weights {
@@ -132,11 +141,9 @@ struct Weights {
 // operands of a quad alone take 64 VGPRs.
 // ---------------------------------------------------------------------------
 template <int R, int NW>
-__global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
+__device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
-  const Work wk = locate(args, R, 16);
-  const LinearDesc& D = args.desc[wk.di];
   const int M = D.M, K = D.K, N = D.N;
   const Weights<R> w(D, wk, lane, wave, NW);
 
@@ -247,6 +254,23 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
   }
 }
 
+// Batched launch: the block finds its linear in the kernel arguments.
+template <int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
+  const Work wk = locate(args, R, 16);
+  mfma_body<R, NW>(args.desc[wk.di], wk);
+}
+
+// Launch of one linear.  Its arguments are plain scalars that the hardware
+// preloads into SGPRs at wave launch, so the kernel does not wait for a
+// kernel-argument fetch before it can issue its first loads.
+template <int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const float* d,
+                                                           uint16_t* y, int M, int K, int N) {
+  const LinearDesc D{x, q, d, y, M, K, N, 0};
+  mfma_body<R, NW>(D, locate_one(N, R, 16));
+}
+
 // ---------------------------------------------------------------------------
 // VALU kernel (v_dot2_f32_bf16).  Lane (row l%16, quarter l/16) multiplies its
 // 32 weights of a group by the matching 32 inputs of each of the MT x rows of
@@ -258,14 +282,12 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
 // cross-lane shuffles at the end.
 // ---------------------------------------------------------------------------
 template <int MT, int R, int NW>
-__global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
+__device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   // LDS: x of the slab, [MT][GP * 16] uint4 (zero past K), then the start
   // values -1.5 * sum(x) of every (row, group, quarter), [MT][GP][4] floats.
   extern __shared__ uint4 xlds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
-  const Work wk = locate(args, R, MT);
-  const LinearDesc& D = args.desc[wk.di];
   const int M = D.M, K = D.K, N = D.N;
   const Weights<R> w(D, wk, lane, wave, NW);
   const int GP = w.GP;
@@ -425,6 +447,19 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
   }
 }
 
+template <int MT, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
+  const Work wk = locate(args, R, MT);
+  gemv_body<MT, R, NW>(args.desc[wk.di], wk);
+}
+
+template <int MT, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_gemv_one(const uint16_t* x, const uint8_t* q, const float* d,
+                                                           uint16_t* y, int M, int K, int N) {
+  const LinearDesc D{x, q, d, y, M, K, N, 0};
+  gemv_body<MT, R, NW>(D, locate_one(N, R, MT));
+}
+
 // ---------------------------------------------------------------------------
 // launch configuration
 // ---------------------------------------------------------------------------
@@ -490,9 +525,15 @@ int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
 template <int MT>
 void launch_gemv_cfg(int ci, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
   switch (ci) {
-#define W4_CASE(i)                                                                              \
-  case i:                                                                                       \
-    linear_gemv_kernel<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(a); \
+#define W4_CASE(i)                                                                                       \
+  case i:                                                                                                \
+    if (a.count == 1) {                                                                                  \
+      const LinearDesc& l = a.desc[0];                                                                   \
+      linear_gemv_one<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(l.x, l.q, l.d, \
+                                                                                         l.y, l.M, l.K, l.N); \
+    } else {                                                                                             \
+      linear_gemv_kernel<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(a);         \
+    }                                                                                                    \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
@@ -509,9 +550,15 @@ hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   switch (ci) {
-#define W4_CASE(i)                                                                               \
-  case i:                                                                                        \
-    linear_mfma_kernel<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(a); \
+#define W4_CASE(i)                                                                                          \
+  case i:                                                                                                   \
+    if (a.count == 1) {                                                                                     \
+      const LinearDesc& l = a.desc[0];                                                                      \
+      linear_mfma_one<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(l.x, l.q, l.d, \
+                                                                                              l.y, l.M, l.K, l.N); \
+    } else {                                                                                                \
+      linear_mfma_kernel<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(a);    \
+    }                                                                                                       \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
