@@ -34,25 +34,11 @@ namespace w4 {
 namespace {
 
 constexpr uint16_t kBf16NegOneHalf = 0xBFC0;  // bf16 -1.5
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
-constexpr int kNonTemporal = 2;               // buffer-load cache policy: non-temporal
 // Offsets at or past these read zeros.  Codes and scales of one matrix stay
 // below 2 GiB and x below 1 GiB (the C ABI refuses larger operands), so an
 // in-range offset plus kOobW or kOobX never wraps around 2^32.
 constexpr uint32_t kOobW = 0x80000000u;
 constexpr uint32_t kOobX = 0x40000000u;
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-template <int AUX>
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -179,20 +165,24 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int s) {
+  // Group s of the current quad: the MFMA chains (which read the group's x
+  // and code registers at issue), then the scaled accumulation (which waits
+  // for the chains' results).
+  auto products = [&](int s, f32x4 (&c)[R]) {
     bf16x8 a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = bitcast<bf16x8>(bx[s][i]);
     f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) off = mfma16x16x32(a[i], kneg, off);
-    f32x4 c[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) c[r] = off;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < R; ++r) c[r] = mfma16x16x32(a[i], unpack_step(word(bw[s][r], i), uc), c[r]);
+  };
+  auto accumulate = [&](int s, const f32x4 (&c)[R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float dv = quad_elem(sc[r], s);
@@ -214,9 +204,13 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
     issue_scales(sn, j + 1);  // past the range: zeros, no memory access
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      compute(s);
+      f32x4 c[R];
+      products(s, c);
+      // refill as soon as the chains have read the registers, not after their
+      // results are in (nor sunk to the loop end)
       issue_group(s, j + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the refill here, not sunk to the loop end
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(s, c);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = sn[r];
@@ -372,30 +366,39 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.f;
 
-  auto compute = [&](int s, int g) {
+  // Group g (slot s of the current quad): its x values and start values from
+  // LDS, the codes widened to bf16 pairs (this frees the slot's registers for
+  // the refill), then the dot products and the scaled accumulation.
+  struct Operands {
     uint32_t xv[MT][16];
     float c0[MT];
+    uint32_t bb[R][16];
+  };
+  auto widen = [&](int s, int g, Operands& o) {
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint4 t = xlds[(mm * GP + g) * 16 + i * 4 + kb];
-        xv[mm][4 * i + 0] = t.x; xv[mm][4 * i + 1] = t.y;
-        xv[mm][4 * i + 2] = t.z; xv[mm][4 * i + 3] = t.w;
+        o.xv[mm][4 * i + 0] = t.x; o.xv[mm][4 * i + 1] = t.y;
+        o.xv[mm][4 * i + 2] = t.z; o.xv[mm][4 * i + 3] = t.w;
       }
-      c0[mm] = offs[(mm * GP + g) * 4 + kb];
+      o.c0[mm] = offs[(mm * GP + g) * 4 + kb];
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t bb[16];
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) unpack_word(word(bw[s][r], i), &bb[4 * i], uc);
+      for (int i = 0; i < 4; ++i) unpack_word(word(bw[s][r], i), &o.bb[r][4 * i], uc);
+  };
+  auto dots = [&](int s, const Operands& o) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
       const float dv = quad_elem(sc[r], s);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
-        float c = c0[mm];
+        float c = o.c0[mm];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c = dot2(bb[e], xv[mm][e], c);
+        for (int e = 0; e < 16; ++e) c = dot2(o.bb[r][e], o.xv[mm][e], c);
         acc[r][mm] += dv * c;
       }
     }
@@ -405,9 +408,12 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
     issue_scales(sn, j + 1);  // past the range: zeros, no memory access
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      compute(s, 4 * j + s);
+      Operands o;
+      widen(s, 4 * j + s, o);
+      // refill as soon as the codes are widened (not sunk to the loop end)
       issue_group(s, j + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the refill here, not sunk to the loop end
+      __builtin_amdgcn_sched_barrier(0);
+      dots(s, o);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = sn[r];
@@ -494,9 +500,12 @@ int find_cfg(int R, int NW) {
 // 256 CUs for the batch's total row blocks, more wavefronts per block when K
 // is long.
 int choose_cfg_mfma(const BatchArgs& a) {
+  // More row blocks per wavefront reuse each x operand across more weights
+  // (x is read through L1 once per row panel), but leave fewer wavefronts.
   int64_t rows = 0;
   for (int i = 0; i < a.count; ++i) rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
-  return rows >= 384 ? find_cfg(2, 4) : find_cfg(1, 4);
+  if (rows < 256) return find_cfg(1, 4);
+  return rows < 600 ? find_cfg(2, 4) : find_cfg(4, 4);
 }
 
 int choose_cfg_gemv(const BatchArgs& a) {

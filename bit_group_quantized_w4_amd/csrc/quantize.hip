@@ -14,8 +14,13 @@
 // 32-input steps), the group max is finished across the four lanes that share
 // a row, and the lane writes its 16 bytes of codes; the 16 scales of the tile
 // are written by the lanes of the first quarter into their rows' scale quads.
-// Tiles of the padding rows (N .. Np-1) and padding groups (G .. 4Q-1) are
-// written as code 0 with scale 0.
+// Weights are read with raw buffer loads over the tile's row block: padding
+// rows (N .. Np-1) and padding groups (G .. 4Q-1) read zeros, so they come out
+// as code 0 with scale 0 without a branch.  The loads keep the default cache
+// policy: each instruction covers every other 16 bytes of its rows' lines and
+// the next one the rest, which a streaming (non-temporal) policy would fetch
+// twice.  One tile per wavefront (rather than a loop over tiles) keeps the
+// most loads in flight.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -58,40 +63,36 @@ __device__ __forceinline__ uint32_t native_word(const int u[8]) {
   return rotl32(v, 3);
 }
 
-__device__ __forceinline__ uint4 zero_code_lane() {
-  int u[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = 8;
-  const uint32_t w = native_word(u);
-  return make_uint4(w, w, w, w);
-}
-
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restrict__ W, int N,
                                                            int K, int G, int GP, int64_t ntiles,
                                                            uint4* __restrict__ qp,
                                                            float* __restrict__ dp) {
 #pragma clang fp contract(off)
-  TileAt t;
-  if (!tile_at(ntiles, GP, t)) return;
-  if (t.g >= G) {  // padding group
-    qp[t.tile * kTileLanes + t.lane] = zero_code_lane();
-    if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = 0.0f;
-    return;
-  }
+  const int lane = threadIdx.x & 63, nl = lane & 15, kb = lane >> 4;
+  // the wavefront index is uniform across the wavefront: keep the tile, and
+  // with it the buffer resource, in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile = (int64_t)blockIdx.x * kTilesPerBlock + wave;
+  if (tile >= ntiles) return;
+  const int64_t r = tile / GP;
+  const int g = (int)(tile - r * GP);
 
+  // The 32 weights of this lane; zeros outside the matrix.
   float v[32];
-  if (t.n < N) {
-    const float4* src = reinterpret_cast<const float4*>(W + t.n * K + (int64_t)t.g * kGroup + 8 * t.kb);
+  {
+    const int64_t n0 = r * kTileRows;
+    const int64_t rows = min((int64_t)kTileRows, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + n0 * K, (uint32_t)(rows * K * 4));
+    const uint32_t off = g < G ? ((uint32_t)nl * K + (uint32_t)g * kGroup + 8u * kb) * 4u : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 a = src[8 * i];
-      const float4 b = src[8 * i + 1];
-      v[8 * i + 0] = a.x; v[8 * i + 1] = a.y; v[8 * i + 2] = a.z; v[8 * i + 3] = a.w;
-      v[8 * i + 4] = b.x; v[8 * i + 5] = b.y; v[8 * i + 6] = b.z; v[8 * i + 7] = b.w;
+      const uint4 a = bload<0>(rs, off + 128u * i);
+      const uint4 b = bload<0>(rs, off + 128u * i + 16u);
+      v[8 * i + 0] = __uint_as_float(a.x); v[8 * i + 1] = __uint_as_float(a.y);
+      v[8 * i + 2] = __uint_as_float(a.z); v[8 * i + 3] = __uint_as_float(a.w);
+      v[8 * i + 4] = __uint_as_float(b.x); v[8 * i + 5] = __uint_as_float(b.y);
+      v[8 * i + 6] = __uint_as_float(b.z); v[8 * i + 7] = __uint_as_float(b.w);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] = 0.0f;  // padding rows quantize as zero rows
   }
 
   // Group range (symmetric min/max): the largest magnitude, plus a flag for
@@ -112,6 +113,30 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
   // Restore scale: +-max maps to code +-7.
   const float d = bad ? __uint_as_float(kNanBits) : amax / kMaxCode;
   const bool usable = !bad && d != 0.0f;
+  // Unusable groups (d = 0 or NaN) divide by 1 and are then forced to code 0,
+  // which keeps the loop free of branches.
+  const float dd = usable ? d : 1.0f;
+
+  // Quotients w / d.  The code depends on the IEEE quotient only through
+  // round-half-away, so w * rcp(d) gives the same code unless the quotient
+  // lies near a half-integer: rcp is within 1 ulp and the product within
+  // half an ulp, so for |w/d| <= 7 both values lie within 1.5e-6 of w/d.
+  // When any lane of the wavefront has a product within 2^-17 (7.6e-6) of a
+  // half-integer, or a scale outside [2^-120, 2^120] (where rcp may lose
+  // range), the wavefront recomputes every quotient with IEEE division.
+  float t[32];
+  const float rd = __builtin_amdgcn_rcpf(dd);
+  bool near = !(dd >= 0x1p-120f && dd <= 0x1p+120f);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    t[j] = v[j] * rd;
+    const float a = fabsf(t[j]);
+    near |= fabsf((a - truncf(a)) - 0.5f) < 0x1p-17f;
+  }
+  if (__ballot(near)) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) t[j] = v[j] / dd;  // IEEE fp32 quotient by the stored scale
+  }
 
   uint32_t words[4];
 #pragma unroll
@@ -119,20 +144,16 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     int u[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int code = 0;
-      if (usable) {
-        const float q = v[8 * i + j] / d;  // IEEE fp32 quotient by the stored scale
-        float rr = truncf(q);
-        if (fabsf(q - rr) >= 0.5f) rr += copysignf(1.0f, q);  // ties away from zero
-        rr = fminf(fmaxf(rr, -8.0f), 7.0f);
-        code = (int)rr;
-      }
-      u[j] = code + 8;
+      const float q = t[8 * i + j];
+      float rr = truncf(q);
+      rr = fabsf(q - rr) >= 0.5f ? rr + copysignf(1.0f, q) : rr;  // ties away from zero
+      rr = fminf(fmaxf(rr, -8.0f), 7.0f);
+      u[j] = (usable ? (int)rr : 0) + 8;
     }
     words[i] = native_word(u);
   }
-  qp[t.tile * kTileLanes + t.lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = d;
+  qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (kb == 0) dp[scale_index(r, GP, g, nl)] = d;
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc,

@@ -64,15 +64,23 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4], const U
   out[3] = (rotr32(w, 12) & c.mask) | c.magic;
 }
 
-// Streaming 16-byte load that does not keep the line in the caches (the
-// packed weights are read exactly once per call).
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// Raw buffer loads.  A resource covers [base, base + bytes); a load at or past
+// `bytes` returns zeros without touching memory, which lets loops issue every
+// load unconditionally (no branches, exact in-order vmcnt waits).
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
+constexpr int kNonTemporal = 2;               // cache policy of streaming loads (each byte read once)
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
-__device__ __forceinline__ float load_stream(const float* p) { return __builtin_nontemporal_load(p); }
+template <int AUX>
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -97,6 +97,41 @@ def test_quantize_shapes(w4, gpu, N, K):
     quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"{N}x{K}")
 
 
+def near_tie_weights(seed, N=64, K=1024, spread_ulps=3, far=2e-5, far_share=0.125):
+    """Groups whose members sit a few ulps from (k + 1/2) * d, where d is the
+    group's scale as the oracle computes it: their codes depend on the last
+    bit of the IEEE quotient w / d.  A share `far_share` of the members is
+    instead placed about `far` (relative) from a half-integer quotient."""
+    rng = np.random.default_rng(seed)
+    W = np.empty((N, K), np.float32)
+    for n in range(N):
+        for g in range(K // 128):
+            a = np.float32(rng.uniform(1e-3, 10.0))
+            probe = np.zeros((1, 128), np.float32)
+            probe[0, 0] = a
+            d = np.float64(oracle.rtn_quantize_ref(probe)[1].reshape(-1)[0])
+            k = rng.integers(-7, 7, size=127).astype(np.float64)  # quotients k + 1/2 in [-6.5, 6.5]
+            shift = np.where(rng.random(127) < far_share, rng.choice([-far, far], 127), 0.0)
+            vals = ((k + 0.5) * (1.0 + shift) * d).astype(np.float32)
+            ulps = rng.integers(-spread_ulps, spread_ulps + 1, size=127)
+            for s in range(spread_ulps):
+                vals = np.where(ulps > s, np.nextafter(vals, np.float32(np.inf)), vals)
+                vals = np.where(ulps < -s, np.nextafter(vals, np.float32(-np.inf)), vals)
+            grp = np.concatenate([[a], vals]).astype(np.float32)
+            W[n, g * 128:(g + 1) * 128] = grp[rng.permutation(128)]
+    return W
+
+
+@pytest.mark.parametrize("seed,far_share", [(0, 0.125), (1, 0.125), (2, 1.0)])
+def test_quantize_near_ties(w4, gpu, seed, far_share):
+    """Codes decided by the last bit of w / d match the oracle's IEEE quotients,
+    both for quotients within a few ulps of a half-integer and (far_share = 1)
+    for quotients just outside that band, everywhere in the tile."""
+    _say(f"quantize near-tie weights seed={seed} far_share={far_share}")
+    W = near_tie_weights(seed, far_share=far_share)
+    quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"near ties {seed}/{far_share}")
+
+
 @pytest.mark.parametrize("workload", ["ffn_2560x9216", "ffn_pair_outliers"])
 def test_quantize_single_matrix_workloads(w4, gpu, workload):
     for m in workloads.WORKLOADS[workload].matrices:
