@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "w4_linear achieved HBM GB/s (% of peak) at M=1 and M=8; equiv decode tok/s"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E nameplate
+PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
 HEADLINE = "ffn_pair_outliers"
 KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_gemv_ffn_pair_outliers_m1_batched_counters.json")
@@ -71,9 +72,20 @@ def graph_steps(steps):
     return 1
 
 
+# Under sustained load the GPU's clocks settle only after tens of milliseconds:
+# replays of the headline launch run ~117 us, then ~180 us, then recover to a
+# steady ~121 us after about 40 ms.  Warmup therefore lasts at least this long.
+MIN_WARMUP_S = 0.15
+
+
 def time_graph(torch, g, replays, warmup):
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < MIN_WARMUP_S:
         g.replay()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()  # keep the host from running far ahead of the clock check
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -143,16 +155,17 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
         out[M] = res
     # quantization throughput (rows a1-a4), same matrices, rotated over 4 fp32 copies
     qout = {}
+    nq = min(4, copies)
     for (m, W, qs, ds) in mats:
-        Ws = [W] + [W.clone() for _ in range(3)]
+        Ws = [W] + [W.clone() for _ in range(nq - 1)]
 
         def qstep():
-            for c in range(4):
+            for c in range(nq):
                 w4.quantize_rtn(Ws[c], out=(qs[c], ds[c]))
 
         g = capture(torch, qstep)
         t = time_graph(torch, g, max(3, steps // 4), 2)
-        n = max(3, steps // 4) * 4
+        n = max(3, steps // 4) * nq
         qb = workloads.quantize_bytes(m.N, m.K)
         qout[m.name] = {"GBps": round(n * qb / t / 1e9, 1), "us_per_call": round(t / n * 1e6, 2),
                         "bytes_per_call": qb}
@@ -179,7 +192,7 @@ def _shared_input_groups(wl):
     return [by_tag[t] for t in order]
 
 
-def bench_stack(torch, w4, workloads, name, steps, warmup):
+def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_modes=None):
     dev = torch.device("cuda:0")
     wl = workloads.WORKLOADS[name]
     t0 = time.time()
@@ -199,7 +212,11 @@ def bench_stack(torch, w4, workloads, name, steps, warmup):
     groups = {"per_call": [[i] for i in range(len(wl.matrices))],
               "fused_shared_input": _shared_input_groups(wl),
               "layer_batched": [list(range(len(wl.matrices)))]}
+    if only_modes:
+        groups = {k: v for k, v in groups.items() if k in only_modes}
     for M in wl.ms:
+        if only_ms and M not in only_ms:
+            continue
         xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
         ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices]
         res[M] = {}
@@ -219,10 +236,13 @@ def bench_stack(torch, w4, workloads, name, steps, warmup):
             per = t / steps
             nbytes = workloads.stack_bytes(name, M)
             gbs = nbytes / per / 1e9
+            flops = 2.0 * M * workloads.stack_weights(name)
             res[M][mode] = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1),
                             "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                             "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(M / per, 1),
-                            "launches_per_pass": len(layers) * len(grp)}
+                            "launches_per_pass": len(layers) * len(grp),
+                            "useful_tflops": round(flops / per / 1e12, 2),
+                            "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3)}
             log(f"[bench] stack {name} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
                 f"{1 / per:.1f} passes/s")
             del g
@@ -263,16 +283,57 @@ def cpu_baseline(workloads, budget_s=12.0):
             if time.perf_counter() - t0 >= budget_s:
                 break
         t = time.perf_counter() - t0
+        # the quantizer on the same matrices, a few seconds' worth
+        qpasses, qbytes = 0, 0
+        t1 = time.perf_counter()
+        while True:
+            for m in wl.matrices:
+                oracle.rtn_quantize_ref(workloads.weight(HEADLINE, 0, m.name, "cpu"))
+                qbytes += workloads.quantize_bytes(m.N, m.K)
+            qpasses += 1
+            if time.perf_counter() - t1 >= budget_s / 3:
+                break
+        tq = time.perf_counter() - t1
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full M=1 passes over both {HEADLINE} matrices "
                       f"(2560x9216 and 9216x2560, fp64 oracle.w4_linear_ref), {t:.1f} s, "
                       "one BLAS/NumPy thread",
-            "seconds": round(t, 2)}
+            "seconds": round(t, 2),
+            "quantize": {"GBps": round(qbytes / tq / 1e9, 4), "seconds": round(tq, 2),
+                         "sample": f"{qpasses} passes of oracle.rtn_quantize_ref over both matrices "
+                                   "(weights drawn again each pass, draw time included)"}}
 
 
 # ----------------------------------------------------------------------------
 
-def roofline(pair_m1, bytes_per_call, copies):
+def measure_read_peak(torch, w4, gib=4, reps=5):
+    """Bandwidth of a plain streaming read (grid-stride, non-temporal 16-byte loads) over
+    `gib` GiB on this GPU: the practical ceiling for a kernel that only reads."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(w4.__file__), "libw4_bench.so"))
+    nb = gib << 30
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    grid = 2048
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda:0")
+
+    def run():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.w4bench_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nb),
+                                ctypes.c_void_p(sink.data_ptr()), grid, s) == 0
+
+    g = capture(torch, run, reps)
+    t = time_graph(torch, g, 2, 1) / (2 * reps)
+    del g, buf
+    torch.cuda.empty_cache()
+    gbs = nb / t / 1e9
+    log(f"[bench] streaming read peak: {gbs:.0f} GB/s")
+    return {"GBps": round(gbs, 1), "pct_of_nameplate": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "kernel": "grid-stride read, non-temporal 16-byte loads, 2048 blocks of 256 threads",
+            "bytes": nb}
+
+
+def roofline(pair_m1, bytes_per_call, copies, read_peak=None):
     """Dominant kernel: the M = 1 dot2 linear on the headline pair, one launch per step."""
     achieved = pair_m1["GBps"]
     traffic = None
@@ -284,6 +345,7 @@ def roofline(pair_m1, bytes_per_call, copies):
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": "linear_gemv_kernel<1, 1, 4> (dot2, x in LDS), 64 linears per launch",
+            "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4) if read_peak else None,
             "algorithmic_bytes_per_launch": copies * sum(bytes_per_call.values()),
             "avg_launch_us": pair_m1["us_per_launch"],
             "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this launch, copy-kernel calibrated"
@@ -294,13 +356,24 @@ def roofline(pair_m1, bytes_per_call, copies):
 # rocprofv3 output summaries (used to write the text files under profiles/)
 # ----------------------------------------------------------------------------
 
-def summarize_trace(path):
-    """Per (kernel, grid, block) duration statistics from a rocprofv3 kernel_trace.csv."""
+def summarize_trace(path, last=0):
+    """Per (kernel, grid, block) duration statistics from a rocprofv3 kernel_trace.csv.
+    With `last`, also the mean duration of the last `last` dispatches of the
+    headline launch (the timed steps of the M = 1 batched pass)."""
     import csv
     import statistics
 
+    rows = list(csv.DictReader(open(path)))
+    if last:
+        head = sorted((r for r in rows if HEADLINE_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
+                       and int(r["Grid_Size_X"]) == HEADLINE_GRID), key=lambda r: int(r["Start_Timestamp"]))
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in head]
+        tail = d[-last:]
+        print(f"headline {HEADLINE_KERNEL}, grid {HEADLINE_GRID} threads: {len(d)} dispatches; "
+              f"last {len(tail)} (the timed steps): mean {statistics.mean(tail):.2f} us, "
+              f"median {statistics.median(tail):.2f} us, min {min(tail):.2f} us, max {max(tail):.2f} us\n")
     groups = {}
-    for r in csv.DictReader(open(path)):
+    for r in rows:
         name = r["Kernel_Name"].replace("w4::(anonymous namespace)::", "")
         key = (name[:70], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])), int(r["Grid_Size_Y"]),
                int(r["Workgroup_Size_X"]))
@@ -373,15 +446,20 @@ def write_counters(fetch_csv, write_csv, copy_mb, out_path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=48)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--copies", type=int, default=32)
     ap.add_argument("--stacks", default="27b,70b")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
+    ap.add_argument("--stack-modes", default="",
+                    help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run the plain copy kernel on this many MiB (counter calibration)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print a duration summary of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--trace-last", type=int, default=0,
+                    help="with --trace-summary: mean of the last N headline dispatches (the timed steps)")
     ap.add_argument("--counter-summary", metavar="COUNTER_COLLECTION_CSV",
                     help="print a summary of a rocprofv3 counter collection and exit")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -393,7 +471,7 @@ def main():
                        COUNTERS_FILE)
         return
     if args.trace_summary:
-        summarize_trace(args.trace_summary)
+        summarize_trace(args.trace_summary, args.trace_last)
         return
     if args.counter_summary:
         summarize_counters(args.counter_summary)
@@ -419,7 +497,11 @@ def main():
     stacks = {}
     for s in [s for s in args.stacks.split(",") if s and s != "none"]:
         stacks["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
-                                           max(2, args.warmup))
+                                           max(2, args.warmup),
+                                           [int(m) for m in args.stack_ms.split(",") if m] or None,
+                                           [m for m in args.stack_modes.split(",") if m] or None)
+
+    read_peak = measure_read_peak(torch, w4)
 
     if args.calibrate_copy_mb:
         import ctypes
@@ -456,14 +538,16 @@ def main():
                    "weight_copies": args.copies, "linears_per_step": 2 * args.copies,
                    "launch": "w4_linear_batched, 64 independent linears per launch",
                    "group": 128, "weights": "int4 codes + fp32 scales", "x": "bf16",
-                   "timing": "hip graph replay, events on the replay stream"},
+                   "timing": "hip graph replay, events on the replay stream",
+                   "min_warmup_ms": int(MIN_WARMUP_S * 1000)},
         "pct_of_peak": m1["pct_of_peak"],
         "us_per_linear": m1["us_per_linear"],
         "per_call_m1": pair[1]["per_call"],
         "pair": pair,
         "quantize": quant,
         "stacks": stacks,
-        "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies),
+        "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies, read_peak),
+        "hbm_read_peak_measured": read_peak,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

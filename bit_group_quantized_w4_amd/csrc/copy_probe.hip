@@ -1,7 +1,8 @@
 // Measurement helpers for bench.py only (built as libw4_bench.so, not part of
 // the w4 C ABI): a plain 16-byte copy kernel of known size, used to calibrate
 // the HBM byte counters read by rocprofv3, and a read-only streaming kernel
-// that gives the bandwidth a plain sequential read reaches on this GPU.
+// (non-temporal 16-byte loads, grid-stride) that gives the
+// bandwidth a plain sequential read reaches on this GPU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,17 +16,21 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict_
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the streaming (non-temporal) policy the linear kernels use.
+__device__ __forceinline__ v4u ld_nt(const uint4* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+}
+
 __global__ __launch_bounds__(kThreads) void read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                         uint32_t* __restrict__ sink) {
+  // consecutive wavefronts read consecutive 1 KiB pieces (one 16-byte load per
+  // lane per step): the friendliest order for the DRAM pages
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-  }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+    const v4u a = ld_nt(src + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   // one value per thread keeps the loads live; the sink is tiny
