@@ -187,7 +187,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
     for (int r = 0; r < R; ++r) {
       const float dv = quad_elem(sc[r], s);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[r][e] += dv * c[r][e];
+      for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(dv, c[r][e], acc[r][e]);
     }
   };
 
@@ -302,9 +302,9 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   // Stage the slab's x rows (rows beyond M repeat row M-1; their outputs are
   // dropped) together with the start value of every (row, group, quarter).
   // Element e = (row, group, quarter) covers 4 x 16 bytes; groups past K read
-  // zeros.  The first element of every thread is loaded before the weight
-  // prologue: loads retire in issue order, so x queued behind the weights
-  // would wait for their HBM round trip.
+  // zeros.  Leading elements are loaded before the weight prologue: loads
+  // retire in issue order, so x queued behind the weights would wait for
+  // their HBM round trip.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
   const int total = MT * GP * 4;
   auto x_off = [&](int e) -> uint32_t {
@@ -334,8 +334,12 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   };
 
   {
-    uint4 v[4];
-    load_x(x_off(threadIdx.x), v);
+    // The first kPre elements of every thread (all of x for M = 1 and K up to
+    // 32 768 with 4+ wavefronts) go out before the weight prologue.
+    constexpr int kPre = 2;
+    uint4 v[kPre][4];
+#pragma unroll
+    for (int p = 0; p < kPre; ++p) load_x(x_off(threadIdx.x + p * NW * 64), v[p]);
     __builtin_amdgcn_sched_barrier(0);
     // Weight prologue in the loop's order (scales, then groups 0..3); a
     // wavefront with no quads (j0 == j1) reads zeros here.
@@ -345,16 +349,21 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
       issue_group(s, w.j0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Consume x here, before the branch, so the loads are not sunk into it
+    // Consume x here, before the branches, so the loads are not sunk into them
     // (behind the weights).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
-    if ((int)threadIdx.x < total) store_x(threadIdx.x, v);
-  }
-  for (int e = threadIdx.x + NW * 64; e < total; e += NW * 64) {
-    uint4 v[4];
-    load_x(x_off(e), v);
-    store_x(e, v);
+    for (int p = 0; p < kPre; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        asm volatile("" : "+v"(v[p][i].x), "+v"(v[p][i].y), "+v"(v[p][i].z), "+v"(v[p][i].w));
+#pragma unroll
+    for (int p = 0; p < kPre; ++p)
+      if ((int)threadIdx.x + p * NW * 64 < total) store_x(threadIdx.x + p * NW * 64, v[p]);
+    for (int e = threadIdx.x + kPre * NW * 64; e < total; e += NW * 64) {
+      uint4 t[4];
+      load_x(x_off(e), t);
+      store_x(e, t);
+    }
   }
   __syncthreads();
 
@@ -399,7 +408,7 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
         float c = o.c0[mm];
 #pragma unroll
         for (int e = 0; e < 16; ++e) c = dot2(o.bb[r][e], o.xv[mm][e], c);
-        acc[r][mm] += dv * c;
+        acc[r][mm] = fmaf(dv, c, acc[r][mm]);
       }
     }
   };
@@ -516,7 +525,8 @@ int choose_cfg_gemv(const BatchArgs& a) {
     kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   }
   if (rows < 256) return find_cfg(1, 8);
-  return find_cfg(1, kmax >= 16384 ? 8 : 4);
+  // long K: more wavefronts per row block, once there are enough row blocks
+  return find_cfg(1, kmax >= 16384 && rows >= 400 ? 8 : 4);
 }
 
 int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
