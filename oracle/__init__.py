@@ -13,7 +13,8 @@ What it computes (sources are the public pages this project is built from):
   compressed": the equation q = clip(round(w/d) + z, qmin, qmax), w_hat = d(q - z)
   with its symbol table, groups of 128 consecutive inputs along each row, and
   section 2's settings table (RTN, symmetric, min/max range, group 128, no
-  clipping search).  Done in fp32, as the kernel does.
+  clipping search).  Done in fp32, as the kernel does; optionally with the
+  scale stored as bf16 (16-bit scales) and the codes taken against it.
 * ``w4_linear_ref`` -- y = W_hat x from the same section 1 (the 2560x9216 FFN
   example) with 4-bit weights and BF16 inputs (section 2 settings table), in
   fp64.
@@ -25,7 +26,7 @@ rational arithmetic, brute force on small inputs, closed forms and hand-derived
 fixtures in ``tests/golden/``; none is "parity unpinned".
 """
 
-from .bf16 import bf16_bits_to_f64
+from .bf16 import bf16_bits_to_f64, f32_to_bf16_bits
 from .linear import dequantize_ref, w4_linear_ref
 from .packing import pack_canonical, unpack_canonical
 from .rtn import GROUP, NAN_BITS, QMAX, QMIN, rtn_quantize_ref
@@ -37,6 +38,7 @@ __all__ = [
     "QMIN",
     "bf16_bits_to_f64",
     "dequantize_ref",
+    "f32_to_bf16_bits",
     "pack_canonical",
     "rtn_quantize_ref",
     "unpack_canonical",

@@ -19,19 +19,23 @@ from .rtn import GROUP
 
 
 def dequantize_ref(q, d):
-    """W_hat[n, k] = d[n, k // 128] * q[n, k] in float64, [N, K]."""
+    """W_hat[n, k] = d[n, k // 128] * q[n, k] in float64, [N, K].
+
+    d: float32 scales, or uint16 bf16 bit patterns (16-bit scales)."""
     q = np.asarray(q)
     d = np.asarray(d)
     N, K = q.shape
     if d.shape != (N, K // GROUP):
         raise ValueError("d must be [N, K/128]")
-    return np.repeat(d.astype(np.float64), GROUP, axis=1) * q.astype(np.float64)
+    d64 = bf16_bits_to_f64(d) if d.dtype == np.uint16 else d.astype(np.float64)
+    return np.repeat(d64, GROUP, axis=1) * q.astype(np.float64)
 
 
 def w4_linear_ref(x_bits, q, d):
     """y[m, n] = sum_k x[m, k] * W_hat[n, k].
 
-    x_bits: uint16 [M, K] bf16 bit patterns; q: int8 [N, K]; d: float32 [N, K/128].
+    x_bits: uint16 [M, K] bf16 bit patterns; q: int8 [N, K]; d: float32 [N, K/128]
+    (or uint16 bf16 bit patterns for 16-bit scales).
     Returns (y, absdot), both float64 [M, N]; absdot = sum_k |x[m,k] * W_hat[n,k]|
     is the scale the output tolerance is stated against.
     """

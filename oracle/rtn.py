@@ -24,9 +24,17 @@ Readings where the pages are silent (each one also listed in the design doc):
 * a group holding a NaN or an infinity gets d = NaN (bit pattern 0x7FC00000)
   and all codes 0; a group whose scale is zero (all-zero group, or a/7
   underflowing to 0) gets all codes 0.
+
+16-bit scales (the study's checkpoint sizes imply about two bytes per group;
+the pages do not name the format): d is computed in fp32 as above, then
+stored as the nearest bf16 value (ties to even, NaN -> 0x7FC0), and the
+codes divide by that stored value widened back to fp32: t = fl32(w / d16).
+bf16 keeps fp32's exponent range, so no scale overflows or needs clamping.
 """
 
 import numpy as np
+
+from .bf16 import f32_to_bf16_bits
 
 GROUP = 128
 QMIN = -8
@@ -48,13 +56,16 @@ def _round_half_away(t32):
     return np.trunc(t + np.copysign(0.5, t))
 
 
-def rtn_quantize_ref(W):
+def rtn_quantize_ref(W, scale_dtype="f32"):
     """Quantize a weight matrix group by group.
 
     W: float32 array [N, K] (N outputs, K inputs), K a positive multiple of 128.
     Returns (q, d): q int8 [N, K] holding codes in [-8, 7] (canonical order),
-    d float32 [N, K/128] holding one restore scale per (row, group).
+    d [N, K/128] holding one restore scale per (row, group): float32 values
+    for scale_dtype "f32", uint16 bf16 bit patterns for "bf16".
     """
+    if scale_dtype not in ("f32", "bf16"):
+        raise ValueError("scale_dtype must be 'f32' or 'bf16'")
     W = np.asarray(W)
     if W.dtype != np.float32 or W.ndim != 2:
         raise TypeError("W must be a 2-D float32 array")
@@ -73,13 +84,18 @@ def rtn_quantize_ref(W):
     with np.errstate(all="ignore"):
         d = (a / np.float32(7.0)).astype(np.float32)
     d[~finite] = _nan_f32()
+    if scale_dtype == "bf16":
+        # Step 2b: the stored scale is the nearest bf16; the codes use it.
+        d_bits = f32_to_bf16_bits(d)
+        d = (d_bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
     usable = finite & (d != 0)
 
     # Step 3: codes q = clip(round(w / d) + z, qmin, qmax), z = 0, dividing by
-    # the stored fp32 scale.
+    # the stored scale (widened to fp32).
     safe_d = np.where(usable, d, np.float32(1.0)).astype(np.float32)
     with np.errstate(all="ignore"):
         t = (Wg / safe_d[:, :, None]).astype(np.float32)
     q = np.clip(_round_half_away(t), QMIN, QMAX)
     q[~usable] = 0
-    return q.reshape(N, K).astype(np.int8), d
+    q = q.reshape(N, K).astype(np.int8)
+    return (q, d_bits) if scale_dtype == "bf16" else (q, d)

@@ -214,6 +214,81 @@ def check_group_count(quantize):
 
 
 # ----------------------------------------------------------------------------
+# 16-bit (bf16) restore scales
+# ----------------------------------------------------------------------------
+
+def bf16_nearest_bits(v32):
+    """bf16 bit pattern nearest to the fp32 value v32 (exact rationals, ties to even)."""
+    b = f32_bits(v32)
+    base = b >> 16
+    best = None
+    for c in (base - 1, base, base + 1):  # same-sign neighbours around v (toward and away)
+        if c < 0 or (c & 0x7F80) == 0x7F80:
+            continue
+        val = Fraction(float(bits_f32((c & 0xFFFF) << 16)))
+        key = (abs(val - Fraction(float(v32))), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c & 0xFFFF)
+    return best[1]
+
+
+def widened(quantize16):
+    """A 16-bit-scale quantizer seen as one returning fp32 scales (the values the codes use)."""
+    def quantize(W):
+        q, d_bits = quantize16(W)
+        return q, (np.asarray(d_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return quantize
+
+
+def scale16_tie_weights(groups=16, seed=0):
+    """Rows of one group each whose fp32 scale fl32(max|w| / 7) lies exactly halfway
+    between two bf16 values (half with an even lower neighbour, half odd)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    while len(rows) < groups:
+        base = int(rng.integers(0x3800, 0x4200))
+        if (base & 1) != (len(rows) & 1):
+            continue
+        d32 = bits_f32((base << 16) | 0x8000)
+        a = np.float32(np.float64(d32) * 7.0)
+        if np.float32(a / np.float32(7.0)) != d32:
+            continue
+        w = (rng.uniform(-1.0, 1.0, 128) * float(a)).astype(np.float32)
+        w[int(rng.integers(0, 128))] = a if rng.random() < 0.5 else -a
+        rows.append(w)
+    return np.stack(rows)
+
+
+def check_scale16_exact(quantize16, W):
+    """d16 is the bf16 nearest to the fp32 scale fl32(max|w| / 7) (exact rationals)."""
+    q, d_bits = quantize16(W)
+    N, K = W.shape
+    for n in range(N):
+        for g in range(K // 128):
+            grp = W[n, 128 * g:128 * g + 128]
+            a = max(abs(Fraction(float(v))) for v in grp)
+            exp = bf16_nearest_bits(f32_nearest(a / 7))
+            _check(int(d_bits[n, g]) == exp,
+                   f"16-bit scale ({n},{g}): got {int(d_bits[n, g]):#06x}, nearest bf16 is {exp:#06x}")
+
+
+def check_bf16_narrowing(to_bf16, reference):
+    """Narrowing fp32 -> bf16 agrees with a library's round-to-nearest-even conversion on
+    random magnitudes, exact ties, the overflow threshold, subnormals and infinities."""
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-85, 85, 20000))).astype(np.float32)
+    ties = ((rng.integers(0, 2 ** 31, 4000).astype(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000))
+    edge = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0xFF7F8000, 0x00008000, 0x00018000, 0x80008000,
+                     0x00000001, 0x7F800000, 0xFF800000, 0x00000000, 0x80000000], dtype=np.uint32)
+    v = np.concatenate([v, ties.view(np.float32), edge.view(np.float32)])
+    v = v[~np.isnan(v)]  # NaN payloads are not specified by round-to-nearest-even
+    got = np.asarray(to_bf16(v), dtype=np.uint16)
+    exp = np.asarray(reference(v), dtype=np.uint16)
+    bad = np.nonzero(got != exp)[0]
+    _check(bad.size == 0, f"bf16 narrowing differs at {v[bad[:4]].tolist()}")
+
+
+# ----------------------------------------------------------------------------
 # pins of the linear
 # ----------------------------------------------------------------------------
 

@@ -237,3 +237,102 @@ def test_packing_mutants_are_caught(kind):
 
     with pytest.raises(pins.PinFailure):
         pins.check_packing(pack, oracle.unpack_canonical)
+
+
+# ----------------------------------------------------------------------------
+# 16-bit (bf16) restore scales
+# ----------------------------------------------------------------------------
+
+def Q16(W):
+    return oracle.rtn_quantize_ref(W, "bf16")
+
+
+def _torch_bf16(v):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_narrowing_matches_library():
+    pins.check_bf16_narrowing(oracle.f32_to_bf16_bits, _torch_bf16)
+
+
+def _all_scale16_pins(quantize16):
+    pins.check_scale16_exact(quantize16, pins.scale16_tie_weights())
+    for seed in (0, 1):
+        W = pins.toy_weights(seed)
+        pins.check_scale16_exact(quantize16, W)
+        pins.check_codes_bruteforce(pins.widened(quantize16), W)
+        pins.check_round_trip(pins.widened(quantize16), W)
+    rng = np.random.default_rng(6)
+    pins.check_invariants(pins.widened(quantize16), (rng.standard_t(4, size=(32, 512)) * 0.01).astype(np.float32))
+
+
+def test_scale16_pins():
+    _all_scale16_pins(Q16)
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    pins.check_scale_equivariance(pins.widened(Q16), W, 5)
+    pins.check_group_permutation(pins.widened(Q16), W)
+
+
+def test_scale16_special_groups():
+    """Zero, NaN/Inf and fp32-subnormal groups under 16-bit scales."""
+    W = np.zeros((4, 128), dtype=np.float32)
+    W[1, 3] = np.nan
+    W[2, :] = (np.arange(128) - 64).astype(np.float32) * np.float32(2.0 ** -140)
+    W[3, 7] = np.inf
+    q, d = Q16(W)
+    assert d.dtype == np.uint16
+    assert d[0, 0] == 0 and not q[0].any()
+    assert d[1, 0] == 0x7FC0 and not q[1].any() and d[3, 0] == 0x7FC0 and not q[3].any()
+    a = np.float32(64 * 2.0 ** -140)
+    assert d[2, 0] == pins.bf16_nearest_bits(pins.f32_nearest(pins.Fraction(float(a)) / 7))
+
+
+def test_scale16_linear_uses_widened_scales():
+    rng = np.random.default_rng(3)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    q, d16 = Q16(W)
+    x = _x_bits(2, 256, 3)
+    y16, _ = L(x, q, d16)
+    y32, _ = L(x, q, (d16.astype(np.uint32) << 16).view(np.float32))
+    assert np.array_equal(y16, y32)
+
+
+def _mutant_quantize16(kind):
+    def quantize(W):
+        N, K = W.shape
+        Wg = W.reshape(N, K // 128, 128)
+        finite = np.isfinite(Wg).all(axis=2)
+        with np.errstate(all="ignore"):
+            d = (np.abs(Wg).max(axis=2) / np.float32(7)).astype(np.float32)
+        d[~finite] = rtn_mod._nan_f32()
+        bits = d.view(np.uint32)
+        if kind == "truncate":
+            d16 = (bits >> 16).astype(np.uint16)
+        elif kind == "ties_away":
+            d16 = ((bits + np.uint32(0x8000)) >> 16).astype(np.uint16)
+        else:
+            d16 = oracle.f32_to_bf16_bits(d)
+        dw = (d16.astype(np.uint32) << 16).view(np.float32)
+        divisor = d if kind == "divide_by_f32" else dw
+        usable = finite & (dw != 0)
+        safe = np.where(usable, divisor, np.float32(1)).astype(np.float32)
+        with np.errstate(all="ignore"):
+            t = (Wg / safe[:, :, None]).astype(np.float32)
+        r = np.clip(rtn_mod._round_half_away(t), -8, 7)
+        r[~usable] = 0
+        return r.reshape(N, K).astype(np.int8), d16
+    return quantize
+
+
+@pytest.mark.parametrize("kind", ["truncate", "ties_away", "divide_by_f32"])
+def test_scale16_mutants_are_caught(kind):
+    _all_scale16_pins(Q16)
+    with pytest.raises(pins.PinFailure):
+        _all_scale16_pins(_mutant_quantize16(kind))
+
+
+def test_bf16_narrowing_mutant_is_caught():
+    with pytest.raises(pins.PinFailure):
+        pins.check_bf16_narrowing(lambda v: (np.asarray(v).view(np.uint32) >> 16).astype(np.uint16), _torch_bf16)
