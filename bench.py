@@ -101,19 +101,22 @@ def time_graph(torch, g, replays, warmup):
 # headline: single-matrix pair, weight copies rotated through HBM
 # ----------------------------------------------------------------------------
 
-def bench_pair(torch, w4, workloads, steps, warmup, copies):
+def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms=None, quantize=True):
     dev = torch.device("cuda:0")
     wl = workloads.WORKLOADS[HEADLINE]
+    scale_dtype = scale_dtype or torch.float32
+    sb = 2 if scale_dtype == torch.bfloat16 else 4
+    tag = "" if sb == 4 else " (16-bit scales)"
     mats = []
     for m in wl.matrices:
         W = torch.from_numpy(workloads.weight(HEADLINE, 0, m.name, "cpu")).to(dev)
-        q0, d0 = w4.quantize_rtn(W)
+        q0, d0 = w4.quantize_rtn(W, scale_dtype=scale_dtype)
         qs = [q0] + [q0.clone() for _ in range(copies - 1)]
         ds = [d0] + [d0.clone() for _ in range(copies - 1)]
         mats.append((m, W, qs, ds))
     torch.cuda.synchronize()
     out = {}
-    for M in wl.ms:
+    for M in (ms or wl.ms):
         xs = [workloads.activations(HEADLINE, 0, m.name, M, dev) for (m, _, _, _) in mats]
         ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
         # batched mode: every linear of a step writes its own output
@@ -131,7 +134,7 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
             for b in range(0, len(items), w4.MAX_BATCH):
                 w4.linear_batched(items[b:b + w4.MAX_BATCH])
 
-        step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats)
+        step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K, sb) for (m, _, _, _) in mats)
         res = {}
         for mode, fn in (("per_call", step), ("batched", step_batched)):
             gs = graph_steps(steps)
@@ -148,15 +151,15 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
                 "ms_per_step": round(t / steps * 1e3, 4),
                 "launches_per_step": launches // steps,
             }
-            log(f"[bench] {HEADLINE} M={M} {mode}: {gbs:.0f} GB/s, "
+            log(f"[bench] {HEADLINE}{tag} M={M} {mode}: {gbs:.0f} GB/s, "
                 f"{t / (steps * copies * len(mats)) * 1e6:.2f} us per linear")
             del g
-        res["bytes_per_call"] = {m.name: workloads.algorithmic_bytes(M, m.N, m.K) for (m, _, _, _) in mats}
+        res["bytes_per_call"] = {m.name: workloads.algorithmic_bytes(M, m.N, m.K, sb) for (m, _, _, _) in mats}
         out[M] = res
     # quantization throughput (rows a1-a4), same matrices, rotated over 4 fp32 copies
     qout = {}
     nq = min(4, copies)
-    for (m, W, qs, ds) in mats:
+    for (m, W, qs, ds) in (mats if quantize else []):
         Ws = [W] + [W.clone() for _ in range(nq - 1)]
 
         def qstep():
@@ -166,7 +169,7 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies):
         g = capture(torch, qstep)
         t = time_graph(torch, g, max(3, steps // 4), 2)
         n = max(3, steps // 4) * nq
-        qb = workloads.quantize_bytes(m.N, m.K)
+        qb = workloads.quantize_bytes(m.N, m.K, sb)
         qout[m.name] = {"GBps": round(n * qb / t / 1e9, 1), "us_per_call": round(t / n * 1e6, 2),
                         "bytes_per_call": qb}
         log(f"[bench] quantize {m.name} {m.N}x{m.K}: {n * qb / t / 1e9:.0f} GB/s")
@@ -192,16 +195,18 @@ def _shared_input_groups(wl):
     return [by_tag[t] for t in order]
 
 
-def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_modes=None):
+def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_modes=None, scale_dtype=None):
     dev = torch.device("cuda:0")
     wl = workloads.WORKLOADS[name]
+    scale_dtype = scale_dtype or torch.float32
+    sb = 2 if scale_dtype == torch.bfloat16 else 4
     t0 = time.time()
     layers = []
     for layer in range(wl.layers):
         mats = []
         for m in wl.matrices:
             W = workloads.weight(name, layer, m.name, dev)
-            q, d = w4.quantize_rtn(W)
+            q, d = w4.quantize_rtn(W, scale_dtype=scale_dtype)
             del W
             mats.append((m, q, d))
         layers.append(mats)
@@ -234,7 +239,7 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
             g = capture(torch, step)
             t = time_graph(torch, g, steps, warmup)
             per = t / steps
-            nbytes = workloads.stack_bytes(name, M)
+            nbytes = workloads.stack_bytes(name, M, sb)
             gbs = nbytes / per / 1e9
             flops = 2.0 * M * workloads.stack_weights(name)
             res[M][mode] = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1),
@@ -243,10 +248,10 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
                             "launches_per_pass": len(layers) * len(grp),
                             "useful_tflops": round(flops / per / 1e12, 2),
                             "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3)}
-            log(f"[bench] stack {name} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
+            log(f"[bench] stack {name}{'' if sb == 4 else ' (16-bit scales)'} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
                 f"{1 / per:.1f} passes/s")
             del g
-        res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M)
+        res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M, sb)
     del layers
     torch.cuda.empty_cache()
     return res
@@ -501,6 +506,14 @@ def main():
                                            [int(m) for m in args.stack_ms.split(",") if m] or None,
                                            [m for m in args.stack_modes.split(",") if m] or None)
 
+    # 16-bit scales: the headline pair at M = 1 and the stacks' realistic launch mode at M = 1
+    s16 = {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
+                              scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
+    for s in [s for s in args.stacks.split(",") if s and s != "none"]:
+        s16["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
+                                        max(2, args.warmup), [1], ["fused_shared_input"],
+                                        scale_dtype=torch.bfloat16)
+
     read_peak = measure_read_peak(torch, w4)
 
     if args.calibrate_copy_mb:
@@ -548,6 +561,7 @@ def main():
         "stacks": stacks,
         "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies, read_peak),
         "hbm_read_peak_measured": read_peak,
+        "scales_16bit": s16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -44,6 +44,12 @@ SIGNATURES = {
     "w4_linear_batched": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
     "w4_pack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_unpack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    # 16-bit (bf16) scales
+    "w4_quantize_rtn_s16": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_linear_s16": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
+    "w4_linear_batched_s16": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
+    "w4_pack_s16": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_unpack_s16": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
 }
 
 
@@ -106,21 +112,38 @@ def scale_count(N, K):
     return int(_lib.w4_scale_count(N, K))
 
 
-def _empty_packed(N, K, device):
+# Scale formats: fp32, or bf16 (16-bit scales; the *_s16 entry points).
+SCALE_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _scale_dtype(d):
+    if not isinstance(d, torch.Tensor) or d.dtype not in SCALE_DTYPES:
+        raise TypeError("scales must be a float32 or bfloat16 torch.Tensor")
+    return d.dtype
+
+
+def _empty_packed(N, K, device, scale_dtype=torch.float32):
     nb, ns = packed_bytes(N, K), scale_count(N, K)
     if nb == 0:
         _check(W4_ERR_SHAPE, "packed buffers")
     return (torch.empty(nb, dtype=torch.uint8, device=device),
-            torch.empty(ns, dtype=torch.float32, device=device))
+            torch.empty(ns, dtype=scale_dtype, device=device))
 
 
-def quantize_rtn(W, out=None):
-    """fp32 weight [N, K] on the GPU -> (codes uint8 [packed_bytes], scales fp32 [scale_count]),
-    both in the library's native layout."""
+def quantize_rtn(W, out=None, scale_dtype=torch.float32):
+    """fp32 weight [N, K] on the GPU -> (codes uint8 [packed_bytes], scales [scale_count]),
+    both in the library's native layout.  scale_dtype torch.bfloat16 stores 16-bit scales
+    (the codes are then taken against the stored bf16 value)."""
     N, K = W.shape
-    q, d = out if out is not None else _empty_packed(N, K, W.device)
-    _check(_lib.w4_quantize_rtn(_dev(W, torch.float32, "W"), N, K, _dev(q, torch.uint8, "q"),
-                                _dev(d, torch.float32, "d"), _stream(W)), "w4_quantize_rtn")
+    if out is not None:
+        scale_dtype = _scale_dtype(out[1])
+    elif scale_dtype not in SCALE_DTYPES:
+        raise TypeError("scale_dtype must be torch.float32 or torch.bfloat16")
+    q, d = out if out is not None else _empty_packed(N, K, W.device, scale_dtype)
+    fn, name = ((_lib.w4_quantize_rtn_s16, "w4_quantize_rtn_s16") if scale_dtype == torch.bfloat16
+                else (_lib.w4_quantize_rtn, "w4_quantize_rtn"))
+    _check(fn(_dev(W, torch.float32, "W"), N, K, _dev(q, torch.uint8, "q"), _dev(d, scale_dtype, "d"),
+              _stream(W)), name)
     return q, d
 
 
@@ -132,9 +155,10 @@ def linear(x, q, d, N, path="auto", out=None):
         raise ValueError("out must be [M, N]")
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
-    _check(_lib.w4_linear_ex(_dev(x, torch.bfloat16, "x"), M, K, _dev(q, torch.uint8, "q"),
-                             _dev(d, torch.float32, "d"), N, _dev(y, torch.bfloat16, "y"),
-                             PATHS[path], _stream(x)), "w4_linear")
+    sd = _scale_dtype(d)
+    fn, name = ((_lib.w4_linear_s16, "w4_linear_s16") if sd == torch.bfloat16 else (_lib.w4_linear_ex, "w4_linear"))
+    _check(fn(_dev(x, torch.bfloat16, "x"), M, K, _dev(q, torch.uint8, "q"), _dev(d, sd, "d"), N,
+              _dev(y, torch.bfloat16, "y"), PATHS[path], _stream(x)), name)
     return y
 
 
@@ -149,34 +173,42 @@ def linear_batched(items, path="auto"):
     items = list(items)
     descs = (LinearDesc * max(1, len(items)))()
     stream = None
+    sd = _scale_dtype(items[0][2]) if items else torch.float32
     for i, (x, q, d, N, y) in enumerate(items):
         M, K = x.shape
         if y.shape != (M, N):
             raise ValueError(f"item {i}: y must be [M, N]")
+        if _scale_dtype(d) != sd:
+            raise TypeError("all items of a batch must use the same scale dtype")
         descs[i] = LinearDesc(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
-                              _dev(d, torch.float32, "d").value, N, _dev(y, torch.bfloat16, "y").value)
+                              _dev(d, sd, "d").value, N, _dev(y, torch.bfloat16, "y").value)
         stream = stream or _stream(x)
-    _check(_lib.w4_linear_batched(descs, len(items), PATHS[path], stream), "w4_linear_batched")
+    # the fp32 and bf16 descriptor structs have the same layout (pointers and int64s)
+    fn, name = ((_lib.w4_linear_batched_s16, "w4_linear_batched_s16") if sd == torch.bfloat16
+                else (_lib.w4_linear_batched, "w4_linear_batched"))
+    _check(fn(descs, len(items), PATHS[path], stream), name)
     return [it[4] for it in items]
 
 
 def pack(q_canon, d_canon, out=None):
-    """Canonical codes int8 [N, K] and scales fp32 [N, K/128] -> native (q, d)."""
+    """Canonical codes int8 [N, K] and scales [N, K/128] (fp32 or bf16) -> native (q, d)."""
     N, K = q_canon.shape
-    q, d = out if out is not None else _empty_packed(N, K, q_canon.device)
-    _check(_lib.w4_pack(_dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, torch.float32, "d_canon"),
-                        N, K, _dev(q, torch.uint8, "q"), _dev(d, torch.float32, "d"),
-                        _stream(q_canon)), "w4_pack")
+    sd = _scale_dtype(d_canon)
+    q, d = out if out is not None else _empty_packed(N, K, q_canon.device, sd)
+    fn, name = (_lib.w4_pack_s16, "w4_pack_s16") if sd == torch.bfloat16 else (_lib.w4_pack, "w4_pack")
+    _check(fn(_dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, sd, "d_canon"), N, K,
+              _dev(q, torch.uint8, "q"), _dev(d, sd, "d"), _stream(q_canon)), name)
     return q, d
 
 
 def unpack(q, d, N, K):
-    """Native (q, d) -> canonical codes int8 [N, K] and scales fp32 [N, K/128]."""
+    """Native (q, d) -> canonical codes int8 [N, K] and scales [N, K/128] (d's dtype)."""
+    sd = _scale_dtype(d)
     qc = torch.empty((N, K), dtype=torch.int8, device=q.device)
-    dc = torch.empty((N, K // GROUP), dtype=torch.float32, device=q.device)
-    _check(_lib.w4_unpack(_dev(q, torch.uint8, "q"), _dev(d, torch.float32, "d"), N, K,
-                          _dev(qc, torch.int8, "q_canon"), _dev(dc, torch.float32, "d_canon"),
-                          _stream(q)), "w4_unpack")
+    dc = torch.empty((N, K // GROUP), dtype=sd, device=q.device)
+    fn, name = (_lib.w4_unpack_s16, "w4_unpack_s16") if sd == torch.bfloat16 else (_lib.w4_unpack, "w4_unpack")
+    _check(fn(_dev(q, torch.uint8, "q"), _dev(d, sd, "d"), N, K, _dev(qc, torch.int8, "q_canon"),
+              _dev(dc, sd, "d_canon"), _stream(q)), name)
     return qc, dc
 
 
@@ -187,8 +219,8 @@ class W4Linear:
         self.q, self.d, self.N, self.K = q, d, N, K
 
     @classmethod
-    def from_float(cls, W):
-        q, d = quantize_rtn(W)
+    def from_float(cls, W, scale_dtype=torch.float32):
+        q, d = quantize_rtn(W, scale_dtype=scale_dtype)
         return cls(q, d, W.shape[0], W.shape[1])
 
     def __call__(self, x, path="auto", out=None):
@@ -196,7 +228,8 @@ class W4Linear:
 
 
 __all__ = [
-    "GROUP", "LIB_PATH", "MAX_BATCH", "PATHS", "SIGNATURES", "LinearDesc", "W4Error", "W4Linear",
+    "GROUP", "LIB_PATH", "MAX_BATCH", "PATHS", "SCALE_DTYPES", "SIGNATURES", "LinearDesc", "W4Error",
+    "W4Linear",
     "library", "linear", "linear_batched",
     "pack", "packed_bytes", "quantize_rtn", "scale_count", "unpack",
 ]

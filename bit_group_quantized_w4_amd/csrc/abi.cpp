@@ -41,19 +41,33 @@ w4_status hip_status(hipError_t e) {
   return W4_ERR_HIP;
 }
 
+// One linear of a call, whatever the scale format (fp32 or bf16 scales).
+struct LinearArgs {
+  const uint16_t* x;
+  int64_t M, K;
+  const uint8_t* q;
+  const void* d;
+  int64_t N;
+  uint16_t* y;
+};
+
+template <typename Desc>
+LinearArgs args_of(const Desc& l) {
+  return LinearArgs{l.x, l.M, l.K, l.q_packed, l.d_packed, l.N, l.y};
+}
+
 // Checks one linear of a call; on success appends it to the batch.
-w4_status check_linear(const w4_linear_desc& l, w4::BatchArgs& a) {
+w4_status check_linear(const LinearArgs& l, w4::BatchArgs& a) {
   if (l.M < 0 || l.M > kMaxM || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
   if (l.M == 0 || l.N == 0) return W4_OK;  // empty: nothing to launch
   // The kernels address codes with 32-bit offsets below 2 GiB and x below 1 GiB.
   if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31 || 2 * (size_t)l.M * l.K > (size_t)1 << 30) return W4_ERR_SHAPE;
-  if (!l.x || !l.q_packed || !l.d_packed || !l.y) return W4_ERR_NULL;
-  if (!aligned(l.x, 16) || !aligned(l.q_packed, 16) || !aligned(l.d_packed, 16) || !aligned(l.y, 2))
-    return W4_ERR_ALIGN;
+  if (!l.x || !l.q || !l.d || !l.y) return W4_ERR_NULL;
+  if (!aligned(l.x, 16) || !aligned(l.q, 16) || !aligned(l.d, 16) || !aligned(l.y, 2)) return W4_ERR_ALIGN;
   w4::LinearDesc& d = a.desc[a.count++];
   d.x = l.x;
-  d.q = l.q_packed;
-  d.d = l.d_packed;
+  d.q = l.q;
+  d.d = l.d;
   d.y = l.y;
   d.M = (int)l.M;
   d.K = (int)l.K;
@@ -63,15 +77,15 @@ w4_status check_linear(const w4_linear_desc& l, w4::BatchArgs& a) {
 }
 
 // Every output must be disjoint from every input and every other output of the call.
-w4_status check_aliasing(const w4_linear_desc* l, int count) {
+w4_status check_aliasing(const LinearArgs* l, int count, size_t scale_elem) {
   for (int i = 0; i < count; ++i) {
     if (l[i].M <= 0 || l[i].N <= 0) continue;
     const size_t yb = 2 * (size_t)l[i].M * l[i].N;
     for (int j = 0; j < count; ++j) {
       if (l[j].M <= 0 || l[j].N <= 0) continue;
       if (overlaps(l[i].y, yb, l[j].x, 2 * (size_t)l[j].M * l[j].K) ||
-          overlaps(l[i].y, yb, l[j].q_packed, w4_packed_bytes(l[j].N, l[j].K)) ||
-          overlaps(l[i].y, yb, l[j].d_packed, 4 * w4_scale_count(l[j].N, l[j].K)))
+          overlaps(l[i].y, yb, l[j].q, w4_packed_bytes(l[j].N, l[j].K)) ||
+          overlaps(l[i].y, yb, l[j].d, scale_elem * w4_scale_count(l[j].N, l[j].K)))
         return W4_ERR_ARG;
       if (j != i && overlaps(l[i].y, yb, l[j].y, 2 * (size_t)l[j].M * l[j].N)) return W4_ERR_ARG;
     }
@@ -79,14 +93,84 @@ w4_status check_aliasing(const w4_linear_desc* l, int count) {
   return W4_OK;
 }
 
-w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, hipStream_t stream) {
+w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, bool s16, hipStream_t stream) {
   if (a.count == 0) return W4_OK;
   if (path == W4_PATH_AUTO) path = auto_path(max_m, max_k);
   if (path == W4_PATH_GEMV) {
     if (w4::gemv_lds_bytes(1, max_k) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
-    return hip_status(w4::launch_linear_gemv(a, w4::gemv_rows_per_slab(max_m, max_k), stream));
+    return hip_status(w4::launch_linear_gemv(a, w4::gemv_rows_per_slab(max_m, max_k), s16, stream));
   }
-  return hip_status(w4::launch_linear_mfma(a, stream));
+  return hip_status(w4::launch_linear_mfma(a, s16, stream));
+}
+
+template <typename Desc>
+w4_status linear_batched(const Desc* linears, int count, int path, bool s16, hipStream_t stream) {
+  if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
+  if (count < 0 || count > W4_MAX_BATCH) return W4_ERR_ARG;
+  if (count == 0) return W4_OK;
+  if (!linears) return W4_ERR_NULL;
+  w4::BatchArgs a;
+  a.count = 0;
+  LinearArgs args[W4_MAX_BATCH];
+  int64_t max_m = 0, max_k = 0;
+  for (int i = 0; i < count; ++i) {
+    args[i] = args_of(linears[i]);
+    const w4_status st = check_linear(args[i], a);
+    if (st != W4_OK) return st;
+    if (args[i].M > 0 && args[i].N > 0) {
+      max_m = args[i].M > max_m ? args[i].M : max_m;
+      max_k = args[i].K > max_k ? args[i].K : max_k;
+    }
+  }
+  const w4_status al = check_aliasing(args, count, s16 ? 2 : 4);
+  if (al != W4_OK) return al;
+  return run_batch(a, path, max_m, max_k, s16, stream);
+}
+
+w4_status quantize(const float* W, int64_t N, int64_t K, uint8_t* q_packed, void* d_packed, bool s16,
+                   hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!W || !q_packed || !d_packed) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16)) return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = (s16 ? 2 : 4) * w4_scale_count(N, K), wb = 4 * (size_t)N * K;
+  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, W, wb) || overlaps(d_packed, db, W, wb))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_quantize_rtn(W, N, K, q_packed, d_packed, s16, stream));
+}
+
+w4_status pack(const int8_t* q_canon, const void* d_canon, int64_t N, int64_t K, uint8_t* q_packed,
+               void* d_packed, bool s16, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
+  const size_t e = s16 ? 2 : 4;
+  if (!aligned(q_canon, 16) || !aligned(d_canon, e) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
+    return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = e * w4_scale_count(N, K);
+  const size_t qcb = (size_t)N * K, dcb = e * (size_t)N * (K / kGroup);
+  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, q_canon, qcb) ||
+      overlaps(q_packed, qb, d_canon, dcb) || overlaps(d_packed, db, q_canon, qcb) ||
+      overlaps(d_packed, db, d_canon, dcb))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_pack(q_canon, d_canon, N, K, q_packed, d_packed, s16, stream));
+}
+
+w4_status unpack(const uint8_t* q_packed, const void* d_packed, int64_t N, int64_t K, int8_t* q_canon,
+                 void* d_canon, bool s16, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
+  const size_t e = s16 ? 2 : 4;
+  if (!aligned(q_canon, 16) || !aligned(d_canon, e) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
+    return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = e * w4_scale_count(N, K);
+  const size_t qcb = (size_t)N * K, dcb = e * (size_t)N * (K / kGroup);
+  if (overlaps(q_canon, qcb, d_canon, dcb) || overlaps(q_canon, qcb, q_packed, qb) ||
+      overlaps(q_canon, qcb, d_packed, db) || overlaps(d_canon, dcb, q_packed, qb) ||
+      overlaps(d_canon, dcb, d_packed, db))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_unpack(q_packed, d_packed, N, K, q_canon, d_canon, s16, stream));
 }
 
 }  // namespace
@@ -121,35 +205,20 @@ size_t w4_scale_count(int64_t N, int64_t K) {
 
 w4_status w4_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed, float* d_packed,
                           hipStream_t stream) {
-  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
-  if (N == 0) return W4_OK;
-  if (!W || !q_packed || !d_packed) return W4_ERR_NULL;
-  if (!aligned(W, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16)) return W4_ERR_ALIGN;
-  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K), wb = 4 * (size_t)N * K;
-  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, W, wb) || overlaps(d_packed, db, W, wb))
-    return W4_ERR_ARG;
-  return hip_status(w4::launch_quantize_rtn(W, N, K, q_packed, d_packed, stream));
+  return quantize(W, N, K, q_packed, d_packed, false, stream);
+}
+
+w4_status w4_quantize_rtn_s16(const float* W, int64_t N, int64_t K, uint8_t* q_packed, uint16_t* d_packed,
+                              hipStream_t stream) {
+  return quantize(W, N, K, q_packed, d_packed, true, stream);
 }
 
 w4_status w4_linear_batched(const w4_linear_desc* linears, int count, int path, hipStream_t stream) {
-  if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
-  if (count < 0 || count > W4_MAX_BATCH) return W4_ERR_ARG;
-  if (count == 0) return W4_OK;
-  if (!linears) return W4_ERR_NULL;
-  w4::BatchArgs a;
-  a.count = 0;
-  int64_t max_m = 0, max_k = 0;
-  for (int i = 0; i < count; ++i) {
-    const w4_status st = check_linear(linears[i], a);
-    if (st != W4_OK) return st;
-    if (linears[i].M > 0 && linears[i].N > 0) {
-      max_m = linears[i].M > max_m ? linears[i].M : max_m;
-      max_k = linears[i].K > max_k ? linears[i].K : max_k;
-    }
-  }
-  const w4_status al = check_aliasing(linears, count);
-  if (al != W4_OK) return al;
-  return run_batch(a, path, max_m, max_k, stream);
+  return linear_batched(linears, count, path, false, stream);
+}
+
+w4_status w4_linear_batched_s16(const w4_linear_desc_s16* linears, int count, int path, hipStream_t stream) {
+  return linear_batched(linears, count, path, true, stream);
 }
 
 w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
@@ -163,36 +232,30 @@ w4_status w4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_pa
   return w4_linear_ex(x, M, K, q_packed, d_packed, N, y, W4_PATH_AUTO, stream);
 }
 
+w4_status w4_linear_s16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                        const uint16_t* d_packed, int64_t N, uint16_t* y, int path, hipStream_t stream) {
+  const w4_linear_desc_s16 l = {x, M, K, q_packed, d_packed, N, y};
+  return w4_linear_batched_s16(&l, 1, path, stream);
+}
+
 w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
                   uint8_t* q_packed, float* d_packed, hipStream_t stream) {
-  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
-  if (N == 0) return W4_OK;
-  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
-  if (!aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
-    return W4_ERR_ALIGN;
-  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K);
-  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, q_canon, (size_t)N * K) ||
-      overlaps(q_packed, qb, d_canon, 4 * (size_t)N * (K / kGroup)) ||
-      overlaps(d_packed, db, q_canon, (size_t)N * K) ||
-      overlaps(d_packed, db, d_canon, 4 * (size_t)N * (K / kGroup)))
-    return W4_ERR_ARG;
-  return hip_status(w4::launch_pack(q_canon, d_canon, N, K, q_packed, d_packed, stream));
+  return pack(q_canon, d_canon, N, K, q_packed, d_packed, false, stream);
+}
+
+w4_status w4_pack_s16(const int8_t* q_canon, const uint16_t* d_canon, int64_t N, int64_t K,
+                      uint8_t* q_packed, uint16_t* d_packed, hipStream_t stream) {
+  return pack(q_canon, d_canon, N, K, q_packed, d_packed, true, stream);
 }
 
 w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
                     int8_t* q_canon, float* d_canon, hipStream_t stream) {
-  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
-  if (N == 0) return W4_OK;
-  if (!q_canon || !d_canon || !q_packed || !d_packed) return W4_ERR_NULL;
-  if (!aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(q_packed, 16) || !aligned(d_packed, 16))
-    return W4_ERR_ALIGN;
-  const size_t qb = w4_packed_bytes(N, K), db = 4 * w4_scale_count(N, K);
-  const size_t qcb = (size_t)N * K, dcb = 4 * (size_t)N * (K / kGroup);
-  if (overlaps(q_canon, qcb, d_canon, dcb) || overlaps(q_canon, qcb, q_packed, qb) ||
-      overlaps(q_canon, qcb, d_packed, db) || overlaps(d_canon, dcb, q_packed, qb) ||
-      overlaps(d_canon, dcb, d_packed, db))
-    return W4_ERR_ARG;
-  return hip_status(w4::launch_unpack(q_packed, d_packed, N, K, q_canon, d_canon, stream));
+  return unpack(q_packed, d_packed, N, K, q_canon, d_canon, false, stream);
+}
+
+w4_status w4_unpack_s16(const uint8_t* q_packed, const uint16_t* d_packed, int64_t N, int64_t K,
+                        int8_t* q_canon, uint16_t* d_canon, hipStream_t stream) {
+  return unpack(q_packed, d_packed, N, K, q_canon, d_canon, true, stream);
 }
 
 }  // extern "C"

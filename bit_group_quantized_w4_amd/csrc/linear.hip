@@ -30,6 +30,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 namespace w4 {
 namespace {
 
@@ -48,7 +50,26 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// One lane's four scales of a quad: fp32 (16 bytes) or bf16 (8 bytes).
+template <bool S16>
+using ScaleQuad = typename std::conditional<S16, uint2, uint4>::type;
+
 __device__ __forceinline__ float quad_elem(const uint4& v, int s) { return __uint_as_float(word(v, s)); }
+__device__ __forceinline__ float quad_elem(const uint2& v, int s) {
+  const uint32_t w = s < 2 ? v.x : v.y;
+  return __uint_as_float((s & 1) ? (w & 0xFFFF0000u) : (w << 16));  // bf16 -> fp32 is exact
+}
+
+template <int AUX>
+__device__ __forceinline__ void bload_into(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4& dst) {
+  dst = bload<AUX>(r, off);
+}
+template <int AUX>
+__device__ __forceinline__ void bload_into(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2& dst) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
+  dst = make_uint2(v.x, v.y);
+}
 
 __device__ __forceinline__ bf16x8 unpack_step(uint32_t w, const UnpackConsts& uc) {
   uint32_t b[4];
@@ -88,9 +109,11 @@ __device__ __forceinline__ Work locate_one(int N, int R, int MT) {
   return Work{0, (b - slab * panels) * R, slab * MT};
 }
 
-// Geometry of one linear and the weight-side buffers of one wavefront.
-template <int R>
+// Geometry of one linear and the weight-side buffers of one wavefront
+// (S16: the scales are bf16, 8 bytes per row and quad instead of 16).
+template <int R, bool S16>
 struct Weights {
+  static constexpr uint32_t kScaleBytes = S16 ? 8u : 16u;  // one row's quad
   int G, Q, GP, nb, rvalid, j0, j1;
   __amdgpu_buffer_rsrc_t rq, rd;
   uint32_t qo[R], so[R];  // byte offsets of this lane's 16 bytes at group 0 / quad 0, per row block
@@ -104,18 +127,20 @@ struct Weights {
     j0 = (int)(((int64_t)Q * wave) / nw);
     j1 = (int)(((int64_t)Q * (wave + 1)) / nw);
     rq = make_rsrc(D.q, (uint32_t)nb * GP * 1024u);
-    rd = make_rsrc(D.d, (uint32_t)nb * GP * 64u);
+    rd = make_rsrc(D.d, (uint32_t)nb * GP * 4u * kScaleBytes);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // row blocks past the end re-read the last one; they are never stored
       const uint32_t rb = (uint32_t)min(wk.rb0 + r, nb - 1);
       qo[r] = (rb * GP * kTileLanes + lane) * 16u;
-      so[r] = (rb * Q * kTileRows + (lane & 15)) * 16u;
+      so[r] = (rb * Q * kTileRows + (lane & 15)) * kScaleBytes;
     }
   }
   // base added to qo / so: the group's (quad's) offset, or past the end
   __device__ __forceinline__ uint32_t qbase(int j, int g) const { return j < j1 ? (uint32_t)g * 1024u : kOobW; }
-  __device__ __forceinline__ uint32_t sbase(int j) const { return j < j1 ? (uint32_t)j * 256u : kOobW; }
+  __device__ __forceinline__ uint32_t sbase(int j) const {
+    return j < j1 ? (uint32_t)j * kTileRows * kScaleBytes : kOobW;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -126,12 +151,12 @@ struct Weights {
 // value is itself one MFMA chain with B = -1.5.  One quad is in flight: the x
 // operands of a quad alone take 64 VGPRs.
 // ---------------------------------------------------------------------------
-template <int R, int NW>
+template <int R, int NW, bool S16>
 __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
   const int M = D.M, K = D.K, N = D.N;
-  const Weights<R> w(D, wk, lane, wave, NW);
+  const Weights<R, S16> w(D, wk, lane, wave, NW);
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
   const int xrow = wk.m0 + nl;
@@ -141,7 +166,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 
   uint4 bx[4][4];
   uint4 bw[4][R];
-  uint4 sc[R], sn[R];  // scale quads: current and next
+  ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
 
   auto issue_group = [&](int s, int j) {
     const int g = 4 * j + s;
@@ -151,10 +176,10 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 #pragma unroll
     for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
-  auto issue_scales = [&](uint4 (&dst)[R], int j) {
+  auto issue_scales = [&](ScaleQuad<S16> (&dst)[R], int j) {
     const uint32_t sb = w.sbase(j);
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = bload<kNonTemporal>(w.rd, w.so[r] + sb);
+    for (int r = 0; r < R; ++r) bload_into<kNonTemporal>(w.rd, w.so[r] + sb, dst[r]);
   };
 
   const UnpackConsts uc = unpack_consts();
@@ -249,20 +274,20 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 }
 
 // Batched launch: the block finds its linear in the kernel arguments.
-template <int R, int NW>
+template <int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
   const Work wk = locate(args, R, 16);
-  mfma_body<R, NW>(args.desc[wk.di], wk);
+  mfma_body<R, NW, S16>(args.desc[wk.di], wk);
 }
 
 // Launch of one linear.  Its arguments are plain scalars that the hardware
 // preloads into SGPRs at wave launch, so the kernel does not wait for a
 // kernel-argument fetch before it can issue its first loads.
-template <int R, int NW>
-__global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const float* d,
+template <int R, int NW, bool S16>
+__global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const void* d,
                                                            uint16_t* y, int M, int K, int N) {
   const LinearDesc D{x, q, d, y, M, K, N, 0};
-  mfma_body<R, NW>(D, locate_one(N, R, 16));
+  mfma_body<R, NW, S16>(D, locate_one(N, R, 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -275,7 +300,7 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, co
 // deeper ring per wavefront.  The four quarters of a row are summed with
 // cross-lane shuffles at the end.
 // ---------------------------------------------------------------------------
-template <int MT, int R, int NW>
+template <int MT, int R, int NW, bool S16>
 __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   // LDS: x of the slab, [MT][GP * 16] uint4 (zero past K), then the start
   // values -1.5 * sum(x) of every (row, group, quarter), [MT][GP][4] floats.
@@ -283,20 +308,20 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
   const int M = D.M, K = D.K, N = D.N;
-  const Weights<R> w(D, wk, lane, wave, NW);
+  const Weights<R, S16> w(D, wk, lane, wave, NW);
   const int GP = w.GP;
 
   uint4 bw[4][R];
-  uint4 sc[R], sn[R];  // scale quads: current and next
+  ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
   auto issue_group = [&](int s, int j) {
     const uint32_t qb = w.qbase(j, 4 * j + s);
 #pragma unroll
     for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
-  auto issue_scales = [&](uint4 (&dst)[R], int j) {
+  auto issue_scales = [&](ScaleQuad<S16> (&dst)[R], int j) {
     const uint32_t sb = w.sbase(j);
 #pragma unroll
-    for (int r = 0; r < R; ++r) dst[r] = bload<kNonTemporal>(w.rd, w.so[r] + sb);
+    for (int r = 0; r < R; ++r) bload_into<kNonTemporal>(w.rd, w.so[r] + sb, dst[r]);
   };
 
   // Stage the slab's x rows (rows beyond M repeat row M-1; their outputs are
@@ -462,17 +487,17 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   }
 }
 
-template <int MT, int R, int NW>
+template <int MT, int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs args) {
   const Work wk = locate(args, R, MT);
-  gemv_body<MT, R, NW>(args.desc[wk.di], wk);
+  gemv_body<MT, R, NW, S16>(args.desc[wk.di], wk);
 }
 
-template <int MT, int R, int NW>
-__global__ __launch_bounds__(NW * 64) void linear_gemv_one(const uint16_t* x, const uint8_t* q, const float* d,
+template <int MT, int R, int NW, bool S16>
+__global__ __launch_bounds__(NW * 64) void linear_gemv_one(const uint16_t* x, const uint8_t* q, const void* d,
                                                            uint16_t* y, int M, int K, int N) {
   const LinearDesc D{x, q, d, y, M, K, N, 0};
-  gemv_body<MT, R, NW>(D, locate_one(N, R, MT));
+  gemv_body<MT, R, NW, S16>(D, locate_one(N, R, MT));
 }
 
 // ---------------------------------------------------------------------------
@@ -482,9 +507,10 @@ struct Cfg {
   int R, NW;
 };
 
-// Every (R, NW) compiled for each kernel.  W4_MFMA_CFG / W4_GEMV_CFG ("R,NW")
-// may pick one of them for measurement; anything else falls back to the
-// built-in choice.
+// Every (R, NW) compiled for each kernel with fp32 scales (16-bit scales:
+// the built-in choices only).  W4_MFMA_CFG / W4_GEMV_CFG ("R,NW") may pick
+// one of them for measurement; anything else falls back to the built-in
+// choice.
 constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {2, 4}, {2, 8}, {1, 16}, {4, 4}, {4, 8}, {1, 2}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -541,43 +567,74 @@ int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
   return total;
 }
 
+template <int MT, bool S16, int I>
+void launch_gemv_at(unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
+  constexpr Cfg c = kCfgs[I];
+  if (a.count == 1) {
+    const LinearDesc& l = a.desc[0];
+    linear_gemv_one<MT, c.R, c.NW, S16><<<blocks, c.NW * 64, lds, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+  } else {
+    linear_gemv_kernel<MT, c.R, c.NW, S16><<<blocks, c.NW * 64, lds, st>>>(a);
+  }
+}
+
 template <int MT>
-void launch_gemv_cfg(int ci, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
+void launch_gemv_cfg(int ci, bool s16, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
+  if (s16) {  // 16-bit scales: the configurations the built-in choice uses
+    if (ci == 1) launch_gemv_at<MT, true, 1>(blocks, lds, st, a);
+    else launch_gemv_at<MT, true, 0>(blocks, lds, st, a);
+    return;
+  }
   switch (ci) {
-#define W4_CASE(i)                                                                                       \
-  case i:                                                                                                \
-    if (a.count == 1) {                                                                                  \
-      const LinearDesc& l = a.desc[0];                                                                   \
-      linear_gemv_one<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(l.x, l.q, l.d, \
-                                                                                         l.y, l.M, l.K, l.N); \
-    } else {                                                                                             \
-      linear_gemv_kernel<MT, kCfgs[i].R, kCfgs[i].NW><<<blocks, kCfgs[i].NW * 64, lds, st>>>(a);         \
-    }                                                                                                    \
+#define W4_CASE(i) \
+  case i:          \
+    launch_gemv_at<MT, false, i>(blocks, lds, st, a); \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
   }
 }
 
+template <bool S16, int I>
+void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
+  constexpr Cfg c = kCfgs[I];
+  if (a.count == 1) {
+    const LinearDesc& l = a.desc[0];
+    linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+  } else {
+    linear_mfma_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
+  }
+}
+
+static_assert(kCfgs[0].R == 1 && kCfgs[0].NW == 4 && kCfgs[1].R == 1 && kCfgs[1].NW == 8 &&
+                  kCfgs[2].R == 2 && kCfgs[2].NW == 4 && kCfgs[5].R == 4 && kCfgs[5].NW == 4,
+              "16-bit-scale launches name these configurations by index");
+
+// Configurations compiled with 16-bit scales: the built-in choices.
+bool s16_cfg_mfma(int ci) { return ci == find_cfg(1, 4) || ci == find_cfg(2, 4) || ci == find_cfg(4, 4); }
+bool s16_cfg_gemv(int ci) { return ci == find_cfg(1, 4) || ci == find_cfg(1, 8); }
+
 }  // namespace
 
-hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream) {
+hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream) {
   const int env = cfg_from_env("W4_MFMA_CFG");
-  const int ci = env >= 0 ? env : choose_cfg_mfma(a);
+  int ci = env >= 0 ? env : choose_cfg_mfma(a);
+  if (s16 && !s16_cfg_mfma(ci)) ci = choose_cfg_mfma(a);
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, 16);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const unsigned nb = (unsigned)blocks;
+  if (s16) {
+    if (ci == find_cfg(4, 4)) launch_mfma_at<true, 5>(nb, stream, a);
+    else if (ci == find_cfg(2, 4)) launch_mfma_at<true, 2>(nb, stream, a);
+    else launch_mfma_at<true, 0>(nb, stream, a);
+    return hipGetLastError();
+  }
   switch (ci) {
-#define W4_CASE(i)                                                                                          \
-  case i:                                                                                                   \
-    if (a.count == 1) {                                                                                     \
-      const LinearDesc& l = a.desc[0];                                                                      \
-      linear_mfma_one<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(l.x, l.q, l.d, \
-                                                                                              l.y, l.M, l.K, l.N); \
-    } else {                                                                                                \
-      linear_mfma_kernel<kCfgs[i].R, kCfgs[i].NW><<<(unsigned)blocks, kCfgs[i].NW * 64, 0, stream>>>(a);    \
-    }                                                                                                       \
+#define W4_CASE(i) \
+  case i:          \
+    launch_mfma_at<false, i>(nb, stream, a); \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
@@ -591,10 +648,11 @@ int gemv_rows_per_slab(int64_t M, int64_t K) {
   return 1;
 }
 
-hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
+hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream) {
   const int env = cfg_from_env("W4_GEMV_CFG");
   int ci = env >= 0 ? env : choose_cfg_gemv(a);
   if (MT == 4 && kCfgs[ci].NW == 16) ci = find_cfg(1, 8);  // 16 wavefronts x 4 rows exceeds 128 VGPRs
+  if (s16 && !s16_cfg_gemv(ci)) ci = choose_cfg_gemv(a);
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, MT);
   if (blocks <= 0) return hipSuccess;
@@ -602,9 +660,9 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream) {
   int kmax = 0;
   for (int i = 0; i < a.count; ++i) kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   const size_t lds = (size_t)gemv_lds_bytes(MT, kmax);
-  if (MT == 4) launch_gemv_cfg<4>(ci, (unsigned)blocks, lds, stream, a);
-  else if (MT == 2) launch_gemv_cfg<2>(ci, (unsigned)blocks, lds, stream, a);
-  else launch_gemv_cfg<1>(ci, (unsigned)blocks, lds, stream, a);
+  if (MT == 4) launch_gemv_cfg<4>(ci, s16, (unsigned)blocks, lds, stream, a);
+  else if (MT == 2) launch_gemv_cfg<2>(ci, s16, (unsigned)blocks, lds, stream, a);
+  else launch_gemv_cfg<1>(ci, s16, (unsigned)blocks, lds, stream, a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 // 32-input steps), the group max is finished across the four lanes that share
 // a row, and the lane writes its 16 bytes of codes; the 16 scales of the tile
 // are written by the lanes of the first quarter into their rows' scale quads.
+// Scales are stored as fp32 or, in the 16-bit variant, as the nearest bf16
+// (the codes then divide by that stored value).
 // Weights are read with raw buffer loads over the tile's row block: padding
 // rows (N .. Np-1) and padding groups (G .. 4Q-1) read zeros, so they come out
 // as code 0 with scale 0 without a branch.  The loads keep the default cache
@@ -63,10 +65,12 @@ __device__ __forceinline__ uint32_t native_word(const int u[8]) {
   return rotl32(v, 3);
 }
 
+// S: the stored scale, float (fp32) or uint16_t (bf16 bit pattern).
+template <typename S>
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restrict__ W, int N,
                                                            int K, int G, int GP, int64_t ntiles,
                                                            uint4* __restrict__ qp,
-                                                           float* __restrict__ dp) {
+                                                           S* __restrict__ dp) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, nl = lane & 15, kb = lane >> 4;
   // the wavefront index is uniform across the wavefront: keep the tile, and
@@ -110,8 +114,18 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
   bad |= __shfl_xor(bad, 16);
   bad |= __shfl_xor(bad, 32);
 
-  // Restore scale: +-max maps to code +-7.
-  const float d = bad ? __uint_as_float(kNanBits) : amax / kMaxCode;
+  // Restore scale: +-max maps to code +-7.  A 16-bit scale is stored as the
+  // nearest bf16, and the codes are taken against that stored value.
+  const float d32 = bad ? __uint_as_float(kNanBits) : amax / kMaxCode;
+  S stored;
+  float d;
+  if constexpr (sizeof(S) == 2) {
+    stored = f32_to_bf16_rne(d32);
+    d = __uint_as_float((uint32_t)stored << 16);
+  } else {
+    stored = d32;
+    d = d32;
+  }
   const bool usable = !bad && d != 0.0f;
   // Unusable groups (d = 0 or NaN) divide by 1 and are then forced to code 0,
   // which keeps the loop free of branches.
@@ -153,13 +167,14 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     words[i] = native_word(u);
   }
   qp[tile * kTileLanes + lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (kb == 0) dp[scale_index(r, GP, g, nl)] = d;
+  if (kb == 0) dp[scale_index(r, GP, g, nl)] = stored;
 }
 
+template <typename S>
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc,
-                                                   const float* __restrict__ dc, int N, int K,
+                                                   const S* __restrict__ dc, int N, int K,
                                                    int G, int GP, int64_t ntiles,
-                                                   uint4* __restrict__ qp, float* __restrict__ dp) {
+                                                   uint4* __restrict__ qp, S* __restrict__ dp) {
   TileAt t;
   if (!tile_at(ntiles, GP, t)) return;
   const bool real = t.n < N && t.g < G;
@@ -182,13 +197,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ qc
     words[i] = native_word(u);
   }
   qp[t.tile * kTileLanes + t.lane] = make_uint4(words[0], words[1], words[2], words[3]);
-  if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = real ? dc[t.n * G + t.g] : 0.0f;
+  if (t.kb == 0) dp[scale_index(t.r, GP, t.g, t.nl)] = real ? dc[t.n * G + t.g] : S(0);
 }
 
+template <typename S>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint4* __restrict__ qp,
-                                                     const float* __restrict__ dp, int N, int K,
+                                                     const S* __restrict__ dp, int N, int K,
                                                      int G, int GP, int64_t ntiles,
-                                                     int8_t* __restrict__ qc, float* __restrict__ dc) {
+                                                     int8_t* __restrict__ qc, S* __restrict__ dc) {
   TileAt t;
   if (!tile_at(ntiles, GP, t)) return;
   if (t.n >= N || t.g >= G) return;
@@ -227,26 +243,43 @@ inline Grid grid_of(int64_t N, int64_t K) {
 }  // namespace
 
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
-                               float* d_packed, hipStream_t stream) {
+                               void* d_packed, bool s16, hipStream_t stream) {
   const Grid g = grid_of(N, K);
-  quantize_rtn_kernel<<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles,
-                                                     reinterpret_cast<uint4*>(q_packed), d_packed);
+  uint4* qp = reinterpret_cast<uint4*>(q_packed);
+  if (s16)
+    quantize_rtn_kernel<uint16_t><<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles, qp,
+                                                                 static_cast<uint16_t*>(d_packed));
+  else
+    quantize_rtn_kernel<float><<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles, qp,
+                                                              static_cast<float*>(d_packed));
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
-                       uint8_t* q_packed, float* d_packed, hipStream_t stream) {
+hipError_t launch_pack(const int8_t* q_canon, const void* d_canon, int64_t N, int64_t K,
+                       uint8_t* q_packed, void* d_packed, bool s16, hipStream_t stream) {
   const Grid g = grid_of(N, K);
-  pack_kernel<<<g.blocks, 256, 0, stream>>>(q_canon, d_canon, (int)N, (int)K, g.G, g.GP, g.ntiles,
-                                            reinterpret_cast<uint4*>(q_packed), d_packed);
+  uint4* qp = reinterpret_cast<uint4*>(q_packed);
+  if (s16)
+    pack_kernel<uint16_t><<<g.blocks, 256, 0, stream>>>(q_canon, static_cast<const uint16_t*>(d_canon), (int)N,
+                                                         (int)K, g.G, g.GP, g.ntiles, qp,
+                                                         static_cast<uint16_t*>(d_packed));
+  else
+    pack_kernel<float><<<g.blocks, 256, 0, stream>>>(q_canon, static_cast<const float*>(d_canon), (int)N, (int)K,
+                                                      g.G, g.GP, g.ntiles, qp, static_cast<float*>(d_packed));
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
-                         int8_t* q_canon, float* d_canon, hipStream_t stream) {
+hipError_t launch_unpack(const uint8_t* q_packed, const void* d_packed, int64_t N, int64_t K,
+                         int8_t* q_canon, void* d_canon, bool s16, hipStream_t stream) {
   const Grid g = grid_of(N, K);
-  unpack_kernel<<<g.blocks, 256, 0, stream>>>(reinterpret_cast<const uint4*>(q_packed), d_packed,
-                                              (int)N, (int)K, g.G, g.GP, g.ntiles, q_canon, d_canon);
+  const uint4* qp = reinterpret_cast<const uint4*>(q_packed);
+  if (s16)
+    unpack_kernel<uint16_t><<<g.blocks, 256, 0, stream>>>(qp, static_cast<const uint16_t*>(d_packed), (int)N,
+                                                           (int)K, g.G, g.GP, g.ntiles, q_canon,
+                                                           static_cast<uint16_t*>(d_canon));
+  else
+    unpack_kernel<float><<<g.blocks, 256, 0, stream>>>(qp, static_cast<const float*>(d_packed), (int)N, (int)K,
+                                                        g.G, g.GP, g.ntiles, q_canon, static_cast<float*>(d_canon));
   return hipGetLastError();
 }
 

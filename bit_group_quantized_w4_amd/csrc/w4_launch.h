@@ -23,7 +23,7 @@ inline int64_t gemv_lds_bytes(int64_t MT, int64_t K) {
 struct LinearDesc {
   const uint16_t* x;  // bf16 [M][K]
   const uint8_t* q;   // native codes
-  const float* d;     // native scale quads
+  const void* d;      // native scale quads: fp32, or bf16 in the 16-bit variant
   uint16_t* y;        // bf16 [M][N]
   int M, K, N, pad;
 };
@@ -35,18 +35,19 @@ struct BatchArgs {
   LinearDesc desc[kMaxBatch];
 };
 
+// s16: scales are bf16 bit patterns (uint16_t) instead of fp32.
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
-                               float* d_packed, hipStream_t stream);
-hipError_t launch_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
-                       uint8_t* q_packed, float* d_packed, hipStream_t stream);
-hipError_t launch_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
-                         int8_t* q_canon, float* d_canon, hipStream_t stream);
+                               void* d_packed, bool s16, hipStream_t stream);
+hipError_t launch_pack(const int8_t* q_canon, const void* d_canon, int64_t N, int64_t K,
+                       uint8_t* q_packed, void* d_packed, bool s16, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* q_packed, const void* d_packed, int64_t N, int64_t K,
+                         int8_t* q_canon, void* d_canon, bool s16, hipStream_t stream);
 
 // MFMA streaming kernel over a batch (16-row slabs of x).
-hipError_t launch_linear_mfma(BatchArgs& a, hipStream_t stream);
+hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream);
 // dot2 streaming kernel over a batch (MT-row slabs of x staged in LDS; every
 // K must satisfy gemv_lds_bytes(MT, K) <= kGemvLdsBytes).
-hipError_t launch_linear_gemv(BatchArgs& a, int MT, hipStream_t stream);
+hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream);
 // Largest slab (4, 2 or 1 rows) the dot2 kernel can stage for M rows of K.
 int gemv_rows_per_slab(int64_t M, int64_t K);
 

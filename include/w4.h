@@ -49,13 +49,16 @@
  *   Scales: the scales of row n for the four groups 4j .. 4j+3 form one
  *     16-byte quad at float index ((r*Q + j)*16 + n%16)*4 (r = n / 16),
  *     group 4j+t at offset t.
+ *   16-bit scales (the *_s16 entry points): the same quads hold bf16 bit
+ *     patterns, 8 bytes per row and quad, at uint16 index
+ *     ((r*Q + j)*16 + n%16)*4 + t.
  *   Rows N .. Np-1 and groups G .. GP-1 are padding: codes 0 (u = 8), scales 0.
  *   Total sizes: w4_packed_bytes(N, K) = Np*GP*64 bytes of codes and
  *   w4_scale_count(N, K) = Np*GP floats of scales.
  *
  * CANONICAL LAYOUT (for exchange and bit-exact comparison)
  *   codes int8 [N][K] row-major, each in [-8, 7];
- *   scales float32 [N][K/128] row-major.
+ *   scales float32 (or bf16 bit patterns for *_s16) [N][K/128] row-major.
  */
 #ifndef W4_H
 #define W4_H
@@ -100,6 +103,17 @@ typedef struct w4_linear_desc {
   int64_t N;
   uint16_t* y;             /* bf16 [M][N]                  */
 } w4_linear_desc;
+
+/* The same with 16-bit scales (bf16 bit patterns), for w4_linear_batched_s16. */
+typedef struct w4_linear_desc_s16 {
+  const uint16_t* x;        /* bf16 [M][K]                  */
+  int64_t M;
+  int64_t K;
+  const uint8_t* q_packed;  /* native codes of the N x K W  */
+  const uint16_t* d_packed; /* native bf16 scales           */
+  int64_t N;
+  uint16_t* y;              /* bf16 [M][N]                  */
+} w4_linear_desc_s16;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* w4_status_str(int status);
@@ -186,6 +200,35 @@ w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_
  */
 w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
                     int8_t* q_canon, float* d_canon, hipStream_t stream);
+
+/*
+ * 16-bit scales.  The study's checkpoint sizes imply about two bytes per
+ * group without naming a format; these entry points store each scale as the
+ * bf16 nearest to the fp32 scale max|w| / 7 (ties to even; NaN groups get
+ * 0x7FC0) and take the codes against that stored value: q = clamp(round(
+ * fl32(w / d16)), -8, 7) with ties away from zero.  Scale storage halves
+ * (2 instead of 4 bytes per group of 128 weights).  Each function has the
+ * contract of its fp32-scale counterpart above, with scales as uint16 bf16
+ * bit patterns: w4_scale_count(N, K) elements of 2 bytes natively (16-byte
+ * aligned), [N][K/128] canonically (2-byte aligned).
+ */
+w4_status w4_quantize_rtn_s16(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
+                              uint16_t* d_packed, hipStream_t stream);
+
+/* y = W_hat x with 16-bit scales; `path` as for w4_linear_ex. */
+w4_status w4_linear_s16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                        const uint16_t* d_packed, int64_t N, uint16_t* y, int path,
+                        hipStream_t stream);
+
+/* Up to W4_MAX_BATCH linears with 16-bit scales in one launch. */
+w4_status w4_linear_batched_s16(const w4_linear_desc_s16* linears, int count, int path,
+                                hipStream_t stream);
+
+/* Canonical <-> native layout with 16-bit scales. */
+w4_status w4_pack_s16(const int8_t* q_canon, const uint16_t* d_canon, int64_t N, int64_t K,
+                      uint8_t* q_packed, uint16_t* d_packed, hipStream_t stream);
+w4_status w4_unpack_s16(const uint8_t* q_packed, const uint16_t* d_packed, int64_t N, int64_t K,
+                        int8_t* q_canon, uint16_t* d_canon, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -121,6 +121,30 @@ def test_batched_validation(w4):
     assert lib.w4_linear_batched(big, 1, 1, None) == ERR_SHAPE
 
 
+def test_s16_validation(w4):
+    """The 16-bit-scale entry points check their arguments like the fp32 ones."""
+    lib = w4.library()
+    src, q, d = FAKE, FAKE + 0x100000, FAKE + 0x200000
+    assert lib.w4_quantize_rtn_s16(src, 16, 100, q, d, None) == ERR_SHAPE
+    assert lib.w4_quantize_rtn_s16(None, 16, 128, q, d, None) == ERR_NULL
+    assert lib.w4_quantize_rtn_s16(src, 16, 128, q, d + 8, None) == ERR_ALIGN
+    assert lib.w4_quantize_rtn_s16(src, 16, 128, q, q + 512, None) == ERR_ARG  # codes/scales overlap
+    assert lib.w4_quantize_rtn_s16(src, 0, 128, None, None, None) == OK
+    x, y = FAKE + 0x300000, FAKE + 0x400000
+    assert lib.w4_linear_s16(x, 1, 100, q, d, 16, y, 0, None) == ERR_SHAPE
+    assert lib.w4_linear_s16(None, 1, 128, q, d, 16, y, 0, None) == ERR_NULL
+    assert lib.w4_linear_s16(x, 1, 128, q, d + 2, 16, y, 0, None) == ERR_ALIGN
+    assert lib.w4_linear_s16(x, 1, 128, q, d, 16, x, 0, None) == ERR_ARG  # output aliases x
+    assert lib.w4_linear_s16(x, 1, 128, q, d, 16, d + 16, 0, None) == ERR_ARG  # output inside the scales
+    assert lib.w4_linear_s16(x, 1, 128, q, d, 16, y, 7, None) == ERR_ARG
+    assert lib.w4_linear_s16(None, 0, 128, None, None, 16, None, 0, None) == OK
+    assert lib.w4_linear_batched_s16(None, 2, 0, None) == ERR_NULL
+    assert lib.w4_linear_batched_s16(None, 0, 0, None) == OK
+    assert lib.w4_pack_s16(src, d + 0x40000, 16, 256, None, d, None) == ERR_NULL
+    assert lib.w4_pack_s16(src, d + 0x40000 + 1, 16, 256, q, d, None) == ERR_ALIGN  # canonical bf16: 2 bytes
+    assert lib.w4_unpack_s16(q, d, -2, 256, src, src + 0x40000, None) == ERR_SHAPE
+
+
 def test_quantize_pack_unpack_validation(w4):
     lib = w4.library()
     q, d, src = FAKE, FAKE + 0x100000, FAKE + 0x200000

@@ -45,21 +45,29 @@ def check_y(y_gpu, y_ref, absdot, what):
     return worst
 
 
-def quantize_and_compare(w4, W_dev, what, rows=None):
+def _scale_bits(d_canon):
+    """Canonical scales (fp32 or bf16 tensor) -> their bit patterns (uint32 / uint16)."""
+    if d_canon.dtype == torch.bfloat16:
+        return d_canon.cpu().view(torch.int16).numpy().view(np.uint16)
+    return d_canon.cpu().numpy().view(np.uint32)
+
+
+def quantize_and_compare(w4, W_dev, what, rows=None, scale_dtype=torch.float32):
     """Quantize on the GPU, unpack, compare with the oracle (all rows or a row sample)."""
     N, K = W_dev.shape
-    q, d = w4.quantize_rtn(W_dev)
+    q, d = w4.quantize_rtn(W_dev, scale_dtype=scale_dtype)
     qc, dc = w4.unpack(q, d, N, K)
     torch.cuda.synchronize()
     if rows is None:
         W_h = W_dev.cpu().numpy()
-        qg, dg = qc.cpu().numpy(), dc.cpu().numpy()
+        qg, dg = qc.cpu().numpy(), _scale_bits(dc)
     else:
         idx = torch.as_tensor(rows, device=W_dev.device)
         W_h = W_dev.index_select(0, idx).cpu().numpy()
-        qg, dg = qc.index_select(0, idx).cpu().numpy(), dc.index_select(0, idx).cpu().numpy()
-    q_ref, d_ref = oracle.rtn_quantize_ref(W_h)
-    assert np.array_equal(dg.view(np.uint32), d_ref.view(np.uint32)), f"{what}: scales differ"
+        qg, dg = qc.index_select(0, idx).cpu().numpy(), _scale_bits(dc.index_select(0, idx))
+    q_ref, d_ref = oracle.rtn_quantize_ref(W_h, "bf16" if scale_dtype == torch.bfloat16 else "f32")
+    d_ref_bits = d_ref if d_ref.dtype == np.uint16 else d_ref.view(np.uint32)
+    assert np.array_equal(dg, d_ref_bits), f"{what}: scales differ"
     bad = np.argwhere(qg != q_ref)
     assert bad.size == 0, f"{what}: {len(bad)} codes differ, first {bad[:4].tolist()}"
     return q, d, q_ref, d_ref
@@ -355,3 +363,100 @@ def test_linear_batched_full_size_layer(w4, gpu):
         for (m, q, d, idx, (q_ref, d_ref)), (x, *_), y in zip(mats, items, ys):
             y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
             check_y(y.index_select(1, idx), y_ref, absdot, f"70b batched {m.name} M={M}")
+
+
+# ----------------------------------------------------------------------------
+# 16-bit (bf16) scales
+# ----------------------------------------------------------------------------
+
+S16 = torch.bfloat16
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_s16_quantize_toys(w4, gpu, seed):
+    _say(f"s16 quantize toys seed={seed}")
+    quantize_and_compare(w4, torch.from_numpy(pins.toy_weights(seed, N=37, K=768)).to(gpu), f"s16 toys{seed}",
+                         scale_dtype=S16)
+
+
+def test_s16_quantize_scale_ties_and_near_ties(w4, gpu):
+    _say("s16 quantize: scales halfway between bf16 values; weights near half-integer quotients")
+    quantize_and_compare(w4, torch.from_numpy(pins.scale16_tie_weights(64)).to(gpu), "s16 scale ties",
+                         scale_dtype=S16)
+    quantize_and_compare(w4, torch.from_numpy(near_tie_weights(3)).to(gpu), "s16 near ties", scale_dtype=S16)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (257, 2560), (2560, 9216)])
+def test_s16_quantize_shapes(w4, gpu, N, K):
+    _say(f"s16 quantize N={N} K={K}")
+    W = workloads.random_weight(N, K, std=0.02, seed=N + K + 1)
+    quantize_and_compare(w4, torch.from_numpy(W).to(gpu), f"s16 {N}x{K}", scale_dtype=S16)
+
+
+def test_s16_pack_unpack_roundtrip(w4, gpu):
+    _say("s16 pack/unpack")
+    N, K = 40, 640
+    rng = np.random.default_rng(4)
+    qc = torch.from_numpy(rng.integers(-8, 8, (N, K)).astype(np.int8)).to(gpu)
+    dc = torch.from_numpy(rng.standard_normal((N, K // 128)).astype(np.float32)).to(gpu).to(torch.bfloat16)
+    q, d = w4.pack(qc, dc)
+    assert d.dtype == torch.bfloat16
+    qc2, dc2 = w4.unpack(q, d, N, K)
+    assert torch.equal(qc, qc2) and torch.equal(dc.view(torch.int16), dc2.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv", "auto"])
+@pytest.mark.parametrize("M,N,K", [(1, 37, 384), (1, 1040, 4096), (4, 100, 640), (8, 200, 1408),
+                                   (16, 160, 896), (33, 24, 256)])
+def test_s16_linear_shapes(w4, gpu, M, N, K, path):
+    _say(f"s16 linear M={M} N={N} K={K} path={path}")
+    W = torch.from_numpy(workloads.random_weight(N, K, seed=M + N + K)).to(gpu)
+    q, d = w4.quantize_rtn(W, scale_dtype=S16)
+    x = workloads.random_activations(M, K, seed=M * 3 + N, device=gpu)
+    y = w4.linear(x, q, d, N, path=path)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W.cpu().numpy(), "bf16")
+    y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+    check_y(y, y_ref, absdot, f"s16 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_s16_linear_batched_and_deterministic(w4, gpu, path):
+    _say(f"s16 batched path={path}")
+    shapes = [(320, 512), (64, 512), (700, 512)]
+    for M in (1, 8):
+        x = workloads.random_activations(M, 512, seed=M, device=gpu)
+        items, refs = [], []
+        for i, (N, K) in enumerate(shapes):
+            W = torch.from_numpy(workloads.random_weight(N, K, seed=300 + i)).to(gpu)
+            q, d = w4.quantize_rtn(W, scale_dtype=S16)
+            items.append((x, q, d, N, torch.empty((M, N), dtype=torch.bfloat16, device=gpu)))
+            refs.append(W.cpu().numpy())
+        ys = w4.linear_batched(items, path=path)
+        for (xx, q, d, N, _), y, Wh in zip(items, ys, refs):
+            y1 = w4.linear(xx, q, d, N, path=path)
+            y2 = w4.linear(xx, q, d, N, path=path)
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "batched != single"
+            assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+            q_ref, d_ref = oracle.rtn_quantize_ref(Wh, "bf16")
+            y_ref, absdot = oracle.w4_linear_ref(_bits(xx), q_ref, d_ref)
+            check_y(y, y_ref, absdot, f"s16 batched N={N} M={M}")
+
+
+def test_s16_linear_full_size_70b_layer_sampled(w4, gpu):
+    """70B-class gate and down matrices at full size with 16-bit scales, M = 1 and 16; sampled rows."""
+    for name in ("gate", "down"):
+        m = next(mm for mm in workloads.WORKLOADS["stack_70b"].matrices if mm.name == name)
+        W = workloads.weight("stack_70b", 5, name, gpu)
+        q, d = w4.quantize_rtn(W, scale_dtype=S16)
+        rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(9).choice(m.N, 62)]))
+        idx = torch.as_tensor(rows, device=gpu)
+        q_ref, d_ref = oracle.rtn_quantize_ref(W.index_select(0, idx).cpu().numpy(), "bf16")
+        del W
+        for M in (1, 16):
+            _say(f"s16 70b {name} M={M}")
+            x = workloads.activations("stack_70b", 5, name, M, gpu)
+            y = w4.linear(x, q, d, m.N)
+            y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+            check_y(y.index_select(1, idx), y_ref, absdot, f"s16 70b {name} M={M}")
+        del q, d
+        torch.cuda.empty_cache()

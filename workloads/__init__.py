@@ -104,19 +104,20 @@ WORKLOADS = {
 # byte accounting (what one call must move; no arithmetic of the method)
 # ----------------------------------------------------------------------------
 
-def algorithmic_bytes(M, N, K):
-    """Bytes one linear call must move: 4-bit codes, fp32 scales, bf16 x and y."""
-    return N * K // 2 + 4 * N * (K // GROUP) + 2 * M * K + 2 * M * N
+def algorithmic_bytes(M, N, K, scale_bytes=4):
+    """Bytes one linear call must move: 4-bit codes, scales (fp32, or 2 bytes for
+    16-bit scales), bf16 x and y."""
+    return N * K // 2 + scale_bytes * N * (K // GROUP) + 2 * M * K + 2 * M * N
 
 
-def quantize_bytes(N, K):
+def quantize_bytes(N, K, scale_bytes=4):
     """Bytes one quantize call must move: fp32 weights in, codes and scales out."""
-    return 4 * N * K + N * K // 2 + 4 * N * (K // GROUP)
+    return 4 * N * K + N * K // 2 + scale_bytes * N * (K // GROUP)
 
 
-def stack_bytes(workload, M):
+def stack_bytes(workload, M, scale_bytes=4):
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
-    return w.layers * sum(algorithmic_bytes(M, m.N, m.K) for m in w.matrices)
+    return w.layers * sum(algorithmic_bytes(M, m.N, m.K, scale_bytes) for m in w.matrices)
 
 
 def stack_weights(workload):
