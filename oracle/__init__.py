@@ -20,22 +20,35 @@ What it computes (sources are the public pages this project is built from):
   fp64.
 * ``pack_canonical`` / ``unpack_canonical`` -- the canonical two-codes-per-byte
   byte order used to compare codes bit for bit.
+* ``awq_search_ref`` and its steps -- activation-aware channel scaling before
+  RTN (study, section 2: the AWQ row of the methods table, the 20-exponent
+  scale search of the settings table, and the channel-scaling and
+  output-error equations).
 
 Every function here is pinned by ``tests/test_oracle.py`` against exact
 rational arithmetic, brute force on small inputs, closed forms and hand-derived
 fixtures in ``tests/golden/``; none is "parity unpinned".
 """
 
+from .awq import (ALPHAS, awq_output_error_ref, awq_search_ref, candidate_scales_ref, channel_absmean_ref,
+                  quantize_scaled_ref, scale_activations_ref)
 from .bf16 import bf16_bits_to_f64, f32_to_bf16_bits
 from .linear import dequantize_ref, w4_linear_ref
 from .packing import pack_canonical, unpack_canonical
 from .rtn import GROUP, NAN_BITS, QMAX, QMIN, rtn_quantize_ref
 
 __all__ = [
+    "ALPHAS",
     "GROUP",
     "NAN_BITS",
     "QMAX",
     "QMIN",
+    "awq_output_error_ref",
+    "awq_search_ref",
+    "candidate_scales_ref",
+    "channel_absmean_ref",
+    "quantize_scaled_ref",
+    "scale_activations_ref",
     "bf16_bits_to_f64",
     "dequantize_ref",
     "f32_to_bf16_bits",

@@ -402,3 +402,92 @@ def nan_mask_equal(a, b):
 
 def is_close_f32(a, b):
     return math.isclose(float(a), float(b), rel_tol=0, abs_tol=0)
+
+
+# ----------------------------------------------------------------------------
+# AWQ channel scaling (study, section 2)
+# ----------------------------------------------------------------------------
+
+def awq_outlier_inputs(seed=0, N=96, K=512, T=64, share=0.01, boost=10.0):
+    """Weights ~ Student-t, and calibration rows whose few 'salient' input channels are
+    `boost` times larger than the rest (the situation channel scaling is for)."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_t(4, size=(N, K)) * 0.01 / np.sqrt(2)).astype(np.float32)
+    S = rng.choice(K, max(1, int(round(share * K))), replace=False)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, S] *= np.float32(boost)
+    return W, (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def check_awq_grid(alphas):
+    """Twenty exponents k/19, k = 0..19 (study, section 2 settings table)."""
+    _check(len(alphas) == 20, "the exponent grid has 20 points")
+    for k, a in enumerate(alphas):
+        _check(Fraction(a).limit_denominator(1000) == Fraction(k, 19), f"alpha[{k}] = {a} is not {k}/19")
+
+
+def check_awq_scales(candidate_scales, m, alpha):
+    """s_j proportional to m_j^alpha with geometric mean 1; inv_s the nearest fp32 to 1/s."""
+    s32, inv32 = candidate_scales(m, alpha)
+    ls = np.log(s32.astype(np.float64))
+    _check(abs(ls.mean()) < 1e-6, "scales must have geometric mean 1")
+    lm = np.log(np.maximum(np.asarray(m, dtype=np.float64), 1e-30))
+    _check(np.allclose(ls - ls[0], alpha * (lm - lm[0]), atol=1e-6), "scales must follow m^alpha")
+    for j in range(0, len(s32), max(1, len(s32) // 16)):
+        exp = f32_nearest(1 / Fraction(float(s32[j])))
+        _check(f32_bits(inv32[j]) == f32_bits(exp), f"inv_s[{j}] is not the nearest fp32 to 1/s")
+
+
+def check_awq_activation_scaling(scale_activations, x_bits, inv32):
+    """x' is the bf16 nearest to fl32(x * inv_s), element by element (exact rationals)."""
+    xs = np.asarray(scale_activations(x_bits, inv32), dtype=np.uint16)
+    T, K = x_bits.shape
+    for t in range(T):
+        for j in range(0, K, 7):
+            xv = Fraction(float(bits_f32(int(x_bits[t, j]) << 16)))
+            p = f32_nearest(xv * Fraction(float(inv32[j])))
+            b = f32_bits(p) >> 16
+            lo, hi = Fraction(float(bits_f32(b << 16))), Fraction(float(bits_f32((b + 1) << 16)))
+            pv = Fraction(float(p))
+            exp = b if (abs(pv - lo), b & 1) < (abs(hi - pv), (b + 1) & 1) else b + 1
+            _check(int(xs[t, j]) == exp, f"x'[{t},{j}]: {int(xs[t, j]):#06x} != {exp:#06x}")
+
+
+def check_awq_error(output_error, quantize_scaled, scale_activations, W, x_bits, s32, inv32):
+    """The search objective is the mean squared *output* error of the scaled, quantized
+    layer against W x, recomputed here with exact rationals."""
+    got = output_error(W, x_bits, s32, inv32)
+    q, d = quantize_scaled(W, s32)
+    xs = np.asarray(scale_activations(x_bits, inv32), dtype=np.uint16)
+    T, K = x_bits.shape
+    N = W.shape[0]
+    total = Fraction(0)
+    for t in range(T):
+        xr = [Fraction(float(bits_f32(int(x_bits[t, j]) << 16))) for j in range(K)]
+        xq = [Fraction(float(bits_f32(int(xs[t, j]) << 16))) for j in range(K)]
+        for n in range(N):
+            yq = sum(xq[j] * Fraction(float(d[n, j // 128])) * int(q[n, j]) for j in range(K) if q[n, j])
+            y = sum(xr[j] * Fraction(float(W[n, j])) for j in range(K))
+            total += (yq - y) ** 2
+    exp = float(total / (T * N))
+    _check(abs(got - exp) <= 1e-9 * abs(exp) + 1e-300, f"output error {got!r} != exact {exp!r}")
+
+
+def check_awq_identity(quantize_scaled_unused, W, x_bits, s32):
+    """Channel-scaling identity W'x' = Wx (study, section 2) for the fp32-scaled weight and
+    the unrounded x / s: equal to fp32 rounding of W * s."""
+    Ws = (W * s32[None, :]).astype(np.float32).astype(np.float64)
+    x = (np.asarray(x_bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    lhs = (x / s32.astype(np.float64)) @ Ws.T
+    rhs = x @ W.astype(np.float64).T
+    scale = np.abs(x) @ np.abs(W.astype(np.float64)).T
+    _check(np.all(np.abs(lhs - rhs) <= 2.0 ** -22 * scale + 1e-30), "W'x' must equal Wx")
+
+
+def check_awq_helps_on_salient_channels(search):
+    """With a few large input channels on ordinary weights, some alpha > 0 lowers the
+    output error clearly below plain RTN (alpha = 0)."""
+    W, xb = awq_outlier_inputs(seed=1)
+    k, s32, inv32, errors = search(W, xb)
+    _check(k > 0 and errors[k] < 0.9 * errors[0], f"expected alpha > 0 to help (k={k}, {errors[k] / errors[0]:.3f})")
+    _check(errors[k] == min(errors), "the chosen exponent must have the smallest error")

@@ -336,3 +336,99 @@ def test_scale16_mutants_are_caught(kind):
 def test_bf16_narrowing_mutant_is_caught():
     with pytest.raises(pins.PinFailure):
         pins.check_bf16_narrowing(lambda v: (np.asarray(v).view(np.uint32) >> 16).astype(np.uint16), _torch_bf16)
+
+
+# ----------------------------------------------------------------------------
+# AWQ channel scaling
+# ----------------------------------------------------------------------------
+
+def test_awq_grid_and_scales():
+    pins.check_awq_grid(oracle.ALPHAS)
+    W, xb = pins.awq_outlier_inputs(seed=2)
+    m = oracle.channel_absmean_ref(xb)
+    assert np.allclose(m, np.abs(pins.bf16_values(xb)).mean(axis=0), rtol=0, atol=0)
+    for a in (0.0, 5 / 19, 1.0):
+        pins.check_awq_scales(oracle.candidate_scales_ref, m, a)
+
+
+def test_awq_alpha_zero_is_rtn():
+    W, xb = pins.awq_outlier_inputs(seed=3)
+    s32, inv32 = oracle.candidate_scales_ref(oracle.channel_absmean_ref(xb), 0.0)
+    assert np.all(s32 == 1) and np.all(inv32 == 1)
+    q1, d1 = oracle.quantize_scaled_ref(W, s32)
+    q0, d0 = oracle.rtn_quantize_ref(W)
+    assert np.array_equal(q1, q0) and np.array_equal(d1.view(np.uint32), d0.view(np.uint32))
+    assert np.array_equal(oracle.scale_activations_ref(xb, inv32), xb)
+
+
+def test_awq_activation_scaling_exact():
+    W, xb = pins.awq_outlier_inputs(seed=4, T=4)
+    s32, inv32 = oracle.candidate_scales_ref(oracle.channel_absmean_ref(xb), 11 / 19)
+    pins.check_awq_activation_scaling(oracle.scale_activations_ref, xb, inv32)
+
+
+def test_awq_error_exact_and_identity():
+    W, xb = pins.awq_outlier_inputs(seed=5, N=6, K=256, T=3)
+    s32, inv32 = oracle.candidate_scales_ref(oracle.channel_absmean_ref(xb), 7 / 19)
+    pins.check_awq_error(oracle.awq_output_error_ref, oracle.quantize_scaled_ref, oracle.scale_activations_ref,
+                         W, xb, s32, inv32)
+    pins.check_awq_identity(None, W, xb, s32)
+
+
+def test_awq_search_helps_on_salient_channels():
+    pins.check_awq_helps_on_salient_channels(oracle.awq_search_ref)
+
+
+def _awq_mutants(kind):
+    """Copies of the oracle's AWQ steps with one plausible mistake each."""
+    from oracle import awq as A
+
+    def scales(m, alpha):
+        a = -alpha if kind == "negative_exponent" else alpha
+        p = np.power(np.maximum(np.asarray(m, dtype=np.float64), 1e-30), float(a))
+        s = p if kind == "no_normalization" else p / np.exp(np.mean(np.log(p)))
+        s32 = s.astype(np.float32)
+        return s32, (1.0 / s32.astype(np.float64)).astype(np.float32)
+
+    def scale_x(x_bits, inv32):
+        if kind == "multiply_x":
+            inv32 = (1.0 / inv32.astype(np.float64)).astype(np.float32)
+        return A.scale_activations_ref(x_bits, inv32)
+
+    def error(W, x_bits, s32, inv32):
+        if kind == "weight_error":
+            q, d = A.quantize_scaled_ref(W, s32)
+            w_hat = np.repeat(d.astype(np.float64), 128, axis=1) * q / s32.astype(np.float64)[None, :]
+            return float(np.mean((w_hat - W.astype(np.float64)) ** 2))
+        q, d = A.quantize_scaled_ref(W, s32)
+        y_q, _ = oracle.w4_linear_ref(scale_x(x_bits, inv32), q, d)
+        y = np.asarray(pins.bf16_values(x_bits), dtype=np.float64) @ W.astype(np.float64).T
+        return float(np.mean((y_q - y) ** 2))
+
+    def search(W, x_bits):
+        m = A.channel_absmean_ref(x_bits)
+        grid = [k / 20 for k in range(20)] if kind == "grid_k_over_20" else A.ALPHAS
+        errs = np.asarray([error(W, x_bits, *scales(m, a)) for a in grid])
+        k = int(np.argmin(errs))
+        return (k, *scales(m, grid[k]), errs)
+
+    return scales, scale_x, error, search, ([k / 20 for k in range(20)] if kind == "grid_k_over_20" else A.ALPHAS)
+
+
+def _all_awq_pins(scales, scale_x, error, search, grid):
+    pins.check_awq_grid(grid)
+    W, xb = pins.awq_outlier_inputs(seed=6, N=6, K=256, T=3)
+    m = oracle.channel_absmean_ref(xb)
+    pins.check_awq_scales(scales, m, 9 / 19)
+    s32, inv32 = scales(m, 9 / 19)
+    pins.check_awq_activation_scaling(scale_x, xb, inv32)
+    pins.check_awq_error(error, oracle.quantize_scaled_ref, scale_x, W, xb, s32, inv32)
+    pins.check_awq_helps_on_salient_channels(search)
+
+
+@pytest.mark.parametrize("kind", ["negative_exponent", "no_normalization", "multiply_x", "weight_error",
+                                  "grid_k_over_20"])
+def test_awq_mutants_are_caught(kind):
+    _all_awq_pins(*_awq_mutants("none"))
+    with pytest.raises(pins.PinFailure):
+        _all_awq_pins(*_awq_mutants(kind))
