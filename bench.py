@@ -258,6 +258,67 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
 
 
 # ----------------------------------------------------------------------------
+# channel scaling before RTN (AWQ): the exponent search and the fused decode linear
+# ----------------------------------------------------------------------------
+
+def bench_awq(torch, w4, workloads, steps, warmup, T=256):
+    """On the 70B-class gate matrix (28672x8192, layer 0) with calibration rows drawn
+    from the same recipe: the search time and the output error relative to RTN, for
+    the recipe as is (its salient input channels also carry x20 weights) and for the
+    same matrix with those weight columns left ordinary; then the decode linear at
+    M = 1 with x/s formed in the kernel's staging against the plain linear."""
+    from bit_group_quantized_w4_amd import awq
+
+    dev = torch.device("cuda:0")
+    name, mat = "stack_70b", "gate"
+    W = workloads.weight(name, 0, mat, dev)
+    N, K = W.shape
+    x_cal = workloads.activations(name, 0, mat, T, dev)
+    chans = workloads.outlier_channels(name, 0, workloads.WORKLOADS[name].input_groups.get(mat, mat), K)
+    mult = workloads.WORKLOADS[name].weight[4]
+    out = {"matrix": f"{N}x{K}", "calibration_rows": T}
+    for tag, Wv in (("recipe", W), ("ordinary_weights_on_salient_channels", None)):
+        if Wv is None:
+            Wv = W.clone()
+            Wv[:, torch.as_tensor(chans, device=dev)] /= mult
+        awq.search(Wv, x_cal)  # warm
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = awq.search(Wv, x_cal)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        e = res["errors"]
+        out[tag] = {"k": res["k"], "alpha": round(res["alpha"], 4), "error_vs_rtn": round(e[res["k"]] / e[0], 4),
+                    "search_ms": round(dt * 1e3, 1)}
+        log(f"[bench] awq {tag}: alpha={res['alpha']:.3f}, output error {e[res['k']] / e[0]:.3f} x RTN, "
+            f"search {dt * 1e3:.0f} ms")
+    # decode: fused x/s staging against the plain linear, same matrix, rotated copies
+    res = awq.search(W, x_cal)
+    copies = 8
+    qs = [res["q"].clone() for _ in range(copies)]
+    ds = [res["d"].clone() for _ in range(copies)]
+    x = workloads.activations(name, 0, mat, 1, dev)
+    y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    nbytes = copies * workloads.algorithmic_bytes(1, N, K) + copies * 4 * K  # + inv_s
+    for mode in ("linear_awq", "linear"):
+        def step():
+            for c in range(copies):
+                if mode == "linear_awq":
+                    w4.linear_awq(x, qs[c], ds[c], N, res["inv_s"], out=y)
+                else:
+                    w4.linear(x, qs[c], ds[c], N, out=y)
+        g = capture(torch, step)
+        t = time_graph(torch, g, max(4, steps // 8), warmup)
+        per = t / (max(4, steps // 8) * copies)
+        out[mode + "_m1"] = {"us_per_call": round(per * 1e6, 2), "GBps": round(nbytes / copies / per / 1e9, 1)}
+        del g
+    log(f"[bench] awq decode M=1: fused {out['linear_awq_m1']['GBps']:.0f} GB/s, plain {out['linear_m1']['GBps']:.0f} GB/s")
+    del W, qs, ds
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample, rank 0, after the GPU phase)
 # ----------------------------------------------------------------------------
 
@@ -456,6 +517,7 @@ def main():
     ap.add_argument("--copies", type=int, default=32)
     ap.add_argument("--stacks", default="27b,70b")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
     ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
     ap.add_argument("--stack-modes", default="",
                     help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
@@ -514,6 +576,7 @@ def main():
                                         max(2, args.warmup), [1], ["fused_shared_input"],
                                         scale_dtype=torch.bfloat16)
 
+    awq_res = None if args.no_awq else bench_awq(torch, w4, workloads, args.steps, args.warmup)
     read_peak = measure_read_peak(torch, w4)
 
     if args.calibrate_copy_mb:
@@ -562,6 +625,7 @@ def main():
         "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies, read_peak),
         "hbm_read_peak_measured": read_peak,
         "scales_16bit": s16,
+        "awq": awq_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

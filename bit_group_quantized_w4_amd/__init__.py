@@ -50,6 +50,14 @@ SIGNATURES = {
     "w4_linear_batched_s16": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
     "w4_pack_s16": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_unpack_s16": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    # channel scaling before RTN (AWQ)
+    "w4_channel_absmean": (_INT, [_VP, _I64, _I64, _VP, _VP]),
+    "w4_awq_scales": (_INT, [_VP, _I64, ctypes.c_double, _VP, _VP, _VP]),
+    "w4_quantize_rtn_scaled": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_quantize_rtn_scaled_s16": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_scale_activations": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
+    "w4_linear_awq": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP, _VP]),
+    "w4_sq_error": (_INT, [_VP, _VP, _I64, _VP, _VP]),
 }
 
 
@@ -212,6 +220,71 @@ def unpack(q, d, N, K):
     return qc, dc
 
 
+# ----------------------------------------------------------------------------
+# channel scaling before RTN (AWQ); the search itself is in .awq
+# ----------------------------------------------------------------------------
+
+def channel_absmean(x):
+    """mean |x[:, j]| over the rows of a bf16 [T, K] tensor -> fp32 [K]."""
+    T, K = x.shape
+    m = torch.empty(K, dtype=torch.float32, device=x.device)
+    _check(_lib.w4_channel_absmean(_dev(x, torch.bfloat16, "x"), T, K, _dev(m, torch.float32, "m"), _stream(x)),
+           "w4_channel_absmean")
+    return m
+
+
+def awq_scales(m, alpha):
+    """Candidate channel scales for one exponent: (s, inv_s), fp32 [K]."""
+    K = m.shape[0]
+    s = torch.empty(K, dtype=torch.float32, device=m.device)
+    inv = torch.empty(K, dtype=torch.float32, device=m.device)
+    _check(_lib.w4_awq_scales(_dev(m, torch.float32, "m"), K, float(alpha), _dev(s, torch.float32, "s"),
+                              _dev(inv, torch.float32, "inv_s"), _stream(m)), "w4_awq_scales")
+    return s, inv
+
+
+def quantize_rtn_scaled(W, s, scale_dtype=torch.float32, out=None):
+    """RTN of W * diag(s) (columns scaled in fp32) -> native (q, d)."""
+    N, K = W.shape
+    if out is not None:
+        scale_dtype = _scale_dtype(out[1])
+    q, d = out if out is not None else _empty_packed(N, K, W.device, scale_dtype)
+    fn, name = ((_lib.w4_quantize_rtn_scaled_s16, "w4_quantize_rtn_scaled_s16") if scale_dtype == torch.bfloat16
+                else (_lib.w4_quantize_rtn_scaled, "w4_quantize_rtn_scaled"))
+    _check(fn(_dev(W, torch.float32, "W"), _dev(s, torch.float32, "s"), N, K, _dev(q, torch.uint8, "q"),
+              _dev(d, scale_dtype, "d"), _stream(W)), name)
+    return q, d
+
+
+def scale_activations(x, inv_s, out=None):
+    """x' = bf16(x * inv_s) column by column, bf16 [M, K]."""
+    M, K = x.shape
+    xo = out if out is not None else torch.empty_like(x)
+    _check(_lib.w4_scale_activations(_dev(x, torch.bfloat16, "x"), M, K, _dev(inv_s, torch.float32, "inv_s"),
+                                     _dev(xo, torch.bfloat16, "x_out"), _stream(x)), "w4_scale_activations")
+    return xo
+
+
+def linear_awq(x, q, d, N, inv_s, out=None):
+    """y = W_hat' (x * inv_s): x is scaled while the dot2 kernel stages it (fp32 scales)."""
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(_lib.w4_linear_awq(_dev(x, torch.bfloat16, "x"), M, K, _dev(q, torch.uint8, "q"),
+                              _dev(d, torch.float32, "d"), N, _dev(inv_s, torch.float32, "inv_s"),
+                              _dev(y, torch.bfloat16, "y"), _stream(x)), "w4_linear_awq")
+    return y
+
+
+def sq_error(y, y_ref, out=None):
+    """Sum of (y - y_ref)^2 in fp64 (y bf16, y_ref fp32, same shape) as a 1-element GPU tensor."""
+    if y.shape != y_ref.shape:
+        raise ValueError("y and y_ref must have the same shape")
+    o = out if out is not None else torch.empty(1, dtype=torch.float64, device=y.device)
+    _check(_lib.w4_sq_error(_dev(y, torch.bfloat16, "y"), _dev(y_ref, torch.float32, "y_ref"), y.numel(),
+                            _dev(o, torch.float64, "out"), _stream(y)), "w4_sq_error")
+    return o
+
+
 class W4Linear:
     """A quantized weight held in native layout, callable on bf16 activations."""
 
@@ -230,6 +303,7 @@ class W4Linear:
 __all__ = [
     "GROUP", "LIB_PATH", "MAX_BATCH", "PATHS", "SCALE_DTYPES", "SIGNATURES", "LinearDesc", "W4Error",
     "W4Linear",
-    "library", "linear", "linear_batched",
+    "awq_scales", "channel_absmean", "library", "linear", "linear_awq", "linear_batched",
+    "quantize_rtn_scaled", "scale_activations", "sq_error",
     "pack", "packed_bytes", "quantize_rtn", "scale_count", "unpack",
 ]

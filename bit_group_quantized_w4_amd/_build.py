@@ -1,6 +1,8 @@
 """Build libw4.so (and the bench-only copy kernel) in-tree with hipcc for gfx950.
 
-Usage: python -m bit_group_quantized_w4_amd._build   (or __graft_entry__.build()).
+Usage: python bit_group_quantized_w4_amd/_build.py   (or __graft_entry__.build()).
+Run it as a script (not with -m): importing the package loads the library,
+which may be missing or stale before this builds it.
 The shared objects land next to this file, so a snapshot of the repository
 carries them to a GPU host without any JIT cache.
 """
@@ -18,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw4.so")
 BENCH_LIB = os.path.join(PKG, "libw4_bench.so")
 
-LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip"]
+LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip"]
 BENCH_SOURCES = ["copy_probe.hip"]
 
 ARCH = "gfx950"

@@ -258,4 +258,89 @@ w4_status w4_unpack_s16(const uint8_t* q_packed, const uint16_t* d_packed, int64
   return unpack(q_packed, d_packed, N, K, q_canon, d_canon, true, stream);
 }
 
+// ---------------------------------------------------------------------------
+// channel scaling before RTN (AWQ)
+// ---------------------------------------------------------------------------
+
+w4_status w4_channel_absmean(const uint16_t* x, int64_t T, int64_t K, float* m, hipStream_t stream) {
+  if (T < 0 || K < 0 || K > kMaxK || T * K * 2 > ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (T == 0 || K == 0) return W4_OK;
+  if (!x || !m) return W4_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(m, 4)) return W4_ERR_ALIGN;
+  if (overlaps(m, 4 * (size_t)K, x, 2 * (size_t)T * K)) return W4_ERR_ARG;
+  return hip_status(w4::launch_channel_absmean(x, T, K, m, stream));
+}
+
+w4_status w4_awq_scales(const float* m, int64_t K, double alpha, float* s, float* inv_s, hipStream_t stream) {
+  if (K < 0 || K > kMaxK) return W4_ERR_SHAPE;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return W4_ERR_ARG;
+  if (K == 0) return W4_OK;
+  if (!m || !s || !inv_s) return W4_ERR_NULL;
+  if (!aligned(m, 4) || !aligned(s, 4) || !aligned(inv_s, 4)) return W4_ERR_ALIGN;
+  const size_t b = 4 * (size_t)K;
+  if (overlaps(s, b, inv_s, b) || overlaps(s, b, m, b) || overlaps(inv_s, b, m, b)) return W4_ERR_ARG;
+  return hip_status(w4::launch_awq_scales(m, K, alpha, s, inv_s, stream));
+}
+
+namespace {
+w4_status quantize_scaled(const float* W, const float* s, int64_t N, int64_t K, uint8_t* q_packed, void* d_packed,
+                          bool s16, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K)) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!W || !s || !q_packed || !d_packed) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(q_packed, 16) || !aligned(d_packed, 16)) return W4_ERR_ALIGN;
+  const size_t qb = w4_packed_bytes(N, K), db = (s16 ? 2 : 4) * w4_scale_count(N, K), wb = 4 * (size_t)N * K;
+  if (overlaps(q_packed, qb, d_packed, db) || overlaps(q_packed, qb, W, wb) || overlaps(d_packed, db, W, wb) ||
+      overlaps(q_packed, qb, s, 4 * (size_t)K) || overlaps(d_packed, db, s, 4 * (size_t)K))
+    return W4_ERR_ARG;
+  return hip_status(w4::launch_quantize_rtn_scaled(W, s, N, K, q_packed, d_packed, s16, stream));
+}
+}  // namespace
+
+w4_status w4_quantize_rtn_scaled(const float* W, const float* s, int64_t N, int64_t K, uint8_t* q_packed,
+                                 float* d_packed, hipStream_t stream) {
+  return quantize_scaled(W, s, N, K, q_packed, d_packed, false, stream);
+}
+
+w4_status w4_quantize_rtn_scaled_s16(const float* W, const float* s, int64_t N, int64_t K, uint8_t* q_packed,
+                                     uint16_t* d_packed, hipStream_t stream) {
+  return quantize_scaled(W, s, N, K, q_packed, d_packed, true, stream);
+}
+
+w4_status w4_scale_activations(const uint16_t* x, int64_t M, int64_t K, const float* inv_s, uint16_t* x_out,
+                               hipStream_t stream) {
+  if (M < 0 || K < 0 || K > kMaxK || 2 * M * K > ((int64_t)1 << 30)) return W4_ERR_SHAPE;
+  if (M == 0 || K == 0) return W4_OK;
+  if (!x || !inv_s || !x_out) return W4_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(inv_s, 4) || !aligned(x_out, 2)) return W4_ERR_ALIGN;
+  const size_t xb = 2 * (size_t)M * K;
+  if (overlaps(x_out, xb, x, xb) || overlaps(x_out, xb, inv_s, 4 * (size_t)K)) return W4_ERR_ARG;
+  return hip_status(w4::launch_scale_activations(x, M, K, inv_s, x_out, stream));
+}
+
+w4_status w4_linear_awq(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed, const float* d_packed,
+                        int64_t N, const float* inv_s, uint16_t* y, hipStream_t stream) {
+  const LinearArgs l{x, M, K, q_packed, d_packed, N, y};
+  w4::BatchArgs a;
+  a.count = 0;
+  const w4_status st = check_linear(l, a);
+  if (st != W4_OK || a.count == 0) return st;
+  if (!inv_s) return W4_ERR_NULL;
+  if (!aligned(inv_s, 16)) return W4_ERR_ALIGN;
+  const w4_status al = check_aliasing(&l, 1, 4);
+  if (al != W4_OK) return al;
+  if (overlaps(y, 2 * (size_t)M * N, inv_s, 4 * (size_t)K)) return W4_ERR_ARG;
+  if (w4::gemv_lds_bytes(1, K) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
+  return hip_status(w4::launch_linear_gemv_xscaled(a.desc[0], inv_s, w4::gemv_rows_per_slab(M, K), stream));
+}
+
+w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, double* out, hipStream_t stream) {
+  if (count < 0) return W4_ERR_SHAPE;
+  if (!out) return W4_ERR_NULL;
+  if (count > 0 && (!y || !y_ref)) return W4_ERR_NULL;
+  if (!aligned(y, 2) || !aligned(y_ref, 4) || !aligned(out, 8)) return W4_ERR_ALIGN;
+  if (overlaps(out, 8, y, 2 * (size_t)count) || overlaps(out, 8, y_ref, 4 * (size_t)count)) return W4_ERR_ARG;
+  return hip_status(w4::launch_sq_error(y, y_ref, count, out, stream));
+}
+
 }  // extern "C"

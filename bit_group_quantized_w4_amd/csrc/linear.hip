@@ -300,8 +300,11 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, co
 // deeper ring per wavefront.  The four quarters of a row are summed with
 // cross-lane shuffles at the end.
 // ---------------------------------------------------------------------------
-template <int MT, int R, int NW, bool S16>
-__device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
+// kXScale: x is divided by channel scales while it is staged,
+// x'[k] = bf16(fl32(x[k] * inv_s[k])) (channel scaling before RTN, the
+// study's section 2 AWQ row; inv_s holds the fp32 reciprocals of the scales).
+template <int MT, int R, int NW, bool S16, bool kXScale = false>
+__device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, const float* inv_s = nullptr) {
   // LDS: x of the slab, [MT][GP * 16] uint4 (zero past K), then the start
   // values -1.5 * sum(x) of every (row, group, quarter), [MT][GP][4] floats.
   extern __shared__ uint4 xlds[];
@@ -345,7 +348,28 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk) {
   };
   const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
   float* offs = reinterpret_cast<float*>(xlds + MT * GP * 16);
-  auto store_x = [&](int e, const uint4 (&v)[4]) {
+  auto store_x = [&](int e, const uint4 (&vin)[4]) {
+    uint4 v[4] = {vin[0], vin[1], vin[2], vin[3]};
+    if constexpr (kXScale) {
+      const int rg = e >> 2;
+      const int g = rg - (rg / GP) * GP;
+      if (g < w.G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4* r4 = reinterpret_cast<const float4*>(inv_s + g * kGroup + 32 * i + 8 * (e & 3));
+          const float4 a = r4[0], b = r4[1];
+          const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t wds[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const float lo = __uint_as_float(wds[h] << 16) * f[2 * h];
+            const float hi = __uint_as_float(wds[h] & 0xFFFF0000u) * f[2 * h + 1];
+            wds[h] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+          }
+          v[i] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        }
+      }
+    }
     float c = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -500,6 +524,15 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_one(const uint16_t* x, co
   gemv_body<MT, R, NW, S16>(D, locate_one(N, R, MT));
 }
 
+// One linear whose x is divided by channel scales while it is staged.
+template <int MT, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x, const uint8_t* q, const void* d,
+                                                               uint16_t* y, int M, int K, int N,
+                                                               const float* inv_s) {
+  const LinearDesc D{x, q, d, y, M, K, N, 0};
+  gemv_body<MT, R, NW, false, true>(D, locate_one(N, R, MT), inv_s);
+}
+
 // ---------------------------------------------------------------------------
 // launch configuration
 // ---------------------------------------------------------------------------
@@ -646,6 +679,28 @@ int gemv_rows_per_slab(int64_t M, int64_t K) {
   for (int mt = 4; mt > 1; mt >>= 1)
     if (M >= mt && gemv_lds_bytes(mt, K) <= kGemvLdsBytes) return mt;
   return 1;
+}
+
+hipError_t launch_linear_gemv_xscaled(const LinearDesc& l, const float* inv_s, int MT, hipStream_t stream) {
+  BatchArgs a;
+  a.count = 1;
+  a.desc[0] = l;
+  const int ci = choose_cfg_gemv(a) == find_cfg(1, 8) ? find_cfg(1, 8) : find_cfg(1, 4);
+  const Cfg c = kCfgs[ci];
+  const int64_t blocks = fill_blocks(a, c.R, MT);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const size_t lds = (size_t)gemv_lds_bytes(MT, l.K);
+  const unsigned nb = (unsigned)blocks;
+#define W4_XS(mt, nw) \
+  linear_gemv_xscaled<mt, 1, nw><<<nb, nw * 64, lds, stream>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N, inv_s)
+  if (c.NW == 8) {
+    if (MT == 4) W4_XS(4, 8); else if (MT == 2) W4_XS(2, 8); else W4_XS(1, 8);
+  } else {
+    if (MT == 4) W4_XS(4, 4); else if (MT == 2) W4_XS(2, 4); else W4_XS(1, 4);
+  }
+#undef W4_XS
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream) {

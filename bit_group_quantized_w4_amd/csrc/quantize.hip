@@ -66,11 +66,14 @@ __device__ __forceinline__ uint32_t native_word(const int u[8]) {
 }
 
 // S: the stored scale, float (fp32) or uint16_t (bf16 bit pattern).
-template <typename S>
+// kColScale: the weights are first multiplied column by column by cs[k] in
+// fp32 (channel scaling before RTN, the study's section 2 AWQ row).
+template <typename S, bool kColScale = false>
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restrict__ W, int N,
                                                            int K, int G, int GP, int64_t ntiles,
                                                            uint4* __restrict__ qp,
-                                                           S* __restrict__ dp) {
+                                                           S* __restrict__ dp,
+                                                           const float* __restrict__ cs = nullptr) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, nl = lane & 15, kb = lane >> 4;
   // the wavefront index is uniform across the wavefront: keep the tile, and
@@ -96,6 +99,17 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
       v[8 * i + 2] = __uint_as_float(a.z); v[8 * i + 3] = __uint_as_float(a.w);
       v[8 * i + 4] = __uint_as_float(b.x); v[8 * i + 5] = __uint_as_float(b.y);
       v[8 * i + 6] = __uint_as_float(b.z); v[8 * i + 7] = __uint_as_float(b.w);
+    }
+    if constexpr (kColScale) {
+      if (g < G) {
+        const float4* c = reinterpret_cast<const float4*>(cs + (int64_t)g * kGroup + 8 * kb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = c[8 * i], b = c[8 * i + 1];
+          v[8 * i + 0] *= a.x; v[8 * i + 1] *= a.y; v[8 * i + 2] *= a.z; v[8 * i + 3] *= a.w;
+          v[8 * i + 4] *= b.x; v[8 * i + 5] *= b.y; v[8 * i + 6] *= b.z; v[8 * i + 7] *= b.w;
+        }
+      }
     }
   }
 
@@ -252,6 +266,19 @@ hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_
   else
     quantize_rtn_kernel<float><<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles, qp,
                                                               static_cast<float*>(d_packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rtn_scaled(const float* W, const float* cs, int64_t N, int64_t K, uint8_t* q_packed,
+                                      void* d_packed, bool s16, hipStream_t stream) {
+  const Grid g = grid_of(N, K);
+  uint4* qp = reinterpret_cast<uint4*>(q_packed);
+  if (s16)
+    quantize_rtn_kernel<uint16_t, true><<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles, qp,
+                                                                       static_cast<uint16_t*>(d_packed), cs);
+  else
+    quantize_rtn_kernel<float, true><<<g.blocks, 256, 0, stream>>>(W, (int)N, (int)K, g.G, g.GP, g.ntiles, qp,
+                                                                    static_cast<float*>(d_packed), cs);
   return hipGetLastError();
 }
 

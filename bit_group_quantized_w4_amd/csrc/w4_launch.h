@@ -38,6 +38,9 @@ struct BatchArgs {
 // s16: scales are bf16 bit patterns (uint16_t) instead of fp32.
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
                                void* d_packed, bool s16, hipStream_t stream);
+// RTN of W * diag(cs) (columns scaled in fp32 first).
+hipError_t launch_quantize_rtn_scaled(const float* W, const float* cs, int64_t N, int64_t K, uint8_t* q_packed,
+                                      void* d_packed, bool s16, hipStream_t stream);
 hipError_t launch_pack(const int8_t* q_canon, const void* d_canon, int64_t N, int64_t K,
                        uint8_t* q_packed, void* d_packed, bool s16, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* q_packed, const void* d_packed, int64_t N, int64_t K,
@@ -50,5 +53,15 @@ hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream);
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream);
 // Largest slab (4, 2 or 1 rows) the dot2 kernel can stage for M rows of K.
 int gemv_rows_per_slab(int64_t M, int64_t K);
+// dot2 kernel for one linear whose x is divided by channel scales while it is
+// staged: x'[k] = bf16(fl32(x[k] * inv_s[k])).
+hipError_t launch_linear_gemv_xscaled(const LinearDesc& l, const float* inv_s, int MT, hipStream_t stream);
+
+// Channel-scaling search steps (awq.hip).
+hipError_t launch_channel_absmean(const uint16_t* x, int64_t T, int64_t K, float* m, hipStream_t stream);
+hipError_t launch_awq_scales(const float* m, int64_t K, double alpha, float* s, float* inv, hipStream_t stream);
+hipError_t launch_scale_activations(const uint16_t* x, int64_t M, int64_t K, const float* inv, uint16_t* xo,
+                                    hipStream_t stream);
+hipError_t launch_sq_error(const uint16_t* y, const float* yref, int64_t n, double* out, hipStream_t stream);
 
 }  // namespace w4

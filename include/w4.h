@@ -230,6 +230,65 @@ w4_status w4_pack_s16(const int8_t* q_canon, const uint16_t* d_canon, int64_t N,
 w4_status w4_unpack_s16(const uint8_t* q_packed, const uint16_t* d_packed, int64_t N, int64_t K,
                         int8_t* q_canon, uint16_t* d_canon, hipStream_t stream);
 
+/*
+ * Channel scaling before RTN (study, section 2: the AWQ row of the methods
+ * table -- same storage as RTN, input channels rescaled before quantizing;
+ * the settings table -- scale candidates from input statistics only, 20
+ * exponents in [0, 1], chosen by the output error on calibration inputs, no
+ * clipping search; and the channel-scaling equation W'_ij = W_ij s_j,
+ * x'_j = x_j / s_j, W'x' = Wx).  The search runs these steps per matrix:
+ *   m = w4_channel_absmean(calibration x)
+ *   for alpha = k/19, k = 0..19:
+ *     w4_awq_scales(m, alpha) -> s, inv_s
+ *     w4_quantize_rtn_scaled(W, s) -> q, d
+ *     w4_scale_activations(x, inv_s) -> x'; w4_linear(x', q, d) -> y'
+ *     w4_sq_error(y', W x) -> error
+ * and keeps the exponent with the smallest error.  Decoding then either
+ * passes x' (1/s folded into the previous operation) to w4_linear, or x and
+ * inv_s to w4_linear_awq.
+ */
+
+/* m[j] = mean over the T rows of |x[t][j]|; x bf16 [T][K] (2-byte aligned),
+ * m fp32 [K] (4-byte aligned).  The sum runs over t in order, in fp32.
+ * W4_ERR_SHAPE if T*K*2 > 2 GiB. */
+w4_status w4_channel_absmean(const uint16_t* x, int64_t T, int64_t K, float* m, hipStream_t stream);
+
+/* Candidate channel scales for one exponent 0 <= alpha <= 1 (else
+ * W4_ERR_ARG): p_j = max(m_j, 1e-30)^alpha in fp64, s_j = fl32(p_j / g) with
+ * g the geometric mean of p (so s has geometric mean 1), inv_s_j =
+ * fl32(1 / s_j).  m, s, inv_s fp32 [K], 4-byte aligned, s and inv_s disjoint
+ * from each other and from m.  One workgroup; fixed summation order. */
+w4_status w4_awq_scales(const float* m, int64_t K, double alpha, float* s, float* inv_s,
+                        hipStream_t stream);
+
+/* w4_quantize_rtn (resp. _s16) of W' = fl32(W[n][k] * s[k]): the columns
+ * are scaled in fp32 first.  s fp32 [K], 16-byte aligned; everything else
+ * as w4_quantize_rtn. */
+w4_status w4_quantize_rtn_scaled(const float* W, const float* s, int64_t N, int64_t K,
+                                 uint8_t* q_packed, float* d_packed, hipStream_t stream);
+w4_status w4_quantize_rtn_scaled_s16(const float* W, const float* s, int64_t N, int64_t K,
+                                     uint8_t* q_packed, uint16_t* d_packed, hipStream_t stream);
+
+/* x_out[m][k] = bf16_rne(fl32(x[m][k] * inv_s[k])); x, x_out bf16 [M][K]
+ * (2-byte aligned, disjoint), inv_s fp32 [K].  W4_ERR_SHAPE if 2*M*K > 1 GiB. */
+w4_status w4_scale_activations(const uint16_t* x, int64_t M, int64_t K, const float* inv_s,
+                               uint16_t* x_out, hipStream_t stream);
+
+/* y = W_hat' x' with x' = x * inv_s formed (as w4_scale_activations does)
+ * while the dot2 kernel stages x: the decode linear of a matrix quantized by
+ * w4_quantize_rtn_scaled when 1/s is not folded into the previous operation.
+ * Arguments as w4_linear, plus inv_s fp32 [K] (16-byte aligned); M > 4 runs in
+ * slabs of up to 4 rows; K <= 30720 (else W4_ERR_SHAPE). */
+w4_status w4_linear_awq(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                        const float* d_packed, int64_t N, const float* inv_s, uint16_t* y,
+                        hipStream_t stream);
+
+/* *out = sum over e < count of (y[e] - y_ref[e])^2 in fp64 (y bf16, y_ref
+ * fp32; one workgroup, fixed summation order); out is device memory,
+ * 8-byte aligned.  count == 0 writes 0. */
+w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, double* out,
+                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,10 +13,16 @@ def pytest_configure(config):
 
 
 def _ensure_built():
-    from bit_group_quantized_w4_amd import _build
+    # The build script is loaded by path: importing the package would first
+    # try to load a library that may not exist yet.
+    import importlib.util
 
-    if not _build.built():
-        _build.build(verbose=False)
+    spec = importlib.util.spec_from_file_location(
+        "w4_build", os.path.join(ROOT, "bit_group_quantized_w4_amd", "_build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    if not build.built():
+        build.build(verbose=False)
 
 
 @pytest.fixture(scope="session")

@@ -460,3 +460,84 @@ def test_s16_linear_full_size_70b_layer_sampled(w4, gpu):
             check_y(y.index_select(1, idx), y_ref, absdot, f"s16 70b {name} M={M}")
         del q, d
         torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# channel scaling before RTN (AWQ)
+# ----------------------------------------------------------------------------
+
+def _awq_case(gpu, seed=0, N=200, K=1024, T=64):
+    W, xb = pins.awq_outlier_inputs(seed=seed, N=N, K=K, T=T)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(gpu)
+    return W, xb, torch.from_numpy(W).to(gpu), x
+
+
+def test_awq_steps_match_oracle(w4, gpu):
+    """Channel means, candidate scales, scaled quantization (fp32 and 16-bit scales),
+    scaled activations and the fused decode linear, each against the oracle."""
+    _say("awq steps")
+    W, xb, W_dev, x = _awq_case(gpu, seed=10)
+    m = w4.channel_absmean(x)
+    m_ref = oracle.channel_absmean_ref(xb)
+    assert np.allclose(m.cpu().numpy(), m_ref, rtol=1e-5, atol=0), "channel means"
+    for alpha in (0.0, 6 / 19, 1.0):
+        s, inv = w4.awq_scales(m, alpha)
+        s_h, inv_h = s.cpu().numpy(), inv.cpu().numpy()
+        s_ref, _ = oracle.candidate_scales_ref(m.cpu().numpy().astype(np.float64), alpha)
+        assert np.allclose(s_h, s_ref, rtol=4e-7, atol=0), f"scales alpha={alpha}"
+        assert np.array_equal(inv_h, (1.0 / s_h.astype(np.float64)).astype(np.float32)), "reciprocals"
+        if alpha == 0.0:
+            assert np.all(s_h == 1) and np.all(inv_h == 1)
+        for sd, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            q, d = w4.quantize_rtn_scaled(W_dev, s, sd)
+            qc, dc = w4.unpack(q, d, W.shape[0], W.shape[1])
+            q_ref, d_ref = oracle.quantize_scaled_ref(W, s_h, tag)
+            assert np.array_equal(qc.cpu().numpy(), q_ref), f"scaled codes alpha={alpha} {tag}"
+            assert np.array_equal(_scale_bits(dc), d_ref if tag == "bf16" else d_ref.view(np.uint32)), \
+                f"scaled scales alpha={alpha} {tag}"
+        xs = w4.scale_activations(x, inv)
+        xs_ref = oracle.scale_activations_ref(xb, inv_h)
+        assert np.array_equal(_bits(xs), xs_ref), f"scaled activations alpha={alpha}"
+        q, d = w4.quantize_rtn_scaled(W_dev, s)
+        q_ref, d_ref = oracle.quantize_scaled_ref(W, s_h)
+        for M in (1, 3, 8):
+            y = w4.linear_awq(x[:M], q, d, W.shape[0], inv)
+            y_sep = w4.linear(w4.scale_activations(x[:M], inv), q, d, W.shape[0], path="gemv")
+            assert torch.equal(y.view(torch.int16), y_sep.view(torch.int16)), "fused scaling != separate"
+            y_ref, absdot = oracle.w4_linear_ref(xs_ref[:M], q_ref, d_ref)
+            check_y(y, y_ref, absdot, f"awq linear alpha={alpha} M={M}")
+
+
+def test_awq_sq_error(w4, gpu):
+    _say("awq squared error")
+    rng = np.random.default_rng(3)
+    y = torch.from_numpy(rng.standard_normal((37, 1001)).astype(np.float32)).to(gpu).to(torch.bfloat16)
+    y_ref = torch.from_numpy(rng.standard_normal((37, 1001)).astype(np.float32)).to(gpu)
+    got = float(w4.sq_error(y, y_ref).cpu()[0])
+    exp = float(np.sum((y.float().cpu().numpy().astype(np.float64) - y_ref.cpu().numpy().astype(np.float64)) ** 2))
+    assert abs(got - exp) <= 1e-12 * exp
+    assert float(w4.sq_error(y[:0], y_ref[:0]).cpu()[0]) == 0.0
+
+
+@pytest.mark.parametrize("seed,salient", [(1, True), (2, False)])
+def test_awq_search_near_oracle_optimum(w4, gpu, seed, salient):
+    """The GPU search picks an exponent whose (oracle) output error is within 2% of the
+    oracle's best; with salient input channels on ordinary weights it improves on RTN."""
+    from bit_group_quantized_w4_amd import awq
+
+    _say(f"awq search seed={seed} salient={salient}")
+    W, xb, W_dev, x = _awq_case(gpu, seed=seed, N=128, K=512, T=64)
+    if not salient:  # outlier channels carry outlier weights too (the 70B-class recipe)
+        S = np.argsort(-np.abs(pins.bf16_values(xb)).mean(axis=0))[:5]
+        W[:, S] *= 20
+        W_dev = torch.from_numpy(W).to(gpu)
+    res = awq.search(W_dev, x)
+    k_ref, _, _, err_ref = oracle.awq_search_ref(W, xb)
+    m = w4.channel_absmean(x).cpu().numpy().astype(np.float64)
+    s_k, inv_k = oracle.candidate_scales_ref(m, awq.ALPHAS[res["k"]])
+    err_at_k = oracle.awq_output_error_ref(W, xb, s_k, inv_k)
+    assert err_at_k <= 1.02 * err_ref.min(), f"k={res['k']} (oracle {k_ref}): {err_at_k} vs {err_ref.min()}"
+    g = np.asarray(res["errors"])
+    assert np.allclose(g, err_ref, rtol=0.05), "per-candidate errors"
+    if salient:
+        assert res["k"] > 0 and g[res["k"]] < 0.9 * g[0], "channel scaling should help here"
