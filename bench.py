@@ -31,7 +31,7 @@ PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
 HEADLINE = "ffn_pair_outliers"
 KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_gemv_ffn_pair_outliers_m1_batched_counters.json")
-HEADLINE_KERNEL = "linear_gemv_kernel<1, 1, 4>"  # dot2 kernel, x in LDS: the batched M = 1 step
+HEADLINE_KERNEL = "linear_gemv_kernel<1, 1, 4, false>"  # dot2 kernel, x in LDS, fp32 scales: the batched M = 1 step
 HEADLINE_GRID = 32 * (160 + 576) * 256           # threads of one 64-linear launch (R = 1, 4 waves)
 
 
@@ -410,7 +410,7 @@ def roofline(pair_m1, bytes_per_call, copies, read_peak=None):
             traffic = c.get("hbm_bytes_per_launch")
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "linear_gemv_kernel<1, 1, 4> (dot2, x in LDS), 64 linears per launch",
+            "kernel": "linear_gemv_kernel<1, 1, 4, false> (dot2, x in LDS, fp32 scales), 64 linears per launch",
             "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4) if read_peak else None,
             "algorithmic_bytes_per_launch": copies * sum(bytes_per_call.values()),
             "avg_launch_us": pair_m1["us_per_launch"],
@@ -518,6 +518,7 @@ def main():
     ap.add_argument("--stacks", default="27b,70b")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
+    ap.add_argument("--no-s16", action="store_true", help="skip the 16-bit-scale measurements")
     ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
     ap.add_argument("--stack-modes", default="",
                     help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
@@ -569,9 +570,9 @@ def main():
                                            [m for m in args.stack_modes.split(",") if m] or None)
 
     # 16-bit scales: the headline pair at M = 1 and the stacks' realistic launch mode at M = 1
-    s16 = {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
-                              scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
-    for s in [s for s in args.stacks.split(",") if s and s != "none"]:
+    s16 = None if args.no_s16 else {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
+                                                       scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
+    for s in [s for s in args.stacks.split(",") if s and s != "none" and not args.no_s16]:
         s16["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
                                         max(2, args.warmup), [1], ["fused_shared_input"],
                                         scale_dtype=torch.bfloat16)
