@@ -11,7 +11,7 @@ M = 8 (verifying 7 drafted tokens + 1), quantization throughput, 27B- and
 70B-class layer stacks as equivalent decode tokens/s, the roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 27b,70b|none] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 4b,27b,70b|none] [--no-cpu]
 """
 
 import argparse
@@ -31,8 +31,8 @@ PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
 HEADLINE = "ffn_pair_outliers"
 KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_gemv_ffn_pair_outliers_m1_batched_counters.json")
-HEADLINE_KERNEL = "linear_gemv_kernel<1, 1, 4, false>"  # dot2 kernel, x in LDS, fp32 scales: the batched M = 1 step
-HEADLINE_GRID = 32 * (160 + 576) * 256           # threads of one 64-linear launch (R = 1, 4 waves)
+HEADLINE_KERNEL = "linear_gemv_kernel<1, 2, 2, false>"  # dot2 kernel, x in LDS, fp32 scales: the batched M = 1 step
+HEADLINE_GRID = 32 * (80 + 288) * 128            # threads of one 64-linear launch (R = 2 row blocks, 2 waves)
 
 
 def log(msg):
@@ -515,7 +515,7 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--copies", type=int, default=32)
-    ap.add_argument("--stacks", default="27b,70b")
+    ap.add_argument("--stacks", default="4b,27b,70b")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
     ap.add_argument("--no-s16", action="store_true", help="skip the 16-bit-scale measurements")

@@ -540,21 +540,22 @@ struct Cfg {
   int R, NW;
 };
 
-// Every (R, NW) compiled for each kernel with fp32 scales (16-bit scales:
-// the built-in choices only).  W4_MFMA_CFG / W4_GEMV_CFG ("R,NW") may pick
-// one of them for measurement; anything else falls back to the built-in
-// choice.
-constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {2, 4}, {2, 8}, {1, 16}, {4, 4}, {4, 8}, {1, 2}};
+// Every (R, NW) compiled for each kernel and scale format.  W4_MFMA_CFG /
+// W4_GEMV_CFG ("R,NW") may pick one of them for measurement; a value naming
+// no compiled configuration makes the launch fail (hipErrorInvalidValue).
+constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {2, 4}, {4, 4}, {1, 2}, {2, 2}, {4, 1}, {4, 2}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+static_assert(kNumCfgs == 8, "the launch switches below list 8 configurations");
 
+// -1: not set; -2: set to something that is not compiled.
 int cfg_from_env(const char* name) {
   const char* s = getenv(name);
   if (!s) return -1;
   int R = 0, NW = 0;
-  if (sscanf(s, "%d,%d", &R, &NW) != 2) return -1;
+  if (sscanf(s, "%d,%d", &R, &NW) != 2) return -2;
   for (int i = 0; i < kNumCfgs; ++i)
     if (kCfgs[i].R == R && kCfgs[i].NW == NW) return i;
-  return -1;
+  return -2;
 }
 
 int find_cfg(int R, int NW) {
@@ -563,32 +564,66 @@ int find_cfg(int R, int NW) {
   return 0;
 }
 
+struct LaunchShape {
+  int64_t rows;  // 16-row blocks over the whole batch
+  int kmin, kmax;
+};
+LaunchShape launch_shape(const BatchArgs& a) {
+  LaunchShape l{0, 1 << 30, 0};
+  for (int i = 0; i < a.count; ++i) {
+    l.rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
+    l.kmin = a.desc[i].K < l.kmin ? a.desc[i].K : l.kmin;
+    l.kmax = a.desc[i].K > l.kmax ? a.desc[i].K : l.kmax;
+  }
+  return l;
+}
+
 // Built-in choices, from graph-replayed sweeps of every (R, NW) on MI355X over
-// the 4B/27B/70B-class projection shapes: enough wavefronts in flight on all
-// 256 CUs for the batch's total row blocks, more wavefronts per block when K
-// is long.
+// the 4B/27B/70B-class projection groups and the 2560x9216 / 9216x2560 pair
+// at M = 1, 8, 13, 16.  Two effects pull against each other:
+//   * enough wavefronts to keep loads in flight on all 256 CUs when the
+//     launch is small (more wavefronts per block, fewer rows per wavefront);
+//   * when it is large, long-lived wavefronts and small blocks: a block of one
+//     wavefront leaves the moment it is done and its slot takes the next,
+//     while a block of four holds its slots until the last of the four ends
+//     and a new block needs four free slots on one CU.  Short K (few scale
+//     quads per wavefront) makes the second effect stronger.
 int choose_cfg_mfma(const BatchArgs& a) {
-  // More row blocks per wavefront reuse each x operand across more weights
-  // (x is read through L1 once per row panel), but leave fewer wavefronts.
-  int64_t rows = 0;
-  for (int i = 0; i < a.count; ++i) rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
-  if (rows < 256) return find_cfg(1, 4);
-  return rows < 600 ? find_cfg(2, 4) : find_cfg(4, 4);
+  // More row blocks per wavefront also reuse each x operand across more
+  // weights (x is read through L1 once per row panel).
+  const LaunchShape l = launch_shape(a);
+  if (l.rows < 256) return find_cfg(1, 4);
+  if (l.rows < 600) return find_cfg(2, 4);
+  if (l.rows < 2048) return l.kmin < 4096 ? find_cfg(2, 2) : find_cfg(4, 4);
+  // Large launch: one wavefront per block, unless the longest K would leave a
+  // few wavefronts streaming far longer than the rest of the launch.
+  const int qmax = (l.kmax / kGroup + 3) / 4;
+  return qmax <= 20 ? find_cfg(4, 1) : find_cfg(4, 4);
 }
 
 int choose_cfg_gemv(const BatchArgs& a) {
-  int64_t rows = 0;
-  int kmax = 0;
-  for (int i = 0; i < a.count; ++i) {
-    rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
-    kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
-  }
-  if (rows < 256) return find_cfg(1, 8);
+  const LaunchShape l = launch_shape(a);
+  if (l.rows < 256) return find_cfg(1, 8);
   // long K: more wavefronts per row block, once there are enough row blocks
-  return find_cfg(1, kmax >= 16384 && rows >= 400 ? 8 : 4);
+  if (l.kmax >= 16384 && l.rows >= 400) return find_cfg(1, 8);
+  if (l.kmin <= 4096 && l.rows >= 8192) return find_cfg(2, 2);
+  if (l.kmax <= 4096 && l.rows >= 1000) return find_cfg(1, 2);
+  return find_cfg(1, 4);
 }
 
+// Block ranges of the batch's linears.  Blocks are dispatched roughly in index
+// order, so the linears are laid out longest K first (stable for equal K):
+// the blocks that run longest start first and the grid ends on short ones,
+// which shortens the tail of a launch that mixes long and short rows.  Each
+// linear's blocks compute the same thing wherever they sit, so the order
+// changes no result.
 int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
+  for (int i = 1; i < a.count; ++i) {
+    const LinearDesc t = a.desc[i];
+    int j = i;
+    for (; j > 0 && a.desc[j - 1].K < t.K; --j) a.desc[j] = a.desc[j - 1];
+    a.desc[j] = t;
+  }
   int64_t total = 0;
   for (int i = 0; i < a.count; ++i) {
     a.block0[i] = (int)total;
@@ -611,17 +646,12 @@ void launch_gemv_at(unsigned blocks, size_t lds, hipStream_t st, const BatchArgs
   }
 }
 
-template <int MT>
-void launch_gemv_cfg(int ci, bool s16, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
-  if (s16) {  // 16-bit scales: the configurations the built-in choice uses
-    if (ci == 1) launch_gemv_at<MT, true, 1>(blocks, lds, st, a);
-    else launch_gemv_at<MT, true, 0>(blocks, lds, st, a);
-    return;
-  }
+template <int MT, bool S16>
+void launch_gemv_cfg(int ci, unsigned blocks, size_t lds, hipStream_t st, const BatchArgs& a) {
   switch (ci) {
 #define W4_CASE(i) \
   case i:          \
-    launch_gemv_at<MT, false, i>(blocks, lds, st, a); \
+    launch_gemv_at<MT, S16, i>(blocks, lds, st, a); \
     break;
     W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
 #undef W4_CASE
@@ -639,39 +669,30 @@ void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
   }
 }
 
-static_assert(kCfgs[0].R == 1 && kCfgs[0].NW == 4 && kCfgs[1].R == 1 && kCfgs[1].NW == 8 &&
-                  kCfgs[2].R == 2 && kCfgs[2].NW == 4 && kCfgs[5].R == 4 && kCfgs[5].NW == 4,
-              "16-bit-scale launches name these configurations by index");
-
-// Configurations compiled with 16-bit scales: the built-in choices.
-bool s16_cfg_mfma(int ci) { return ci == find_cfg(1, 4) || ci == find_cfg(2, 4) || ci == find_cfg(4, 4); }
-bool s16_cfg_gemv(int ci) { return ci == find_cfg(1, 4) || ci == find_cfg(1, 8); }
+template <bool S16>
+void launch_mfma_cfg(int ci, unsigned blocks, hipStream_t st, const BatchArgs& a) {
+  switch (ci) {
+#define W4_CASE(i) \
+  case i:          \
+    launch_mfma_at<S16, i>(blocks, st, a); \
+    break;
+    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
+#undef W4_CASE
+  }
+}
 
 }  // namespace
 
 hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream) {
   const int env = cfg_from_env("W4_MFMA_CFG");
-  int ci = env >= 0 ? env : choose_cfg_mfma(a);
-  if (s16 && !s16_cfg_mfma(ci)) ci = choose_cfg_mfma(a);
+  if (env == -2) return hipErrorInvalidValue;
+  const int ci = env >= 0 ? env : choose_cfg_mfma(a);
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, 16);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const unsigned nb = (unsigned)blocks;
-  if (s16) {
-    if (ci == find_cfg(4, 4)) launch_mfma_at<true, 5>(nb, stream, a);
-    else if (ci == find_cfg(2, 4)) launch_mfma_at<true, 2>(nb, stream, a);
-    else launch_mfma_at<true, 0>(nb, stream, a);
-    return hipGetLastError();
-  }
-  switch (ci) {
-#define W4_CASE(i) \
-  case i:          \
-    launch_mfma_at<false, i>(nb, stream, a); \
-    break;
-    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
-#undef W4_CASE
-  }
+  if (s16) launch_mfma_cfg<true>(ci, (unsigned)blocks, stream, a);
+  else launch_mfma_cfg<false>(ci, (unsigned)blocks, stream, a);
   return hipGetLastError();
 }
 
@@ -705,9 +726,8 @@ hipError_t launch_linear_gemv_xscaled(const LinearDesc& l, const float* inv_s, i
 
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream) {
   const int env = cfg_from_env("W4_GEMV_CFG");
-  int ci = env >= 0 ? env : choose_cfg_gemv(a);
-  if (MT == 4 && kCfgs[ci].NW == 16) ci = find_cfg(1, 8);  // 16 wavefronts x 4 rows exceeds 128 VGPRs
-  if (s16 && !s16_cfg_gemv(ci)) ci = choose_cfg_gemv(a);
+  if (env == -2) return hipErrorInvalidValue;
+  const int ci = env >= 0 ? env : choose_cfg_gemv(a);
   const Cfg c = kCfgs[ci];
   const int64_t blocks = fill_blocks(a, c.R, MT);
   if (blocks <= 0) return hipSuccess;
@@ -715,9 +735,16 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream
   int kmax = 0;
   for (int i = 0; i < a.count; ++i) kmax = a.desc[i].K > kmax ? a.desc[i].K : kmax;
   const size_t lds = (size_t)gemv_lds_bytes(MT, kmax);
-  if (MT == 4) launch_gemv_cfg<4>(ci, s16, (unsigned)blocks, lds, stream, a);
-  else if (MT == 2) launch_gemv_cfg<2>(ci, s16, (unsigned)blocks, lds, stream, a);
-  else launch_gemv_cfg<1>(ci, s16, (unsigned)blocks, lds, stream, a);
+  const unsigned nb = (unsigned)blocks;
+  if (s16) {
+    if (MT == 4) launch_gemv_cfg<4, true>(ci, nb, lds, stream, a);
+    else if (MT == 2) launch_gemv_cfg<2, true>(ci, nb, lds, stream, a);
+    else launch_gemv_cfg<1, true>(ci, nb, lds, stream, a);
+  } else {
+    if (MT == 4) launch_gemv_cfg<4, false>(ci, nb, lds, stream, a);
+    else if (MT == 2) launch_gemv_cfg<2, false>(ci, nb, lds, stream, a);
+    else launch_gemv_cfg<1, false>(ci, nb, lds, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -342,6 +342,50 @@ def test_linear_batched_matches_single_calls(w4, gpu, path, monkeypatch):
             check_y(y, y_ref, absdot, f"batched {name} M={M}")
 
 
+# Every compiled (row blocks per wavefront, wavefronts per block) pair; the
+# built-in choice picks among them by launch size, so each is checked here on
+# ragged shapes: partial row panels, K not a whole number of scale quads, and
+# more wavefronts per block than the matrix has quads.
+CONFIGS = ["1,4", "1,8", "2,4", "4,4", "1,2", "2,2", "4,1", "4,2"]
+CFG_SHAPES = [(700, 1408), (37, 384), (260, 2560)]
+
+
+@pytest.mark.parametrize("scale_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_linear_every_config(w4, gpu, cfg, path, scale_dtype, monkeypatch):
+    monkeypatch.setenv("W4_MFMA_CFG" if path == "mfma" else "W4_GEMV_CFG", cfg)
+    sd = torch.bfloat16 if scale_dtype == "bf16" else torch.float32
+    mats = []
+    for i, (N, K) in enumerate(CFG_SHAPES):
+        W = torch.from_numpy(workloads.random_weight(N, K, seed=500 + i)).to(gpu)
+        q, d = w4.quantize_rtn(W, scale_dtype=sd)
+        mats.append((N, K, q, d, oracle.rtn_quantize_ref(W.cpu().numpy(), scale_dtype)))
+    for M in ((1, 2, 3) if path == "gemv" else (1, 8, 16, 17)):
+        _say(f"config {cfg} path={path} scales={scale_dtype} M={M}")
+        xs = [workloads.random_activations(M, K, seed=M * 11 + i, device=gpu) for i, (_, K, _, _, _) in enumerate(mats)]
+        items = [(x, q, d, N, torch.empty((M, N), dtype=torch.bfloat16, device=gpu))
+                 for x, (N, K, q, d, _) in zip(xs, mats)]
+        ys = w4.linear_batched(items, path=path)
+        for x, y, (N, K, q, d, (q_ref, d_ref)) in zip(xs, ys, mats):
+            y1 = w4.linear(x, q, d, N, path=path)
+            y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+            check_y(y, y_ref, absdot, f"cfg {cfg} batched {N}x{K} M={M}")
+            check_y(y1, y_ref, absdot, f"cfg {cfg} single {N}x{K} M={M}")
+
+
+def test_linear_unknown_config_is_an_error(w4, gpu, monkeypatch):
+    q = torch.zeros(w4.packed_bytes(16, 128), dtype=torch.uint8, device=gpu)
+    d = torch.zeros(w4.scale_count(16, 128), dtype=torch.float32, device=gpu)
+    x = torch.zeros((1, 128), dtype=torch.bfloat16, device=gpu)
+    for var, path in (("W4_MFMA_CFG", "mfma"), ("W4_GEMV_CFG", "gemv")):
+        monkeypatch.setenv(var, "3,3")
+        with pytest.raises(w4.W4Error):
+            w4.linear(x, q, d, 16, path=path)
+        monkeypatch.delenv(var)
+    w4.linear(x, q, d, 16)  # and the library still works
+
+
 def test_linear_batched_full_size_layer(w4, gpu):
     """One 70B-class layer (seven full-size matrices) in one launch at M = 1 and 16."""
     wl = workloads.WORKLOADS["stack_70b"]
