@@ -410,7 +410,7 @@ def roofline(pair_m1, bytes_per_call, copies, read_peak=None):
             traffic = c.get("hbm_bytes_per_launch")
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "linear_gemv_kernel<1, 1, 4, false> (dot2, x in LDS, fp32 scales), 64 linears per launch",
+            "kernel": f"{HEADLINE_KERNEL} (dot2, x in LDS, fp32 scales), 64 linears per launch",
             "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4) if read_peak else None,
             "algorithmic_bytes_per_launch": copies * sum(bytes_per_call.values()),
             "avg_launch_us": pair_m1["us_per_launch"],
