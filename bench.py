@@ -174,6 +174,20 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms
                         "bytes_per_call": qb}
         log(f"[bench] quantize {m.name} {m.N}x{m.K}: {n * qb / t / 1e9:.0f} GB/s")
         del g, Ws
+    if quantize:
+        # one full-size 70B-class gate matrix (28672 x 8192, 0.94 GB of fp32
+        # weights): the size the quantizer meets when a large model is converted
+        m = next(mm for mm in workloads.WORKLOADS["stack_70b"].matrices if mm.name == "gate")
+        Wg = workloads.weight("stack_70b", 0, "gate", dev)
+        qg, dg = w4.quantize_rtn(Wg, scale_dtype=scale_dtype)
+        g = capture(torch, lambda: w4.quantize_rtn(Wg, out=(qg, dg)))
+        n = max(3, steps // 16)
+        t = time_graph(torch, g, n, 2)
+        qb = workloads.quantize_bytes(m.N, m.K, sb)
+        qout["stack_70b_gate"] = {"GBps": round(n * qb / t / 1e9, 1), "us_per_call": round(t / n * 1e6, 2),
+                                  "bytes_per_call": qb}
+        log(f"[bench] quantize 70B gate {m.N}x{m.K}: {n * qb / t / 1e9:.0f} GB/s")
+        del g, Wg, qg, dg
     del mats
     torch.cuda.empty_cache()
     return out, qout

@@ -18,11 +18,13 @@
 // (the codes then divide by that stored value).
 // Weights are read with raw buffer loads over the tile's row block: padding
 // rows (N .. Np-1) and padding groups (G .. 4Q-1) read zeros, so they come out
-// as code 0 with scale 0 without a branch.  The loads keep the default cache
-// policy: each instruction covers every other 16 bytes of its rows' lines and
-// the next one the rest, which a streaming (non-temporal) policy would fetch
-// twice.  One tile per wavefront (rather than a loop over tiles) keeps the
-// most loads in flight.
+// as code 0 with scale 0 without a branch.  Each load instruction covers two
+// whole rows of the group (eight full 128-byte lines), so the loads can use
+// the streaming (non-temporal) policy without fetching any line twice; the
+// tile then goes through LDS (one 16 x 128 tile per wavefront, rows padded to
+// 132 floats so the read-back is free of bank conflicts) to the lanes that own
+// each weight in the native layout.  One tile per wavefront (rather than a
+// loop over tiles) keeps the most loads in flight.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -85,16 +87,29 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
   const int g = (int)(tile - r * GP);
 
   // The 32 weights of this lane; zeros outside the matrix.
+  __shared__ float tile_lds[kTilesPerBlock][kTileRows][132];
+  float(&tl)[kTileRows][132] = tile_lds[wave];
   float v[32];
   {
     const int64_t n0 = r * kTileRows;
     const int64_t rows = min((int64_t)kTileRows, (int64_t)N - n0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + n0 * K, (uint32_t)(rows * K * 4));
-    const uint32_t off = g < G ? ((uint32_t)nl * K + (uint32_t)g * kGroup + 8u * kb) * 4u : 0x80000000u;
+    // instruction p: lanes 0-31 read row 2p, lanes 32-63 row 2p+1, 16 bytes each
+    const int hr = lane >> 5, c4 = lane & 31;
+    const uint32_t off = g < G ? ((uint32_t)hr * K + (uint32_t)g * kGroup + 4u * c4) * 4u : 0x80000000u;
+    uint4 raw[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) raw[p] = bload<kNonTemporal>(rs, off + (uint32_t)(2 * p) * (uint32_t)K * 4u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4*>(&tl[2 * p + hr][4 * c4]) = raw[p];
+    // the tile is private to this wavefront: order its LDS writes before the reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 a = bload<0>(rs, off + 128u * i);
-      const uint4 b = bload<0>(rs, off + 128u * i + 16u);
+      const uint4 a = *reinterpret_cast<const uint4*>(&tl[nl][32 * i + 8 * kb]);
+      const uint4 b = *reinterpret_cast<const uint4*>(&tl[nl][32 * i + 8 * kb + 4]);
       v[8 * i + 0] = __uint_as_float(a.x); v[8 * i + 1] = __uint_as_float(a.y);
       v[8 * i + 2] = __uint_as_float(a.z); v[8 * i + 3] = __uint_as_float(a.w);
       v[8 * i + 4] = __uint_as_float(b.x); v[8 * i + 5] = __uint_as_float(b.y);
