@@ -566,14 +566,15 @@ int find_cfg(int R, int NW) {
 
 struct LaunchShape {
   int64_t rows;  // 16-row blocks over the whole batch
-  int kmin, kmax;
+  int kmin, kmax, mmax;
 };
 LaunchShape launch_shape(const BatchArgs& a) {
-  LaunchShape l{0, 1 << 30, 0};
+  LaunchShape l{0, 1 << 30, 0, 0};
   for (int i = 0; i < a.count; ++i) {
     l.rows += (a.desc[i].N + kTileRows - 1) / kTileRows;
     l.kmin = a.desc[i].K < l.kmin ? a.desc[i].K : l.kmin;
     l.kmax = a.desc[i].K > l.kmax ? a.desc[i].K : l.kmax;
+    l.mmax = a.desc[i].M > l.mmax ? a.desc[i].M : l.mmax;
   }
   return l;
 }
@@ -593,7 +594,9 @@ int choose_cfg_mfma(const BatchArgs& a) {
   // weights (x is read through L1 once per row panel).
   const LaunchShape l = launch_shape(a);
   if (l.rows < 256) return find_cfg(1, 4);
-  if (l.rows < 600) return find_cfg(2, 4);
+  // with more than 8 rows of x every lane of the x operand carries data, and
+  // fewer, longer wavefronts pay off sooner
+  if (l.rows < 600) return l.mmax > 8 ? find_cfg(2, 2) : find_cfg(2, 4);
   if (l.rows < 2048) return l.kmin < 4096 ? find_cfg(2, 2) : find_cfg(4, 4);
   // Large launch: one wavefront per block, unless the longest K would leave a
   // few wavefronts streaming far longer than the rest of the launch.
