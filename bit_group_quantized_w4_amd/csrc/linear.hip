@@ -273,6 +273,153 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernel, shared-x form.  A block of NWN wavefronts owns NWN * R row
+// blocks and all of K; wavefront w takes row blocks w*R .. w*R+R-1 and every
+// wavefront walks the same groups in the same order.  The 16-row x tile of a
+// group is read from memory once per block (each wavefront a 16/NWN-row
+// slice), written to a double-buffered LDS tile and read from there as the
+// MFMA A operand, so x costs one load per group and block instead of one per
+// wavefront.  One barrier per group keeps the block in step; it also makes
+// the two-slot tile safe (a slot is rewritten two groups later, after every
+// wavefront has passed the barrier that follows its reads).  Per output row
+// the arithmetic and its order are those of the one-wavefront-per-row-panel
+// kernel with all of K (NW = 1), so the two give identical bits.
+// ---------------------------------------------------------------------------
+template <int R, int NWN, bool S16>
+__device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work& wkb) {
+  static_assert(16 % NWN == 0, "x rows split evenly over the wavefronts");
+  constexpr int kRowsPerWave = 16 / NWN;
+  constexpr int XL = kRowsPerWave >= 4 ? kRowsPerWave / 4 : 1;  // x loads per lane and group
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 15, kb = lane >> 4;
+  const int M = D.M, K = D.K, N = D.N;
+  const Work wk{wkb.di, wkb.rb0 + wave * R, wkb.m0};
+  const Weights<R, S16> w(D, wk, lane, 0, 1);  // all of K
+
+  // This wavefront's slice of the x tile: rows xr[t] of the slab, 16-byte
+  // chunk xc of the group's 256 bytes per row.  With fewer than four rows per
+  // wavefront the lanes past the slice load nothing.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
+  const bool xlane = (lane >> 4) < kRowsPerWave;
+  const int xc = lane & 15;
+  int xr[XL];
+  uint32_t xo[XL];
+#pragma unroll
+  for (int t = 0; t < XL; ++t) {
+    xr[t] = wave * kRowsPerWave + (lane >> 4) % kRowsPerWave + 4 * t;
+    xo[t] = (xlane && wk.m0 + xr[t] < M) ? ((uint32_t)(wk.m0 + xr[t]) * K + 8u * xc) * 2u : kOobX;
+  }
+  const int j1 = w.j1;
+  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
+
+  __shared__ uint4 xs[2][kTileRows][17];  // rows padded to 272 bytes: conflict-free A reads
+
+  uint4 bx[4][XL];
+  uint4 bw[4][R];
+  ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
+
+  auto issue_group = [&](int s, int j) {
+    const int g = 4 * j + s;
+    const uint32_t xb = xbase(j, g), qb = w.qbase(j, g);
+#pragma unroll
+    for (int t = 0; t < XL; ++t) bx[s][t] = bload<0>(rx, xo[t] + xb);
+#pragma unroll
+    for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
+  };
+  auto issue_scales = [&](ScaleQuad<S16> (&dst)[R], int j) {
+    const uint32_t sb = w.sbase(j);
+#pragma unroll
+    for (int r = 0; r < R; ++r) bload_into<kNonTemporal>(w.rd, w.so[r] + sb, dst[r]);
+  };
+
+  const UnpackConsts uc = unpack_consts();
+  const uint32_t kneg2 = (uint32_t)kBf16NegOneHalf | ((uint32_t)kBf16NegOneHalf << 16);
+  const bf16x8 kneg = bitcast<bf16x8>(u32x4{kneg2, kneg2, kneg2, kneg2});
+
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto products = [&](int s, int buf, f32x4 (&c)[R]) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = bitcast<bf16x8>(xs[buf][nl][4 * i + kb]);
+    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) off = mfma16x16x32(a[i], kneg, off);
+#pragma unroll
+    for (int r = 0; r < R; ++r) c[r] = off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < R; ++r) c[r] = mfma16x16x32(a[i], unpack_step(word(bw[s][r], i), uc), c[r]);
+  };
+  auto accumulate = [&](int s, const f32x4 (&c)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float dv = quad_elem(sc[r], s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(dv, c[r][e], acc[r][e]);
+    }
+  };
+
+  // Same ring as the split-K kernel, with the x tile staged through LDS.
+  // Every wavefront of the block runs the same number of iterations, so the
+  // barriers line up.
+  issue_scales(sc, w.j0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    issue_group(s, w.j0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int j = w.j0; j < j1; ++j) {
+    issue_scales(sn, j + 1);  // past the range: zeros, no memory access
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int buf = s & 1;
+      if (xlane) {
+#pragma unroll
+        for (int t = 0; t < XL; ++t) xs[buf][xr[t]][xc] = bx[s][t];
+      }
+      __syncthreads();
+      f32x4 c[R];
+      products(s, buf, c);
+      issue_group(s, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(s, c);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) sc[r] = sn[r];
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= w.rvalid) continue;  // row blocks past the end (a partial panel)
+    const int n = (wk.rb0 + r) * kTileRows + nl;
+    if (n >= N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = wk.m0 + 4 * kb + e;
+      if (m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * acc[r][e]);
+    }
+  }
+}
+
+template <int R, int NWN, bool S16>
+__global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_kernel(const BatchArgs args) {
+  const Work wk = locate(args, R * NWN, 16);
+  mfma_shared_body<R, NWN, S16>(args.desc[wk.di], wk);
+}
+
+template <int R, int NWN, bool S16>
+__global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_one(const uint16_t* x, const uint8_t* q,
+                                                                   const void* d, uint16_t* y, int M, int K,
+                                                                   int N) {
+  const LinearDesc D{x, q, d, y, M, K, N, 0};
+  mfma_shared_body<R, NWN, S16>(D, locate_one(N, R * NWN, 16));
+}
+
 // Batched launch: the block finds its linear in the kernel arguments.
 template <int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
@@ -536,31 +683,48 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
 // ---------------------------------------------------------------------------
 // launch configuration
 // ---------------------------------------------------------------------------
+// R row blocks per wavefront and NW wavefronts per block.  Split-K
+// configurations (shared = false) divide K among the block's wavefronts,
+// which share one row panel; shared-x configurations (MFMA only) give each
+// wavefront its own R row blocks and all of K and share the x tile.
 struct Cfg {
   int R, NW;
+  bool shared;
 };
 
-// Every (R, NW) compiled for each kernel and scale format.  W4_MFMA_CFG /
-// W4_GEMV_CFG ("R,NW") may pick one of them for measurement; a value naming
-// no compiled configuration makes the launch fail (hipErrorInvalidValue).
-constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {2, 4}, {4, 4}, {1, 2}, {2, 2}, {4, 1}, {4, 2}};
+// Every configuration compiled for each kernel and scale format (the first
+// kNumSplitCfgs for both kernels, the shared-x ones for the MFMA kernel).
+// W4_MFMA_CFG / W4_GEMV_CFG ("R,NW", or "R,NWs" for shared x) may pick one of
+// them for measurement; a value naming no configuration compiled for that
+// kernel makes the launch fail (hipErrorInvalidValue).
+constexpr Cfg kCfgs[] = {{1, 4, false}, {1, 8, false}, {2, 4, false}, {4, 4, false}, {1, 2, false},
+                         {2, 2, false}, {4, 1, false}, {4, 2, false}, {2, 8, true},  {2, 4, true}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
-static_assert(kNumCfgs == 8, "the launch switches below list 8 configurations");
+constexpr int kNumSplitCfgs = 8;
+static_assert(kNumCfgs == 10, "the launch switches below list 10 configurations");
+static_assert(!kCfgs[0].shared && !kCfgs[1].shared && !kCfgs[2].shared && !kCfgs[3].shared && !kCfgs[4].shared &&
+                  !kCfgs[5].shared && !kCfgs[6].shared && !kCfgs[7].shared && kCfgs[8].shared && kCfgs[9].shared,
+              "split-K configurations first: the dot2 launch compiles only those");
 
-// -1: not set; -2: set to something that is not compiled.
-int cfg_from_env(const char* name) {
+// -1: not set; -2: set to something that is not compiled for this kernel.
+int cfg_from_env(const char* name, bool allow_shared) {
   const char* s = getenv(name);
   if (!s) return -1;
   int R = 0, NW = 0;
-  if (sscanf(s, "%d,%d", &R, &NW) != 2) return -2;
+  char tail[4] = {0, 0, 0, 0};
+  const int got = sscanf(s, "%d,%d%3s", &R, &NW, tail);
+  if (got < 2) return -2;
+  const bool shared = got == 3 && tail[0] == 's' && tail[1] == 0;
+  if (got == 3 && !shared) return -2;
   for (int i = 0; i < kNumCfgs; ++i)
-    if (kCfgs[i].R == R && kCfgs[i].NW == NW) return i;
+    if (kCfgs[i].R == R && kCfgs[i].NW == NW && kCfgs[i].shared == shared)
+      return shared && !allow_shared ? -2 : i;
   return -2;
 }
 
-int find_cfg(int R, int NW) {
+int find_cfg(int R, int NW, bool shared = false) {
   for (int i = 0; i < kNumCfgs; ++i)
-    if (kCfgs[i].R == R && kCfgs[i].NW == NW) return i;
+    if (kCfgs[i].R == R && kCfgs[i].NW == NW && kCfgs[i].shared == shared) return i;
   return 0;
 }
 
@@ -598,10 +762,15 @@ int choose_cfg_mfma(const BatchArgs& a) {
   // fewer, longer wavefronts pay off sooner
   if (l.rows < 600) return l.mmax > 8 ? find_cfg(2, 2) : find_cfg(2, 4);
   if (l.rows < 2048) return l.kmin < 4096 ? find_cfg(2, 2) : find_cfg(4, 4);
-  // Large launch: one wavefront per block, unless the longest K would leave a
-  // few wavefronts streaming far longer than the rest of the launch.
+  // Large launch: each wavefront streams all of K for its row blocks, unless
+  // the longest K would leave a few wavefronts streaming far longer than the
+  // rest of the launch.  With more than 8 rows of x (every lane of the x
+  // operand carries data), or with very many row blocks, blocks of eight such
+  // wavefronts share each x tile through LDS; otherwise one wavefront per
+  // block.
   const int qmax = (l.kmax / kGroup + 3) / 4;
-  return qmax <= 20 ? find_cfg(4, 1) : find_cfg(4, 4);
+  if (qmax > 20) return find_cfg(4, 4);
+  return l.mmax > 8 || l.rows >= 8192 ? find_cfg(2, 8, true) : find_cfg(4, 1);
 }
 
 int choose_cfg_gemv(const BatchArgs& a) {
@@ -664,11 +833,17 @@ void launch_gemv_cfg(int ci, unsigned blocks, size_t lds, hipStream_t st, const 
 template <bool S16, int I>
 void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
   constexpr Cfg c = kCfgs[I];
-  if (a.count == 1) {
-    const LinearDesc& l = a.desc[0];
-    linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+  const LinearDesc& l = a.desc[0];
+  if constexpr (c.shared) {
+    if (a.count == 1)
+      linear_mfma_shared_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+    else
+      linear_mfma_shared_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   } else {
-    linear_mfma_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
+    if (a.count == 1)
+      linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+    else
+      linear_mfma_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   }
 }
 
@@ -679,7 +854,7 @@ void launch_mfma_cfg(int ci, unsigned blocks, hipStream_t st, const BatchArgs& a
   case i:          \
     launch_mfma_at<S16, i>(blocks, st, a); \
     break;
-    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
+    W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7) W4_CASE(8) W4_CASE(9)
 #undef W4_CASE
   }
 }
@@ -687,11 +862,11 @@ void launch_mfma_cfg(int ci, unsigned blocks, hipStream_t st, const BatchArgs& a
 }  // namespace
 
 hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream) {
-  const int env = cfg_from_env("W4_MFMA_CFG");
+  const int env = cfg_from_env("W4_MFMA_CFG", true);
   if (env == -2) return hipErrorInvalidValue;
   const int ci = env >= 0 ? env : choose_cfg_mfma(a);
   const Cfg c = kCfgs[ci];
-  const int64_t blocks = fill_blocks(a, c.R, 16);
+  const int64_t blocks = fill_blocks(a, c.shared ? c.R * c.NW : c.R, 16);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (s16) launch_mfma_cfg<true>(ci, (unsigned)blocks, stream, a);
@@ -728,7 +903,7 @@ hipError_t launch_linear_gemv_xscaled(const LinearDesc& l, const float* inv_s, i
 }
 
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream) {
-  const int env = cfg_from_env("W4_GEMV_CFG");
+  const int env = cfg_from_env("W4_GEMV_CFG", false);
   if (env == -2) return hipErrorInvalidValue;
   const int ci = env >= 0 ? env : choose_cfg_gemv(a);
   const Cfg c = kCfgs[ci];

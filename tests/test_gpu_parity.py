@@ -345,8 +345,10 @@ def test_linear_batched_matches_single_calls(w4, gpu, path, monkeypatch):
 # Every compiled (row blocks per wavefront, wavefronts per block) pair; the
 # built-in choice picks among them by launch size, so each is checked here on
 # ragged shapes: partial row panels, K not a whole number of scale quads, and
-# more wavefronts per block than the matrix has quads.
-CONFIGS = ["1,4", "1,8", "2,4", "4,4", "1,2", "2,2", "4,1", "4,2"]
+# more wavefronts per block than the matrix has quads.  "s" marks the MFMA
+# kernel's shared-x form (each wavefront all of K, the x tile shared through
+# LDS); it is not compiled for the dot2 kernel.
+CONFIGS = ["1,4", "1,8", "2,4", "4,4", "1,2", "2,2", "4,1", "4,2", "2,8s", "2,4s"]
 CFG_SHAPES = [(700, 1408), (37, 384), (260, 2560)]
 
 
@@ -355,6 +357,13 @@ CFG_SHAPES = [(700, 1408), (37, 384), (260, 2560)]
 @pytest.mark.parametrize("cfg", CONFIGS)
 def test_linear_every_config(w4, gpu, cfg, path, scale_dtype, monkeypatch):
     monkeypatch.setenv("W4_MFMA_CFG" if path == "mfma" else "W4_GEMV_CFG", cfg)
+    if cfg.endswith("s") and path == "gemv":
+        _say(f"config {cfg} is not compiled for the dot2 kernel")
+        q = torch.zeros(w4.packed_bytes(16, 128), dtype=torch.uint8, device=gpu)
+        d = torch.zeros(w4.scale_count(16, 128), dtype=torch.float32, device=gpu)
+        with pytest.raises(w4.W4Error):
+            w4.linear(torch.zeros((1, 128), dtype=torch.bfloat16, device=gpu), q, d, 16, path="gemv")
+        return
     sd = torch.bfloat16 if scale_dtype == "bf16" else torch.float32
     mats = []
     for i, (N, K) in enumerate(CFG_SHAPES):
@@ -374,14 +383,40 @@ def test_linear_every_config(w4, gpu, cfg, path, scale_dtype, monkeypatch):
             check_y(y1, y_ref, absdot, f"cfg {cfg} single {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("scale_dtype", ["f32", "bf16"])
+def test_shared_x_matches_one_wavefront_panels(w4, gpu, scale_dtype, monkeypatch):
+    """The shared-x MFMA form computes every output row with the same
+    arithmetic in the same order as one wavefront per row panel over all of K:
+    identical bits, whatever the row blocks per wavefront."""
+    sd = torch.bfloat16 if scale_dtype == "bf16" else torch.float32
+    shapes = [(700, 1408), (2048, 2560), (37, 384)]
+    mats = []
+    for i, (N, K) in enumerate(shapes):
+        W = torch.from_numpy(workloads.random_weight(N, K, seed=700 + i)).to(gpu)
+        mats.append((N, K) + w4.quantize_rtn(W, scale_dtype=sd))
+    for M in (1, 8, 16, 23):
+        _say(f"shared x vs one-wavefront panels, scales={scale_dtype} M={M}")
+        xs = [workloads.random_activations(M, K, seed=M + 31 * i, device=gpu) for i, (_, K, _, _) in enumerate(mats)]
+        outs = {}
+        for cfg in ("4,1", "2,8s", "2,4s"):
+            monkeypatch.setenv("W4_MFMA_CFG", cfg)
+            items = [(x, q, d, N, torch.empty((M, N), dtype=torch.bfloat16, device=gpu))
+                     for x, (N, K, q, d) in zip(xs, mats)]
+            outs[cfg] = [y.view(torch.int16).clone() for y in w4.linear_batched(items, path="mfma")]
+        for cfg in ("2,8s", "2,4s"):
+            for a, b, (N, K, _, _) in zip(outs["4,1"], outs[cfg], mats):
+                assert torch.equal(a, b), f"{cfg} differs from 4,1 on {N}x{K} M={M}"
+
+
 def test_linear_unknown_config_is_an_error(w4, gpu, monkeypatch):
     q = torch.zeros(w4.packed_bytes(16, 128), dtype=torch.uint8, device=gpu)
     d = torch.zeros(w4.scale_count(16, 128), dtype=torch.float32, device=gpu)
     x = torch.zeros((1, 128), dtype=torch.bfloat16, device=gpu)
     for var, path in (("W4_MFMA_CFG", "mfma"), ("W4_GEMV_CFG", "gemv")):
-        monkeypatch.setenv(var, "3,3")
-        with pytest.raises(w4.W4Error):
-            w4.linear(x, q, d, 16, path=path)
+        for bad in ("3,3", "2,8x", "4"):
+            monkeypatch.setenv(var, bad)
+            with pytest.raises(w4.W4Error):
+                w4.linear(x, q, d, 16, path=path)
         monkeypatch.delenv(var)
     w4.linear(x, q, d, 16)  # and the library still works
 
