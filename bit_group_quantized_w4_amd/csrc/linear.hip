@@ -761,7 +761,12 @@ int choose_cfg_mfma(const BatchArgs& a) {
   // with more than 8 rows of x every lane of the x operand carries data, and
   // fewer, longer wavefronts pay off sooner
   if (l.rows < 600) return l.mmax > 8 ? find_cfg(2, 2) : find_cfg(2, 4);
-  if (l.rows < 2048) return l.kmin < 4096 ? find_cfg(2, 2) : find_cfg(4, 4);
+  if (l.rows < 2048) {
+    if (l.kmin >= 4096) return find_cfg(4, 4);
+    // short K: few quads per wavefront; with more than 8 rows of x and every
+    // K short, sharing the x tile beats splitting K
+    return l.mmax > 8 && l.kmax < 4096 ? find_cfg(2, 4, true) : find_cfg(2, 2);
+  }
   // Large launch: each wavefront streams all of K for its row blocks, unless
   // the longest K would leave a few wavefronts streaming far longer than the
   // rest of the launch.  With more than 8 rows of x (every lane of the x
