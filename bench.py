@@ -16,6 +16,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 4b,27b,70b|
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,10 +41,15 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the headline kernel's source code: comments and whitespace are
+    dropped, so that editing a comment does not retire the stored counters."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

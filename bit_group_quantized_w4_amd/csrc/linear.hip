@@ -5,11 +5,14 @@
 // stage 2), so it is bound by streaming the packed weights from HBM.
 //
 // One launch serves a batch of up to kMaxBatch independent linears (a single
-// w4_linear call is a batch of one).  Work decomposition, per linear:
+// w4_linear call is a batch of one), laid out longest K first.  Work
+// decomposition, per linear:
 //   * a workgroup owns R consecutive 16-row blocks, all K, and one slab of
 //     x rows (16 for the MFMA kernel, MT for the dot2 kernel);
 //   * its NW wavefronts split K into contiguous ranges of whole scale quads
-//     (4 groups of 128 inputs);
+//     (4 groups of 128 inputs) -- or, in the MFMA kernel's shared-x form,
+//     each of the NW wavefronts takes R row blocks of its own over all of K
+//     and the block shares each x tile through LDS;
 //   * each wavefront walks its range quad by quad with a ring of loads in
 //     flight, issued in exactly the order they are consumed;
 //   * weight, scale and x loads are raw buffer loads: a quad beyond the
