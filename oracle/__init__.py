@@ -24,6 +24,9 @@ What it computes (sources are the public pages this project is built from):
   RTN (study, section 2: the AWQ row of the methods table, the 20-exponent
   scale search of the settings table, and the channel-scaling and
   output-error equations).
+* ``gptq_ref`` and its steps -- GPTQ's column-by-column quantization with
+  error feedback (study, section 2: the GPTQ row, damping 0.01, 128-column
+  blocks, no reordering; the update rule of the published GPTQ algorithm).
 
 Every function here is pinned by ``tests/test_oracle.py`` against exact
 rational arithmetic, brute force on small inputs, closed forms and hand-derived
@@ -33,6 +36,7 @@ fixtures in ``tests/golden/``; none is "parity unpinned".
 from .awq import (ALPHAS, awq_output_error_ref, awq_search_ref, candidate_scales_ref, channel_absmean_ref,
                   quantize_scaled_ref, scale_activations_ref)
 from .bf16 import bf16_bits_to_f64, f32_to_bf16_bits
+from .gptq import gptq_factor_ref, gptq_hessian_ref, gptq_quantize_ref, gptq_ref, output_error_ref
 from .linear import dequantize_ref, w4_linear_ref
 from .packing import pack_canonical, unpack_canonical
 from .rtn import GROUP, NAN_BITS, QMAX, QMIN, rtn_quantize_ref
@@ -52,6 +56,11 @@ __all__ = [
     "bf16_bits_to_f64",
     "dequantize_ref",
     "f32_to_bf16_bits",
+    "gptq_factor_ref",
+    "gptq_hessian_ref",
+    "gptq_quantize_ref",
+    "gptq_ref",
+    "output_error_ref",
     "pack_canonical",
     "rtn_quantize_ref",
     "unpack_canonical",

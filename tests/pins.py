@@ -491,3 +491,118 @@ def check_awq_helps_on_salient_channels(search):
     k, s32, inv32, errors = search(W, xb)
     _check(k > 0 and errors[k] < 0.9 * errors[0], f"expected alpha > 0 to help (k={k}, {errors[k] / errors[0]:.3f})")
     _check(errors[k] == min(errors), "the chosen exponent must have the smallest error")
+
+
+# ----------------------------------------------------------------------------
+# GPTQ (study, section 2: the GPTQ row and settings; update rule of the
+# published GPTQ algorithm).  The brute-force reference below re-solves, after
+# every column, for the remaining columns that minimise the damped quadratic
+# error given the columns fixed so far -- the property the Cholesky-based
+# update realises -- with direct linear solves instead of the factor, and
+# takes every code and scale decision in exact rationals.
+# ----------------------------------------------------------------------------
+
+def gptq_correlated_inputs(seed=0, N=3, K=256, T=64):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = rng.standard_normal((K, K)) * 0.15 + np.eye(K)
+    X = (rng.standard_normal((T, K)) @ A).astype(np.float32)
+    xb = (X.view(np.uint32) >> 16).astype(np.uint16)  # truncation to bf16 is fine for inputs
+    return W, xb
+
+
+def gptq_damped_hessian(x_bits, damp=0.01):
+    # bf16 -> fp32 by placing the 16 bits in the top half (exact), then fp64
+    X = (np.asarray(x_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    H = (2.0 / X.shape[0]) * (X.T @ X)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))
+    return H
+
+
+def gptq_bruteforce(W, x_bits, damp=0.01):
+    H = gptq_damped_hessian(x_bits, damp)
+    N, K = W.shape
+    q = np.zeros((N, K), dtype=np.int8)
+    d = np.zeros((N, K // 128), dtype=np.float32)
+    for n in range(N):
+        w0 = W[n].astype(np.float64)
+        w = w0.copy()
+        what = np.zeros(K)
+        for j in range(K):
+            if j % 128 == 0:
+                a = max(abs(Fraction(float(np.float32(v)))) for v in w[j:j + 128])
+                d[n, j // 128] = f32_nearest(a / 7)
+            dv = d[n, j // 128]
+            if dv == 0:
+                qj = 0
+            else:
+                t = f32_nearest(Fraction(float(np.float32(w[j]))) / Fraction(float(dv)))
+                qj = nearest_level(Fraction(float(t)))
+            q[n, j] = qj
+            what[j] = float(dv) * qj
+            if j + 1 < K:
+                F, R = slice(0, j + 1), slice(j + 1, K)
+                w[R] = w0[R] - np.linalg.solve(H[R, R], H[R, F] @ (what[F] - w0[F]))
+    return q, d
+
+
+def check_gptq_bruteforce(gptq):
+    """Codes and scales equal the sequential re-solve with exact-rational decisions."""
+    W, xb = gptq_correlated_inputs(seed=3)
+    q, d = gptq(W, xb)
+    qb, db = gptq_bruteforce(W, xb)
+    _check(np.array_equal(d.view(np.uint32), db.view(np.uint32)), "GPTQ scales differ from the brute-force re-solve")
+    bad = np.argwhere(q != qb)
+    _check(bad.size == 0, f"GPTQ codes differ from the brute-force re-solve at {bad[:4].tolist()}")
+
+
+def check_gptq_identity_hessian_is_rtn(gptq):
+    """With calibration inputs whose Hessian is a multiple of the identity nothing
+    propagates, so GPTQ is RTN: the RTN pins hold for it."""
+    K = 256
+    xb = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0))  # X = I in bf16
+    W = toy_weights(4, N=4, K=K)
+    quantize = lambda Wm: gptq(Wm, xb)
+    check_scale_exact(quantize, W)
+    check_codes_bruteforce(quantize, W)
+
+
+def check_gptq_block_width(quantize_with_block, factor, hessian):
+    """The lazy block width changes only the order of the corrections: 128 and K agree."""
+    W, xb = gptq_correlated_inputs(seed=5, N=4, K=512, T=96)
+    U = factor(hessian(xb))
+    q1, d1 = quantize_with_block(W, U, 128)
+    q2, d2 = quantize_with_block(W, U, 512)
+    _check(np.array_equal(q1, q2) and np.array_equal(d1, d2), "block width 128 and K must give the same codes")
+
+
+def check_gptq_beats_rtn(gptq, rtn, output_error):
+    """On correlated calibration inputs the column feedback lowers the output error well below RTN."""
+    W, xb = gptq_correlated_inputs(seed=7, N=16, K=512, T=256)
+    eg = output_error(W, *gptq(W, xb), xb)
+    er = output_error(W, *rtn(W), xb)
+    _check(eg < 0.6 * er, f"GPTQ error {eg:.3e} should be well below RTN {er:.3e}")
+
+
+def check_gptq_dead_columns(factor, hessian):
+    """A column with all-zero inputs is decoupled: its row and column of U are zero off the diagonal."""
+    W, xb = gptq_correlated_inputs(seed=9, N=2, K=256, T=64)
+    xb = xb.copy()
+    xb[:, 17] = 0
+    U = factor(hessian(xb))
+    _check(np.isfinite(U).all(), "the factor must exist with a dead column")
+    off = np.concatenate([U[17, :17], U[17, 18:], U[:17, 17], U[18:, 17]])
+    _check(np.all(off == 0), "a dead column must not couple to the others")
+
+
+def check_gptq_all_inputs_zero_is_rtn(gptq):
+    """With all-zero calibration inputs every column is dead: the factor must still exist,
+    nothing couples, and GPTQ is RTN."""
+    K = 256
+    xb = np.zeros((8, K), dtype=np.uint16)
+    W = toy_weights(6, N=3, K=K)
+    quantize = lambda Wm: gptq(Wm, xb)
+    check_scale_exact(quantize, W)
+    check_codes_bruteforce(quantize, W)

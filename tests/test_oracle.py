@@ -432,3 +432,106 @@ def test_awq_mutants_are_caught(kind):
     _all_awq_pins(*_awq_mutants("none"))
     with pytest.raises(pins.PinFailure):
         _all_awq_pins(*_awq_mutants(kind))
+
+
+# ----------------------------------------------------------------------------
+# GPTQ
+# ----------------------------------------------------------------------------
+
+def _gptq_quantize_with_block(W, U, block):
+    return oracle.gptq_quantize_ref(W, U, block)
+
+
+def test_gptq_bruteforce():
+    pins.check_gptq_bruteforce(oracle.gptq_ref)
+
+
+def test_gptq_identity_hessian_is_rtn():
+    pins.check_gptq_identity_hessian_is_rtn(oracle.gptq_ref)
+
+
+def test_gptq_block_width():
+    pins.check_gptq_block_width(_gptq_quantize_with_block, oracle.gptq_factor_ref, oracle.gptq_hessian_ref)
+
+
+def test_gptq_beats_rtn():
+    pins.check_gptq_beats_rtn(oracle.gptq_ref, Q, oracle.output_error_ref)
+
+
+def test_gptq_dead_columns():
+    pins.check_gptq_dead_columns(oracle.gptq_factor_ref, oracle.gptq_hessian_ref)
+
+
+def test_gptq_all_inputs_zero_is_rtn():
+    pins.check_gptq_all_inputs_zero_is_rtn(oracle.gptq_ref)
+
+
+def test_gptq_rejects_non_finite():
+    W, xb = pins.gptq_correlated_inputs()
+    W = W.copy()
+    W[0, 3] = np.inf
+    with pytest.raises(ValueError):
+        oracle.gptq_ref(W, xb)
+
+
+def _gptq_mutant(kind):
+    """A copy of the GPTQ oracle with one plausible mistake."""
+    def factor(H):
+        H = np.array(H, dtype=np.float64, copy=True)
+        dead = np.diag(H) == 0
+        if kind != "no_dead_fix":
+            H[dead, dead] = 1.0
+        damp = {"damp_tenth": 0.1, "no_damping": 0.0}.get(kind, 0.01)
+        H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))
+        if kind == "factor_of_hessian":
+            return np.linalg.cholesky(H).T
+        L = np.linalg.cholesky(np.linalg.inv(H))
+        return L if kind == "lower_factor" else L.T
+
+    def quantize(W, U, block=128):
+        N, K = W.shape
+        Wk = W.astype(np.float64)
+        W0 = Wk.copy()
+        q = np.zeros((N, K), dtype=np.int8)
+        d = np.zeros((N, K // 128), dtype=np.float32)
+        for b0 in range(0, K, block):
+            b1 = min(b0 + block, K)
+            E = np.zeros((N, b1 - b0))
+            for j in range(b0, b1):
+                if j % 128 == 0:
+                    src = W0 if kind == "scale_from_original" else Wk
+                    d[:, j // 128] = oracle.gptq.group_scale_ref(src[:, j:j + 128])
+                dg = d[:, j // 128]
+                qj = oracle.gptq.code_ref(Wk[:, j], dg)
+                q[:, j] = qj.astype(np.int8)
+                err = Wk[:, j] - dg.astype(np.float64) * qj
+                if kind != "no_divide":
+                    err = err / U[j, j]
+                if kind != "no_in_block":
+                    Wk[:, j + 1:b1] -= np.outer(err, U[j, j + 1:b1])
+                E[:, j - b0] = err
+            if kind != "no_trailing":
+                Wk[:, b1:] -= E @ U[b0:b1, b1:]
+        return q, d
+
+    hessian = oracle.gptq_hessian_ref
+    gptq = lambda W, xb: quantize(W, factor(hessian(xb)))
+    return gptq, quantize, factor, hessian
+
+
+def _all_gptq_pins(gptq, quantize, factor, hessian):
+    pins.check_gptq_bruteforce(gptq)
+    pins.check_gptq_identity_hessian_is_rtn(gptq)
+    pins.check_gptq_block_width(quantize, factor, hessian)
+    pins.check_gptq_beats_rtn(gptq, Q, oracle.output_error_ref)
+    pins.check_gptq_dead_columns(factor, hessian)
+    pins.check_gptq_all_inputs_zero_is_rtn(gptq)
+
+
+@pytest.mark.parametrize("kind", ["no_trailing", "no_in_block", "no_divide", "scale_from_original",
+                                  "factor_of_hessian", "lower_factor", "damp_tenth", "no_damping",
+                                  "no_dead_fix"])
+def test_gptq_mutants_are_caught(kind):
+    _all_gptq_pins(*_gptq_mutant("none"))
+    with pytest.raises((pins.PinFailure, np.linalg.LinAlgError)):
+        _all_gptq_pins(*_gptq_mutant(kind))
