@@ -338,6 +338,60 @@ def bench_awq(torch, w4, workloads, steps, warmup, T=256):
     return out
 
 
+def bench_gptq(torch, w4, workloads, T=16384, T_eval=1024):
+    """GPTQ of the 70B-class gate matrix (28672x8192, layer 0) calibrated on T rows
+    (T = 2K, so the Hessian is well determined): time per phase, and the output error
+    against RTN's (both through the library's linear) on the calibration rows and on
+    T_eval held-out rows, for two input recipes:
+      * "recipe": the 70B recipe's activations, whose channels are independent
+        (diagonal covariance), so column feedback can only fit the sample
+        Hessian's noise;
+      * "correlated": the same rows mixed by one fixed matrix A = I + 2 G / sqrt(K)
+        (G standard normal, seeded), so the channels are strongly correlated."""
+    from bit_group_quantized_w4_amd import gptq
+
+    dev = torch.device("cuda:0")
+    name, mat = "stack_70b", "gate"
+    W = workloads.weight(name, 0, mat, dev)
+    N, K = W.shape
+    q_rtn, d_rtn = w4.quantize_rtn(W)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20)
+    A = torch.randn((K, K), generator=gen, device=dev).mul_(2.0 / K ** 0.5)
+    A.diagonal().add_(1.0)
+    out = {"matrix": f"{N}x{K}", "calibration_rows": T, "held_out_rows": T_eval}
+    for case in ("recipe", "correlated"):
+        x_cal = workloads.activations(name, 0, mat, T, dev)
+        x_eval = workloads.activations(name, 0, mat, T_eval, dev)
+        if case == "correlated":
+            x_cal = (x_cal.float() @ A).to(torch.bfloat16)
+            x_eval = (x_eval.float() @ A).to(torch.bfloat16)
+        if case == "recipe":
+            gptq.quantize(W, x_cal)  # warm: libraries load their kernels
+        torch.cuda.synchronize()
+        tm = {}
+        t0 = time.perf_counter()
+        q, d = gptq.quantize(W, x_cal, timings=tm)
+        torch.cuda.synchronize()
+        total = time.perf_counter() - t0
+        ratios = {}
+        for rows, x in (("calibration", x_cal[:T_eval]), ("held_out", x_eval)):
+            y_ref = torch.matmul(x.float(), W.t())
+            e = {tag: float(w4.sq_error(w4.linear(x, qq, dd, N), y_ref).item())
+                 for tag, (qq, dd) in (("gptq", (q, d)), ("rtn", (q_rtn, d_rtn)))}
+            ratios[rows] = round(e["gptq"] / e["rtn"], 4)
+            del y_ref
+        out[case] = {"ms_total": round(total * 1e3, 1), "ms_phases": {k: round(v, 2) for k, v in tm.items()},
+                     "output_error_vs_rtn": ratios}
+        log(f"[bench] gptq {N}x{K} {case} (T={T}): {total * 1e3:.0f} ms "
+            f"({', '.join(f'{k} {v:.1f}' for k, v in tm.items())} ms), output error x RTN: "
+            f"calibration rows {ratios['calibration']:.3f}, held-out rows {ratios['held_out']:.3f}")
+        del q, d, x_cal, x_eval
+    del W, A
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample, rank 0, after the GPU phase)
 # ----------------------------------------------------------------------------
@@ -539,6 +593,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
     ap.add_argument("--no-s16", action="store_true", help="skip the 16-bit-scale measurements")
+    ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQ quantizer measurement")
     ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
     ap.add_argument("--stack-modes", default="",
                     help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
@@ -598,6 +653,7 @@ def main():
                                         scale_dtype=torch.bfloat16)
 
     awq_res = None if args.no_awq else bench_awq(torch, w4, workloads, args.steps, args.warmup)
+    gptq_res = None if args.no_gptq else bench_gptq(torch, w4, workloads)
     read_peak = measure_read_peak(torch, w4)
 
     if args.calibrate_copy_mb:
@@ -647,6 +703,7 @@ def main():
         "hbm_read_peak_measured": read_peak,
         "scales_16bit": s16,
         "awq": awq_res,
+        "gptq": gptq_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -58,6 +58,9 @@ SIGNATURES = {
     "w4_scale_activations": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_linear_awq": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP, _VP]),
     "w4_sq_error": (_INT, [_VP, _VP, _I64, _VP, _VP]),
+    # GPTQ steps
+    "w4_gptq_damp": (_INT, [_VP, _I64, ctypes.c_double, _VP]),
+    "w4_gptq_block": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
 }
 
 
@@ -283,6 +286,26 @@ def sq_error(y, y_ref, out=None):
     _check(_lib.w4_sq_error(_dev(y, torch.bfloat16, "y"), _dev(y_ref, torch.float32, "y_ref"), y.numel(),
                             _dev(o, torch.float64, "out"), _stream(y)), "w4_sq_error")
     return o
+
+
+def gptq_damp(H, damp=0.01):
+    """In place on H (fp64 [K, K]): zero diagonal entries become 1, then damp * mean(diag) is added."""
+    if H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be square")
+    _check(_lib.w4_gptq_damp(_dev(H, torch.float64, "H"), H.shape[0], float(damp), _stream(H)), "w4_gptq_damp")
+    return H
+
+
+def gptq_block(W, U, b0, q_canon, d_canon, err):
+    """GPTQ column loop over columns b0 .. b0+127 of W (fp32 [N, K], not modified): codes into
+    q_canon (int8 [N, K]), the group scale into d_canon (fp32 [N, K/128]), the column errors into
+    err (fp32 [128, N])."""
+    N, K = W.shape
+    if U.shape != (K, K) or q_canon.shape != (N, K) or d_canon.shape != (N, K // 128) or err.shape != (128, N):
+        raise ValueError("shape mismatch")
+    _check(_lib.w4_gptq_block(_dev(W, torch.float32, "W"), N, K, int(b0), _dev(U, torch.float32, "U"),
+                              _dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, torch.float32, "d_canon"),
+                              _dev(err, torch.float32, "err"), _stream(W)), "w4_gptq_block")
 
 
 class W4Linear:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw4.so")
 BENCH_LIB = os.path.join(PKG, "libw4_bench.so")
 
-LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip"]
+LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip", "gptq.hip"]
 BENCH_SOURCES = ["copy_probe.hip"]
 
 ARCH = "gfx950"

@@ -4,6 +4,8 @@
 #include "w4.h"
 #include "w4_launch.h"
 
+#include <float.h>
+
 #include <stdint.h>
 
 namespace {
@@ -341,6 +343,33 @@ w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, doub
   if (!aligned(y, 2) || !aligned(y_ref, 4) || !aligned(out, 8)) return W4_ERR_ALIGN;
   if (overlaps(out, 8, y, 2 * (size_t)count) || overlaps(out, 8, y_ref, 4 * (size_t)count)) return W4_ERR_ARG;
   return hip_status(w4::launch_sq_error(y, y_ref, count, out, stream));
+}
+
+w4_status w4_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream) {
+  if (K < 1 || K > (int64_t)1 << 20) return W4_ERR_SHAPE;
+  if (!(damp >= 0.0) || !(damp <= DBL_MAX)) return W4_ERR_ARG;
+  if (!H) return W4_ERR_NULL;
+  if (!aligned(H, 8)) return W4_ERR_ALIGN;
+  return hip_status(w4::launch_gptq_damp(H, K, damp, stream));
+}
+
+w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                        float* d_canon, float* err, hipStream_t stream) {
+  if (!n_ok(N) || !k_ok(K) || N > ((int64_t)1 << 31) - 1 || b0 < 0 || b0 >= K || b0 % kGroup) return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!W || !U || !q_canon || !d_canon || !err) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(U, 4) || !aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(err, 4))
+    return W4_ERR_ALIGN;
+  const size_t wb = 4 * (size_t)N * K, ub = 4 * (size_t)K * K, qb = (size_t)N * K,
+               db = 4 * (size_t)N * (K / kGroup), eb = 4 * (size_t)kGroup * N;
+  const void* outs[3] = {q_canon, d_canon, err};
+  const size_t ob[3] = {qb, db, eb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], ob[i], W, wb) || overlaps(outs[i], ob[i], U, ub)) return W4_ERR_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return W4_ERR_ARG;
+  }
+  return hip_status(w4::launch_gptq_block(W, N, K, b0, U, q_canon, d_canon, err, stream));
 }
 
 }  // extern "C"

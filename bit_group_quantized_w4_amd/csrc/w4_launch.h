@@ -64,4 +64,10 @@ hipError_t launch_scale_activations(const uint16_t* x, int64_t M, int64_t K, con
                                     hipStream_t stream);
 hipError_t launch_sq_error(const uint16_t* y, const float* yref, int64_t n, double* out, hipStream_t stream);
 
+// GPTQ steps (gptq.hip): the column loop over the 128-column block at b0, and
+// the damping of the Hessian.
+hipError_t launch_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                             float* d_canon, float* errT, hipStream_t stream);
+hipError_t launch_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream);
+
 }  // namespace w4

@@ -289,6 +289,46 @@ w4_status w4_linear_awq(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
 w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, double* out,
                       hipStream_t stream);
 
+/*
+ * GPTQ (study, section 2: the GPTQ row of the methods table -- same storage
+ * as RTN, one input column quantized at a time with the columns not yet
+ * quantized corrected through a Hessian of calibration inputs; the settings
+ * table -- damping 0.01 of the mean Hessian diagonal, blocks of 128 columns,
+ * no reordering).  The update rule is the published GPTQ algorithm.  The
+ * quantizer runs, per matrix W [N][K] (fp32, finite) and calibration rows
+ * x [T][K]:
+ *   H = (2/T) x^T x                          (fp64 [K][K], a plain product)
+ *   w4_gptq_damp(H, 0.01)
+ *   U = upper triangular with H^-1 = U^T U   (a plain fp64 factorization,
+ *                                             then rounded to fp32)
+ *   for b0 = 0, 128, ...:
+ *     w4_gptq_block(W, b0, U) -> codes and scales of columns b0..b0+127, err
+ *     W[:, b0+128:] -= err^T U[b0:b0+128, b0+128:]   (a plain product)
+ *   w4_pack(codes, scales) -> the native layout w4_linear reads.
+ */
+
+/* H [K][K] fp64 row-major, in place: a zero diagonal entry becomes 1, then
+ * damp * mean(diag) is added to every diagonal entry (fixed summation
+ * order).  K >= 1; damp finite and >= 0 (else W4_ERR_ARG); H 8-byte aligned. */
+w4_status w4_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream);
+
+/* The GPTQ column loop over the block of columns b0 .. b0+127 (one group):
+ * for every row n < N of W (fp32 [N][K], the current, already corrected
+ * weights; only the block's columns are read), the group scale
+ * d = fl32(max|w| / 7) of the block's current weights, then for each column j
+ * in order the RTN code decision against d, err_j = (w_j - d q_j) / U[j][j]
+ * and w_k -= err_j U[j][k] for the block's later columns k.  Writes the codes
+ * to q_canon (int8 [N][K], canonical layout, the block's columns), the scale
+ * to d_canon[n][b0/128] (fp32 [N][K/128]) and err_j to err[j][n] (fp32
+ * [128][N], column-major).  U is fp32 [K][K] row-major (its diagonal block at
+ * b0 is read).  W is not modified.  K a positive multiple of 128, b0 a
+ * multiple of 128 below K, N >= 0 (else W4_ERR_SHAPE); W and q_canon 16-byte
+ * aligned, U, d_canon and err 4-byte aligned (else W4_ERR_ALIGN); outputs must
+ * not overlap each other or the inputs (W4_ERR_ARG).  Non-finite weights or U
+ * give unspecified codes. */
+w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                        float* d_canon, float* err, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,29 @@ def test_algorithmic_bytes():
     assert round(workloads.stack_bytes("stack_27b", 1) / 1e9, 3) == 11.600
     assert round(workloads.stack_bytes("stack_70b", 1) / 1e9, 3) == 36.391
     assert workloads.stack_weights("stack_70b") == 80 * (2 * 8192 * 8192 + 2 * 1024 * 8192 + 3 * 28672 * 8192)
+
+
+def test_gptq_validation(w4):
+    lib = w4.library()
+    W, U, qc, dc, err = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000
+
+    def block(W=W, N=64, K=256, b0=0, U=U, qc=qc, dc=dc, err=err):
+        return lib.w4_gptq_block(W, N, K, b0, U, qc, dc, err, None)
+
+    assert block(N=0) == OK  # empty: nothing launched
+    for bad in (dict(K=200), dict(K=0), dict(N=-1), dict(b0=64), dict(b0=256), dict(b0=-128)):
+        assert block(**bad) == ERR_SHAPE, bad
+    for none in ("W", "U", "qc", "dc", "err"):
+        assert block(**{none: None}) == ERR_NULL, none
+    assert block(W=W + 4) == ERR_ALIGN
+    assert block(qc=qc + 8) == ERR_ALIGN
+    assert block(U=U + 2) == ERR_ALIGN
+    assert block(err=W + 64) == ERR_ARG  # output inside the weights
+    assert block(dc=qc + 16) == ERR_ARG  # two outputs overlap
+    assert block(qc=U + 1024) == ERR_ARG  # output inside U
+
+    assert lib.w4_gptq_damp(FAKE, 0, 0.01, None) == ERR_SHAPE
+    assert lib.w4_gptq_damp(None, 16, 0.01, None) == ERR_NULL
+    assert lib.w4_gptq_damp(FAKE + 4, 16, 0.01, None) == ERR_ALIGN
+    for bad in (-0.5, float("nan"), float("inf")):
+        assert lib.w4_gptq_damp(FAKE, 16, bad, None) == ERR_ARG, bad

@@ -620,3 +620,87 @@ def test_awq_search_near_oracle_optimum(w4, gpu, seed, salient):
     assert np.allclose(g, err_ref, rtol=0.05), "per-candidate errors"
     if salient:
         assert res["k"] > 0 and g[res["k"]] < 0.9 * g[0], "channel scaling should help here"
+
+
+# ----------------------------------------------------------------------------
+# GPTQ (the library runs it in fp32; the oracle in fp64)
+# ----------------------------------------------------------------------------
+
+def _gptq(w4, W_np, xb_np, gpu):
+    from bit_group_quantized_w4_amd import gptq
+    W = torch.from_numpy(W_np).to(gpu)
+    x = torch.from_numpy(xb_np.view(np.int16)).to(gpu).view(torch.bfloat16)
+    q, d = gptq.quantize(W, x)
+    qc, dc = w4.unpack(q, d, *W_np.shape)
+    torch.cuda.synchronize()
+    return qc.cpu().numpy(), dc.cpu().numpy()
+
+
+@pytest.mark.parametrize("inputs", ["identity", "zero"])
+def test_gptq_without_coupling_is_rtn(w4, gpu, inputs):
+    """Calibration inputs whose Hessian couples no columns (a multiple of the identity, or all
+    zero): nothing propagates, so codes and scales equal RTN's bit for bit."""
+    _say(f"gptq {inputs} inputs")
+    K = 256
+    W = pins.toy_weights(4, N=70, K=K)  # 70 rows: a partial wavefront
+    if inputs == "identity":
+        xb = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    else:
+        xb = np.zeros((8, K), dtype=np.uint16)
+    qc, dc = _gptq(w4, W, xb, gpu)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W)
+    assert np.array_equal(dc.view(np.uint32), d_ref.view(np.uint32)), "scales differ from RTN"
+    assert np.array_equal(qc, q_ref), "codes differ from RTN"
+
+
+def _gptq_compare(W, xb, qc, dc, q_ref, d_ref, what, rows=None):
+    Wr = W if rows is None else W[rows]
+    frac = float(np.mean(qc == q_ref))
+    assert frac >= 0.99, f"{what}: only {frac:.4f} of the codes equal the fp64 oracle's"
+    # a code decided the other way near a tie changes the later, error-fed weights of its
+    # row, and with them that row's later group maxima: most scales agree to rounding,
+    # a few move by a few percent
+    rel = np.abs(dc.astype(np.float64) / d_ref.astype(np.float64) - 1.0)
+    assert np.mean(rel <= 1e-5) >= 0.95 and rel.max() <= 0.25, f"{what}: scales drift (max {rel.max():.2e})"
+    e_gpu = oracle.output_error_ref(Wr, qc, dc, xb)
+    e_ref = oracle.output_error_ref(Wr, q_ref, d_ref, xb)
+    q_rtn, d_rtn = oracle.rtn_quantize_ref(Wr)
+    e_rtn = oracle.output_error_ref(Wr, q_rtn, d_rtn, xb)
+    assert abs(e_gpu / e_ref - 1.0) <= 0.02, f"{what}: output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
+    assert e_gpu < 0.9 * e_rtn, f"{what}: GPTQ {e_gpu:.4e} should beat RTN {e_rtn:.4e}"
+    return frac, e_gpu / e_rtn
+
+
+def test_gptq_matches_oracle(w4, gpu):
+    """Correlated calibration inputs, ragged rows, eight blocks: the fp32 library against the
+    fp64 oracle -- codes equal but for near-tie decisions, scales equal or within rounding,
+    the same output error, well below RTN's."""
+    _say("gptq 300x1024, T=256, correlated inputs")
+    W, xb = pins.gptq_correlated_inputs(seed=11, N=300, K=1024, T=256)
+    qc, dc = _gptq(w4, W, xb, gpu)
+    q_ref, d_ref = oracle.gptq_ref(W, xb)
+    _gptq_compare(W, xb, qc, dc, q_ref, d_ref, "300x1024")
+
+
+def test_gptq_full_size_70b_gate_sampled(w4, gpu):
+    """The 70B-class gate matrix (28672 x 8192) with 256 calibration rows of the 70B recipe
+    (outlier channels).  Rows are independent given the factor, so the oracle quantizes a
+    sample of rows with its own fp64 factor."""
+    from bit_group_quantized_w4_amd import gptq
+    _say("gptq 70b gate full size")
+    m = next(mm for mm in workloads.WORKLOADS["stack_70b"].matrices if mm.name == "gate")
+    W = workloads.weight("stack_70b", 2, "gate", gpu)
+    x = workloads.activations("stack_70b", 2, "gate", 256, gpu)
+    q, d = gptq.quantize(W, x)
+    qc, dc = w4.unpack(q, d, m.N, m.K)
+    rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(4).choice(m.N, 30)]))
+    idx = torch.as_tensor(rows, device=gpu)
+    qc = qc.index_select(0, idx).cpu().numpy()
+    dc = dc.index_select(0, idx).cpu().numpy()
+    W_rows = W.index_select(0, idx).cpu().numpy()
+    xb = _bits(x)
+    del q, d, W
+    torch.cuda.empty_cache()
+    U = oracle.gptq_factor_ref(oracle.gptq_hessian_ref(xb))
+    q_ref, d_ref = oracle.gptq_quantize_ref(W_rows, U)
+    _gptq_compare(W_rows, xb, qc, dc, q_ref, d_ref, "70b gate sampled")
