@@ -704,3 +704,16 @@ def test_gptq_full_size_70b_gate_sampled(w4, gpu):
     U = oracle.gptq_factor_ref(oracle.gptq_hessian_ref(xb))
     q_ref, d_ref = oracle.gptq_quantize_ref(W_rows, U)
     _gptq_compare(W_rows, xb, qc, dc, q_ref, d_ref, "70b gate sampled")
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (65, 128), (3, 384)])
+def test_gptq_small_shapes(w4, gpu, N, K):
+    """One row, one block (no correction product after it), a row past a full wavefront."""
+    _say(f"gptq small {N}x{K}")
+    W, xb = pins.gptq_correlated_inputs(seed=N + K, N=N, K=K, T=96)
+    qc, dc = _gptq(w4, W, xb, gpu)
+    q_ref, d_ref = oracle.gptq_ref(W, xb)
+    assert np.mean(qc == q_ref) >= 0.98
+    e_gpu = oracle.output_error_ref(W, qc, dc, xb)
+    e_ref = oracle.output_error_ref(W, q_ref, d_ref, xb)
+    assert abs(e_gpu / e_ref - 1.0) <= 0.03, f"output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
