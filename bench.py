@@ -621,7 +621,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -44,9 +44,17 @@ def quantize(W, x_cal, damp=DAMP, timings=None):
     With a dict `timings`, the milliseconds of each phase (GPU events on the
     current stream) are stored in it: "hessian", "factor", "columns" (the block
     loops with their corrections) and "pack"."""
+    if W.dim() != 2 or W.dtype != torch.float32 or not W.is_cuda:
+        raise TypeError("W must be a 2-D float32 tensor on the GPU")
+    if x_cal.dim() != 2 or x_cal.dtype != torch.bfloat16 or x_cal.device != W.device:
+        raise TypeError("x_cal must be a 2-D bfloat16 tensor on W's device")
     N, K = W.shape
-    if K % BLOCK:
-        raise ValueError("K must be a multiple of 128")
+    if K == 0 or K % BLOCK:
+        raise ValueError("K must be a positive multiple of 128")
+    if x_cal.shape[1] != K or x_cal.shape[0] < 1:
+        raise ValueError("x_cal must have at least one row of K inputs")
+    if not (damp >= 0.0 and damp < float("inf")):
+        raise ValueError("damp must be finite and >= 0")
     marks = []
 
     def mark():

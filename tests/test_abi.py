@@ -210,3 +210,12 @@ def test_gptq_validation(w4):
     assert lib.w4_gptq_damp(FAKE + 4, 16, 0.01, None) == ERR_ALIGN
     for bad in (-0.5, float("nan"), float("inf")):
         assert lib.w4_gptq_damp(FAKE, 16, bad, None) == ERR_ARG, bad
+
+
+def test_gptq_driver_rejects_bad_inputs(w4):
+    import torch
+    from bit_group_quantized_w4_amd import gptq
+    W = torch.zeros((16, 256))
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        gptq.quantize(W, x)  # CPU tensors

@@ -1,0 +1,80 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, graph step
+grouping, the source hash that keys stored counters, and the copy-kernel
+calibration of the HBM byte counters."""
+
+import csv
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_graph_steps_divides_the_timed_steps(bench):
+    for steps in range(1, 130):
+        r = bench.graph_steps(steps)
+        assert r in (1, 2, 4, 8) and steps % r == 0
+        assert all(steps % c for c in (1, 2, 4, 8) if c > r)
+
+
+def test_source_hash_ignores_comments_only(bench, tmp_path, monkeypatch):
+    code = "__global__ void k(int* p) {\n  p[0] = 1;  // store\n}\n"
+    f = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ["k.hip"])
+    f.write_text(code)
+    h0 = bench.kernel_source_hash()
+    f.write_text("/* a new\n   block comment */\n" + code.replace("// store", "// a different comment"))
+    assert bench.kernel_source_hash() == h0
+    f.write_text(code.replace("p[0] = 1", "p[0] = 2"))
+    assert bench.kernel_source_hash() != h0
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, grid, value in rows:
+            w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counters_are_scaled_by_the_copy_kernel(bench, tmp_path, monkeypatch):
+    mb = 256
+    copy_bytes = mb << 20
+    fetch_factor, read, written = 0.5, 803_000_000, 753_664
+    head = f"void {bench.HEADLINE_KERNEL}(w4::BatchArgs)"
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [
+        ("copy_kernel(x)", 524288, fetch_factor * copy_bytes / 1024),
+        (head, bench.HEADLINE_GRID, fetch_factor * read / 1024),
+        (head, bench.HEADLINE_GRID, fetch_factor * read / 1024),
+        ("other_kernel", 1024, 123.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [
+        ("copy_kernel(x)", 524288, copy_bytes / 1024),
+        (head, bench.HEADLINE_GRID, written / 1024)])
+    out = tmp_path / "counters.json"
+    bench.write_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), mb, str(out))
+    res = json.load(open(out))
+    assert res["counters"]["FETCH_SIZE"]["bytes_per_dispatch"] == read
+    assert res["counters"]["WRITE_SIZE"]["bytes_per_dispatch"] == written
+    assert res["hbm_bytes_per_launch"] == read + written
+    assert res["kernel"] == bench.HEADLINE_KERNEL
