@@ -788,6 +788,9 @@ int choose_cfg_gemv(const BatchArgs& a) {
   if (l.kmax >= 16384 && l.rows >= 400) return find_cfg(1, 8);
   if (l.kmin <= 4096 && l.rows >= 8192) return find_cfg(2, 2);
   if (l.kmax <= 4096 && l.rows >= 1000) return find_cfg(1, 2);
+  // few row blocks but long rows: two row blocks per wavefront halve the x
+  // staging per weight byte and still leave enough wavefronts
+  if (l.rows < 400 && l.kmin >= 6144) return find_cfg(2, 4);
   return find_cfg(1, 4);
 }
 
