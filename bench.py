@@ -296,7 +296,8 @@ def bench_awq(torch, w4, workloads, steps, warmup, T=256):
     x_cal = workloads.activations(name, 0, mat, T, dev)
     chans = workloads.outlier_channels(name, 0, workloads.WORKLOADS[name].input_groups.get(mat, mat), K)
     mult = workloads.WORKLOADS[name].weight[4]
-    out = {"matrix": f"{N}x{K}", "calibration_rows": T}
+    x_eval = workloads.activations(name, 0, mat, 1024, dev)  # held-out rows: an independent draw
+    out = {"matrix": f"{N}x{K}", "calibration_rows": T, "held_out_rows": x_eval.shape[0]}
     for tag, Wv in (("recipe", W), ("ordinary_weights_on_salient_channels", None)):
         if Wv is None:
             Wv = W.clone()
@@ -308,10 +309,17 @@ def bench_awq(torch, w4, workloads, steps, warmup, T=256):
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         e = res["errors"]
+        # the chosen scaling against plain RTN on rows the search never saw
+        y_ref = torch.matmul(x_eval.float(), Wv.t())
+        q0, d0 = w4.quantize_rtn(Wv)
+        e_awq = float(w4.sq_error(w4.linear(w4.scale_activations(x_eval, res["inv_s"]), res["q"], res["d"], N),
+                                  y_ref).item())
+        e_rtn = float(w4.sq_error(w4.linear(x_eval, q0, d0, N), y_ref).item())
+        del y_ref, q0, d0
         out[tag] = {"k": res["k"], "alpha": round(res["alpha"], 4), "error_vs_rtn": round(e[res["k"]] / e[0], 4),
-                    "search_ms": round(dt * 1e3, 1)}
-        log(f"[bench] awq {tag}: alpha={res['alpha']:.3f}, output error {e[res['k']] / e[0]:.3f} x RTN, "
-            f"search {dt * 1e3:.0f} ms")
+                    "held_out_error_vs_rtn": round(e_awq / e_rtn, 4), "search_ms": round(dt * 1e3, 1)}
+        log(f"[bench] awq {tag}: alpha={res['alpha']:.3f}, output error {e[res['k']] / e[0]:.3f} x RTN "
+            f"(held-out rows {e_awq / e_rtn:.3f}), search {dt * 1e3:.0f} ms")
     # decode: fused x/s staging against the plain linear, same matrix, rotated copies
     res = awq.search(W, x_cal)
     copies = 8
