@@ -655,18 +655,19 @@ def test_gptq_without_coupling_is_rtn(w4, gpu, inputs):
 
 def _gptq_compare(W, xb, qc, dc, q_ref, d_ref, what, rows=None):
     Wr = W if rows is None else W[rows]
+    # The library's column loop and corrections run in fp32 (the factor in fp64), the
+    # oracle's in fp64: a code decided the other way next to a tie is possible, and it
+    # changes the later, error-fed weights of its row and with them that row's later
+    # group maxima.  In measured runs every code was equal and scales agreed within 3e-5.
     frac = float(np.mean(qc == q_ref))
-    assert frac >= 0.99, f"{what}: only {frac:.4f} of the codes equal the fp64 oracle's"
-    # a code decided the other way near a tie changes the later, error-fed weights of its
-    # row, and with them that row's later group maxima: most scales agree to rounding,
-    # a few move by a few percent
+    assert frac >= 0.999, f"{what}: only {frac:.5f} of the codes equal the fp64 oracle's"
     rel = np.abs(dc.astype(np.float64) / d_ref.astype(np.float64) - 1.0)
-    assert np.mean(rel <= 1e-5) >= 0.95 and rel.max() <= 0.25, f"{what}: scales drift (max {rel.max():.2e})"
+    assert np.mean(rel <= 1e-5) >= 0.99 and rel.max() <= 0.05, f"{what}: scales drift (max {rel.max():.2e})"
     e_gpu = oracle.output_error_ref(Wr, qc, dc, xb)
     e_ref = oracle.output_error_ref(Wr, q_ref, d_ref, xb)
     q_rtn, d_rtn = oracle.rtn_quantize_ref(Wr)
     e_rtn = oracle.output_error_ref(Wr, q_rtn, d_rtn, xb)
-    assert abs(e_gpu / e_ref - 1.0) <= 0.02, f"{what}: output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
+    assert abs(e_gpu / e_ref - 1.0) <= 0.005, f"{what}: output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
     assert e_gpu < 0.9 * e_rtn, f"{what}: GPTQ {e_gpu:.4e} should beat RTN {e_rtn:.4e}"
     return frac, e_gpu / e_rtn
 
@@ -713,7 +714,7 @@ def test_gptq_small_shapes(w4, gpu, N, K):
     W, xb = pins.gptq_correlated_inputs(seed=N + K, N=N, K=K, T=96)
     qc, dc = _gptq(w4, W, xb, gpu)
     q_ref, d_ref = oracle.gptq_ref(W, xb)
-    assert np.mean(qc == q_ref) >= 0.98
+    assert np.mean(qc == q_ref) >= 0.99
     e_gpu = oracle.output_error_ref(W, qc, dc, xb)
     e_ref = oracle.output_error_ref(W, q_ref, d_ref, xb)
-    assert abs(e_gpu / e_ref - 1.0) <= 0.03, f"output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
+    assert abs(e_gpu / e_ref - 1.0) <= 0.005, f"output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
