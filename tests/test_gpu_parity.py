@@ -718,3 +718,44 @@ def test_gptq_small_shapes(w4, gpu, N, K):
     e_gpu = oracle.output_error_ref(W, qc, dc, xb)
     e_ref = oracle.output_error_ref(W, q_ref, d_ref, xb)
     assert abs(e_gpu / e_ref - 1.0) <= 0.005, f"output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
+
+
+def _random_cases(n_cases=36, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        N = int(rng.integers(1, 3000))
+        K = 128 * int(rng.integers(1, 40))
+        M = int(rng.choice([1, 1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 33, 40]))
+        path = ["auto", "mfma", "gemv"][i % 3]
+        sd = ["f32", "bf16"][(i // 3) % 2]
+        cases.append((N, K, M, path, sd))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,M,path,scale_dtype", _random_cases())
+def test_linear_random_shapes(w4, gpu, N, K, M, path, scale_dtype):
+    """Seeded random shapes (ragged rows, any group count, 1-40 rows of x), every path and
+    both scale formats, single and batched with a second linear of another K."""
+    _say(f"random N={N} K={K} M={M} path={path} scales={scale_dtype}")
+    sd = torch.bfloat16 if scale_dtype == "bf16" else torch.float32
+    W = torch.from_numpy(workloads.random_weight(N, K, seed=N * 131 + K)).to(gpu)
+    q, d = w4.quantize_rtn(W, scale_dtype=sd)
+    x = workloads.random_activations(M, K, seed=M * 7 + K, device=gpu)
+    y = w4.linear(x, q, d, N, path=path)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W.cpu().numpy(), scale_dtype)
+    y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+    check_y(y, y_ref, absdot, f"random {N}x{K} M={M} {path} {scale_dtype}")
+    # the same linear batched with another of a different K: identical bits
+    K2 = 128 * (1 + (K // 128) % 7)
+    W2 = torch.from_numpy(workloads.random_weight(37, K2, seed=K2)).to(gpu)
+    q2, d2 = w4.quantize_rtn(W2, scale_dtype=sd)
+    x2 = workloads.random_activations(M, K2, seed=M + K2, device=gpu)
+    # (the batch may run another configuration than the single call, so both are held to
+    # the oracle rather than to each other)
+    ys = w4.linear_batched([(x, q, d, N, torch.empty((M, N), dtype=torch.bfloat16, device=gpu)),
+                            (x2, q2, d2, 37, torch.empty((M, 37), dtype=torch.bfloat16, device=gpu))], path=path)
+    check_y(ys[0], y_ref, absdot, "random batched")
+    q2r, d2r = oracle.rtn_quantize_ref(W2.cpu().numpy(), scale_dtype)
+    y2_ref, absdot2 = oracle.w4_linear_ref(_bits(x2), q2r, d2r)
+    check_y(ys[1], y2_ref, absdot2, "random batched second")
