@@ -36,12 +36,15 @@ Readings where the pages and the paper leave a step open (also in the design doc):
   gets codes 0;
 * a column whose calibration inputs are all zero (diag H = 0) gets
   H_jj = 1 before damping, so the factorization exists; its weights are kept;
-* weights and calibration inputs must be finite.
+* weights and calibration inputs must be finite;
+* with 16-bit scales (the optional storage of RTN, same rule): the group's
+  scale is stored as the nearest bf16 of the fp32 scale, and the codes and
+  the corrections use that stored value, widened back to fp32.
 """
 
 import numpy as np
 
-from .bf16 import bf16_bits_to_f64
+from .bf16 import bf16_bits_to_f64, f32_to_bf16_bits
 from .rtn import GROUP, QMAX, QMIN
 
 DAMP = 0.01
@@ -89,14 +92,17 @@ def code_ref(w, d):
     return np.where(usable, q, 0.0)
 
 
-def gptq_quantize_ref(W, U, block=GROUP):
+def gptq_quantize_ref(W, U, block=GROUP, scale_dtype="f32"):
     """Codes and scales for W [N, K] (fp32, finite) given the inverse factor U [K, K].
 
-    Returns (q int8 [N, K], d float32 [N, K/128]): the same arrays RTN returns.
-    `block` is the lazy-update width; the group scale is always taken every 128
-    columns (a block width that is a multiple of 128 changes only the rounding
-    order of the corrections).
+    Returns (q int8 [N, K], d [N, K/128]): the same arrays RTN returns -- float32
+    scales, or uint16 bf16 bit patterns for scale_dtype "bf16".  `block` is the
+    lazy-update width; the group scale is always taken every 128 columns (a
+    block width that is a multiple of 128 changes only the rounding order of the
+    corrections).
     """
+    if scale_dtype not in ("f32", "bf16"):
+        raise ValueError("scale_dtype must be 'f32' or 'bf16'")
     W = np.asarray(W)
     if W.dtype != np.float32 or W.ndim != 2:
         raise TypeError("W must be a 2-D float32 array")
@@ -108,13 +114,16 @@ def gptq_quantize_ref(W, U, block=GROUP):
     U = np.asarray(U, dtype=np.float64)
     Wk = W.astype(np.float64)
     q = np.zeros((N, K), dtype=np.int8)
-    d = np.zeros((N, K // GROUP), dtype=np.float32)
+    d = np.zeros((N, K // GROUP), dtype=np.float32)  # the scales the codes use
     for b0 in range(0, K, block):
         b1 = min(b0 + block, K)
         E = np.zeros((N, b1 - b0))
         for j in range(b0, b1):
             if j % GROUP == 0:
-                d[:, j // GROUP] = group_scale_ref(Wk[:, j:j + GROUP])
+                dj = group_scale_ref(Wk[:, j:j + GROUP])
+                if scale_dtype == "bf16":  # stored as bf16; used widened back to fp32
+                    dj = (f32_to_bf16_bits(dj).astype(np.uint32) << np.uint32(16)).view(np.float32)
+                d[:, j // GROUP] = dj
             dg = d[:, j // GROUP]
             qj = code_ref(Wk[:, j], dg)
             q[:, j] = qj.astype(np.int8)
@@ -122,17 +131,22 @@ def gptq_quantize_ref(W, U, block=GROUP):
             Wk[:, j + 1:b1] -= np.outer(err, U[j, j + 1:b1])
             E[:, j - b0] = err
         Wk[:, b1:] -= E @ U[b0:b1, b1:]
+    if scale_dtype == "bf16":
+        return q, (d.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     return q, d
 
 
-def gptq_ref(W, x_bits, damp=DAMP):
+def gptq_ref(W, x_bits, damp=DAMP, scale_dtype="f32"):
     """The whole procedure: Hessian from calibration rows, factor, column loop."""
-    return gptq_quantize_ref(W, gptq_factor_ref(gptq_hessian_ref(x_bits), damp))
+    return gptq_quantize_ref(W, gptq_factor_ref(gptq_hessian_ref(x_bits), damp), scale_dtype=scale_dtype)
 
 
 def output_error_ref(W, q, d, x_bits):
     """Mean squared output error of (q, d) against W on the rows x: mean((x W_hat^T - x W^T)^2), fp64."""
     X = bf16_bits_to_f64(x_bits)
     G = W.shape[1] // GROUP
+    d = np.asarray(d)
+    if d.dtype == np.uint16:  # bf16 scales
+        d = bf16_bits_to_f64(d)
     What = (np.asarray(d, dtype=np.float64)[:, :, None] * q.reshape(q.shape[0], G, GROUP)).reshape(q.shape)
     return float(np.mean((X @ (What - np.asarray(W, dtype=np.float64)).T) ** 2))

@@ -521,7 +521,7 @@ def gptq_damped_hessian(x_bits, damp=0.01):
     return H
 
 
-def gptq_bruteforce(W, x_bits, damp=0.01):
+def gptq_bruteforce(W, x_bits, damp=0.01, scale16=False):
     H = gptq_damped_hessian(x_bits, damp)
     N, K = W.shape
     q = np.zeros((N, K), dtype=np.int8)
@@ -533,7 +533,10 @@ def gptq_bruteforce(W, x_bits, damp=0.01):
         for j in range(K):
             if j % 128 == 0:
                 a = max(abs(Fraction(float(np.float32(v)))) for v in w[j:j + 128])
-                d[n, j // 128] = f32_nearest(a / 7)
+                d32 = f32_nearest(a / 7)
+                if scale16:  # stored as the nearest bf16, used widened
+                    d32 = bits_f32(bf16_nearest_bits(d32) << 16)
+                d[n, j // 128] = d32
             dv = d[n, j // 128]
             if dv == 0:
                 qj = 0
@@ -548,11 +551,14 @@ def gptq_bruteforce(W, x_bits, damp=0.01):
     return q, d
 
 
-def check_gptq_bruteforce(gptq):
-    """Codes and scales equal the sequential re-solve with exact-rational decisions."""
+def check_gptq_bruteforce(gptq, scale16=False):
+    """Codes and scales equal the sequential re-solve with exact-rational decisions
+    (with 16-bit scales: the scales the codes use, i.e. the stored bf16 widened)."""
     W, xb = gptq_correlated_inputs(seed=3)
     q, d = gptq(W, xb)
-    qb, db = gptq_bruteforce(W, xb)
+    if scale16:
+        d = (np.asarray(d, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    qb, db = gptq_bruteforce(W, xb, scale16=scale16)
     _check(np.array_equal(d.view(np.uint32), db.view(np.uint32)), "GPTQ scales differ from the brute-force re-solve")
     bad = np.argwhere(q != qb)
     _check(bad.size == 0, f"GPTQ codes differ from the brute-force re-solve at {bad[:4].tolist()}")
@@ -606,3 +612,14 @@ def check_gptq_all_inputs_zero_is_rtn(gptq):
     quantize = lambda Wm: gptq(Wm, xb)
     check_scale_exact(quantize, W)
     check_codes_bruteforce(quantize, W)
+
+
+def check_gptq16_identity_hessian_is_rtn16(gptq16):
+    """With 16-bit scales and an identity Hessian GPTQ is RTN with 16-bit scales: the
+    16-bit-scale pins hold for it."""
+    K = 256
+    xb = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    W = toy_weights(5, N=4, K=K)
+    quantize16 = lambda Wm: gptq16(Wm, xb)
+    check_scale16_exact(quantize16, W)
+    check_codes_bruteforce(widened(quantize16), W)

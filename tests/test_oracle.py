@@ -462,6 +462,27 @@ def test_gptq_dead_columns():
     pins.check_gptq_dead_columns(oracle.gptq_factor_ref, oracle.gptq_hessian_ref)
 
 
+def test_gptq_16bit_scales():
+    g16 = lambda W, xb: oracle.gptq_ref(W, xb, scale_dtype="bf16")
+    pins.check_gptq_bruteforce(g16, scale16=True)
+    pins.check_gptq16_identity_hessian_is_rtn16(g16)
+
+
+@pytest.mark.parametrize("kind", ["fp32_scale_used", "fp32_scale_stored"])
+def test_gptq_16bit_scale_mutants_are_caught(kind):
+    """Codes taken against the fp32 scale while the bf16 one is stored, or the fp32 scale
+    stored truncated: the 16-bit pins catch both."""
+    def g16(W, xb):
+        U = oracle.gptq_factor_ref(oracle.gptq_hessian_ref(xb))
+        q, d32 = oracle.gptq_quantize_ref(W, U)  # decisions against the fp32 scale
+        if kind == "fp32_scale_used":
+            return q, oracle.f32_to_bf16_bits(d32)
+        return q, (d32.view(np.uint32) >> 16).astype(np.uint16)  # truncation instead of nearest
+    with pytest.raises(pins.PinFailure):
+        pins.check_gptq_bruteforce(g16, scale16=True)
+        pins.check_gptq16_identity_hessian_is_rtn16(g16)
+
+
 def test_gptq_all_inputs_zero_is_rtn():
     pins.check_gptq_all_inputs_zero_is_rtn(oracle.gptq_ref)
 
