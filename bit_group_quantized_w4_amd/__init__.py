@@ -61,6 +61,7 @@ SIGNATURES = {
     # GPTQ steps
     "w4_gptq_damp": (_INT, [_VP, _I64, ctypes.c_double, _VP]),
     "w4_gptq_block": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "w4_gptq_block_s16": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
 }
 
 
@@ -298,14 +299,16 @@ def gptq_damp(H, damp=0.01):
 
 def gptq_block(W, U, b0, q_canon, d_canon, err):
     """GPTQ column loop over columns b0 .. b0+127 of W (fp32 [N, K], not modified): codes into
-    q_canon (int8 [N, K]), the group scale into d_canon (fp32 [N, K/128]), the column errors into
-    err (fp32 [128, N])."""
+    q_canon (int8 [N, K]), the group scale into d_canon ([N, K/128], fp32, or bfloat16 for
+    16-bit scales), the column errors into err (fp32 [128, N])."""
     N, K = W.shape
     if U.shape != (K, K) or q_canon.shape != (N, K) or d_canon.shape != (N, K // 128) or err.shape != (128, N):
         raise ValueError("shape mismatch")
-    _check(_lib.w4_gptq_block(_dev(W, torch.float32, "W"), N, K, int(b0), _dev(U, torch.float32, "U"),
-                              _dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, torch.float32, "d_canon"),
-                              _dev(err, torch.float32, "err"), _stream(W)), "w4_gptq_block")
+    sd = _scale_dtype(d_canon)
+    fn = _lib.w4_gptq_block_s16 if sd == torch.bfloat16 else _lib.w4_gptq_block
+    _check(fn(_dev(W, torch.float32, "W"), N, K, int(b0), _dev(U, torch.float32, "U"),
+              _dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, sd, "d_canon"),
+              _dev(err, torch.float32, "err"), _stream(W)), "w4_gptq_block")
 
 
 class W4Linear:

@@ -353,15 +353,17 @@ w4_status w4_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream) {
   return hip_status(w4::launch_gptq_damp(H, K, damp, stream));
 }
 
-w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
-                        float* d_canon, float* err, hipStream_t stream) {
+namespace {
+w4_status gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                     void* d_canon, bool s16, float* err, hipStream_t stream) {
   if (!n_ok(N) || !k_ok(K) || N > ((int64_t)1 << 31) - 1 || b0 < 0 || b0 >= K || b0 % kGroup) return W4_ERR_SHAPE;
   if (N == 0) return W4_OK;
   if (!W || !U || !q_canon || !d_canon || !err) return W4_ERR_NULL;
-  if (!aligned(W, 16) || !aligned(U, 4) || !aligned(q_canon, 16) || !aligned(d_canon, 4) || !aligned(err, 4))
+  const size_t e = s16 ? 2 : 4;
+  if (!aligned(W, 16) || !aligned(U, 4) || !aligned(q_canon, 16) || !aligned(d_canon, e) || !aligned(err, 4))
     return W4_ERR_ALIGN;
   const size_t wb = 4 * (size_t)N * K, ub = 4 * (size_t)K * K, qb = (size_t)N * K,
-               db = 4 * (size_t)N * (K / kGroup), eb = 4 * (size_t)kGroup * N;
+               db = e * (size_t)N * (K / kGroup), eb = 4 * (size_t)kGroup * N;
   const void* outs[3] = {q_canon, d_canon, err};
   const size_t ob[3] = {qb, db, eb};
   for (int i = 0; i < 3; ++i) {
@@ -369,7 +371,18 @@ w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const 
     for (int j = i + 1; j < 3; ++j)
       if (overlaps(outs[i], ob[i], outs[j], ob[j])) return W4_ERR_ARG;
   }
-  return hip_status(w4::launch_gptq_block(W, N, K, b0, U, q_canon, d_canon, err, stream));
+  return hip_status(w4::launch_gptq_block(W, N, K, b0, U, q_canon, d_canon, s16, err, stream));
+}
+}  // namespace
+
+w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                        float* d_canon, float* err, hipStream_t stream) {
+  return gptq_block(W, N, K, b0, U, q_canon, d_canon, false, err, stream);
+}
+
+w4_status w4_gptq_block_s16(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                            uint16_t* d_canon, float* err, hipStream_t stream) {
+  return gptq_block(W, N, K, b0, U, q_canon, d_canon, true, err, stream);
 }
 
 }  // extern "C"

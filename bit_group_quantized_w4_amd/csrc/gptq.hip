@@ -29,11 +29,14 @@ namespace {
 
 constexpr int kGptqRowsPerBlock = 64;  // one wavefront, one row per lane
 
+// S: the stored scale, float (fp32) or uint16_t (bf16 bit pattern; the codes
+// and the corrections then use that stored value widened to fp32).
+template <typename S>
 __global__ __launch_bounds__(kGptqRowsPerBlock) void gptq_block_kernel(const float* __restrict__ W, int N,
                                                                         int K, int b0,
                                                                         const float* __restrict__ U,
                                                                         int8_t* __restrict__ qc,
-                                                                        float* __restrict__ dc,
+                                                                        S* __restrict__ dc,
                                                                         float* __restrict__ errT) {
   const int n = blockIdx.x * kGptqRowsPerBlock + threadIdx.x;
   const bool live = n < N;
@@ -53,7 +56,16 @@ __global__ __launch_bounds__(kGptqRowsPerBlock) void gptq_block_kernel(const flo
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < kGroup; ++k) amax = fmaxf(amax, fabsf(v[k]));
-  const float d = amax / kMaxCode;  // IEEE fp32 division
+  const float d32 = amax / kMaxCode;  // IEEE fp32 division
+  S stored;
+  float d;
+  if constexpr (sizeof(S) == 2) {
+    stored = f32_to_bf16_rne(d32);
+    d = __uint_as_float((uint32_t)stored << 16);
+  } else {
+    stored = d32;
+    d = d32;
+  }
   const bool usable = d != 0.0f;
   const float dd = usable ? d : 1.0f;
 
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(kGptqRowsPerBlock) void gptq_block_kernel(const flo
 #pragma unroll
   for (int i = 0; i < kGroup / 16; ++i)
     qo[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
-  dc[(int64_t)n * (K / kGroup) + b0 / kGroup] = d;
+  dc[(int64_t)n * (K / kGroup) + b0 / kGroup] = stored;
 }
 
 // Damping of the fp64 Hessian in place: a zero diagonal entry (a column
@@ -112,11 +124,15 @@ __global__ __launch_bounds__(kDampThreads) void gptq_damp_kernel(double* __restr
 }  // namespace
 
 hipError_t launch_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
-                             float* d_canon, float* errT, hipStream_t stream) {
+                             void* d_canon, bool s16, float* errT, hipStream_t stream) {
   const unsigned blocks = (unsigned)((N + kGptqRowsPerBlock - 1) / kGptqRowsPerBlock);
   if (blocks == 0) return hipSuccess;
-  gptq_block_kernel<<<blocks, kGptqRowsPerBlock, 0, stream>>>(W, (int)N, (int)K, (int)b0, U, q_canon, d_canon,
-                                                               errT);
+  if (s16)
+    gptq_block_kernel<uint16_t><<<blocks, kGptqRowsPerBlock, 0, stream>>>(
+        W, (int)N, (int)K, (int)b0, U, q_canon, static_cast<uint16_t*>(d_canon), errT);
+  else
+    gptq_block_kernel<float><<<blocks, kGptqRowsPerBlock, 0, stream>>>(W, (int)N, (int)K, (int)b0, U, q_canon,
+                                                                       static_cast<float*>(d_canon), errT);
   return hipGetLastError();
 }
 

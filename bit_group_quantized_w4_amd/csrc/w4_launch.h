@@ -67,7 +67,7 @@ hipError_t launch_sq_error(const uint16_t* y, const float* yref, int64_t n, doub
 // GPTQ steps (gptq.hip): the column loop over the 128-column block at b0, and
 // the damping of the Hessian.
 hipError_t launch_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
-                             float* d_canon, float* errT, hipStream_t stream);
+                             void* d_canon, bool s16, float* errT, hipStream_t stream);
 hipError_t launch_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream);
 
 }  // namespace w4

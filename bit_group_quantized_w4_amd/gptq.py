@@ -37,9 +37,10 @@ def inverse_factor(H):
     return torch.flip(torch.linalg.solve_triangular(L, eye, upper=False), [0, 1]).contiguous()
 
 
-def quantize(W, x_cal, damp=DAMP, timings=None):
+def quantize(W, x_cal, damp=DAMP, timings=None, scale_dtype=torch.float32):
     """GPTQ of W (fp32 [N, K], K a multiple of 128, finite) with calibration rows x_cal
-    (bf16 [T, K]).  Returns (q, d) in the native layout, as quantize_rtn does.
+    (bf16 [T, K]).  Returns (q, d) in the native layout, as quantize_rtn does; with
+    scale_dtype=torch.bfloat16 the scales are 16-bit (the codes use the stored values).
 
     With a dict `timings`, the milliseconds of each phase (GPU events on the
     current stream) are stored in it: "hessian", "factor", "columns" (the block
@@ -72,7 +73,9 @@ def quantize(W, x_cal, damp=DAMP, timings=None):
     mark()
     Wk = W.clone()
     q_canon = torch.empty((N, K), dtype=torch.int8, device=W.device)
-    d_canon = torch.empty((N, K // BLOCK), dtype=torch.float32, device=W.device)
+    if scale_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("scale_dtype must be torch.float32 or torch.bfloat16")
+    d_canon = torch.empty((N, K // BLOCK), dtype=scale_dtype, device=W.device)
     err = torch.empty((BLOCK, N), dtype=torch.float32, device=W.device)
     for b0 in range(0, K, BLOCK):
         gptq_block(Wk, U, b0, q_canon, d_canon, err)

@@ -329,6 +329,13 @@ w4_status w4_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream);
 w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
                         float* d_canon, float* err, hipStream_t stream);
 
+/* w4_gptq_block with 16-bit scales: the group scale is stored in d_canon
+ * (bf16 bit patterns [N][K/128], 2-byte aligned) as the nearest bf16 of the
+ * fp32 scale, and the codes and corrections use that stored value (the rule
+ * of w4_quantize_rtn_s16). */
+w4_status w4_gptq_block_s16(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
+                            uint16_t* d_canon, float* err, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

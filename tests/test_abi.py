@@ -205,6 +205,10 @@ def test_gptq_validation(w4):
     assert block(dc=qc + 16) == ERR_ARG  # two outputs overlap
     assert block(qc=U + 1024) == ERR_ARG  # output inside U
 
+    assert lib.w4_gptq_block_s16(W, 64, 256, 0, U, qc, dc + 1, err, None) == ERR_ALIGN
+    assert lib.w4_gptq_block_s16(W, 64, 256, 64, U, qc, dc, err, None) == ERR_SHAPE
+    assert lib.w4_gptq_block_s16(W, 64, 256, 0, U, qc, W + 2, err, None) == ERR_ARG
+
     assert lib.w4_gptq_damp(FAKE, 0, 0.01, None) == ERR_SHAPE
     assert lib.w4_gptq_damp(None, 16, 0.01, None) == ERR_NULL
     assert lib.w4_gptq_damp(FAKE + 4, 16, 0.01, None) == ERR_ALIGN

@@ -626,14 +626,14 @@ def test_awq_search_near_oracle_optimum(w4, gpu, seed, salient):
 # GPTQ (the library runs it in fp32; the oracle in fp64)
 # ----------------------------------------------------------------------------
 
-def _gptq(w4, W_np, xb_np, gpu):
+def _gptq(w4, W_np, xb_np, gpu, scale_dtype=torch.float32):
     from bit_group_quantized_w4_amd import gptq
     W = torch.from_numpy(W_np).to(gpu)
     x = torch.from_numpy(xb_np.view(np.int16)).to(gpu).view(torch.bfloat16)
-    q, d = gptq.quantize(W, x)
+    q, d = gptq.quantize(W, x, scale_dtype=scale_dtype)
     qc, dc = w4.unpack(q, d, *W_np.shape)
     torch.cuda.synchronize()
-    return qc.cpu().numpy(), dc.cpu().numpy()
+    return qc.cpu().numpy(), _scale_bits(dc) if scale_dtype == torch.bfloat16 else dc.cpu().numpy()
 
 
 @pytest.mark.parametrize("inputs", ["identity", "zero"])
@@ -759,3 +759,23 @@ def test_linear_random_shapes(w4, gpu, N, K, M, path, scale_dtype):
     q2r, d2r = oracle.rtn_quantize_ref(W2.cpu().numpy(), scale_dtype)
     y2_ref, absdot2 = oracle.w4_linear_ref(_bits(x2), q2r, d2r)
     check_y(ys[1], y2_ref, absdot2, "random batched second")
+
+
+def test_gptq_16bit_scales(w4, gpu):
+    """16-bit scales: with an identity Hessian, RTN's 16-bit codes and scales bit for bit;
+    with correlated inputs, the fp64 oracle's codes and bf16 scales."""
+    _say("gptq 16-bit scales")
+    K = 256
+    W = pins.toy_weights(5, N=70, K=K)
+    xI = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    qc, dc = _gptq(w4, W, xI, gpu, S16)
+    q_ref, d_ref = oracle.rtn_quantize_ref(W, "bf16")
+    assert np.array_equal(dc, d_ref) and np.array_equal(qc, q_ref), "identity Hessian must give RTN (16-bit)"
+    W, xb = pins.gptq_correlated_inputs(seed=13, N=200, K=768, T=192)
+    qc, dc = _gptq(w4, W, xb, gpu, S16)
+    q_ref, d_ref = oracle.gptq_ref(W, xb, scale_dtype="bf16")
+    assert np.mean(qc == q_ref) >= 0.999
+    assert np.mean(dc == d_ref) >= 0.99
+    e_gpu = oracle.output_error_ref(W, qc, dc, xb)
+    e_ref = oracle.output_error_ref(W, q_ref, d_ref, xb)
+    assert abs(e_gpu / e_ref - 1.0) <= 0.005, f"output error {e_gpu:.4e} vs oracle {e_ref:.4e}"
