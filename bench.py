@@ -346,6 +346,48 @@ def bench_awq(torch, w4, workloads, steps, warmup, T=256):
     return out
 
 
+# Path comparison: both linear kernels, one launch per linear, on a short-K and a
+# long-K matrix; eight weight copies rotated so every launch streams from HBM.
+PC_SHAPES = ((2560, 9216), (28672, 8192))
+PC_MS = (1, 2, 3, 4, 8, 16)
+PC_PATHS = ("gemv", "mfma")
+PC_STEPS = 64
+PC_COPIES = 8
+
+
+def path_compare(torch, w4, workloads):
+    """Both linear kernels on the same matrices at M = 1..4, 8 and 16: the evidence
+    behind the automatic path choice (dot2 at M = 1, MFMA from M = 2).  Logs one line
+    per (shape, M) and returns the rows; the timed dispatches are the last
+    PC_STEPS * PC_COPIES of each (shape, M, path) in a kernel trace."""
+    dev = torch.device("cuda:0")
+    rows = []
+    copies = PC_COPIES
+    for (N, K) in PC_SHAPES:
+        W = torch.from_numpy(workloads.random_weight(N, K, seed=N + K)).to(dev)
+        q0, d0 = w4.quantize_rtn(W)
+        del W
+        qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+        ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+        for M in PC_MS:
+            x = workloads.random_activations(M, K, seed=M, device=dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            res = {}
+            for path in PC_PATHS:
+                def step():
+                    for c in range(copies):
+                        w4.linear(x, qs[c], ds[c], N, path=path, out=y)
+                g = capture(torch, step)
+                t = time_graph(torch, g, PC_STEPS, 4) / (PC_STEPS * copies)
+                res[path] = round(workloads.algorithmic_bytes(M, N, K) / t / 1e9, 1)
+                del g
+            rows.append({"N": N, "K": K, "M": M, **res})
+            log(f"[bench] path compare {N}x{K} M={M}: dot2 {res['gemv']:.0f} GB/s, MFMA {res['mfma']:.0f} GB/s")
+        del qs, ds
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_gptq(torch, w4, workloads, T=16384, T_eval=1024):
     """GPTQ of the 70B-class gate matrix (28672x8192, layer 0) calibrated on T rows
     (T = 2K, so the Hessian is well determined): time per phase, and the output error
@@ -533,6 +575,49 @@ def summarize_trace(path, last=0):
               f"{statistics.median(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
 
 
+def summarize_path_compare(path):
+    """Per-case kernel durations of a `--path-compare` run from its kernel_trace.csv.
+    Dispatches are split into runs of one (kernel, grid); the runs of linear kernels
+    long enough to hold a timed case are matched, in order, with the cases
+    path_compare runs, and the last PC_STEPS * PC_COPIES dispatches of each are used."""
+    import csv
+    import statistics
+
+    import workloads
+
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(dur)
+        else:
+            runs.append((key, [dur]))
+    timed = PC_STEPS * PC_COPIES
+    runs = [(k, v) for k, v in runs if "linear_" in k[0] and len(v) >= timed]
+    cases = [(N, K, M, p) for (N, K) in PC_SHAPES for M in PC_MS for p in PC_PATHS]
+    if len(runs) != len(cases):
+        raise SystemExit(f"expected {len(cases)} timed runs of linear kernels, found {len(runs)}")
+    print("| N x K | M | path | kernel | blocks | timed dispatches | mean us | median us | GB/s (mean) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    best = {}
+    for (N, K, M, p), ((name, blocks), v) in zip(cases, runs):
+        t = v[-timed:]
+        mean = statistics.mean(t) / 1e3
+        gbs = workloads.algorithmic_bytes(M, N, K) / (mean * 1e-6) / 1e9
+        best.setdefault((N, K, M), {})[p] = gbs
+        name = name.replace("w4::(anonymous namespace)::", "")
+        print(f"| {N}x{K} | {M} | {'dot2' if p == 'gemv' else 'MFMA'} | {name[:60]} | {blocks} | {len(t)} | "
+              f"{mean:.2f} | {statistics.median(t) / 1e3:.2f} | {gbs:.0f} |")
+    print()
+    print("| N x K | M | dot2 GB/s | MFMA GB/s | faster |")
+    print("|---|---|---|---|---|")
+    for (N, K, M), r in best.items():
+        print(f"| {N}x{K} | {M} | {r['gemv']:.0f} | {r['mfma']:.0f} | "
+              f"{'dot2' if r['gemv'] > r['mfma'] else 'MFMA'} ({max(r.values()) / min(r.values()):.2f}x) |")
+
+
 def summarize_counters(path):
     """Mean of each counter per (kernel, grid) from a rocprofv3 counter_collection.csv."""
     import csv
@@ -602,6 +687,8 @@ def main():
     ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
     ap.add_argument("--no-s16", action="store_true", help="skip the 16-bit-scale measurements")
     ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQ quantizer measurement")
+    ap.add_argument("--path-compare", action="store_true",
+                    help="only time both linear kernels at M = 1..4, 8, 16 (profiling runs)")
     ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
     ap.add_argument("--stack-modes", default="",
                     help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
@@ -611,6 +698,8 @@ def main():
                     help="print a duration summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--trace-last", type=int, default=0,
                     help="with --trace-summary: mean of the last N headline dispatches (the timed steps)")
+    ap.add_argument("--path-compare-summary", metavar="KERNEL_TRACE_CSV",
+                    help="per-case kernel durations of a --path-compare run")
     ap.add_argument("--counter-summary", metavar="COUNTER_COLLECTION_CSV",
                     help="print a summary of a rocprofv3 counter collection and exit")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -620,6 +709,9 @@ def main():
     if args.write_counters:
         write_counters(args.write_counters[0], args.write_counters[1], args.calibrate_copy_mb or 256,
                        COUNTERS_FILE)
+        return
+    if args.path_compare_summary:
+        summarize_path_compare(args.path_compare_summary)
         return
     if args.trace_summary:
         summarize_trace(args.trace_summary, args.trace_last)
@@ -642,6 +734,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.init()
+
+    if args.path_compare:
+        print(json.dumps({"path_compare": path_compare(torch, w4, workloads)}), flush=True)
+        return
 
     pair, quant = bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies)
 

@@ -784,8 +784,14 @@ int choose_cfg_mfma(const BatchArgs& a) {
 int choose_cfg_gemv(const BatchArgs& a) {
   const LaunchShape l = launch_shape(a);
   if (l.rows < 256) return find_cfg(1, 8);
-  // long K: more wavefronts per row block, once there are enough row blocks
-  if (l.kmax >= 16384 && l.rows >= 400) return find_cfg(1, 8);
+  // long K: more wavefronts per row block, once there are enough row blocks --
+  // but only when every linear of the batch is long.  One configuration
+  // serves the whole batch, and an eight-way split leaves the wavefronts of a
+  // short-K linear (a whole decoder layer in one launch) a quad or two each.
+  if (l.kmax >= 16384 && l.rows >= 400) {
+    if (l.kmin >= 16384) return find_cfg(1, 8);
+    return l.kmin >= 8192 ? find_cfg(2, 4) : find_cfg(1, 4);
+  }
   if (l.kmin <= 4096 && l.rows >= 8192) return find_cfg(2, 2);
   if (l.kmax <= 4096 && l.rows >= 1000) return find_cfg(1, 2);
   // few row blocks but long rows: two row blocks per wavefront halve the x

@@ -78,3 +78,54 @@ def test_counters_are_scaled_by_the_copy_kernel(bench, tmp_path, monkeypatch):
     assert res["counters"]["WRITE_SIZE"]["bytes_per_dispatch"] == written
     assert res["hbm_bytes_per_launch"] == read + written
     assert res["kernel"] == bench.HEADLINE_KERNEL
+
+
+def test_path_compare_summary_matches_runs_to_cases(bench, tmp_path, capsys):
+    timed = bench.PC_STEPS * bench.PC_COPIES
+    cases = [(N, K, M, p) for (N, K) in bench.PC_SHAPES for M in bench.PC_MS for p in bench.PC_PATHS]
+    fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    t = 0
+    rows = []
+
+    def dispatch(name, grid, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Grid_Size_X": grid, "Workgroup_Size_X": 256,
+                     "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur + 10
+
+    for i, (N, K, M, p) in enumerate(cases):
+        if M == bench.PC_MS[0] and p == bench.PC_PATHS[0]:
+            for _ in range(3):
+                dispatch("quantize_kernel", 4096, 500)  # a short run of a non-linear kernel
+        name = f"linear_{p}_kernel<{i}>"
+        for _ in range(40):
+            dispatch(name, 256 * 100, 99_000)  # eager run and warmup: excluded
+        for _ in range(timed):
+            dispatch(name, 256 * 100, 1000 + i)  # the timed dispatches: 1 us + i ns
+    with open(tmp_path / "trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows[::-1])  # order must come from the timestamps
+    bench.summarize_path_compare(str(tmp_path / "trace.csv"))
+    out = capsys.readouterr().out
+    lines = [ln for ln in out.splitlines() if ln.startswith("| ") and "kernel<" in ln]
+    assert len(lines) == len(cases)
+    for i, ln in enumerate(lines):
+        cells = [c.strip() for c in ln.strip("|").split("|")]
+        N, K, M, p = cases[i]
+        assert cells[0] == f"{N}x{K}" and cells[1] == str(M)
+        assert cells[4] == "100" and cells[5] == str(timed)
+        assert float(cells[6]) == pytest.approx((1000 + i) / 1e3, abs=0.006)
+    # the comparison table names the faster path: MFMA runs always end 1 ns later here
+    assert out.count("| dot2 (") == len(bench.PC_SHAPES) * len(bench.PC_MS)
+
+
+def test_path_compare_summary_rejects_a_short_trace(bench, tmp_path):
+    with open(tmp_path / "trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp",
+                                           "End_Timestamp"])
+        w.writeheader()
+        w.writerow({"Kernel_Name": "linear_gemv_kernel<0>", "Grid_Size_X": 256, "Workgroup_Size_X": 256,
+                    "Start_Timestamp": 0, "End_Timestamp": 1000})
+    with pytest.raises(SystemExit):
+        bench.summarize_path_compare(str(tmp_path / "trace.csv"))

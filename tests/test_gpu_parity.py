@@ -421,27 +421,31 @@ def test_linear_unknown_config_is_an_error(w4, gpu, monkeypatch):
     w4.linear(x, q, d, 16)  # and the library still works
 
 
-def test_linear_batched_full_size_layer(w4, gpu):
-    """One 70B-class layer (seven full-size matrices) in one launch at M = 1 and 16."""
-    wl = workloads.WORKLOADS["stack_70b"]
+@pytest.mark.parametrize("workload,ms", [("stack_70b", (1, 16)), ("stack_27b", (1, 2))])
+def test_linear_batched_full_size_layer(w4, gpu, workload, ms):
+    """One decoder layer (seven full-size matrices, short and long K mixed) in one
+    launch: at M = 1 the dot2 kernel's mixed-K configurations (two row blocks per
+    wavefront when the shortest K is 8192, one otherwise), then the MFMA kernel."""
+    wl = workloads.WORKLOADS[workload]
+    tag = workload.split("_")[1]
     mats = []
     for m in wl.matrices:
-        W = workloads.weight("stack_70b", 3, m.name, gpu)
+        W = workloads.weight(workload, 3, m.name, gpu)
         q, d = w4.quantize_rtn(W)
         rows = np.unique(np.concatenate([[0, m.N - 1], np.random.default_rng(7).choice(m.N, 62)]))
         idx = torch.as_tensor(rows, device=gpu)
         mats.append((m, q, d, idx, oracle.rtn_quantize_ref(W.index_select(0, idx).cpu().numpy())))
         del W
-    for M in (1, 16):
-        _say(f"batched 70b layer M={M}")
+    for M in ms:
+        _say(f"batched {tag} layer M={M}")
         items = []
         for (m, q, d, idx, _) in mats:
-            x = workloads.activations("stack_70b", 3, m.name, M, gpu)
+            x = workloads.activations(workload, 3, m.name, M, gpu)
             items.append((x, q, d, m.N, torch.empty((M, m.N), dtype=torch.bfloat16, device=gpu)))
         ys = w4.linear_batched(items)
         for (m, q, d, idx, (q_ref, d_ref)), (x, *_), y in zip(mats, items, ys):
             y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
-            check_y(y.index_select(1, idx), y_ref, absdot, f"70b batched {m.name} M={M}")
+            check_y(y.index_select(1, idx), y_ref, absdot, f"{tag} batched {m.name} M={M}")
 
 
 # ----------------------------------------------------------------------------
