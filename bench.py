@@ -271,10 +271,48 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
             log(f"[bench] stack {name}{'' if sb == 4 else ' (16-bit scales)'} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
                 f"{1 / per:.1f} passes/s")
             del g
+        if M == 1 and sb == 4 and (not only_modes or "chained" in only_modes):
+            res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name)
         res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M, sb)
     del layers
     torch.cuda.empty_cache()
     return res
+
+
+def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name):
+    """One decode pass of the whole stack as one chained launch (w4_chain_run):
+    the shared-input groups of every layer become stages, and each stage reads
+    the output of the previous one (q|k|v <- previous down, o <- q, gate|up <- o,
+    down <- gate), so every stage waits for the whole previous stage, as in a
+    real decode step."""
+    dev = torch.device("cuda:0")
+    groups = _shared_input_groups(wl)
+    stages, prev = [], []  # prev: (N, y) of the previous stage's linears
+    for mats in layers:
+        # outputs of every layer in buffers of their own: a chain writes each line once
+        ys = {m.name: torch.empty((1, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+        for gi in groups:
+            K = mats[gi[0]][0].K
+            x = next((y for n, y in prev if n == K), xs[K])
+            stages.append([(x, mats[i][1], mats[i][2], mats[i][0].N, ys[mats[i][0].name]) for i in gi])
+            prev = [(mats[i][0].N, ys[mats[i][0].name]) for i in gi]
+    plan = w4.chain_prepare(stages)
+    g = capture(torch, plan.run)
+    t = time_graph(torch, g, steps, warmup)
+    err = plan.error()
+    per = t / steps
+    nbytes = workloads.stack_bytes(name, 1, 4)
+    gbs = nbytes / per / 1e9
+    flops = 2.0 * workloads.stack_weights(name)
+    out = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+           "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(1 / per, 1), "launches_per_pass": 1,
+           "stages_per_pass": len(stages), "useful_tflops": round(flops / per / 1e12, 2),
+           "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3),
+           "plan": plan.info, "wait_timeouts": err}
+    log(f"[bench] stack {name} M=1 chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
+        f"(plan {plan.info}, timeouts {err})")
+    del g, plan
+    return out
 
 
 # ----------------------------------------------------------------------------

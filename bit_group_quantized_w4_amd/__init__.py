@@ -31,6 +31,21 @@ class LinearDesc(ctypes.Structure):
                 ("N", _I64), ("y", _VP)]
 
 
+class ChainLinear(ctypes.Structure):
+    """ctypes mirror of w4_chain_linear."""
+
+    _fields_ = [("x", _VP), ("M", _I64), ("K", _I64), ("q_packed", _VP), ("d_packed", _VP),
+                ("N", _I64), ("y", _VP), ("stage", _I64)]
+
+
+class ChainPlanC(ctypes.Structure):
+    """ctypes mirror of w4_chain_plan."""
+
+    _I32 = ctypes.c_int32
+    _fields_ = [("workspace", _VP), ("linears", _I32), ("stages", _I32), ("items", _I32), ("blocks", _I32),
+                ("config", _I32), ("lds_bytes", _I32), ("rows_per_item", _I32), ("waves_per_block", _I32)]
+
+
 # (name, restype, argtypes) of every symbol include/w4.h declares
 SIGNATURES = {
     "w4_status_str": (ctypes.c_char_p, [_INT]),
@@ -58,6 +73,11 @@ SIGNATURES = {
     "w4_scale_activations": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_linear_awq": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP, _VP]),
     "w4_sq_error": (_INT, [_VP, _VP, _I64, _VP, _VP]),
+    # chained decode pass
+    "w4_chain_workspace_bytes": (_SZ, [_I64]),
+    "w4_chain_prepare": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
+    "w4_chain_run": (_INT, [ctypes.POINTER(ChainPlanC), _VP]),
+    "w4_chain_error": (_INT, [ctypes.POINTER(ChainPlanC), ctypes.POINTER(ctypes.c_uint32), _VP]),
     # GPTQ steps
     "w4_gptq_damp": (_INT, [_VP, _I64, ctypes.c_double, _VP]),
     "w4_gptq_block": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
@@ -200,6 +220,65 @@ def linear_batched(items, path="auto"):
                 else (_lib.w4_linear_batched, "w4_linear_batched"))
     _check(fn(descs, len(items), PATHS[path], stream), name)
     return [it[4] for it in items]
+
+
+class ChainPlan:
+    """A prepared chain (w4_chain_prepare): its device workspace, the plan, and
+    references to every tensor it names, which must stay alive while it is used."""
+
+    def __init__(self, workspace, plan, tensors):
+        self.workspace = workspace
+        self.plan = plan
+        self._tensors = tensors
+
+    def run(self):
+        """Enqueue one pass on the current stream (w4_chain_run)."""
+        _check(_lib.w4_chain_run(ctypes.byref(self.plan), _stream(self.workspace)), "w4_chain_run")
+
+    def error(self):
+        """The workspace's error flag (synchronises the current stream; w4_chain_error)."""
+        flag = ctypes.c_uint32(0)
+        _check(_lib.w4_chain_error(ctypes.byref(self.plan), ctypes.byref(flag), _stream(self.workspace)),
+               "w4_chain_error")
+        return int(flag.value)
+
+    @property
+    def info(self):
+        p = self.plan
+        return {"linears": p.linears, "stages": p.stages, "items": p.items, "blocks": p.blocks,
+                "rows_per_item": p.rows_per_item * 16, "waves_per_block": p.waves_per_block,
+                "lds_bytes": p.lds_bytes}
+
+
+def chain_prepare(stages):
+    """Prepare a chained decode pass (w4_chain_prepare).
+
+    stages: sequence of stages, each a sequence of (x [1, K] bf16, q, d fp32, N,
+    y [1, N] bf16).  Every linear of a stage writes y before any linear of the
+    next stage reads x.  Returns a ChainPlan; plan.run() enqueues one pass.
+    """
+    flat = [(s, it) for s, stage in enumerate(stages) for it in stage]
+    if not flat:
+        raise ValueError("a chain needs at least one linear")
+    descs = (ChainLinear * len(flat))()
+    tensors = []
+    dev = None
+    for i, (s, (x, q, d, N, y)) in enumerate(flat):
+        M, K = x.shape
+        if y.shape != (M, N):
+            raise ValueError(f"linear {i}: y must be [M, N]")
+        descs[i] = ChainLinear(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
+                               _dev(d, torch.float32, "d").value, N, _dev(y, torch.bfloat16, "y").value, s)
+        tensors += [x, q, d, y]
+        dev = dev or x.device
+    nbytes = int(_lib.w4_chain_workspace_bytes(len(flat)))
+    if nbytes == 0:
+        _check(W4_ERR_ARG, "w4_chain_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    plan = ChainPlanC()
+    _check(_lib.w4_chain_prepare(descs, len(flat), ctypes.c_void_p(ws.data_ptr()), nbytes, ctypes.byref(plan),
+                                 _stream(ws)), "w4_chain_prepare")
+    return ChainPlan(ws, plan, tensors)
 
 
 def pack(q_canon, d_canon, out=None):

@@ -5,8 +5,13 @@
 #include "w4_launch.h"
 
 #include <float.h>
-
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
 
 namespace {
 
@@ -383,6 +388,180 @@ w4_status w4_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, const 
 w4_status w4_gptq_block_s16(const float* W, int64_t N, int64_t K, int64_t b0, const float* U, int8_t* q_canon,
                             uint16_t* d_canon, float* err, hipStream_t stream) {
   return gptq_block(W, N, K, b0, U, q_canon, d_canon, true, err, stream);
+}
+
+// ---------------------------------------------------------------------------
+// chained decode pass
+// ---------------------------------------------------------------------------
+size_t w4_chain_workspace_bytes(int64_t count) {
+  if (count < 1 || count > W4_CHAIN_MAX) return 0;
+  return w4::chain_workspace_bytes(count);
+}
+
+namespace {
+// Does [a, a + na) lie within the union of the byte ranges r?
+bool covered(uintptr_t a, size_t na, std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
+  std::sort(r.begin(), r.end());
+  uintptr_t at = a;
+  const uintptr_t end = a + na;
+  for (const auto& iv : r) {
+    if (iv.first > at) break;
+    if (iv.second > at) at = iv.second;
+    if (at >= end) return true;
+  }
+  return at >= end;
+}
+}  // namespace
+
+w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace, size_t workspace_bytes,
+                           w4_chain_plan* plan, hipStream_t stream) {
+  if (count < 1 || count > W4_CHAIN_MAX) return W4_ERR_ARG;
+  if (!linears || !workspace || !plan) return W4_ERR_NULL;
+  if (!aligned(workspace, 16)) return W4_ERR_ALIGN;
+  // shapes, pointers and stage numbering
+  int64_t kmax = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const w4_chain_linear& l = linears[i];
+    if (l.M != 1 || l.N < 1 || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
+    if (w4::gemv_lds_bytes(1, l.K) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
+    if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31) return W4_ERR_SHAPE;
+    if (!l.x || !l.q_packed || !l.d_packed || !l.y) return W4_ERR_NULL;
+    if (!aligned(l.x, 16) || !aligned(l.q_packed, 16) || !aligned(l.d_packed, 16) || !aligned(l.y, 2))
+      return W4_ERR_ALIGN;
+    const int64_t prev = i == 0 ? 0 : linears[i - 1].stage;
+    if (i == 0 ? l.stage != 0 : (l.stage != prev && l.stage != prev + 1)) return W4_ERR_ARG;
+    kmax = l.K > kmax ? l.K : kmax;
+  }
+  // Aliasing.  The launch keeps the eight L2s coherent only for chains that
+  // write each byte once and never write a cache line (128 bytes) that the
+  // pass reads before the write: no y overlaps any weights, any other y, or
+  // the line of any x of its own or an earlier stage.  A y read as x by a
+  // later stage is the intended use; such an x must then be written entirely
+  // by earlier stages (it is read once no value of it is unwritten).
+  std::vector<int> wait_x(count, 0), fill(count, 0);
+  for (int64_t i = 0; i < count; ++i) {
+    const w4_chain_linear& a = linears[i];
+    const size_t yb = 2 * (size_t)a.N;
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(a.y) & ~(uintptr_t)127;
+    const size_t ylines = ((reinterpret_cast<uintptr_t>(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
+    for (int64_t j = 0; j < count; ++j) {
+      const w4_chain_linear& b = linears[j];
+      if (overlaps(a.y, yb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
+          overlaps(a.y, yb, b.d_packed, 4 * w4_scale_count(b.N, b.K)))
+        return W4_ERR_ARG;
+      if (j != i && overlaps(a.y, yb, b.y, 2 * (size_t)b.N)) return W4_ERR_ARG;
+      if (b.stage <= a.stage && overlaps(reinterpret_cast<const void*>(y0), ylines, b.x, 2 * (size_t)b.K))
+        return W4_ERR_ARG;
+      if (b.stage > a.stage && overlaps(a.y, yb, b.x, 2 * (size_t)b.K)) {
+        fill[i] = 1;
+        wait_x[j] = 1;
+      }
+    }
+  }
+  for (int64_t j = 0; j < count; ++j) {
+    if (!wait_x[j]) continue;
+    std::vector<std::pair<uintptr_t, uintptr_t>> r;
+    for (int64_t i = 0; i < count; ++i)
+      if (linears[i].stage < linears[j].stage) {
+        const uintptr_t y = reinterpret_cast<uintptr_t>(linears[i].y);
+        r.emplace_back(y, y + 2 * (size_t)linears[i].N);
+      }
+    if (!covered(reinterpret_cast<uintptr_t>(linears[j].x), 2 * (size_t)linears[j].K, r)) return W4_ERR_ARG;
+  }
+  const int stages = (int)linears[count - 1].stage + 1;
+  const size_t need = w4::chain_workspace_bytes(count);
+  if (workspace_bytes < need) return W4_ERR_ARG;
+
+  const int ci = w4::chain_choose_cfg((int)kmax);
+  if (ci < 0) return W4_ERR_ARG;
+  int R = 0, NW = 0;
+  w4::chain_cfg(ci, &R, &NW);
+  const size_t lds = (size_t)w4::gemv_lds_bytes(1, kmax);
+
+  // Table: the linears of each stage laid out longest K first (stable), as a
+  // batched launch does, each followed by its panels of R row blocks.
+  std::vector<uint8_t> host(need, 0);
+  auto* tab = reinterpret_cast<w4::ChainLinear*>(host.data() + sizeof(w4::ChainHeader));
+  std::vector<int64_t> order;
+  order.reserve(count);
+  int64_t items = 0;
+  for (int64_t i = 0; i < count;) {
+    int64_t e = i;
+    while (e < count && linears[e].stage == linears[i].stage) ++e;
+    const size_t first = order.size();
+    for (int64_t j = i; j < e; ++j) {
+      size_t at = order.size();
+      order.push_back(j);
+      while (at > first && linears[order[at - 1]].K < linears[j].K) {
+        order[at] = order[at - 1];
+        --at;
+      }
+      order[at] = j;
+    }
+    for (size_t t = first; t < order.size(); ++t) {
+      const int64_t src = order[t];
+      const w4_chain_linear& l = linears[src];
+      w4::ChainLinear& c = tab[t];
+      c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, 1, (int)l.K, (int)l.N, 0};
+      c.item0 = (int)items;
+      c.stage = (int)l.stage;
+      c.wait_x = wait_x[src];
+      c.fill = fill[src];
+      const int64_t nb = (l.N + 15) / 16;
+      items += (nb + R - 1) / R;
+      if (items > 0x7FFFFFFF) return W4_ERR_SHAPE;
+    }
+    i = e;
+  }
+  tab[count].item0 = (int)items;
+  tab[count].stage = stages;
+
+  // Grid: every block resident at once (waits look only at earlier items).
+  // Two blocks per CU measured fastest; W4_CHAIN_BLOCKS may ask for another
+  // count, up to what is resident.
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_status(e);
+  if (hipError_t e = w4::chain_blocks_per_cu(ci, lds, &per_cu)) return hip_status(e);
+  if (per_cu < 1 || cus < 1) return hip_status(hipErrorInvalidConfiguration);
+  const int64_t resident = (int64_t)per_cu * cus;
+  int64_t blocks = resident < 2 * (int64_t)cus ? resident : 2 * (int64_t)cus;
+  if (const char* e = getenv("W4_CHAIN_BLOCKS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) blocks = v < resident ? v : resident;
+  }
+  if (blocks > items) blocks = items;
+
+  if (hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, stream)) return hip_status(e);
+  if (hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
+
+  plan->workspace = workspace;
+  plan->linears = (int32_t)count;
+  plan->stages = stages;
+  plan->items = (int32_t)items;
+  plan->blocks = (int32_t)blocks;
+  plan->config = ci;
+  plan->lds_bytes = (int32_t)lds;
+  plan->rows_per_item = R;
+  plan->waves_per_block = NW;
+  return W4_OK;
+}
+
+w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream) {
+  if (!plan || !plan->workspace) return W4_ERR_NULL;
+  if (plan->config < 0 || plan->config >= w4::chain_num_cfgs() || plan->blocks < 0) return W4_ERR_ARG;
+  if (plan->blocks == 0) return W4_OK;
+  return hip_status(w4::launch_linear_chain(plan->workspace, plan->linears, plan->items, plan->config, plan->blocks,
+                                            (size_t)plan->lds_bytes, stream));
+}
+
+w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream) {
+  if (!plan || !plan->workspace || !flag) return W4_ERR_NULL;
+  uint32_t v = 0;
+  if (hipError_t e = hipMemcpyAsync(&v, plan->workspace, sizeof(v), hipMemcpyDeviceToHost, stream)) return hip_status(e);
+  if (hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
+  *flag = v;
+  return W4_OK;
 }
 
 }  // extern "C"

@@ -453,8 +453,16 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, co
 // kXScale: x is divided by channel scales while it is staged,
 // x'[k] = bf16(fl32(x[k] * inv_s[k])) (channel scaling before RTN, the
 // study's section 2 AWQ row; inv_s holds the fp32 reciprocals of the scales).
-template <int MT, int R, int NW, bool S16, bool kXScale = false>
-__device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, const float* inv_s = nullptr) {
+// No dependency to wait for: x is read as soon as the block starts.
+struct NoGate {
+  static constexpr bool kActive = false;
+};
+
+// Gate (kActive, chained launches): the block's weight prologue is issued
+// first, then x is staged once it is completely written (see ChainGate).
+template <int MT, int R, int NW, bool S16, bool kXScale = false, class Gate = NoGate>
+__device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, const float* inv_s = nullptr,
+                                          const Gate& gate = Gate()) {
   // LDS: x of the slab, [MT][GP * 16] uint4 (zero past K), then the start
   // values -1.5 * sum(x) of every (row, group, quarter), [MT][GP][4] floats.
   extern __shared__ uint4 xlds[];
@@ -537,9 +545,12 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
     // 32 768 with 4+ wavefronts) go out before the weight prologue.
     constexpr int kPre = 2;
     uint4 v[kPre][4];
+    (void)v;
+    if constexpr (!Gate::kActive) {
 #pragma unroll
-    for (int p = 0; p < kPre; ++p) load_x(x_off(threadIdx.x + p * NW * 64), v[p]);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int p = 0; p < kPre; ++p) load_x(x_off(threadIdx.x + p * NW * 64), v[p]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Weight prologue in the loop's order (scales, then groups 0..3); a
     // wavefront with no quads (j0 == j1) reads zeros here.
     issue_scales(sc, w.j0);
@@ -548,20 +559,50 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
       issue_group(s, w.j0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Consume x here, before the branches, so the loads are not sunk into them
-    // (behind the weights).
+    if constexpr (Gate::kActive) {
+      // The weights do not depend on earlier stages; x may still be being
+      // written by them.  Wait until a sample of x is written, then stage all
+      // of it (coherent loads), checking every value, and start over if any
+      // is still unwritten.
+      if (gate.reuse) {
+        // the previous item of this block staged the same x (and found it written)
+      } else if (gate.wait_x) {
+        for (uint32_t t = 0;; ++t) {
+          bool unwritten = false;
+          for (int e = threadIdx.x; e < total; e += NW * 64) {
+            uint4 tt[4];
 #pragma unroll
-    for (int p = 0; p < kPre; ++p)
+            for (int i = 0; i < 4; ++i) tt[i] = bload<Gate::kCoherent>(rx, x_off(e) + 64u * i);
+            unwritten |= Gate::unwritten(tt);
+            store_x(e, tt);
+          }
+          if (!__syncthreads_or(unwritten) || gate.give_up(t)) break;
+          // poll a sample of x before loading all of it again
+          gate.wait_sample(rx, K);
+        }
+      } else {
+        for (int e = threadIdx.x; e < total; e += NW * 64) {
+          uint4 tt[4];
+          load_x(x_off(e), tt);
+          store_x(e, tt);
+        }
+      }
+    } else {
+      // Consume x here, before the branches, so the loads are not sunk into
+      // them (behind the weights).
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        asm volatile("" : "+v"(v[p][i].x), "+v"(v[p][i].y), "+v"(v[p][i].z), "+v"(v[p][i].w));
+      for (int p = 0; p < kPre; ++p)
 #pragma unroll
-    for (int p = 0; p < kPre; ++p)
-      if ((int)threadIdx.x + p * NW * 64 < total) store_x(threadIdx.x + p * NW * 64, v[p]);
-    for (int e = threadIdx.x + kPre * NW * 64; e < total; e += NW * 64) {
-      uint4 t[4];
-      load_x(x_off(e), t);
-      store_x(e, t);
+        for (int i = 0; i < 4; ++i)
+          asm volatile("" : "+v"(v[p][i].x), "+v"(v[p][i].y), "+v"(v[p][i].z), "+v"(v[p][i].w));
+#pragma unroll
+      for (int p = 0; p < kPre; ++p)
+        if ((int)threadIdx.x + p * NW * 64 < total) store_x(threadIdx.x + p * NW * 64, v[p]);
+      for (int e = threadIdx.x + kPre * NW * 64; e < total; e += NW * 64) {
+        uint4 t[4];
+        load_x(x_off(e), t);
+        store_x(e, t);
+      }
     }
   }
   __syncthreads();
@@ -656,7 +697,13 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
       for (int ww = 1; ww < NW; ++ww) v += red[ww][r][mm][row];
       const int n = (wk.rb0 + r) * kTileRows + row;
       const int m = wk.m0 + mm;
-      if (n < N && m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v);
+      if (n < N && m < M) {
+        const uint16_t b = f32_to_bf16_rne(16.0f * v);
+        if constexpr (Gate::kActive)
+          Gate::store(D.y + (int64_t)m * N + n, b);
+        else
+          D.y[(int64_t)m * N + n] = b;
+      }
     }
   }
 }
@@ -681,6 +728,112 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
                                                                const float* inv_s) {
   const LinearDesc D{x, q, d, y, M, K, N, 0};
   gemv_body<MT, R, NW, false, true>(D, locate_one(N, R, MT), inv_s);
+}
+
+// ---------------------------------------------------------------------------
+// Chained launch of dependent M = 1 linears (layout and protocol in
+// w4_launch.h).  Each item runs the dot2 body above with a gate: the item's
+// weight prologue is issued first (weights never depend on earlier stages),
+// then, when its x is produced by earlier stages, the block waits until every
+// value of x is written, then stages x.  Per item the arithmetic is exactly
+// the batched dot2 kernel's with the same (R, NW), so results are identical
+// bits (NaN outputs aside: the unwritten marker is never written).
+//
+// Completion is the data itself: a fill launch marks every output that a
+// later linear reads with kUnwritten before the pass; outputs are written
+// through to memory (agent-scope stores), and x that may still be being
+// written is read with coherent loads, so no L2 of the eight can serve a
+// stale copy.  A chain writes each byte at most once and never writes a
+// cache line that the pass reads earlier (the C ABI refuses such chains).
+// ---------------------------------------------------------------------------
+constexpr uint16_t kUnwritten = 0xFFFF;     // a NaN pattern the chain never writes
+constexpr uint16_t kNanForUnwritten = 0xFFC0;
+// Polls before a wait gives up (each poll is a round trip to memory of at
+// least ~0.5 us, so this is tens of milliseconds: far longer than any stage,
+// far shorter than a hang).
+constexpr uint32_t kChainSpinLimit = 1u << 17;
+constexpr int kChainPollSleep = 2;  // s_sleep units (64 clocks) between polls
+
+struct ChainGate {
+  static constexpr bool kActive = true;
+  static constexpr int kCoherent = 16;  // buffer-load cache policy: agent-scope coherent (sc1)
+  bool wait_x;                          // x is written by earlier stages of this pass
+  bool reuse;                           // LDS already holds this x, staged by the block's previous item
+  uint32_t* error;
+
+  __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
+    __hip_atomic_store(p, v == kUnwritten ? kNanForUnwritten : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ static bool unwritten(const uint32_t w) {
+    return (~w & 0xFFFFu) == 0u || (~w & 0xFFFF0000u) == 0u;
+  }
+  __device__ __forceinline__ static bool unwritten(const uint4 (&v)[4]) {
+    bool u = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u |= unwritten(v[i].x) | unwritten(v[i].y) | unwritten(v[i].z) | unwritten(v[i].w);
+    return u;
+  }
+  // true (and the launch's error flag set) once waiting has gone on too long,
+  // or when a wait anywhere has timed out (this launch or an earlier one)
+  __device__ __forceinline__ bool give_up(uint32_t t) const {
+    if (t < kChainSpinLimit && ((t & 31) != 31 || __hip_atomic_load(error, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT) == 0u)) {
+      __builtin_amdgcn_s_sleep(kChainPollSleep);
+      return false;
+    }
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  // Wavefront 0 polls 64 16-byte chunks spread over x (1 KiB) until none is
+  // unwritten; the block then proceeds together.
+  __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, int K) const {
+    if (threadIdx.x < 64) {
+      const uint32_t chunks = (uint32_t)K / 8u;
+      const uint32_t off = (uint32_t)(((uint64_t)threadIdx.x * chunks) / 64u) * 16u;
+      for (uint32_t t = 0;; ++t) {
+        const uint4 v = bload<kCoherent>(rx, off);
+        const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
+        if (!__any(u)) break;
+        if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
+                                                                         __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+          if (threadIdx.x == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(kChainPollSleep);
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// lin: the table (linears + 1 entries, the last a sentinel); hdr: the
+// workspace header's error word.
+template <int R, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear* __restrict__ lin, uint32_t* hdr,
+                                                               int items) {
+  const int P = gridDim.x;
+  int i = blockIdx.x;
+  int li = 0;
+  int li_end = lin[1].item0;  // first item past linear li
+  while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
+  const uint16_t* staged = nullptr;  // x held in LDS (and its K)
+  int staged_k = 0;
+  while (i < items) {
+    const LinearDesc& D = lin[li].desc;
+    const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, hdr};
+    gemv_body<1, R, NW, false, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
+    staged = D.x;
+    staged_k = D.K;
+    i += P;
+    while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
+  }
+}
+
+// Marks the outputs that later linears read as unwritten (one block per linear).
+__global__ __launch_bounds__(256) void chain_fill_kernel(const ChainLinear* __restrict__ lin) {
+  const ChainLinear& l = lin[blockIdx.x];
+  if (!l.fill) return;
+  for (int n = threadIdx.x; n < l.desc.N; n += 256) l.desc.y[n] = kUnwritten;
 }
 
 // ---------------------------------------------------------------------------
@@ -939,6 +1092,75 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream
     if (MT == 4) launch_gemv_cfg<4, false>(ci, nb, lds, stream, a);
     else if (MT == 2) launch_gemv_cfg<2, false>(ci, nb, lds, stream, a);
     else launch_gemv_cfg<1, false>(ci, nb, lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// chained launch
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kChainCfgs[][2] = {{1, 4}, {1, 8}, {2, 4}, {2, 2}, {1, 2}, {4, 4}};
+constexpr int kNumChainCfgs = sizeof(kChainCfgs) / sizeof(kChainCfgs[0]);
+
+template <int I>
+const void* chain_kernel_ptr() {
+  return reinterpret_cast<const void*>(&linear_chain_kernel<kChainCfgs[I][0], kChainCfgs[I][1]>);
+}
+const void* chain_kernel(int ci) {
+  switch (ci) {
+    case 0: return chain_kernel_ptr<0>();
+    case 1: return chain_kernel_ptr<1>();
+    case 2: return chain_kernel_ptr<2>();
+    case 3: return chain_kernel_ptr<3>();
+    case 4: return chain_kernel_ptr<4>();
+    default: return chain_kernel_ptr<5>();
+  }
+}
+}  // namespace
+
+int chain_num_cfgs() { return kNumChainCfgs; }
+
+void chain_cfg(int ci, int* R, int* NW) {
+  *R = kChainCfgs[ci][0];
+  *NW = kChainCfgs[ci][1];
+}
+
+int chain_choose_cfg(int kmax) {
+  if (const char* e = getenv("W4_CHAIN_CFG")) {
+    int R = 0, NW = 0;
+    if (sscanf(e, "%d,%d", &R, &NW) != 2) return -1;
+    for (int i = 0; i < kNumChainCfgs; ++i)
+      if (kChainCfgs[i][0] == R && kChainCfgs[i][1] == NW) return i;
+    return -1;
+  }
+  // Measured on MI355X over the 27B- and 70B-class stacks (448 / 560
+  // linears, 256 / 320 stages): two row blocks per item and four wavefronts
+  // per block, two blocks per CU (the grid size is chosen by the C ABI).
+  (void)kmax;
+  return 2;
+}
+
+hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, chain_kernel(ci), kChainCfgs[ci][1] * 64, lds);
+}
+
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, int blocks, size_t lds,
+                               hipStream_t stream) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
+  const ChainLinear* lin = reinterpret_cast<const ChainLinear*>(w + sizeof(ChainHeader));
+  chain_fill_kernel<<<linears, 256, 0, stream>>>(lin);
+  switch (ci) {
+#define W4_CHAIN(i)                                                                      \
+  case i:                                                                                \
+    linear_chain_kernel<kChainCfgs[i][0], kChainCfgs[i][1]>                              \
+        <<<blocks, kChainCfgs[i][1] * 64, lds, stream>>>(lin, hdr, items);               \
+    break;
+    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4) W4_CHAIN(5)
+#undef W4_CHAIN
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -35,6 +35,50 @@ struct BatchArgs {
   LinearDesc desc[kMaxBatch];
 };
 
+// ---------------------------------------------------------------------------
+// Chained launch: a dependent sequence of M = 1 linears in stages (a decode
+// layer's q|k|v, then o, then gate|up, then down, layer after layer).  A
+// linear whose x is written by earlier stages reads it only once all of it is
+// written.  One persistent grid of co-resident blocks walks the items
+// (R-row-block panels) of every stage in order; block b takes items b, b+P,
+// b+2P, ...  Before the pass a fill launch marks every output that a later
+// linear reads with an unwritten-value pattern; a block about to stage such
+// an x first issues its item's weight loads, then waits until no value of x
+// is unwritten.  Waits only ever look at outputs of earlier items, which
+// co-resident blocks hold, so every wait ends; it is also bounded (a timeout
+// sets `error` and lets the launch drain).
+// ---------------------------------------------------------------------------
+// Workspace layout (device): ChainHeader | ChainLinear[linears + 1] (the last
+// is a sentinel with item0 = items).
+struct ChainHeader {
+  uint32_t error;  // sticky: nonzero once a wait has timed out
+  uint32_t pad[7];
+};
+struct ChainLinear {
+  LinearDesc desc;
+  int item0;   // first item of this linear
+  int stage;
+  int wait_x;  // x is written by earlier stages of the pass
+  int fill;    // y is read by later stages: marked unwritten before the pass
+};
+static_assert(sizeof(ChainHeader) == 32 && sizeof(ChainLinear) == 64, "workspace layout");
+
+inline size_t chain_workspace_bytes(int64_t linears) {
+  return sizeof(ChainHeader) + (size_t)(linears + 1) * sizeof(ChainLinear);
+}
+
+// Chain configurations: (R row blocks per item, NW wavefronts per block).
+int chain_num_cfgs();
+void chain_cfg(int ci, int* R, int* NW);
+// Configuration for a chain whose longest K is kmax (W4_CHAIN_CFG "R,NW"
+// overrides; -1 if it names no compiled configuration).
+int chain_choose_cfg(int kmax);
+// Co-resident blocks per CU of configuration ci with `lds` bytes of dynamic LDS.
+hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks);
+// The fill launch, then the chain launch.
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, int blocks, size_t lds,
+                               hipStream_t stream);
+
 // s16: scales are bf16 bit patterns (uint16_t) instead of fp32.
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,
                                void* d_packed, bool s16, hipStream_t stream);

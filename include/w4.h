@@ -29,7 +29,8 @@
  * caller owns every buffer; the library allocates nothing and keeps no state
  * besides a per-thread copy of the last HIP error.  Every call is enqueued
  * asynchronously on `stream` (0 = the null stream) and performs no host
- * synchronisation.  Argument errors are detected on the host before anything
+ * synchronisation (except the set-up and status calls of the chained pass,
+ * which say so).  Argument errors are detected on the host before anything
  * is enqueued and leave outputs untouched.  A launch failure returns
  * W4_ERR_HIP (w4_last_hip_error() gives the hipError_t); faults during
  * execution surface at the caller's next synchronisation, as in HIP.
@@ -200,6 +201,80 @@ w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_
  */
 w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, int64_t K,
                     int8_t* q_canon, float* d_canon, hipStream_t stream);
+
+/*
+ * Chained decode pass -- a dependent sequence of M = 1 linears run as one
+ * pass of two launches.  Every generated token runs each linear of every
+ * layer once, one after the other (27B quantization-and-drafter ladder,
+ * stage 1: decode reads all weights per token); within a layer q|k|v read
+ * the layer input, o reads what they lead to, gate|up read o's result and
+ * down reads theirs.  The linears are given in stages; a linear whose x lies
+ * in outputs of earlier stages reads it only once all of it is written.  Each
+ * linear computes exactly what w4_linear computes (study, section 1: y = W x
+ * with the group-quantization equation): its bits equal those of one
+ * w4_linear_batched call per stage run with the dot2 kernel in the chain's
+ * (R, NW) configuration, except that a NaN output with bits 0xFFFF is
+ * written as 0xFFC0 (0xFFFF marks unwritten values inside the pass).
+ *
+ * Unlike one launch per stage, the pass does not drain between stages: a
+ * persistent grid walks the stages' row panels in order, issues the weight
+ * loads of its next panel before that panel's input is ready, and stages the
+ * input once no value of it is unwritten.  A first, small launch marks every
+ * output that a later stage reads as unwritten.
+ *
+ *   w4_chain_workspace_bytes(count) -- bytes of device workspace for `count`
+ *       linears (a header and a table of the linears).
+ *   w4_chain_prepare(linears, count, workspace, bytes, plan, stream) --
+ *       validates the chain, writes its table into `workspace` (device,
+ *       16-byte aligned, >= w4_chain_workspace_bytes(count) bytes, owned by
+ *       the caller and kept alive and untouched while the plan is used),
+ *       fills `*plan` (host), and SYNCHRONISES `stream` once (a set-up call,
+ *       not part of the pass).  `linears` is host memory, read before the
+ *       call returns.  Requirements (W4_ERR_SHAPE / _NULL / _ALIGN / _ARG as
+ *       for w4_linear): 1 <= count <= W4_CHAIN_MAX; every M == 1; every K a
+ *       multiple of 128 up to 30720; N >= 1; stage[0] == 0 and each stage
+ *       equal to the previous one or one more.  Each byte is written at most
+ *       once per pass and never after the pass has read it: no y overlaps any
+ *       q or d, any other y, or the 128-byte cache lines of any x of its own
+ *       or an earlier stage.  An x that overlaps outputs of earlier stages
+ *       must lie entirely within them (W4_ERR_ARG otherwise).  The buffers
+ *       named in `linears` must stay allocated while the plan is used.
+ *   w4_chain_run(plan, stream) -- enqueues one pass (asynchronous, no
+ *       allocation, capturable in a HIP graph).  Passes on one workspace must
+ *       not overlap in time (one stream, or ordered streams).
+ *   w4_chain_error(plan, &flag, stream) -- synchronises `stream` and reads
+ *       the workspace's error flag: nonzero if a wait of some pass ran out of
+ *       time (it is bounded at tens of milliseconds; it can only run out if
+ *       the grid's blocks were not all resident at once, e.g. while another
+ *       process held the GPU's compute units).  The results of such a pass
+ *       are undefined; the flag stays set, and later passes stop waiting,
+ *       until the next w4_chain_prepare.
+ */
+#define W4_CHAIN_MAX 8192
+
+typedef struct w4_chain_linear {
+  const uint16_t* x;       /* bf16 [1][K]                                  */
+  int64_t M;               /* must be 1                                    */
+  int64_t K;
+  const uint8_t* q_packed; /* native codes of the N x K W                  */
+  const float* d_packed;   /* native fp32 scales                           */
+  int64_t N;
+  uint16_t* y;             /* bf16 [1][N]                                  */
+  int64_t stage;           /* 0, 1, 2 ... non-decreasing, steps of 0 or 1  */
+} w4_chain_linear;
+
+/* Filled by w4_chain_prepare; read by w4_chain_run (treat as opaque). */
+typedef struct w4_chain_plan {
+  void* workspace;
+  int32_t linears, stages, items, blocks;
+  int32_t config, lds_bytes, rows_per_item, waves_per_block;
+} w4_chain_plan;
+
+size_t w4_chain_workspace_bytes(int64_t count);
+w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace,
+                           size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
+w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream);
+w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream);
 
 /*
  * 16-bit scales.  The study's checkpoint sizes imply about two bytes per

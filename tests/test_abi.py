@@ -121,6 +121,58 @@ def test_batched_validation(w4):
     assert lib.w4_linear_batched(big, 1, 1, None) == ERR_SHAPE
 
 
+def test_chain_validation(w4):
+    """w4_chain_prepare refuses bad chains on the host, before any HIP call."""
+    lib = w4.library()
+    C = w4.ChainLinear
+    plan = w4.ChainPlanC()
+    assert lib.w4_chain_workspace_bytes(0) == 0
+    assert lib.w4_chain_workspace_bytes(8193) == 0
+    n = lib.w4_chain_workspace_bytes(4)
+    assert n > 0 and lib.w4_chain_workspace_bytes(8) > n
+    ws = FAKE + 0x4000000
+
+    def lin(i, stage, **kw):
+        base = FAKE + i * 0x100000
+        d = dict(x=base, M=1, K=256, q_packed=base + 0x10000, d_packed=base + 0x20000, N=32,
+                 y=base + 0x30000, stage=stage)
+        d.update(kw)
+        return C(**d)
+
+    def prep(items, nbytes=None, workspace=ws):
+        arr = (C * max(1, len(items)))(*items)
+        nb = nbytes if nbytes is not None else lib.w4_chain_workspace_bytes(max(1, len(items)))
+        return lib.w4_chain_prepare(arr, len(items), workspace, nb, ctypes.byref(plan), None)
+
+    assert prep([]) == ERR_ARG                                      # count 0
+    assert lib.w4_chain_prepare(None, 1, ws, n, ctypes.byref(plan), None) == ERR_NULL
+    assert prep([lin(0, 0)], workspace=None) == ERR_NULL
+    assert prep([lin(0, 0)], workspace=ws + 4) == ERR_ALIGN
+    assert prep([lin(0, 0, M=2)]) == ERR_SHAPE                      # decode only: M = 1
+    assert prep([lin(0, 0, K=100)]) == ERR_SHAPE
+    assert prep([lin(0, 0, K=30720 + 512)]) == ERR_SHAPE            # x must fit the LDS stage
+    assert prep([lin(0, 0, N=0)]) == ERR_SHAPE
+    assert prep([lin(0, 0, q_packed=None)]) == ERR_NULL
+    assert prep([lin(0, 0, x=FAKE + 2)]) == ERR_ALIGN
+    assert prep([lin(0, 1)]) == ERR_ARG                             # stages start at 0
+    assert prep([lin(0, 0), lin(1, 2)]) == ERR_ARG                  # and step by 0 or 1
+    assert prep([lin(0, 0), lin(1, 1), lin(2, 0)]) == ERR_ARG       # never go back
+    # two outputs of one chain overlap
+    assert prep([lin(0, 0), lin(1, 1, y=FAKE + 0x30000 + 16)]) == ERR_ARG
+    # an output on weights
+    assert prep([lin(0, 0), lin(1, 1, y=FAKE + 0x10000)]) == ERR_ARG
+    # an output over the input of its own stage, or of an earlier one, or the
+    # same 128-byte line
+    assert prep([lin(0, 0, y=FAKE)]) == ERR_ARG
+    assert prep([lin(0, 0), lin(1, 1, y=FAKE + 256)]) == ERR_ARG
+    # x of stage 0 ends at byte 0x310 of its line; y of stage 1 starts at 0x320
+    assert prep([lin(0, 0, x=FAKE + 0x210, K=128), lin(1, 1, y=FAKE + 0x320)]) == ERR_ARG
+    # an input that lies partly in an earlier output and partly outside all of them
+    assert prep([lin(0, 0, N=64), lin(1, 1, x=FAKE + 0x30000, K=256)]) == ERR_ARG
+    # workspace too small
+    assert prep([lin(0, 0), lin(1, 1)], nbytes=64) == ERR_ARG
+
+
 def test_s16_validation(w4):
     """The 16-bit-scale entry points check their arguments like the fp32 ones."""
     lib = w4.library()

@@ -1,0 +1,219 @@
+"""Chained decode pass (w4_chain_prepare / w4_chain_run) on an MI355X.
+
+A chain runs the linears of several decoder layers in stages, in one launch:
+q|k|v read the layer input, o reads q's output, gate|up read o's output, down
+reads gate's output, and the next layer reads down's output.  Each output must
+be (a) bitwise equal to one w4_linear_batched call per stage with the dot2
+kernel in the chain's configuration, run on the very inputs the chain saw, and
+(b) within 2e-3 * sum|w_hat x| + 1e-6 of the fp64 oracle on those inputs.
+Repeated passes, eager and graph-replayed, each with a new layer-0 input,
+check that no pass reads a stale input and that the completion counters
+return to zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.test_gpu_parity import _bits, _say, check_y
+
+pytestmark = pytest.mark.gpu
+
+CHAIN_CFGS = ["1,4", "1,8", "2,4", "2,2", "1,2"]
+
+
+def _build_chain(w4, gpu, layers, hidden, nq, nkv, ffn, seed=0, side=True):
+    """Stages of `layers` decoder layers with real dataflow between them.
+
+    Returns (stages, records, x0): records[i] = (name, stage, W fp32 host, x, q, d, N, y)
+    in stage order.  Optional side linears with ragged N read inputs of their own.
+    """
+    x0 = workloads.random_activations(1, hidden, seed=seed, device=gpu)
+    stages, records = [], []
+
+    def add(stage_items, name, N, K, x, wseed):
+        W = workloads.random_weight(N, K, std=0.02, seed=wseed)
+        q, d = w4.quantize_rtn(torch.from_numpy(W).to(gpu))
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=gpu)
+        stage_items.append((x, q, d, N, y))
+        records.append((name, len(stages), W, x, q, d, N, y))
+        return y
+
+    x = x0
+    for layer in range(layers):
+        s = 1000 * seed + 10 * layer
+        st = []
+        yq = add(st, f"L{layer}.q", nq, hidden, x, s + 0)
+        add(st, f"L{layer}.k", nkv, hidden, x, s + 1)
+        add(st, f"L{layer}.v", nkv, hidden, x, s + 2)
+        stages.append(st)
+        st = []
+        yo = add(st, f"L{layer}.o", hidden, nq, yq, s + 3)
+        if side and layer == 0:
+            add(st, "side.ragged", 77, 384, workloads.random_activations(1, 384, seed=seed + 7, device=gpu), s + 7)
+        stages.append(st)
+        st = []
+        yg = add(st, f"L{layer}.gate", ffn, hidden, yo, s + 4)
+        add(st, f"L{layer}.up", ffn, hidden, yo, s + 5)
+        if side and layer == 0:
+            add(st, "side.one_row", 1, 128, workloads.random_activations(1, 128, seed=seed + 8, device=gpu), s + 8)
+        stages.append(st)
+        st = []
+        x = add(st, f"L{layer}.down", hidden, ffn, yg, s + 6)
+        stages.append(st)
+    return stages, records, x0
+
+
+def _check_pass(w4, records, cfg, monkeypatch, what):
+    """Bitwise against per-stage batched dot2 launches, and within tolerance of the oracle."""
+    torch.cuda.synchronize()
+    monkeypatch.setenv("W4_GEMV_CFG", cfg)
+    by_stage = {}
+    for rec in records:
+        by_stage.setdefault(rec[1], []).append(rec)
+    for st in sorted(by_stage):
+        recs = by_stage[st]
+        outs = [torch.empty_like(r[7]) for r in recs]
+        w4.linear_batched([(r[3], r[4], r[5], r[6], o) for r, o in zip(recs, outs)], path="gemv")
+        for r, o in zip(recs, outs):
+            assert torch.equal(r[7].view(torch.int16), o.view(torch.int16)), f"{what} {r[0]}: chain != batched"
+    monkeypatch.delenv("W4_GEMV_CFG")
+    worst = 0.0
+    for name, _, W, x, _, _, _, y in records:
+        q_ref, d_ref = oracle.rtn_quantize_ref(W)
+        y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+        worst = max(worst, check_y(y, y_ref, absdot, f"{what} {name}"))
+    return worst
+
+
+@pytest.mark.parametrize("cfg", CHAIN_CFGS)
+def test_chain_matches_batched_and_oracle(w4, gpu, cfg, monkeypatch):
+    monkeypatch.setenv("W4_CHAIN_CFG", cfg)
+    _say(f"chain cfg={cfg}: 3 layers (hidden 512, q 768, kv 256, ffn 1408) + ragged side linears")
+    stages, records, x0 = _build_chain(w4, gpu, layers=3, hidden=512, nq=768, nkv=256, ffn=1408, seed=1)
+    plan = w4.chain_prepare(stages)
+    monkeypatch.delenv("W4_CHAIN_CFG")
+    info = plan.info
+    assert info["stages"] == 12 and info["linears"] == len(records)
+    for rep in range(3):
+        x0.copy_(workloads.random_activations(1, x0.shape[1], seed=50 + rep, device=gpu))
+        plan.run()
+        assert plan.error() == 0, "a chain wait timed out"
+        _check_pass(w4, records, cfg, monkeypatch, f"cfg={cfg} pass {rep}")
+
+
+def test_chain_graph_replays(w4, gpu, monkeypatch):
+    """Graph-captured passes replayed with eager input changes and synchronisations between them."""
+    _say("chain in a HIP graph: 2 layers, 4 replays with new inputs")
+    stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=1024, nq=1024, nkv=256, ffn=2816, seed=2)
+    plan = w4.chain_prepare(stages)
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.run()  # warm (outside the graph)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run()
+    for rep in range(4):
+        x0.copy_(workloads.random_activations(1, x0.shape[1], seed=70 + rep, device=gpu))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert plan.error() == 0, "a chain wait timed out"
+        _check_pass(w4, records, cfg, monkeypatch, f"graph replay {rep}")
+
+
+def test_chain_full_size_27b_layers(w4, gpu, monkeypatch):
+    """Two 27B-class decoder layers at their real shapes (hidden 5120, q 6144,
+    k/v 1024, ffn 17408): bitwise against per-stage batched launches; oracle on
+    sampled output rows."""
+    _say("chain 27B-class: 2 layers at full size")
+    hidden, nq, nkv, ffn = 5120, 6144, 1024, 17408
+    x0 = workloads.random_activations(1, hidden, seed=3, device=gpu)
+    stages, records = [], []
+    x = x0
+    rng = np.random.default_rng(3)
+    for layer in range(2):
+        def mk(N, K, xin, name, st):
+            W = torch.randn((N, K), device=gpu, generator=torch.Generator(gpu).manual_seed(100 * layer + len(records)))
+            W.mul_(0.015)
+            q, d = w4.quantize_rtn(W)
+            rows = np.sort(rng.choice(N, size=24, replace=False))
+            W_rows = W.index_select(0, torch.as_tensor(rows, device=gpu)).cpu().numpy()
+            del W
+            y = torch.empty((1, N), dtype=torch.bfloat16, device=gpu)
+            st.append((xin, q, d, N, y))
+            records.append((name, len(stages), rows, W_rows, xin, q, d, N, y))
+            return y
+        st = []
+        yq = mk(nq, hidden, x, f"L{layer}.q", st)
+        mk(nkv, hidden, x, f"L{layer}.k", st)
+        mk(nkv, hidden, x, f"L{layer}.v", st)
+        stages.append(st)
+        st = []
+        yo = mk(hidden, nq, yq, f"L{layer}.o", st)
+        stages.append(st)
+        st = []
+        yg = mk(ffn, hidden, yo, f"L{layer}.gate", st)
+        mk(ffn, hidden, yo, f"L{layer}.up", st)
+        stages.append(st)
+        st = []
+        x = mk(hidden, ffn, yg, f"L{layer}.down", st)
+        stages.append(st)
+    plan = w4.chain_prepare(stages)
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    plan.run()
+    assert plan.error() == 0, "a chain wait timed out"
+    torch.cuda.synchronize()
+    monkeypatch.setenv("W4_GEMV_CFG", cfg)
+    for st_i, st in enumerate(stages):
+        recs = [r for r in records if r[1] == st_i]
+        outs = [torch.empty_like(r[8]) for r in recs]
+        w4.linear_batched([(r[4], r[5], r[6], r[7], o) for r, o in zip(recs, outs)], path="gemv")
+        for r, o in zip(recs, outs):
+            assert torch.equal(r[8].view(torch.int16), o.view(torch.int16)), f"{r[0]}: chain != batched"
+    monkeypatch.delenv("W4_GEMV_CFG")
+    for name, _, rows, W_rows, xin, _, _, _, y in records:
+        q_ref, d_ref = oracle.rtn_quantize_ref(W_rows)
+        y_ref, absdot = oracle.w4_linear_ref(_bits(xin), q_ref, d_ref)
+        check_y(y[:, rows], y_ref, absdot, f"27B chain {name} (24 sampled rows)")
+
+
+def test_chain_rejects_bad_chains(w4, gpu):
+    _say("chain argument errors")
+    W = torch.from_numpy(workloads.random_weight(32, 256, seed=4)).to(gpu)
+    q, d = w4.quantize_rtn(W)
+    x = workloads.random_activations(1, 256, seed=4, device=gpu)
+    y = torch.empty((1, 32), dtype=torch.bfloat16, device=gpu)
+    x2 = workloads.random_activations(2, 256, seed=4, device=gpu)
+    y2 = torch.empty((2, 32), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(w4.W4Error, match="W4_ERR_SHAPE"):
+        w4.chain_prepare([[(x2, q, d, 32, y2)]])           # M must be 1
+    with pytest.raises(w4.W4Error, match="W4_ERR_ARG"):
+        w4.chain_prepare([[(x, q, d, 32, y), (x, q, d, 32, y)]])   # two outputs of a stage overlap
+    xy = torch.empty((1, 256), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(w4.W4Error, match="W4_ERR_ARG"):
+        w4.chain_prepare([[(xy, q, d, 32, xy[:, :32])]])   # y overlaps x within a stage
+    # a later stage writing over an earlier stage's input (or the line it sits
+    # in) is refused: the launch relies on each line being written before it
+    # is read
+    y_a = torch.empty((1, 256), dtype=torch.bfloat16, device=gpu)
+    W2 = torch.from_numpy(workloads.random_weight(256, 256, seed=5)).to(gpu)
+    q2, d2 = w4.quantize_rtn(W2)
+    with pytest.raises(w4.W4Error, match="W4_ERR_ARG"):
+        w4.chain_prepare([[(x, q2, d2, 256, y_a)], [(y_a, q, d, 32, y)], [(y_a, q2, d2, 256, x)]])
+    # y of one stage read as x by the next: the intended use
+    x_in = x.clone()
+    plan = w4.chain_prepare([[(x, q2, d2, 256, y_a)], [(y_a, q, d, 32, y)]])
+    plan.run()
+    assert plan.error() == 0
+    q_ref, d_ref = oracle.rtn_quantize_ref(W.cpu().numpy())
+    q2_ref, d2_ref = oracle.rtn_quantize_ref(W2.cpu().numpy())
+    for xin, (qr, dr), out, what in ((x_in, (q2_ref, d2_ref), y_a, "stage 0"), (y_a, (q_ref, d_ref), y, "stage 1")):
+        y_ref, absdot = oracle.w4_linear_ref(_bits(xin), qr, dr)
+        check_y(out, y_ref, absdot, what)
