@@ -279,6 +279,31 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
     return res
 
 
+# launch modes that keep a decode layer's dependencies (o after q|k|v, down after gate|up)
+DEPENDENT_MODES = ("per_call", "fused_shared_input", "chained")
+
+
+def decode_summary(stacks):
+    """Per stack at M = 1: the fastest launch mode that keeps the layer's
+    dependencies, as equivalent decode tokens/s of the linear layers (1 / pass
+    time) and % of the 8 TB/s roofline; the independent-launch upper bound
+    beside it."""
+    out = {}
+    for name, res in stacks.items():
+        m1 = res.get(1) or res.get("1") or {}
+        dep = {k: v for k, v in m1.items() if k in DEPENDENT_MODES}
+        if not dep:
+            continue
+        mode, best = min(dep.items(), key=lambda kv: kv[1]["ms_per_pass"])
+        entry = {"mode": mode, "tokens_per_s": round(1e3 / best["ms_per_pass"], 1), "ms_per_pass": best["ms_per_pass"],
+                 "GBps": best["GBps"], "pct_of_peak": best["pct_of_peak"]}
+        if "layer_batched" in m1:
+            entry["upper_bound_independent_launches"] = {"tokens_per_s": round(1e3 / m1["layer_batched"]["ms_per_pass"], 1),
+                                                         "pct_of_peak": m1["layer_batched"]["pct_of_peak"]}
+        out[name] = entry
+    return out
+
+
 def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name):
     """One decode pass of the whole stack as one chained launch (w4_chain_run):
     the shared-input groups of every layer become stages, and each stage reads
@@ -841,6 +866,7 @@ def main():
         "pair": pair,
         "quantize": quant,
         "stacks": stacks,
+        "equiv_decode_tokens_per_s": decode_summary(stacks),
         "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies, read_peak),
         "hbm_read_peak_measured": read_peak,
         "scales_16bit": s16,

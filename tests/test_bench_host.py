@@ -129,3 +129,17 @@ def test_path_compare_summary_rejects_a_short_trace(bench, tmp_path):
                     "Start_Timestamp": 0, "End_Timestamp": 1000})
     with pytest.raises(SystemExit):
         bench.summarize_path_compare(str(tmp_path / "trace.csv"))
+
+
+def test_decode_summary_takes_the_fastest_dependent_mode(bench):
+    """Equivalent decode tokens/s come from a launch mode that keeps the layer's
+    dependencies; the independent-launch upper bound is reported beside it, never
+    instead of it."""
+    m = lambda ms, pct: {"ms_per_pass": ms, "GBps": 1.0, "pct_of_peak": pct}
+    stacks = {"stack_x": {1: {"per_call": m(4.0, 10), "fused_shared_input": m(3.0, 20), "chained": m(2.5, 30),
+                              "layer_batched": m(2.0, 40)}, 8: {"fused_shared_input": m(1.0, 90)}},
+              "stack_y": {"1": {"per_call": m(5.0, 10), "fused_shared_input": m(4.0, 20)}}}
+    s = bench.decode_summary(stacks)
+    assert s["stack_x"]["mode"] == "chained" and s["stack_x"]["tokens_per_s"] == 400.0
+    assert s["stack_x"]["upper_bound_independent_launches"]["tokens_per_s"] == 500.0
+    assert s["stack_y"]["mode"] == "fused_shared_input" and "upper_bound_independent_launches" not in s["stack_y"]
