@@ -217,3 +217,25 @@ def test_chain_rejects_bad_chains(w4, gpu):
     for xin, (qr, dr), out, what in ((x_in, (q2_ref, d2_ref), y_a, "stage 0"), (y_a, (q_ref, d_ref), y, "stage 1")):
         y_ref, absdot = oracle.w4_linear_ref(_bits(xin), qr, dr)
         check_y(out, y_ref, absdot, what)
+
+
+def test_chain_error_flag_is_sticky_until_prepare(w4, gpu, monkeypatch):
+    """A pass that starts with the workspace's error flag set (as after a timed-out
+    wait) stops waiting, still completes, and leaves the flag set; the next
+    w4_chain_prepare clears it and passes are correct again."""
+    _say("chain error flag: set from the host, pass completes, prepare clears it")
+    stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=512, nq=768, nkv=256, ffn=1408, seed=6, side=False)
+    plan = w4.chain_prepare(stages)
+    assert plan.error() == 0
+    plan.workspace[0] = 1  # the error word is the first 32 bits of the workspace
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 1
+    plan.run()
+    assert plan.error() == 1
+    plan = w4.chain_prepare(stages)
+    assert plan.error() == 0
+    plan.run()
+    assert plan.error() == 0
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    _check_pass(w4, records, cfg, monkeypatch, "after prepare")
