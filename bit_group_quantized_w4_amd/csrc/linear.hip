@@ -752,7 +752,7 @@ constexpr uint16_t kNanForUnwritten = 0xFFC0;
 // least ~0.5 us, so this is tens of milliseconds: far longer than any stage,
 // far shorter than a hang).
 constexpr uint32_t kChainSpinLimit = 1u << 17;
-constexpr int kChainPollSleep = 2;  // s_sleep units (64 clocks) between polls
+constexpr int kChainPollSleep = 4;  // s_sleep units (64 clocks) between polls
 
 struct ChainGate {
   static constexpr bool kActive = true;
@@ -789,7 +789,7 @@ struct ChainGate {
   __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, int K) const {
     if (threadIdx.x < 64) {
       const uint32_t chunks = (uint32_t)K / 8u;
-      const uint32_t off = (uint32_t)(((uint64_t)threadIdx.x * chunks) / 64u) * 16u;
+      const uint32_t off = threadIdx.x < 4 ? (uint32_t)(((uint64_t)threadIdx.x * chunks) / 4u) * 16u : kOobX;
       for (uint32_t t = 0;; ++t) {
         const uint4 v = bload<kCoherent>(rx, off);
         const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
