@@ -567,6 +567,7 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
       if (gate.reuse) {
         // the previous item of this block staged the same x (and found it written)
       } else if (gate.wait_x) {
+        if (!gate.same_stage) gate.wait_sample(rx, K);
         for (uint32_t t = 0;; ++t) {
           bool unwritten = false;
           for (int e = threadIdx.x; e < total; e += NW * 64) {
@@ -759,6 +760,7 @@ struct ChainGate {
   static constexpr int kCoherent = 16;  // buffer-load cache policy: agent-scope coherent (sc1)
   bool wait_x;                          // x is written by earlier stages of this pass
   bool reuse;                           // LDS already holds this x, staged by the block's previous item
+  bool same_stage;                      // the block's previous item was in this stage
   uint32_t* error;
 
   __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
@@ -818,9 +820,11 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
   while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
   const uint16_t* staged = nullptr;  // x held in LDS (and its K)
   int staged_k = 0;
+  int prev_stage = -1;
   while (i < items) {
     const LinearDesc& D = lin[li].desc;
-    const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, hdr};
+    const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage, hdr};
+    prev_stage = lin[li].stage;
     gemv_body<1, R, NW, false, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
     staged = D.x;
     staged_k = D.K;
