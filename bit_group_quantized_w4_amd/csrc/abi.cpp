@@ -472,7 +472,9 @@ w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* 
   const size_t need = w4::chain_workspace_bytes(count);
   if (workspace_bytes < need) return W4_ERR_ARG;
 
-  const int ci = w4::chain_choose_cfg((int)kmax);
+  double code_bytes = 0;
+  for (int64_t i = 0; i < count; ++i) code_bytes += (double)w4_packed_bytes(linears[i].N, linears[i].K);
+  const int ci = w4::chain_choose_cfg((int)kmax, code_bytes / stages);
   if (ci < 0) return W4_ERR_ARG;
   int R = 0, NW = 0;
   w4::chain_cfg(ci, &R, &NW);

@@ -1130,7 +1130,7 @@ void chain_cfg(int ci, int* R, int* NW) {
   *NW = kChainCfgs[ci][1];
 }
 
-int chain_choose_cfg(int kmax) {
+int chain_choose_cfg(int kmax, double stage_bytes) {
   if (const char* e = getenv("W4_CHAIN_CFG")) {
     int R = 0, NW = 0;
     if (sscanf(e, "%d,%d", &R, &NW) != 2) return -1;
@@ -1138,11 +1138,13 @@ int chain_choose_cfg(int kmax) {
       if (kChainCfgs[i][0] == R && kChainCfgs[i][1] == NW) return i;
     return -1;
   }
-  // Measured on MI355X over the 27B- and 70B-class stacks (448 / 560
-  // linears, 256 / 320 stages): two row blocks per item and four wavefronts
-  // per block, two blocks per CU (the grid size is chosen by the C ABI).
+  // Measured on MI355X (two blocks per CU; the grid size is chosen by the C
+  // ABI): with stages of tens of MB or more (27B- and 70B-class stacks, 45
+  // and 110 MB of codes per stage on average) two row blocks per item and
+  // four wavefronts per block; with small stages (4B-class, 12 MB) one row
+  // block and eight wavefronts, so that every stage has more, shorter items.
   (void)kmax;
-  return 2;
+  return stage_bytes < 24e6 ? 1 : 2;
 }
 
 hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks) {

@@ -70,9 +70,10 @@ inline size_t chain_workspace_bytes(int64_t linears) {
 // Chain configurations: (R row blocks per item, NW wavefronts per block).
 int chain_num_cfgs();
 void chain_cfg(int ci, int* R, int* NW);
-// Configuration for a chain whose longest K is kmax (W4_CHAIN_CFG "R,NW"
-// overrides; -1 if it names no compiled configuration).
-int chain_choose_cfg(int kmax);
+// Configuration for a chain whose longest K is kmax and whose stages hold
+// stage_bytes of codes on average (W4_CHAIN_CFG "R,NW" overrides; -1 if it
+// names no compiled configuration).
+int chain_choose_cfg(int kmax, double stage_bytes);
 // Co-resident blocks per CU of configuration ci with `lds` bytes of dynamic LDS.
 hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks);
 // The fill launch, then the chain launch.
