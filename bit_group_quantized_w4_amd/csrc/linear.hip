@@ -786,8 +786,9 @@ struct ChainGate {
     if (threadIdx.x == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
-  // Wavefront 0 polls 64 16-byte chunks spread over x (1 KiB) until none is
-  // unwritten; the block then proceeds together.
+  // Wavefront 0 polls four 16-byte chunks spread over x (64 bytes: polls
+  // compete with the producers' last reads, so they are kept small) until
+  // none is unwritten; the block then proceeds together.
   __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, int K) const {
     if (threadIdx.x < 64) {
       const uint32_t chunks = (uint32_t)K / 8u;
