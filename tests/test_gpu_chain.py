@@ -21,7 +21,7 @@ from tests.test_gpu_parity import _bits, _say, check_y
 
 pytestmark = pytest.mark.gpu
 
-CHAIN_CFGS = ["1,4", "1,8", "2,4", "2,2", "1,2"]
+CHAIN_CFGS = ["1,4", "1,8", "2,4", "2,2", "1,2", "4,4"]
 
 
 def _build_chain(w4, gpu, layers, hidden, nq, nkv, ffn, seed=0, side=True):
