@@ -271,8 +271,8 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
             log(f"[bench] stack {name}{'' if sb == 4 else ' (16-bit scales)'} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
                 f"{1 / per:.1f} passes/s")
             del g
-        if M == 1 and sb == 4 and (not only_modes or "chained" in only_modes):
-            res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name)
+        if M == 1 and (not only_modes or "chained" in only_modes):
+            res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, sb)
         res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M, sb)
     del layers
     torch.cuda.empty_cache()
@@ -304,7 +304,7 @@ def decode_summary(stacks):
     return out
 
 
-def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name):
+def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4):
     """One decode pass of the whole stack as one chained launch (w4_chain_run):
     the shared-input groups of every layer become stages, and each stage reads
     the output of the previous one (q|k|v <- previous down, o <- q, gate|up <- o,
@@ -326,7 +326,7 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name):
     t = time_graph(torch, g, steps, warmup)
     err = plan.error()
     per = t / steps
-    nbytes = workloads.stack_bytes(name, 1, 4)
+    nbytes = workloads.stack_bytes(name, 1, scale_bytes)
     gbs = nbytes / per / 1e9
     flops = 2.0 * workloads.stack_weights(name)
     out = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
@@ -334,7 +334,7 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name):
            "stages_per_pass": len(stages), "useful_tflops": round(flops / per / 1e12, 2),
            "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3),
            "plan": plan.info, "wait_timeouts": err}
-    log(f"[bench] stack {name} M=1 chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
+    log(f"[bench] stack {name}{'' if scale_bytes == 4 else ' (16-bit scales)'} M=1 chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
         f"(plan {plan.info}, timeouts {err})")
     del g, plan
     return out
@@ -811,12 +811,13 @@ def main():
                                            [int(m) for m in args.stack_ms.split(",") if m] or None,
                                            [m for m in args.stack_modes.split(",") if m] or None)
 
-    # 16-bit scales: the headline pair at M = 1 and the stacks' realistic launch mode at M = 1
+    # 16-bit scales: the headline pair at M = 1 and the stacks at M = 1 in the two launch modes that keep
+    # a layer's dependencies (one launch per stage, chained)
     s16 = None if args.no_s16 else {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
                                                        scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
     for s in [s for s in args.stacks.split(",") if s and s != "none" and not args.no_s16]:
         s16["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
-                                        max(2, args.warmup), [1], ["fused_shared_input"],
+                                        max(2, args.warmup), [1], ["fused_shared_input", "chained"],
                                         scale_dtype=torch.bfloat16)
 
     awq_res = None if args.no_awq else bench_awq(torch, w4, workloads, args.steps, args.warmup)

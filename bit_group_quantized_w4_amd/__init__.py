@@ -43,7 +43,8 @@ class ChainPlanC(ctypes.Structure):
 
     _I32 = ctypes.c_int32
     _fields_ = [("workspace", _VP), ("linears", _I32), ("stages", _I32), ("items", _I32), ("blocks", _I32),
-                ("config", _I32), ("lds_bytes", _I32), ("rows_per_item", _I32), ("waves_per_block", _I32)]
+                ("config", _I32), ("lds_bytes", _I32), ("rows_per_item", _I32), ("waves_per_block", _I32),
+                ("scale_bytes", _I32), ("reserved", _I32)]
 
 
 # (name, restype, argtypes) of every symbol include/w4.h declares
@@ -76,6 +77,7 @@ SIGNATURES = {
     # chained decode pass
     "w4_chain_workspace_bytes": (_SZ, [_I64]),
     "w4_chain_prepare": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
+    "w4_chain_prepare_s16": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_run": (_INT, [ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_error": (_INT, [ctypes.POINTER(ChainPlanC), ctypes.POINTER(ctypes.c_uint32), _VP]),
     # GPTQ steps
@@ -247,15 +249,17 @@ class ChainPlan:
         p = self.plan
         return {"linears": p.linears, "stages": p.stages, "items": p.items, "blocks": p.blocks,
                 "rows_per_item": p.rows_per_item * 16, "waves_per_block": p.waves_per_block,
-                "lds_bytes": p.lds_bytes}
+                "lds_bytes": p.lds_bytes, "scale_bytes": p.scale_bytes}
 
 
 def chain_prepare(stages):
     """Prepare a chained decode pass (w4_chain_prepare).
 
-    stages: sequence of stages, each a sequence of (x [1, K] bf16, q, d fp32, N,
-    y [1, N] bf16).  Every linear of a stage writes y before any linear of the
-    next stage reads x.  Returns a ChainPlan; plan.run() enqueues one pass.
+    stages: sequence of stages, each a sequence of (x [1, K] bf16, q, d, N,
+    y [1, N] bf16), with d fp32 scales throughout or bf16 (16-bit) scales
+    throughout.  A linear whose x lies in outputs of earlier stages reads it
+    once all of it is written.  Returns a ChainPlan; plan.run() enqueues one
+    pass.
     """
     flat = [(s, it) for s, stage in enumerate(stages) for it in stage]
     if not flat:
@@ -263,12 +267,16 @@ def chain_prepare(stages):
     descs = (ChainLinear * len(flat))()
     tensors = []
     dev = None
+    sd = _scale_dtype(flat[0][1][2])
     for i, (s, (x, q, d, N, y)) in enumerate(flat):
         M, K = x.shape
         if y.shape != (M, N):
             raise ValueError(f"linear {i}: y must be [M, N]")
+        if _scale_dtype(d) != sd:
+            raise TypeError("all linears of a chain must use the same scale dtype")
+        # the fp32- and bf16-scale descriptor structs have the same layout
         descs[i] = ChainLinear(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
-                               _dev(d, torch.float32, "d").value, N, _dev(y, torch.bfloat16, "y").value, s)
+                               _dev(d, sd, "d").value, N, _dev(y, torch.bfloat16, "y").value, s)
         tensors += [x, q, d, y]
         dev = dev or x.device
     nbytes = int(_lib.w4_chain_workspace_bytes(len(flat)))
@@ -276,8 +284,9 @@ def chain_prepare(stages):
         _check(W4_ERR_ARG, "w4_chain_workspace_bytes")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan = ChainPlanC()
-    _check(_lib.w4_chain_prepare(descs, len(flat), ctypes.c_void_p(ws.data_ptr()), nbytes, ctypes.byref(plan),
-                                 _stream(ws)), "w4_chain_prepare")
+    fn, name = ((_lib.w4_chain_prepare_s16, "w4_chain_prepare_s16") if sd == torch.bfloat16
+                else (_lib.w4_chain_prepare, "w4_chain_prepare"))
+    _check(fn(descs, len(flat), ctypes.c_void_p(ws.data_ptr()), nbytes, ctypes.byref(plan), _stream(ws)), name)
     return ChainPlan(ws, plan, tensors)
 
 

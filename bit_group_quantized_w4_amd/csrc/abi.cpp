@@ -398,6 +398,7 @@ size_t w4_chain_workspace_bytes(int64_t count) {
   return w4::chain_workspace_bytes(count);
 }
 
+extern "C++" {
 namespace {
 // Does [a, a + na) lie within the union of the byte ranges r?
 bool covered(uintptr_t a, size_t na, std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
@@ -411,17 +412,17 @@ bool covered(uintptr_t a, size_t na, std::vector<std::pair<uintptr_t, uintptr_t>
   }
   return at >= end;
 }
-}  // namespace
 
-w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace, size_t workspace_bytes,
-                           w4_chain_plan* plan, hipStream_t stream) {
+template <typename Desc>
+w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, size_t workspace_bytes,
+                        w4_chain_plan* plan, bool s16, hipStream_t stream) {
   if (count < 1 || count > W4_CHAIN_MAX) return W4_ERR_ARG;
   if (!linears || !workspace || !plan) return W4_ERR_NULL;
   if (!aligned(workspace, 16)) return W4_ERR_ALIGN;
   // shapes, pointers and stage numbering
   int64_t kmax = 0;
   for (int64_t i = 0; i < count; ++i) {
-    const w4_chain_linear& l = linears[i];
+    const Desc& l = linears[i];
     if (l.M != 1 || l.N < 1 || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
     if (w4::gemv_lds_bytes(1, l.K) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
     if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31) return W4_ERR_SHAPE;
@@ -440,14 +441,14 @@ w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* 
   // by earlier stages (it is read once no value of it is unwritten).
   std::vector<int> wait_x(count, 0), fill(count, 0);
   for (int64_t i = 0; i < count; ++i) {
-    const w4_chain_linear& a = linears[i];
+    const Desc& a = linears[i];
     const size_t yb = 2 * (size_t)a.N;
     const uintptr_t y0 = reinterpret_cast<uintptr_t>(a.y) & ~(uintptr_t)127;
     const size_t ylines = ((reinterpret_cast<uintptr_t>(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
     for (int64_t j = 0; j < count; ++j) {
-      const w4_chain_linear& b = linears[j];
+      const Desc& b = linears[j];
       if (overlaps(a.y, yb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
-          overlaps(a.y, yb, b.d_packed, 4 * w4_scale_count(b.N, b.K)))
+          overlaps(a.y, yb, b.d_packed, (s16 ? 2 : 4) * w4_scale_count(b.N, b.K)))
         return W4_ERR_ARG;
       if (j != i && overlaps(a.y, yb, b.y, 2 * (size_t)b.N)) return W4_ERR_ARG;
       if (b.stage <= a.stage && overlaps(reinterpret_cast<const void*>(y0), ylines, b.x, 2 * (size_t)b.K))
@@ -502,7 +503,7 @@ w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* 
     }
     for (size_t t = first; t < order.size(); ++t) {
       const int64_t src = order[t];
-      const w4_chain_linear& l = linears[src];
+      const Desc& l = linears[src];
       w4::ChainLinear& c = tab[t];
       c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, 1, (int)l.K, (int)l.N, 0};
       c.item0 = (int)items;
@@ -524,7 +525,7 @@ w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* 
   int dev = 0, cus = 0, per_cu = 0;
   if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
   if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_status(e);
-  if (hipError_t e = w4::chain_blocks_per_cu(ci, lds, &per_cu)) return hip_status(e);
+  if (hipError_t e = w4::chain_blocks_per_cu(ci, s16, lds, &per_cu)) return hip_status(e);
   if (per_cu < 1 || cus < 1) return hip_status(hipErrorInvalidConfiguration);
   const int64_t resident = (int64_t)per_cu * cus;
   int64_t blocks = resident < 2 * (int64_t)cus ? resident : 2 * (int64_t)cus;
@@ -546,15 +547,30 @@ w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* 
   plan->lds_bytes = (int32_t)lds;
   plan->rows_per_item = R;
   plan->waves_per_block = NW;
+  plan->scale_bytes = s16 ? 2 : 4;
+  plan->reserved = 0;
   return W4_OK;
+}
+}  // namespace
+}  // extern "C++"
+
+w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace, size_t workspace_bytes,
+                           w4_chain_plan* plan, hipStream_t stream) {
+  return chain_prepare(linears, count, workspace, workspace_bytes, plan, false, stream);
+}
+
+w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count, void* workspace,
+                               size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream) {
+  return chain_prepare(linears, count, workspace, workspace_bytes, plan, true, stream);
 }
 
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream) {
   if (!plan || !plan->workspace) return W4_ERR_NULL;
   if (plan->config < 0 || plan->config >= w4::chain_num_cfgs() || plan->blocks < 0) return W4_ERR_ARG;
+  if (plan->scale_bytes != 2 && plan->scale_bytes != 4) return W4_ERR_ARG;
   if (plan->blocks == 0) return W4_OK;
-  return hip_status(w4::launch_linear_chain(plan->workspace, plan->linears, plan->items, plan->config, plan->blocks,
-                                            (size_t)plan->lds_bytes, stream));
+  return hip_status(w4::launch_linear_chain(plan->workspace, plan->linears, plan->items, plan->config,
+                                            plan->scale_bytes == 2, plan->blocks, (size_t)plan->lds_bytes, stream));
 }
 
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream) {

@@ -811,7 +811,7 @@ struct ChainGate {
 
 // lin: the table (linears + 1 entries, the last a sentinel); hdr: the
 // workspace header's error word.
-template <int R, int NW>
+template <int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear* __restrict__ lin, uint32_t* hdr,
                                                                int items) {
   const int P = gridDim.x;
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
     const LinearDesc& D = lin[li].desc;
     const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage, hdr};
     prev_stage = lin[li].stage;
-    gemv_body<1, R, NW, false, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
+    gemv_body<1, R, NW, S16, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
     staged = D.x;
     staged_k = D.K;
     i += P;
@@ -1108,18 +1108,32 @@ namespace {
 constexpr int kChainCfgs[][2] = {{1, 4}, {1, 8}, {2, 4}, {2, 2}, {1, 2}, {4, 4}};
 constexpr int kNumChainCfgs = sizeof(kChainCfgs) / sizeof(kChainCfgs[0]);
 
-template <int I>
+template <int I, bool S16>
 const void* chain_kernel_ptr() {
-  return reinterpret_cast<const void*>(&linear_chain_kernel<kChainCfgs[I][0], kChainCfgs[I][1]>);
+  return reinterpret_cast<const void*>(&linear_chain_kernel<kChainCfgs[I][0], kChainCfgs[I][1], S16>);
 }
+template <bool S16>
 const void* chain_kernel(int ci) {
   switch (ci) {
-    case 0: return chain_kernel_ptr<0>();
-    case 1: return chain_kernel_ptr<1>();
-    case 2: return chain_kernel_ptr<2>();
-    case 3: return chain_kernel_ptr<3>();
-    case 4: return chain_kernel_ptr<4>();
-    default: return chain_kernel_ptr<5>();
+    case 0: return chain_kernel_ptr<0, S16>();
+    case 1: return chain_kernel_ptr<1, S16>();
+    case 2: return chain_kernel_ptr<2, S16>();
+    case 3: return chain_kernel_ptr<3, S16>();
+    case 4: return chain_kernel_ptr<4, S16>();
+    default: return chain_kernel_ptr<5, S16>();
+  }
+}
+template <bool S16>
+void launch_chain_cfg(int ci, int blocks, size_t lds, hipStream_t stream, const ChainLinear* lin, uint32_t* hdr,
+                      int items) {
+  switch (ci) {
+#define W4_CHAIN(i)                                                                      \
+  case i:                                                                                \
+    linear_chain_kernel<kChainCfgs[i][0], kChainCfgs[i][1], S16>                         \
+        <<<blocks, kChainCfgs[i][1] * 64, lds, stream>>>(lin, hdr, items);               \
+    break;
+    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4) W4_CHAIN(5)
+#undef W4_CHAIN
   }
 }
 }  // namespace
@@ -1148,27 +1162,20 @@ int chain_choose_cfg(int kmax, double stage_bytes) {
   return stage_bytes < 24e6 ? 1 : 2;
 }
 
-hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, chain_kernel(ci), kChainCfgs[ci][1] * 64, lds);
+hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, s16 ? chain_kernel<true>(ci) : chain_kernel<false>(ci),
+                                                      kChainCfgs[ci][1] * 64, lds);
 }
 
-hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, int blocks, size_t lds,
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds,
                                hipStream_t stream) {
+  if (ci < 0 || ci >= kNumChainCfgs) return hipErrorInvalidValue;
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
   const ChainLinear* lin = reinterpret_cast<const ChainLinear*>(w + sizeof(ChainHeader));
   chain_fill_kernel<<<linears, 256, 0, stream>>>(lin);
-  switch (ci) {
-#define W4_CHAIN(i)                                                                      \
-  case i:                                                                                \
-    linear_chain_kernel<kChainCfgs[i][0], kChainCfgs[i][1]>                              \
-        <<<blocks, kChainCfgs[i][1] * 64, lds, stream>>>(lin, hdr, items);               \
-    break;
-    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4) W4_CHAIN(5)
-#undef W4_CHAIN
-    default:
-      return hipErrorInvalidValue;
-  }
+  if (s16) launch_chain_cfg<true>(ci, blocks, lds, stream, lin, hdr, items);
+  else launch_chain_cfg<false>(ci, blocks, lds, stream, lin, hdr, items);
   return hipGetLastError();
 }
 

@@ -74,10 +74,11 @@ void chain_cfg(int ci, int* R, int* NW);
 // stage_bytes of codes on average (W4_CHAIN_CFG "R,NW" overrides; -1 if it
 // names no compiled configuration).
 int chain_choose_cfg(int kmax, double stage_bytes);
-// Co-resident blocks per CU of configuration ci with `lds` bytes of dynamic LDS.
-hipError_t chain_blocks_per_cu(int ci, size_t lds, int* blocks);
+// Co-resident blocks per CU of configuration ci (s16: bf16 scales) with
+// `lds` bytes of dynamic LDS.
+hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int* blocks);
 // The fill launch, then the chain launch.
-hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, int blocks, size_t lds,
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds,
                                hipStream_t stream);
 
 // s16: scales are bf16 bit patterns (uint16_t) instead of fp32.

@@ -263,16 +263,33 @@ typedef struct w4_chain_linear {
   int64_t stage;           /* 0, 1, 2 ... non-decreasing, steps of 0 or 1  */
 } w4_chain_linear;
 
-/* Filled by w4_chain_prepare; read by w4_chain_run (treat as opaque). */
+/* The same with 16-bit scales (bf16 bit patterns, as the *_s16 entry points
+ * store them), for w4_chain_prepare_s16. */
+typedef struct w4_chain_linear_s16 {
+  const uint16_t* x;        /* bf16 [1][K]                                  */
+  int64_t M;                /* must be 1                                    */
+  int64_t K;
+  const uint8_t* q_packed;  /* native codes of the N x K W                  */
+  const uint16_t* d_packed; /* native bf16 scales                           */
+  int64_t N;
+  uint16_t* y;              /* bf16 [1][N]                                  */
+  int64_t stage;
+} w4_chain_linear_s16;
+
+/* Filled by w4_chain_prepare(_s16); read by w4_chain_run (treat as opaque). */
 typedef struct w4_chain_plan {
   void* workspace;
   int32_t linears, stages, items, blocks;
   int32_t config, lds_bytes, rows_per_item, waves_per_block;
+  int32_t scale_bytes, reserved;
 } w4_chain_plan;
 
 size_t w4_chain_workspace_bytes(int64_t count);
 w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace,
                            size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
+/* w4_chain_prepare for linears with 16-bit scales (same contract). */
+w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count, void* workspace,
+                               size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream);
 

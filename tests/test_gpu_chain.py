@@ -239,3 +239,60 @@ def test_chain_error_flag_is_sticky_until_prepare(w4, gpu, monkeypatch):
     assert plan.error() == 0
     cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
     _check_pass(w4, records, cfg, monkeypatch, "after prepare")
+
+
+def test_chain_16bit_scales(w4, gpu, monkeypatch):
+    """The chained pass with bf16 scales: bitwise equal to per-stage batched
+    launches with 16-bit scales in the same configuration, and within tolerance
+    of the oracle's 16-bit-scale quantization, over two passes with new inputs."""
+    _say("chain with 16-bit scales: 2 layers + ragged side linears")
+    x0 = workloads.random_activations(1, 512, seed=9, device=gpu)
+    stages, records = [], []
+
+    def add(st, name, N, K, x, wseed):
+        W = workloads.random_weight(N, K, std=0.02, seed=wseed)
+        q, d = w4.quantize_rtn(torch.from_numpy(W).to(gpu), scale_dtype=torch.bfloat16)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=gpu)
+        st.append((x, q, d, N, y))
+        records.append((name, len(stages), W, x, q, d, N, y))
+        return y
+
+    x = x0
+    for layer in range(2):
+        s = 500 + 10 * layer
+        st = []
+        yq = add(st, f"L{layer}.q", 768, 512, x, s)
+        add(st, f"L{layer}.k", 256, 512, x, s + 1)
+        stages.append(st)
+        st = []
+        yo = add(st, f"L{layer}.o", 512, 768, yq, s + 2)
+        if layer == 0:
+            add(st, "side.ragged", 77, 384, workloads.random_activations(1, 384, seed=11, device=gpu), s + 7)
+        stages.append(st)
+        st = []
+        yg = add(st, f"L{layer}.gate", 1408, 512, yo, s + 3)
+        add(st, f"L{layer}.up", 1408, 512, yo, s + 4)
+        stages.append(st)
+        st = []
+        x = add(st, f"L{layer}.down", 512, 1408, yg, s + 5)
+        stages.append(st)
+    plan = w4.chain_prepare(stages)
+    assert plan.info["scale_bytes"] == 2
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    for rep in range(2):
+        x0.copy_(workloads.random_activations(1, 512, seed=90 + rep, device=gpu))
+        plan.run()
+        assert plan.error() == 0
+        torch.cuda.synchronize()
+        monkeypatch.setenv("W4_GEMV_CFG", cfg)
+        for st_i in range(len(stages)):
+            recs = [r for r in records if r[1] == st_i]
+            outs = [torch.empty_like(r[7]) for r in recs]
+            w4.linear_batched([(r[3], r[4], r[5], r[6], o) for r, o in zip(recs, outs)], path="gemv")
+            for r, o in zip(recs, outs):
+                assert torch.equal(r[7].view(torch.int16), o.view(torch.int16)), f"pass {rep} {r[0]}: chain != batched"
+        monkeypatch.delenv("W4_GEMV_CFG")
+        for name, _, W, xin, _, _, _, y in records:
+            q_ref, d_ref = oracle.rtn_quantize_ref(W, "bf16")
+            y_ref, absdot = oracle.w4_linear_ref(_bits(xin), q_ref, d_ref)
+            check_y(y, y_ref, absdot, f"s16 chain pass {rep} {name}")
