@@ -171,6 +171,14 @@ def test_chain_validation(w4):
     assert prep([lin(0, 0, N=64), lin(1, 1, x=FAKE + 0x30000, K=256)]) == ERR_ARG
     # workspace too small
     assert prep([lin(0, 0), lin(1, 1)], nbytes=64) == ERR_ARG
+    # the 16-bit-scale variant checks the same (its descriptors have the same layout)
+    arr = (C * 2)(lin(0, 0), lin(1, 2))
+    assert lib.w4_chain_prepare_s16(arr, 2, ws, n, ctypes.byref(plan), None) == ERR_ARG
+    arr = (C * 1)(lin(0, 0, M=2))
+    assert lib.w4_chain_prepare_s16(arr, 1, ws, n, ctypes.byref(plan), None) == ERR_SHAPE
+    # an output over 16-bit scales (32 x 256: 128 native scale slots of 2 bytes)
+    arr = (C * 2)(lin(0, 0), lin(1, 1, y=FAKE + 0x20000 + 64))
+    assert lib.w4_chain_prepare_s16(arr, 2, ws, n, ctypes.byref(plan), None) == ERR_ARG
 
 
 def test_s16_validation(w4):
