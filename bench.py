@@ -7,9 +7,12 @@ the 2 x C weight copies is multiplied once at M = 1 (C copies, > 2x the 256 MB
 Infinity Cache, so every step streams from HBM).  Steps are replayed from one
 HIP graph; the timed region is bracketed by synchronisations and measured with
 events on the replay stream.  Also reported in the same line: the same pass at
-M = 8 (verifying 7 drafted tokens + 1), quantization throughput, 27B- and
-70B-class layer stacks as equivalent decode tokens/s, the roofline of the
-dominant kernel, and the CPU oracle timed on a bounded sample.
+M = 8 (verifying 7 drafted tokens + 1), quantization throughput, 4B-, 27B- and
+70B-class layer stacks in several launch modes (one launch per matrix, per
+shared-input stage, per layer, and the whole pass as one chained launch) with
+the equivalent decode tokens/s of the fastest mode that keeps a layer's
+dependencies, the roofline of the dominant kernel, and the CPU oracle timed on
+a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 4b,27b,70b|none] [--no-cpu]
 """
@@ -754,7 +757,7 @@ def main():
                     help="only time both linear kernels at M = 1..4, 8, 16 (profiling runs)")
     ap.add_argument("--stack-ms", default="", help="comma list: only these M for the stacks (profiling runs)")
     ap.add_argument("--stack-modes", default="",
-                    help="comma list of per_call, fused_shared_input, layer_batched (profiling runs)")
+                    help="comma list of per_call, fused_shared_input, layer_batched, chained (profiling runs)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run the plain copy kernel on this many MiB (counter calibration)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
