@@ -561,9 +561,10 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
     }
     if constexpr (Gate::kActive) {
       // The weights do not depend on earlier stages; x may still be being
-      // written by them.  Wait until a sample of x is written, then stage all
-      // of it (coherent loads), checking every value, and start over if any
-      // is still unwritten.
+      // written by them.  At the block's first item of a stage, wait until a
+      // sample of x is written; then stage all of x (coherent loads),
+      // checking every value, and poll and start over while any is still
+      // unwritten.
       if (gate.reuse) {
         // the previous item of this block staged the same x (and found it written)
       } else if (gate.wait_x) {
