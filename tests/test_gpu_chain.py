@@ -128,12 +128,17 @@ def test_chain_graph_replays(w4, gpu, monkeypatch):
         _check_pass(w4, records, cfg, monkeypatch, f"graph replay {rep}")
 
 
-def test_chain_full_size_27b_layers(w4, gpu, monkeypatch):
-    """Two 27B-class decoder layers at their real shapes (hidden 5120, q 6144,
-    k/v 1024, ffn 17408): bitwise against per-stage batched launches; oracle on
-    sampled output rows."""
-    _say("chain 27B-class: 2 layers at full size")
-    hidden, nq, nkv, ffn = 5120, 6144, 1024, 17408
+FULL_SIZE = {"27b": (5120, 6144, 1024, 17408, 0.015), "70b": (8192, 8192, 1024, 28672, 0.01)}
+
+
+@pytest.mark.parametrize("size", sorted(FULL_SIZE))
+def test_chain_full_size_layers(w4, gpu, size, monkeypatch):
+    """Two decoder layers at their real shapes (27B class: hidden 5120, q 6144,
+    k/v 1024, ffn 17408; 70B class: hidden 8192, q 8192, k/v 1024, ffn 28672,
+    the largest x a chain stages): bitwise against per-stage batched launches;
+    oracle on sampled output rows."""
+    _say(f"chain {size}-class: 2 layers at full size")
+    hidden, nq, nkv, ffn, std = FULL_SIZE[size]
     x0 = workloads.random_activations(1, hidden, seed=3, device=gpu)
     stages, records = [], []
     x = x0
@@ -141,7 +146,7 @@ def test_chain_full_size_27b_layers(w4, gpu, monkeypatch):
     for layer in range(2):
         def mk(N, K, xin, name, st):
             W = torch.randn((N, K), device=gpu, generator=torch.Generator(gpu).manual_seed(100 * layer + len(records)))
-            W.mul_(0.015)
+            W.mul_(std)
             q, d = w4.quantize_rtn(W)
             rows = np.sort(rng.choice(N, size=24, replace=False))
             W_rows = W.index_select(0, torch.as_tensor(rows, device=gpu)).cpu().numpy()
@@ -181,7 +186,7 @@ def test_chain_full_size_27b_layers(w4, gpu, monkeypatch):
     for name, _, rows, W_rows, xin, _, _, _, y in records:
         q_ref, d_ref = oracle.rtn_quantize_ref(W_rows)
         y_ref, absdot = oracle.w4_linear_ref(_bits(xin), q_ref, d_ref)
-        check_y(y[:, rows], y_ref, absdot, f"27B chain {name} (24 sampled rows)")
+        check_y(y[:, rows], y_ref, absdot, f"{size} chain {name} (24 sampled rows)")
 
 
 def test_chain_rejects_bad_chains(w4, gpu):
