@@ -13,7 +13,7 @@ Qwen3.5-4B quantization study, section 2 ("what each method fixed"):
   separate clipping search; s_j is not restricted to powers of two and is
   distinct from the group scale d.
 
-Readings where the pages are silent (each one also listed in the design doc):
+Readings where the pages are silent:
 
 * "proportional to": the constant is fixed by giving the scales a geometric
   mean of 1 (channels with mean |x_j| = 0 are treated as 1e-30);

@@ -26,7 +26,7 @@ generative pre-trained transformers", 2022), restated here:
   remaining columns that minimise (w - w_orig)^T H' (w - w_orig) given every
   column fixed so far -- the property tests/pins.py checks by brute force.
 
-Readings where the pages and the paper leave a step open (also in the design doc):
+Readings where the pages and the paper leave a step open:
 
 * the group's scale is taken when the group starts, from its current
   (already corrected) weights, by the RTN rule d = fl32(max |fl32(w)| / 7);

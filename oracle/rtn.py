@@ -14,7 +14,7 @@ table fixes RTN at group size 128 with a symmetric range taken from the
 group's min/max and no clipping-ratio search, and notes RTN uses no
 calibration input.
 
-Readings where the pages are silent (each one also listed in the design doc):
+Readings where the pages are silent:
 
 * range and scale: a = max |w| over the group, d = fl32(a / 7) (symmetric
   min/max; the largest magnitude maps to code +-7);
