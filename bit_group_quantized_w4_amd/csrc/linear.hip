@@ -561,33 +561,34 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
     }
     if constexpr (Gate::kActive) {
       // The weights do not depend on earlier stages; x may still be being
-      // written by them.  At the block's first item of a stage, wait until a
-      // sample of x is written; then stage all of x (coherent loads),
-      // checking every value, and poll and start over while any is still
-      // unwritten.
-      if (gate.reuse) {
-        // the previous item of this block staged the same x (and found it written)
-      } else if (gate.wait_x) {
-        if (!gate.same_stage) gate.wait_sample(rx, K);
+      // written by them.  Each wavefront stages only its own range of x (the
+      // groups of its quads) and waits only for that range: at the block's
+      // first item of a stage it polls a sample of the range until it is
+      // written; then it stages the range (coherent loads), checking every
+      // value, and polls and starts over while any is still unwritten.  No
+      // block barrier follows: a wavefront reads back only what it staged.
+      if (!gate.reuse) {  // else the block's previous item staged this x (and found it written)
+        const int e0 = 16 * w.j0, e1 = 16 * w.j1;  // elements (group, quarter) of this wavefront's quads
+        const uint32_t xb1 = min(1024u * w.j1, (uint32_t)K * 2u);  // its bytes of x: [1024 j0, xb1)
+        if (gate.wait_x && !gate.same_stage) gate.wait_sample(rx, 1024u * w.j0, xb1);
         for (uint32_t t = 0;; ++t) {
           bool unwritten = false;
-          for (int e = threadIdx.x; e < total; e += NW * 64) {
+          for (int e = e0 + lane; e < e1; e += 64) {
             uint4 tt[4];
+            if (gate.wait_x) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tt[i] = bload<Gate::kCoherent>(rx, x_off(e) + 64u * i);
-            unwritten |= Gate::unwritten(tt);
+              for (int i = 0; i < 4; ++i) tt[i] = bload<Gate::kCoherent>(rx, x_off(e) + 64u * i);
+              unwritten |= Gate::unwritten(tt);
+            } else {
+              load_x(x_off(e), tt);
+            }
             store_x(e, tt);
           }
-          if (!__syncthreads_or(unwritten) || gate.give_up(t)) break;
-          // poll a sample of x before loading all of it again
-          gate.wait_sample(rx, K);
+          if (!__any(unwritten) || gate.give_up(t)) break;
+          // poll a sample of the range before loading all of it again
+          gate.wait_sample(rx, 1024u * w.j0, xb1);
         }
-      } else {
-        for (int e = threadIdx.x; e < total; e += NW * 64) {
-          uint4 tt[4];
-          load_x(x_off(e), tt);
-          store_x(e, tt);
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's LDS writes land before its reads
       }
     } else {
       // Consume x here, before the branches, so the loads are not sunk into
@@ -607,7 +608,7 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
       }
     }
   }
-  __syncthreads();
+  if constexpr (!Gate::kActive) __syncthreads();
 
   const UnpackConsts uc = unpack_consts();
 
@@ -784,29 +785,27 @@ struct ChainGate {
       __builtin_amdgcn_s_sleep(kChainPollSleep);
       return false;
     }
-    if (threadIdx.x == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
-  // Wavefront 0 polls four 16-byte chunks spread over x (64 bytes: polls
-  // compete with the producers' last reads, so they are kept small) until
-  // none is unwritten; the block then proceeds together.
-  __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, int K) const {
-    if (threadIdx.x < 64) {
-      const uint32_t chunks = (uint32_t)K / 8u;
-      const uint32_t off = threadIdx.x < 4 ? (uint32_t)(((uint64_t)threadIdx.x * chunks) / 4u) * 16u : kOobX;
-      for (uint32_t t = 0;; ++t) {
-        const uint4 v = bload<kCoherent>(rx, off);
-        const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
-        if (!__any(u)) break;
-        if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
-                                                                         __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-          if (threadIdx.x == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(kChainPollSleep);
+  // The calling wavefront polls the last 16-byte chunk of bytes [b0, b1) of
+  // x (a block's four wavefronts poll 64 bytes in all: polls compete with
+  // the producers' last reads, so they are kept small) until it is written.
+  // An empty range, or one past the end of x, reads zeros.
+  __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, uint32_t b0, uint32_t b1) const {
+    const int lane = threadIdx.x & 63;
+    const uint32_t off = (lane == 0 && b1 > b0) ? b1 - 16u : kOobX;
+    for (uint32_t t = 0;; ++t) {
+      const uint4 v = bload<kCoherent>(rx, off);
+      const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
+      if (!__any(u)) break;
+      if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+        if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
+      __builtin_amdgcn_s_sleep(kChainPollSleep);
     }
-    __syncthreads();
   }
 };
 
