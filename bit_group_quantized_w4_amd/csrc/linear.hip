@@ -737,8 +737,8 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
 // Chained launch of dependent M = 1 linears (layout and protocol in
 // w4_launch.h).  Each item runs the dot2 body above with a gate: the item's
 // weight prologue is issued first (weights never depend on earlier stages),
-// then, when its x is produced by earlier stages, the block waits until every
-// value of x is written, then stages x.  Per item the arithmetic is exactly
+// then, when its x is produced by earlier stages, each wavefront waits until
+// every value of its own range of x is written, and stages that range.  Per item the arithmetic is exactly
 // the batched dot2 kernel's with the same (R, NW), so results are identical
 // bits (NaN outputs aside: the unwritten marker is never written).
 //

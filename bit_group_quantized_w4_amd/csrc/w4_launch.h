@@ -43,8 +43,8 @@ struct BatchArgs {
 // (R-row-block panels) of every stage in order; block b takes items b, b+P,
 // b+2P, ...  Before the pass a fill launch marks every output that a later
 // linear reads with an unwritten-value pattern; a block about to stage such
-// an x first issues its item's weight loads, then waits until no value of x
-// is unwritten.  Waits only ever look at outputs of earlier items, which
+// an x first issues its item's weight loads, then each of its wavefronts
+// waits until no value of its own range of x is unwritten.  Waits only ever look at outputs of earlier items, which
 // co-resident blocks hold, so every wait ends; it is also bounded (a timeout
 // sets `error` and lets the launch drain).
 // ---------------------------------------------------------------------------
