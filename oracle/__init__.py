@@ -18,6 +18,9 @@ What it computes (sources are the public pages this project is built from):
 * ``w4_linear_ref`` -- y = W_hat x from the same section 1 (the 2560x9216 FFN
   example) with 4-bit weights and BF16 inputs (section 2 settings table), in
   fp64.
+* ``admissible`` -- when an output counts as correct: within 2e-3 of
+  sum |w_hat x| (plus 1e-6) of the exact value for fp32 outputs, and the
+  nearest-even bf16 of such a value for bf16 outputs.
 * ``pack_canonical`` / ``unpack_canonical`` -- the canonical two-codes-per-byte
   byte order used to compare codes bit for bit.
 * ``awq_search_ref`` and its steps -- activation-aware channel scaling before
@@ -40,13 +43,17 @@ from .gptq import gptq_factor_ref, gptq_hessian_ref, gptq_quantize_ref, gptq_ref
 from .linear import dequantize_ref, w4_linear_ref
 from .packing import pack_canonical, unpack_canonical
 from .rtn import GROUP, NAN_BITS, QMAX, QMIN, rtn_quantize_ref
+from .tolerance import ABS_TOL, REL_TOL, admissible, rounding_interval, worst_ratio
 
 __all__ = [
+    "ABS_TOL",
     "ALPHAS",
     "GROUP",
     "NAN_BITS",
     "QMAX",
     "QMIN",
+    "REL_TOL",
+    "admissible",
     "awq_output_error_ref",
     "awq_search_ref",
     "candidate_scales_ref",
@@ -62,7 +69,9 @@ __all__ = [
     "gptq_ref",
     "output_error_ref",
     "pack_canonical",
+    "rounding_interval",
     "rtn_quantize_ref",
     "unpack_canonical",
     "w4_linear_ref",
+    "worst_ratio",
 ]

@@ -10,6 +10,11 @@ M = K + 1 rows in one pass (27B quantization-and-drafter ladder, stage 2).
 Everything is widened to fp64 first: d * q is exact in fp64 (a 24-bit
 significand times an integer below 16), bf16 -> fp64 is exact, and the
 product is an ordinary float64 matrix product.
+
+Non-finite activations (the pages are silent): a NaN or infinity anywhere in
+row m of x makes every output of that row NaN -- the row is poisoned, as a
+non-finite weight group poisons the outputs that use it -- instead of the
+mix of +-inf and NaN that IEEE arithmetic of the sum would give.
 """
 
 import numpy as np
@@ -37,12 +42,17 @@ def w4_linear_ref(x_bits, q, d):
     x_bits: uint16 [M, K] bf16 bit patterns; q: int8 [N, K]; d: float32 [N, K/128]
     (or uint16 bf16 bit patterns for 16-bit scales).
     Returns (y, absdot), both float64 [M, N]; absdot = sum_k |x[m,k] * W_hat[n,k]|
-    is the scale the output tolerance is stated against.
+    is the scale the output tolerance is stated against (oracle/tolerance.py).
+    Rows of x holding a NaN or an infinity give NaN in y and absdot.
     """
     x = bf16_bits_to_f64(x_bits)
     w_hat = dequantize_ref(q, d)
     if x.ndim != 2 or x.shape[1] != w_hat.shape[1]:
         raise ValueError("x must be [M, K]")
+    poisoned = ~np.isfinite(x).all(axis=1)
+    x = np.where(poisoned[:, None], 0.0, x)
     y = x @ w_hat.T
     absdot = np.abs(x) @ np.abs(w_hat).T
+    y[poisoned, :] = np.nan
+    absdot[poisoned, :] = np.nan
     return y, absdot

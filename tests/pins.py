@@ -623,3 +623,138 @@ def check_gptq16_identity_hessian_is_rtn16(gptq16):
     quantize16 = lambda Wm: gptq16(Wm, xb)
     check_scale16_exact(quantize16, W)
     check_codes_bruteforce(widened(quantize16), W)
+
+
+# ----------------------------------------------------------------------------
+# when an output counts as correct (oracle/tolerance.py)
+# ----------------------------------------------------------------------------
+
+def _fmt_params(fmt):
+    # (bits of significand kept, exponent-field shift into a binary32 pattern)
+    return (8, 16) if fmt == "bf16" else (24, 0)
+
+
+def pattern_value(bits, fmt):
+    """Exact value (Fraction) of a finite bf16 / fp32 bit pattern."""
+    _, shift = _fmt_params(fmt)
+    v = np.array([int(bits) << shift], dtype=np.uint32).view(np.float32)[0]
+    return Fraction(float(v))
+
+
+def nearest_pattern(fr, fmt):
+    """Bit pattern of the finite value nearest to the rational fr, ties to the even
+    pattern (exact search over the patterns next to fr's truncation).  Values at or
+    past halfway from the largest finite value to 2^128 give the infinity pattern."""
+    _, shift = _fmt_params(fmt)
+    sign = 0x8000 if fmt == "bf16" else 0x80000000
+    inf = 0x7F80 if fmt == "bf16" else 0x7F800000
+    mag = abs(fr)
+    top = pattern_value(inf - 1, fmt)
+    s = sign if fr < 0 else 0
+    if mag >= (top + Fraction(2) ** 128) / 2:
+        return s | inf
+    t = int(np.array([abs(float(fr))], dtype=np.float32).view(np.uint32)[0]) >> shift  # near fr
+    best = None
+    for c in range(max(0, t - 2), min(inf - 1, t + 2) + 1):
+        key = (abs(pattern_value(c, fmt) - mag), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return s | best[1]
+
+
+def _ordered(bits, fmt):
+    """Bit pattern -> an integer that orders patterns by value (for finite and +-inf)."""
+    sign = 0x8000 if fmt == "bf16" else 0x80000000
+    return -(bits & (sign - 1)) if bits & sign else bits
+
+
+def check_admissible(admissible, fmt, seed=0, cases=300):
+    """Brute force: the correct outputs for y_ref, tol are exactly the patterns from
+    nearest(y_ref - tol) to nearest(y_ref + tol) in value order (rounding is
+    monotone), computed with exact rationals; plus NaN and infinity cases."""
+    rng = np.random.default_rng(seed)
+    dtype = np.uint16 if fmt == "bf16" else np.uint32
+    p, _ = _fmt_params(fmt)
+    for _ in range(cases):
+        # |y_ref| in [2^(e-1), 2^e), with e large enough that the absolute term
+        # (1e-6) stays below a step of the format there
+        e = int(rng.integers(-10 if fmt == "bf16" else 5, 40))
+        y_ref = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.5, 1.0)) * 2.0 ** e
+        # tolerances from a fraction of one step of the format to a few dozen steps
+        step = 2.0 ** (e - p + 1)
+        absdot = abs(float(rng.uniform(0, 1))) * step * float(rng.choice([0.01, 0.3, 1.0, 8.0, 40.0])) / 2e-3
+        tol = 2e-3 * absdot + 1e-6
+        lo_b = nearest_pattern(Fraction(y_ref) - Fraction(tol), fmt)
+        hi_b = nearest_pattern(Fraction(y_ref) + Fraction(tol), fmt)
+        lo, hi = _ordered(lo_b, fmt), _ordered(hi_b, fmt)
+        assert hi - lo < 4096, "test case spans too many patterns"
+        cands = []
+        for o in range(lo - 3, hi + 4):
+            b = o if o >= 0 else (-o) | (0x8000 if fmt == "bf16" else 0x80000000)
+            cands.append((b, lo <= o <= hi))
+        bits = np.array([c[0] for c in cands], dtype=dtype)
+        got = admissible(bits, np.full(len(cands), y_ref), np.full(len(cands), absdot), fmt)
+        want = np.array([c[1] for c in cands])
+        _check(np.array_equal(got, want),
+               f"{fmt}: y_ref={y_ref!r} tol={tol!r}: admissible set differs at "
+               f"{[hex(int(b)) for b, g, w in zip(bits, got, want) if g != w][:4]}")
+    # NaN exactly where the reference is NaN; infinities only past the halfway point
+    inf = 0x7F80 if fmt == "bf16" else 0x7F800000
+    nan = 0x7FC0 if fmt == "bf16" else 0x7FC00000
+    top = float(pattern_value(inf - 1, fmt))
+    half = (top + 2.0 ** 128) / 2
+    bits = np.array([nan, nan, inf, inf, inf - 1, inf | (0x8000 if fmt == "bf16" else 0x80000000)], dtype=dtype)
+    y_ref = np.array([np.nan, 1.0, half * (1 + 1e-9), top, top, -half * (1 + 1e-9)])
+    got = admissible(bits, y_ref, np.zeros(6), fmt)
+    _check(list(got) == [True, False, True, False, True, True], f"{fmt}: special values {list(got)}")
+
+
+def check_exact_rounding_is_admissible(admissible, seed=0):
+    """A bf16 output that is the exactly rounded y_ref is correct even where the
+    bound is tighter than half a bf16 step (|y| close to sum |w_hat x|)."""
+    rng = np.random.default_rng(seed)
+    y_ref = rng.uniform(0.5, 4.0, 200).astype(np.float32).astype(np.float64)
+    bits = np.array([nearest_pattern(Fraction(float(v)), "bf16") for v in y_ref], dtype=np.uint16)
+    got = admissible(bits, y_ref, np.abs(y_ref), "bf16")  # absdot = |y|: a same-sign row
+    _check(bool(np.all(got)), "an exactly rounded bf16 output is rejected")
+
+
+def check_output_error_exact(output_error, seed=0):
+    """mean((x W_hat^T - x W^T)^2) against exact rationals on a toy."""
+    rng = np.random.default_rng(seed)
+    N, K, T = 3, 256, 2
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    q = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    d = (rng.uniform(0.001, 0.02, (N, K // 128))).astype(np.float32)
+    xf = (rng.standard_normal((T, K))).astype(np.float32)
+    x_bits = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    xv = bf16_values(x_bits)
+    total = Fraction(0)
+    for t in range(T):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(xv[t][k]) * (Fraction(float(d[n, k // 128])) * int(q[n, k]) - Fraction(float(W[n, k])))
+            total += acc * acc
+    exact = total / (T * N)
+    got = output_error(W, q, d, x_bits)
+    _check(abs(Fraction(got) - exact) <= exact * Fraction(1, 10 ** 12), f"output error {got!r} != exact {float(exact)!r}")
+
+
+def check_linear_nonfinite_rows(linear, seed=0):
+    """A row of x holding +inf, -inf or NaN gives NaN in every output of that row
+    (even where IEEE arithmetic would give an infinity: all codes nonzero here);
+    the other rows are unaffected (exact rational sums)."""
+    rng = np.random.default_rng(seed)
+    N, K, M = 3, 256, 4
+    q = rng.integers(1, 8, (N, K)).astype(np.int8)
+    d = rng.uniform(0.01, 0.1, (N, K // 128)).astype(np.float32)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[1, 5] = np.inf
+    xf[2, 200] = -np.inf
+    xf[3, 77] = np.nan
+    x_bits = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    y, absdot = linear(x_bits, q, d)
+    _check(bool(np.all(np.isnan(y[1:]))), "a non-finite activation must poison its whole row")
+    _check(bool(np.all(np.isnan(absdot[1:]))), "absdot of a poisoned row must be NaN")
+    check_linear_exact(linear, x_bits[:1], q, d)

@@ -556,3 +556,98 @@ def test_gptq_mutants_are_caught(kind):
     _all_gptq_pins(*_gptq_mutant("none"))
     with pytest.raises((pins.PinFailure, np.linalg.LinAlgError)):
         _all_gptq_pins(*_gptq_mutant(kind))
+
+
+# ----------------------------------------------------------------------------
+# when an output counts as correct; non-finite activations; the output error
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_admissible_bruteforce(fmt):
+    pins.check_admissible(oracle.admissible, fmt)
+
+
+def test_exact_rounding_is_admissible():
+    pins.check_exact_rounding_is_admissible(oracle.admissible)
+
+
+def _admissible_mutant(kind):
+    def admissible(y_bits, y_ref, absdot, fmt):
+        shift = 16 if fmt == "bf16" else 0
+        b = np.asarray(y_bits).astype(np.uint32) << np.uint32(shift)
+        y = b.view(np.float32).astype(np.float64)
+        tol = 2e-3 * np.asarray(absdot) + 1e-6
+        if kind == "plain_bound":  # the bound without the output rounding
+            ok = np.abs(y - y_ref) <= tol
+        else:
+            lo, hi = oracle.rounding_interval(np.asarray(y_bits), fmt)
+            g_up, g_dn = hi - y, y - lo
+            if kind == "whole_step":  # a whole step on either side instead of half
+                lo, hi = y - 2 * g_dn, y + 2 * g_up
+            elif kind == "symmetric_gap":  # the step above used below too (wrong at powers of two)
+                lo = y - g_up
+            ok = (y_ref - tol <= hi) & (y_ref + tol >= lo)
+        return np.where(np.isnan(y_ref), np.isnan(y), ok)
+
+    return admissible
+
+
+@pytest.mark.parametrize("kind", ["plain_bound", "whole_step", "symmetric_gap"])
+def test_admissible_mutants_are_caught(kind):
+    mutant = _admissible_mutant(kind)
+
+    def all_pins(adm):
+        pins.check_admissible(adm, "bf16", cases=300)
+        pins.check_exact_rounding_is_admissible(adm)
+        # powers of two: the step below is half the step above
+        y_ref = np.array([1.0 - 2.0 ** -10, 2.0 - 1.5 * 2.0 ** -8])
+        bits = np.array([0x3F80, 0x4000], dtype=np.uint16)
+        # 1 - 2^-10 rounds to 1.0; 2 - 1.5*2^-8 lies below 2.0's interval [2 - 2^-8, 2 + 2^-7]
+        want = np.array([True, False])
+        got = adm(bits, y_ref, np.zeros(2), "bf16")
+        if not np.array_equal(got, want):
+            raise pins.PinFailure(f"powers of two: {got}")
+
+    all_pins(oracle.admissible)
+    with pytest.raises(pins.PinFailure):
+        all_pins(mutant)
+
+
+def test_output_error_exact():
+    pins.check_output_error_exact(oracle.output_error_ref)
+
+
+@pytest.mark.parametrize("kind", ["f32", "mean_over_rows_only", "scale_group_index"])
+def test_output_error_mutants_are_caught(kind):
+    def output_error(W, q, d, x_bits):
+        X = oracle.bf16_bits_to_f64(x_bits)
+        G = W.shape[1] // 128
+        if kind == "scale_group_index":
+            What = np.asarray(d, np.float64)[:, np.arange(W.shape[1]) % G] * q
+        else:
+            What = (np.asarray(d, np.float64)[:, :, None] * q.reshape(q.shape[0], G, 128)).reshape(q.shape)
+        if kind == "f32":
+            e = (X.astype(np.float32) @ (What - W).astype(np.float32).T).astype(np.float64)
+        else:
+            e = X @ (What - np.asarray(W, np.float64)).T
+        if kind == "mean_over_rows_only":
+            return float(np.mean(np.sum(e ** 2, axis=1)))
+        return float(np.mean(e ** 2))
+
+    with pytest.raises(pins.PinFailure):
+        pins.check_output_error_exact(output_error)
+
+
+def test_nonfinite_activation_rows():
+    pins.check_linear_nonfinite_rows(oracle.w4_linear_ref)
+
+
+def test_nonfinite_activation_ieee_mutant_is_caught():
+    def ieee(x_bits, q, d):  # the plain IEEE sum: +-inf where every code is nonzero
+        x = oracle.bf16_bits_to_f64(x_bits)
+        w = oracle.dequantize_ref(q, d)
+        with np.errstate(invalid="ignore"):
+            return x @ w.T, np.abs(x) @ np.abs(w).T
+
+    with pytest.raises(pins.PinFailure):
+        pins.check_linear_nonfinite_rows(ieee)
