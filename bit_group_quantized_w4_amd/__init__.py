@@ -58,6 +58,10 @@ SIGNATURES = {
     "w4_linear": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP]),
     "w4_linear_ex": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
     "w4_linear_batched": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
+    # fp32 outputs
+    "w4_linear_f32": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
+    "w4_linear_f32_s16": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _INT, _VP]),
+    "w4_linear_batched_f32": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP]),
     "w4_pack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_unpack": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP, _VP]),
     # 16-bit (bf16) scales
@@ -181,26 +185,42 @@ def quantize_rtn(W, out=None, scale_dtype=torch.float32):
     return q, d
 
 
-def linear(x, q, d, N, path="auto", out=None):
-    """y [M, N] bf16 = x [M, K] bf16 times the dequantized weight (native q, d)."""
+OUT_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16):
+    """y [M, N] = x [M, K] bf16 times the dequantized weight (native q, d).
+
+    y is bf16 by default; with out_dtype=torch.float32 (or an fp32 `out`) it is the
+    fp32 value the kernel accumulated, before rounding (the *_f32 entry points)."""
     M, K = x.shape
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
     if y.shape != (M, N):
         raise ValueError("out must be [M, N]")
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
     sd = _scale_dtype(d)
-    fn, name = ((_lib.w4_linear_s16, "w4_linear_s16") if sd == torch.bfloat16 else (_lib.w4_linear_ex, "w4_linear"))
+    if out_dtype == torch.float32:
+        fn, name = ((_lib.w4_linear_f32_s16, "w4_linear_f32_s16") if sd == torch.bfloat16
+                    else (_lib.w4_linear_f32, "w4_linear_f32"))
+    else:
+        fn, name = ((_lib.w4_linear_s16, "w4_linear_s16") if sd == torch.bfloat16
+                    else (_lib.w4_linear_ex, "w4_linear"))
     _check(fn(_dev(x, torch.bfloat16, "x"), M, K, _dev(q, torch.uint8, "q"), _dev(d, sd, "d"), N,
-              _dev(y, torch.bfloat16, "y"), PATHS[path], _stream(x)), name)
+              _dev(y, out_dtype, "y"), PATHS[path], _stream(x)), name)
     return y
 
 
 def linear_batched(items, path="auto"):
     """Several independent linears in one launch.
 
-    items: sequence of (x [M, K] bf16, q, d, N, y [M, N] bf16) with every y
-    preallocated; at most MAX_BATCH items.  Returns the list of y.
+    items: sequence of (x [M, K] bf16, q, d, N, y [M, N]) with every y
+    preallocated; at most MAX_BATCH items.  y is bf16 throughout, or fp32
+    throughout (fp32 scales only: w4_linear_batched_f32).  Returns the list of y.
     """
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
@@ -208,6 +228,9 @@ def linear_batched(items, path="auto"):
     descs = (LinearDesc * max(1, len(items)))()
     stream = None
     sd = _scale_dtype(items[0][2]) if items else torch.float32
+    od = items[0][4].dtype if items else torch.bfloat16
+    if od not in OUT_DTYPES or (od == torch.float32 and sd != torch.float32):
+        raise TypeError("outputs must be bf16, or fp32 with fp32 scales")
     for i, (x, q, d, N, y) in enumerate(items):
         M, K = x.shape
         if y.shape != (M, N):
@@ -215,11 +238,14 @@ def linear_batched(items, path="auto"):
         if _scale_dtype(d) != sd:
             raise TypeError("all items of a batch must use the same scale dtype")
         descs[i] = LinearDesc(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
-                              _dev(d, sd, "d").value, N, _dev(y, torch.bfloat16, "y").value)
+                              _dev(d, sd, "d").value, N, _dev(y, od, "y").value)
         stream = stream or _stream(x)
-    # the fp32 and bf16 descriptor structs have the same layout (pointers and int64s)
-    fn, name = ((_lib.w4_linear_batched_s16, "w4_linear_batched_s16") if sd == torch.bfloat16
-                else (_lib.w4_linear_batched, "w4_linear_batched"))
+    # the descriptor structs of every variant have the same layout (pointers and int64s)
+    if od == torch.float32:
+        fn, name = _lib.w4_linear_batched_f32, "w4_linear_batched_f32"
+    else:
+        fn, name = ((_lib.w4_linear_batched_s16, "w4_linear_batched_s16") if sd == torch.bfloat16
+                    else (_lib.w4_linear_batched, "w4_linear_batched"))
     _check(fn(descs, len(items), PATHS[path], stream), name)
     return [it[4] for it in items]
 
@@ -415,7 +441,7 @@ class W4Linear:
 
 
 __all__ = [
-    "GROUP", "LIB_PATH", "MAX_BATCH", "PATHS", "SCALE_DTYPES", "SIGNATURES", "LinearDesc", "W4Error",
+    "GROUP", "LIB_PATH", "MAX_BATCH", "OUT_DTYPES", "PATHS", "SCALE_DTYPES", "SIGNATURES", "LinearDesc", "W4Error",
     "W4Linear",
     "awq_scales", "channel_absmean", "library", "linear", "linear_awq", "linear_batched",
     "quantize_rtn_scaled", "scale_activations", "sq_error",

@@ -1,4 +1,4 @@
-"""Build libw4.so (and the bench-only copy kernel) in-tree with hipcc for gfx950.
+"""Build libw4.so in-tree with hipcc for gfx950.
 
 Usage: python bit_group_quantized_w4_amd/_build.py   (or __graft_entry__.build()).
 Run it as a script (not with -m): importing the package loads the library,
@@ -18,10 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 
 LIB = os.path.join(PKG, "libw4.so")
-BENCH_LIB = os.path.join(PKG, "libw4_bench.so")
 
 LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip", "gptq.hip"]
-BENCH_SOURCES = ["copy_probe.hip"]
 
 ARCH = "gfx950"
 
@@ -76,14 +74,13 @@ def _compile(sources, out, verbose):
 
 def build(verbose=True):
     _compile(LIB_SOURCES, LIB, verbose)
-    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
     return LIB
 
 
 def built():
-    return os.path.exists(LIB) and os.path.exists(BENCH_LIB)
+    return os.path.exists(LIB)
 
 
 if __name__ == "__main__":
     build(verbose=True)
-    print("built", LIB, BENCH_LIB)
+    print("built", LIB)

@@ -55,12 +55,13 @@ struct LinearArgs {
   const uint8_t* q;
   const void* d;
   int64_t N;
-  uint16_t* y;
+  void* y;
+  size_t ybytes;  // per output element: 2 (bf16) or 4 (fp32)
 };
 
 template <typename Desc>
 LinearArgs args_of(const Desc& l) {
-  return LinearArgs{l.x, l.M, l.K, l.q_packed, l.d_packed, l.N, l.y};
+  return LinearArgs{l.x, l.M, l.K, l.q_packed, l.d_packed, l.N, l.y, sizeof(*l.y)};
 }
 
 // Checks one linear of a call; on success appends it to the batch.
@@ -70,7 +71,7 @@ w4_status check_linear(const LinearArgs& l, w4::BatchArgs& a) {
   // The kernels address codes with 32-bit offsets below 2 GiB and x below 1 GiB.
   if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31 || 2 * (size_t)l.M * l.K > (size_t)1 << 30) return W4_ERR_SHAPE;
   if (!l.x || !l.q || !l.d || !l.y) return W4_ERR_NULL;
-  if (!aligned(l.x, 16) || !aligned(l.q, 16) || !aligned(l.d, 16) || !aligned(l.y, 2)) return W4_ERR_ALIGN;
+  if (!aligned(l.x, 16) || !aligned(l.q, 16) || !aligned(l.d, 16) || !aligned(l.y, l.ybytes)) return W4_ERR_ALIGN;
   w4::LinearDesc& d = a.desc[a.count++];
   d.x = l.x;
   d.q = l.q;
@@ -79,7 +80,7 @@ w4_status check_linear(const LinearArgs& l, w4::BatchArgs& a) {
   d.M = (int)l.M;
   d.K = (int)l.K;
   d.N = (int)l.N;
-  d.pad = 0;
+  d.flags = l.ybytes == 4 ? w4::kOutF32 : 0;
   return W4_OK;
 }
 
@@ -87,14 +88,14 @@ w4_status check_linear(const LinearArgs& l, w4::BatchArgs& a) {
 w4_status check_aliasing(const LinearArgs* l, int count, size_t scale_elem) {
   for (int i = 0; i < count; ++i) {
     if (l[i].M <= 0 || l[i].N <= 0) continue;
-    const size_t yb = 2 * (size_t)l[i].M * l[i].N;
+    const size_t yb = l[i].ybytes * (size_t)l[i].M * l[i].N;
     for (int j = 0; j < count; ++j) {
       if (l[j].M <= 0 || l[j].N <= 0) continue;
       if (overlaps(l[i].y, yb, l[j].x, 2 * (size_t)l[j].M * l[j].K) ||
           overlaps(l[i].y, yb, l[j].q, w4_packed_bytes(l[j].N, l[j].K)) ||
           overlaps(l[i].y, yb, l[j].d, scale_elem * w4_scale_count(l[j].N, l[j].K)))
         return W4_ERR_ARG;
-      if (j != i && overlaps(l[i].y, yb, l[j].y, 2 * (size_t)l[j].M * l[j].N)) return W4_ERR_ARG;
+      if (j != i && overlaps(l[i].y, yb, l[j].y, l[j].ybytes * (size_t)l[j].M * l[j].N)) return W4_ERR_ARG;
     }
   }
   return W4_OK;
@@ -245,6 +246,29 @@ w4_status w4_linear_s16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
   return w4_linear_batched_s16(&l, 1, path, stream);
 }
 
+w4_status w4_linear_batched_f32(const w4_linear_desc_f32* linears, int count, int path, hipStream_t stream) {
+  return linear_batched(linears, count, path, false, stream);
+}
+
+w4_status w4_linear_f32(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed, const float* d_packed,
+                        int64_t N, float* y, int path, hipStream_t stream) {
+  const w4_linear_desc_f32 l = {x, M, K, q_packed, d_packed, N, y};
+  return w4_linear_batched_f32(&l, 1, path, stream);
+}
+
+w4_status w4_linear_f32_s16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                            const uint16_t* d_packed, int64_t N, float* y, int path, hipStream_t stream) {
+  struct {
+    const uint16_t* x;
+    int64_t M, K;
+    const uint8_t* q_packed;
+    const uint16_t* d_packed;
+    int64_t N;
+    float* y;
+  } l = {x, M, K, q_packed, d_packed, N, y};
+  return linear_batched(&l, 1, path, true, stream);
+}
+
 w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
                   uint8_t* q_packed, float* d_packed, hipStream_t stream) {
   return pack(q_canon, d_canon, N, K, q_packed, d_packed, false, stream);
@@ -327,7 +351,7 @@ w4_status w4_scale_activations(const uint16_t* x, int64_t M, int64_t K, const fl
 
 w4_status w4_linear_awq(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed, const float* d_packed,
                         int64_t N, const float* inv_s, uint16_t* y, hipStream_t stream) {
-  const LinearArgs l{x, M, K, q_packed, d_packed, N, y};
+  const LinearArgs l{x, M, K, q_packed, d_packed, N, y, 2};
   w4::BatchArgs a;
   a.count = 0;
   const w4_status st = check_linear(l, a);
@@ -435,28 +459,30 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   }
   // Aliasing.  The launch keeps the eight L2s coherent only for chains that
   // write each byte once and never write a cache line (128 bytes) that the
-  // pass reads before the write: no y overlaps any weights, any other y, or
-  // the line of any x of its own or an earlier stage.  A y read as x by a
-  // later stage is the intended use; such an x must then be written entirely
-  // by earlier stages (it is read once no value of it is unwritten).
+  // pass may read before the write: no y overlaps any other y, and no line
+  // of a y holds any byte of the weights, of an x of its own or an earlier
+  // stage, or of an x of a later stage that does not read this y.  A y read
+  // as x by a later stage is the intended use; such an x must then be
+  // written entirely by earlier stages (it is read once no value of it is
+  // unwritten).
   std::vector<int> wait_x(count, 0), fill(count, 0);
   for (int64_t i = 0; i < count; ++i) {
     const Desc& a = linears[i];
     const size_t yb = 2 * (size_t)a.N;
     const uintptr_t y0 = reinterpret_cast<uintptr_t>(a.y) & ~(uintptr_t)127;
-    const size_t ylines = ((reinterpret_cast<uintptr_t>(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
+    const void* ylines = reinterpret_cast<const void*>(y0);
+    const size_t ylb = ((reinterpret_cast<uintptr_t>(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
     for (int64_t j = 0; j < count; ++j) {
       const Desc& b = linears[j];
-      if (overlaps(a.y, yb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
-          overlaps(a.y, yb, b.d_packed, (s16 ? 2 : 4) * w4_scale_count(b.N, b.K)))
+      if (overlaps(ylines, ylb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
+          overlaps(ylines, ylb, b.d_packed, (s16 ? 2 : 4) * w4_scale_count(b.N, b.K)))
         return W4_ERR_ARG;
       if (j != i && overlaps(a.y, yb, b.y, 2 * (size_t)b.N)) return W4_ERR_ARG;
-      if (b.stage <= a.stage && overlaps(reinterpret_cast<const void*>(y0), ylines, b.x, 2 * (size_t)b.K))
-        return W4_ERR_ARG;
-      if (b.stage > a.stage && overlaps(a.y, yb, b.x, 2 * (size_t)b.K)) {
-        fill[i] = 1;
-        wait_x[j] = 1;
-      }
+      if (!overlaps(ylines, ylb, b.x, 2 * (size_t)b.K)) continue;
+      // b reads a line that a writes: only as a later stage reading a's output
+      if (b.stage <= a.stage || !overlaps(a.y, yb, b.x, 2 * (size_t)b.K)) return W4_ERR_ARG;
+      fill[i] = 1;
+      wait_x[j] = 1;
     }
   }
   for (int64_t j = 0; j < count; ++j) {

@@ -49,6 +49,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Output element i of a linear: fp32 as accumulated, or rounded to bf16.
+__device__ __forceinline__ void store_out(const LinearDesc& D, int64_t i, float v) {
+  if (D.flags & kOutF32)
+    static_cast<float*>(D.y)[i] = v;
+  else
+    static_cast<uint16_t*>(D.y)[i] = f32_to_bf16_rne(v);
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -250,7 +258,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = wk.m0 + 4 * kb + e;
-      if (m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * v[e]);
+      if (m < M) store_out(D, (int64_t)m * N + n, 16.0f * v[e]);
     }
   };
 
@@ -404,7 +412,7 @@ __device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = wk.m0 + 4 * kb + e;
-      if (m < M) D.y[(int64_t)m * N + n] = f32_to_bf16_rne(16.0f * acc[r][e]);
+      if (m < M) store_out(D, (int64_t)m * N + n, 16.0f * acc[r][e]);
     }
   }
 }
@@ -417,9 +425,9 @@ __global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_kernel(const Batc
 
 template <int R, int NWN, bool S16>
 __global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_one(const uint16_t* x, const uint8_t* q,
-                                                                   const void* d, uint16_t* y, int M, int K,
-                                                                   int N) {
-  const LinearDesc D{x, q, d, y, M, K, N, 0};
+                                                                   const void* d, void* y, int M, int K, int N,
+                                                                   int flags) {
+  const LinearDesc D{x, q, d, y, M, K, N, flags};
   mfma_shared_body<R, NWN, S16>(D, locate_one(N, R * NWN, 16));
 }
 
@@ -435,8 +443,8 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs ar
 // kernel-argument fetch before it can issue its first loads.
 template <int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const void* d,
-                                                           uint16_t* y, int M, int K, int N) {
-  const LinearDesc D{x, q, d, y, M, K, N, 0};
+                                                           void* y, int M, int K, int N, int flags) {
+  const LinearDesc D{x, q, d, y, M, K, N, flags};
   mfma_body<R, NW, S16>(D, locate_one(N, R, 16));
 }
 
@@ -456,6 +464,7 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, co
 // No dependency to wait for: x is read as soon as the block starts.
 struct NoGate {
   static constexpr bool kActive = false;
+  static constexpr int parity = 0;
 };
 
 // Gate (kActive, chained launches): the block's weight prologue is issued
@@ -682,12 +691,18 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
       acc[r][mm] = v;
     }
 
-  __shared__ float red[NW][R][MT][16];
+  // A chained block runs item after item with no barrier between them, so its
+  // reduction array alternates between two copies by item parity: a wavefront
+  // can write item i+1's copy while the reducing lanes still read item i's,
+  // and it reaches item i+2 (the same copy) only after item i+1's barrier,
+  // which those lanes pass only once they are done reading.
+  __shared__ float red[Gate::kActive ? 2 : 1][NW][R][MT][16];
+  const int rp = Gate::kActive ? gate.parity : 0;
   if (kb == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) red[wave][r][mm][nl] = acc[r][mm];
+      for (int mm = 0; mm < MT; ++mm) red[rp][wave][r][mm][nl] = acc[r][mm];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < R * MT * 16; e += NW * 64) {
@@ -695,17 +710,16 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
     const int mm = (e >> 4) % MT;
     const int r = (e >> 4) / MT;
     if (r < w.rvalid) {
-      float v = red[0][r][mm][row];
+      float v = red[rp][0][r][mm][row];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) v += red[ww][r][mm][row];
+      for (int ww = 1; ww < NW; ++ww) v += red[rp][ww][r][mm][row];
       const int n = (wk.rb0 + r) * kTileRows + row;
       const int m = wk.m0 + mm;
       if (n < N && m < M) {
-        const uint16_t b = f32_to_bf16_rne(16.0f * v);
         if constexpr (Gate::kActive)
-          Gate::store(D.y + (int64_t)m * N + n, b);
+          Gate::store(static_cast<uint16_t*>(D.y) + (int64_t)m * N + n, f32_to_bf16_rne(16.0f * v));
         else
-          D.y[(int64_t)m * N + n] = b;
+          store_out(D, (int64_t)m * N + n, 16.0f * v);
       }
     }
   }
@@ -719,15 +733,15 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_kernel(const BatchArgs ar
 
 template <int MT, int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_gemv_one(const uint16_t* x, const uint8_t* q, const void* d,
-                                                           uint16_t* y, int M, int K, int N) {
-  const LinearDesc D{x, q, d, y, M, K, N, 0};
+                                                           void* y, int M, int K, int N, int flags) {
+  const LinearDesc D{x, q, d, y, M, K, N, flags};
   gemv_body<MT, R, NW, S16>(D, locate_one(N, R, MT));
 }
 
 // One linear whose x is divided by channel scales while it is staged.
 template <int MT, int R, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x, const uint8_t* q, const void* d,
-                                                               uint16_t* y, int M, int K, int N,
+                                                               void* y, int M, int K, int N,
                                                                const float* inv_s) {
   const LinearDesc D{x, q, d, y, M, K, N, 0};
   gemv_body<MT, R, NW, false, true>(D, locate_one(N, R, MT), inv_s);
@@ -763,6 +777,7 @@ struct ChainGate {
   bool wait_x;                          // x is written by earlier stages of this pass
   bool reuse;                           // LDS already holds this x, staged by the block's previous item
   bool same_stage;                      // the block's previous item was in this stage
+  int parity;                           // the block's item count mod 2 (reduction buffer)
   uint32_t* error;
 
   __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
@@ -822,10 +837,13 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
   const uint16_t* staged = nullptr;  // x held in LDS (and its K)
   int staged_k = 0;
   int prev_stage = -1;
+  int parity = 0;
   while (i < items) {
     const LinearDesc& D = lin[li].desc;
-    const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage, hdr};
+    const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage,
+                         parity, hdr};
     prev_stage = lin[li].stage;
+    parity ^= 1;
     gemv_body<1, R, NW, S16, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
     staged = D.x;
     staged_k = D.K;
@@ -838,7 +856,8 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
 __global__ __launch_bounds__(256) void chain_fill_kernel(const ChainLinear* __restrict__ lin) {
   const ChainLinear& l = lin[blockIdx.x];
   if (!l.fill) return;
-  for (int n = threadIdx.x; n < l.desc.N; n += 256) l.desc.y[n] = kUnwritten;
+  uint16_t* y = static_cast<uint16_t*>(l.desc.y);
+  for (int n = threadIdx.x; n < l.desc.N; n += 256) y[n] = kUnwritten;
 }
 
 // ---------------------------------------------------------------------------
@@ -987,7 +1006,8 @@ void launch_gemv_at(unsigned blocks, size_t lds, hipStream_t st, const BatchArgs
   constexpr Cfg c = kCfgs[I];
   if (a.count == 1) {
     const LinearDesc& l = a.desc[0];
-    linear_gemv_one<MT, c.R, c.NW, S16><<<blocks, c.NW * 64, lds, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+    linear_gemv_one<MT, c.R, c.NW, S16><<<blocks, c.NW * 64, lds, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N,
+                                                                         l.flags);
   } else {
     linear_gemv_kernel<MT, c.R, c.NW, S16><<<blocks, c.NW * 64, lds, st>>>(a);
   }
@@ -1011,12 +1031,13 @@ void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
   const LinearDesc& l = a.desc[0];
   if constexpr (c.shared) {
     if (a.count == 1)
-      linear_mfma_shared_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+      linear_mfma_shared_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N,
+                                                                            l.flags);
     else
       linear_mfma_shared_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   } else {
     if (a.count == 1)
-      linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N);
+      linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags);
     else
       linear_mfma_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   }

@@ -19,13 +19,16 @@ inline int64_t gemv_lds_bytes(int64_t MT, int64_t K) {
   return MT * gp * (128 * 2 + 4 * 4);
 }
 
+// LinearDesc::flags
+constexpr int kOutF32 = 1;  // y is fp32 (the accumulated value before rounding to bf16)
+
 // One linear of a batch, as the kernels see it (validated by the ABI layer).
 struct LinearDesc {
   const uint16_t* x;  // bf16 [M][K]
   const uint8_t* q;   // native codes
   const void* d;      // native scale quads: fp32, or bf16 in the 16-bit variant
-  uint16_t* y;        // bf16 [M][N]
-  int M, K, N, pad;
+  void* y;            // [M][N]: bf16, or fp32 with kOutF32
+  int M, K, N, flags;
 };
 
 // Kernel argument block: block0[i] is the first workgroup of linear i.

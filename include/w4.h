@@ -23,7 +23,19 @@
  *   degenerate groups: a NaN or infinity in the group gives d = NaN (bits
  *   0x7FC00000) and codes 0; d == 0 gives codes 0;
  *   y[m][n]  = bf16_rne( sum_g d[n][g] * sum_{k in g} q[n][k] x[m][k] ),
- *            accumulated in fp32 per 128-group.
+ *            accumulated in fp32 per 128-group (the *_f32 entry points store
+ *            the fp32 value itself, before rounding).
+ *   Accuracy: the fp32 value v lies within 2e-3 * sum_k |w_hat[n][k] x[m][k]|
+ *            + 1e-6 of the exact y; a bf16 output is the nearest-even bf16 of
+ *            such a v, so it may differ from the exact y by that bound plus
+ *            half a bf16 step (bf16 keeps 8 significant bits).
+ *   Activations: a NaN or infinity anywhere in row m of x makes every
+ *            y[m][n] NaN (the row is poisoned, as a non-finite weight group
+ *            poisons its outputs).  The bound above is guaranteed while no
+ *            fp32 intermediate can overflow: |x| <= 2^64 and |w| <= 2^38 are
+ *            enough.  Past that range an output may be +-infinity or NaN
+ *            where the exact y is finite, but it is never a wrong finite
+ *            value.
  *
  * All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
  * caller owns every buffer; the library allocates nothing and keeps no state
@@ -185,6 +197,33 @@ w4_status w4_linear_ex(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q
  */
 w4_status w4_linear_batched(const w4_linear_desc* linears, int count, int path,
                             hipStream_t stream);
+
+/*
+ * fp32 outputs: the same linears storing each output as the fp32 value the
+ * kernel accumulated, before it is rounded to bf16 (the bf16 entry points
+ * store exactly bf16_rne of it, bitwise).  For checking the accumulation
+ * against the bound above without the output rounding, and for callers that
+ * sum partial outputs themselves (a K-split layer).  Same contracts as
+ * w4_linear_ex / w4_linear_s16 / w4_linear_batched except that y is fp32
+ * [M][N], 4-byte aligned, and occupies 4*M*N bytes for the overlap checks.
+ */
+typedef struct w4_linear_desc_f32 {
+  const uint16_t* x;       /* bf16 [M][K]                  */
+  int64_t M;
+  int64_t K;
+  const uint8_t* q_packed; /* native codes of the N x K W  */
+  const float* d_packed;   /* native fp32 scales           */
+  int64_t N;
+  float* y;                /* fp32 [M][N]                  */
+} w4_linear_desc_f32;
+
+w4_status w4_linear_f32(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                        const float* d_packed, int64_t N, float* y, int path, hipStream_t stream);
+w4_status w4_linear_f32_s16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* q_packed,
+                            const uint16_t* d_packed, int64_t N, float* y, int path,
+                            hipStream_t stream);
+w4_status w4_linear_batched_f32(const w4_linear_desc_f32* linears, int count, int path,
+                                hipStream_t stream);
 
 /*
  * w4_pack -- canonical codes and scales -> native layout (for codes computed

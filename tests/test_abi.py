@@ -94,6 +94,22 @@ def test_linear_validation(w4):
     assert lib.w4_linear(None, 0, 128, None, None, 16, None, None) == OK
 
 
+def test_f32_output_validation(w4):
+    """fp32 outputs: 4-byte alignment, and 4 bytes per output in the overlap checks."""
+    lib = w4.library()
+    x, q, d, y = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    assert lib.w4_linear_f32(x, 16, 128, q, d, 16, y + 2, 0, None) == ERR_ALIGN
+    assert lib.w4_linear_f32(x, 16, 128, q, d, 16, x - 768, 0, None) == ERR_ARG  # 1 KiB from x - 768 reaches x
+    assert lib.w4_linear_f32(x, 1, 100, q, d, 16, y, 0, None) == ERR_SHAPE
+    assert lib.w4_linear_f32(x, 1, 128, q, d, 16, None, 0, None) == ERR_NULL
+    assert lib.w4_linear_f32(x, 1, 128, q, d, 16, y, 9, None) == ERR_ARG
+    assert lib.w4_linear_f32_s16(x, 1, 128, q, d + 2, 16, y, 0, None) == ERR_ALIGN
+    assert lib.w4_linear_f32_s16(x, 1, 128, q, d, 16, d + 16, 0, None) == ERR_ARG  # inside the scales
+    assert lib.w4_linear_f32(None, 0, 128, None, None, 16, None, 0, None) == OK
+    arr = (w4.LinearDesc * 2)(w4.LinearDesc(x, 1, 128, q, d, 16, y), w4.LinearDesc(x, 1, 128, q, d, 16, y + 32))
+    assert lib.w4_linear_batched_f32(arr, 2, 0, None) == ERR_ARG  # 64 fp32 bytes from y overlap y + 32
+
+
 def test_batched_validation(w4):
     lib = w4.library()
     D = w4.LinearDesc
@@ -169,6 +185,14 @@ def test_chain_validation(w4):
     assert prep([lin(0, 0, x=FAKE + 0x210, K=128), lin(1, 1, y=FAKE + 0x320)]) == ERR_ARG
     # an input that lies partly in an earlier output and partly outside all of them
     assert prep([lin(0, 0, N=64), lin(1, 1, x=FAKE + 0x30000, K=256)]) == ERR_ARG
+    # an output sharing a 128-byte line (but no byte) with weights: the codes of
+    # linear 0 end at 0x12010, linear 1 writes from 0x12040
+    assert prep([lin(0, 0, q_packed=FAKE + 0x10010), lin(1, 1, y=FAKE + 0x12040)]) == ERR_ARG
+    # the same with scales (32 x 256 fp32: 512 bytes from 0x20010)
+    assert prep([lin(0, 0, d_packed=FAKE + 0x20010), lin(1, 1, y=FAKE + 0x20220)]) == ERR_ARG
+    # a later stage reading x from the line of an earlier output without reading
+    # that output (stage 0 writes 64 bytes at 0x30000; stage 1 reads from 0x30040)
+    assert prep([lin(0, 0), lin(1, 1, x=FAKE + 0x30040, K=128)]) == ERR_ARG
     # workspace too small
     assert prep([lin(0, 0), lin(1, 1)], nbytes=64) == ERR_ARG
     # the 16-bit-scale variant checks the same (its descriptors have the same layout)

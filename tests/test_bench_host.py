@@ -62,15 +62,16 @@ def test_counters_are_scaled_by_the_copy_kernel(bench, tmp_path, monkeypatch):
     mb = 256
     copy_bytes = mb << 20
     fetch_factor, read, written = 0.5, 803_000_000, 753_664
-    head = f"void {bench.HEADLINE_KERNEL}(w4::BatchArgs)"
+    head = f"void w4::{bench.HEADLINE_KERNEL}<2, 4, false>(w4::ChainLinear const*, unsigned int*, int)"
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [
         ("copy_kernel(x)", 524288, fetch_factor * copy_bytes / 1024),
-        (head, bench.HEADLINE_GRID, fetch_factor * read / 1024),
-        (head, bench.HEADLINE_GRID, fetch_factor * read / 1024),
+        (head, 131072, fetch_factor * read / 1024),
+        (head, 131072, fetch_factor * read / 1024),
+        (head, 131072, fetch_factor * (read + 4096) / 1024),  # an outlier: the median is taken
         ("other_kernel", 1024, 123.0)])
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [
         ("copy_kernel(x)", 524288, copy_bytes / 1024),
-        (head, bench.HEADLINE_GRID, written / 1024)])
+        (head, 131072, written / 1024)])
     out = tmp_path / "counters.json"
     bench.write_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), mb, str(out))
     res = json.load(open(out))
@@ -78,6 +79,7 @@ def test_counters_are_scaled_by_the_copy_kernel(bench, tmp_path, monkeypatch):
     assert res["counters"]["WRITE_SIZE"]["bytes_per_dispatch"] == written
     assert res["hbm_bytes_per_launch"] == read + written
     assert res["kernel"] == bench.HEADLINE_KERNEL
+    assert res["counters"]["FETCH_SIZE"]["dispatches"] == 3
 
 
 def test_path_compare_summary_matches_runs_to_cases(bench, tmp_path, capsys):

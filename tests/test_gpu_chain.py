@@ -5,7 +5,8 @@ q|k|v read the layer input, o reads q's output, gate|up read o's output, down
 reads gate's output, and the next layer reads down's output.  Each output must
 be (a) bitwise equal to one w4_linear_batched call per stage with the dot2
 kernel in the chain's configuration, run on the very inputs the chain saw, and
-(b) within 2e-3 * sum|w_hat x| + 1e-6 of the fp64 oracle on those inputs.
+(b) correct against the fp64 oracle on those inputs (oracle.admissible: the
+bf16 rounding of a value within 2e-3 * sum|w_hat x| + 1e-6).
 Repeated passes, eager and graph-replayed, each with a new layer-0 input,
 check that no pass reads a stale input and that the completion counters
 return to zero.
@@ -24,17 +25,24 @@ pytestmark = pytest.mark.gpu
 CHAIN_CFGS = ["1,4", "1,8", "2,4", "2,2", "1,2", "4,4"]
 
 
-def _build_chain(w4, gpu, layers, hidden, nq, nkv, ffn, seed=0, side=True):
+def _build_chain(w4, gpu, layers, hidden, nq, nkv, ffn, seed=0, side=True, same_sign=False):
     """Stages of `layers` decoder layers with real dataflow between them.
 
     Returns (stages, records, x0): records[i] = (name, stage, W fp32 host, x, q, d, N, y)
     in stage order.  Optional side linears with ragged N read inputs of their own.
+    With same_sign, every weight is positive and x0 non-negative, so every
+    output of the pass has |y| = sum |w_hat x| (the tightest case of the bound).
     """
     x0 = workloads.random_activations(1, hidden, seed=seed, device=gpu)
+    if same_sign:
+        x0 = x0.abs()
     stages, records = [], []
 
     def add(stage_items, name, N, K, x, wseed):
-        W = workloads.random_weight(N, K, std=0.02, seed=wseed)
+        if same_sign:
+            W = (0.02 * (np.abs(np.random.default_rng(wseed).standard_normal((N, K))) + 0.25)).astype(np.float32)
+        else:
+            W = workloads.random_weight(N, K, std=0.02, seed=wseed)
         q, d = w4.quantize_rtn(torch.from_numpy(W).to(gpu))
         y = torch.empty((1, N), dtype=torch.bfloat16, device=gpu)
         stage_items.append((x, q, d, N, y))
@@ -102,6 +110,43 @@ def test_chain_matches_batched_and_oracle(w4, gpu, cfg, monkeypatch):
         plan.run()
         assert plan.error() == 0, "a chain wait timed out"
         _check_pass(w4, records, cfg, monkeypatch, f"cfg={cfg} pass {rep}")
+
+
+def test_chain_same_sign_rows(w4, gpu, monkeypatch):
+    """Positive weights and non-negative inputs through every stage: each output
+    is the bf16 rounding of a value within the bound where the bound is tightest."""
+    _say("chain with same-sign rows: 3 layers (hidden 512, q 768, kv 256, ffn 1408)")
+    stages, records, x0 = _build_chain(w4, gpu, layers=3, hidden=512, nq=768, nkv=256, ffn=1408, seed=12,
+                                       side=False, same_sign=True)
+    plan = w4.chain_prepare(stages)
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    plan.run()
+    assert plan.error() == 0, "a chain wait timed out"
+    _check_pass(w4, records, cfg, monkeypatch, "same-sign")
+    for name, _, W, x, *_ in records:
+        assert (W > 0).all() and (x >= 0).all(), name
+
+
+def test_chain_nonfinite_input_poisons_the_pass(w4, gpu, monkeypatch):
+    """An infinity in the first stage's input makes every output of the pass NaN
+    (each stage's input row is then non-finite); no wait times out, and every
+    output equals the per-stage launches bit for bit."""
+    _say("chain with an infinite input value: 2 layers")
+    stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=512, nq=768, nkv=256, ffn=1408, seed=13,
+                                       side=False)
+    plan = w4.chain_prepare(stages)
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    x0[0, 100] = float("inf")
+    plan.run()
+    assert plan.error() == 0, "a chain wait timed out"
+    for name, *_, y in records:
+        assert torch.isnan(y).all(), f"{name}: not every output is NaN"
+    _check_pass(w4, records, cfg, monkeypatch, "non-finite input")
+    # and a finite input afterwards gives ordinary outputs again
+    x0.copy_(workloads.random_activations(1, 512, seed=14, device=gpu))
+    plan.run()
+    assert plan.error() == 0
+    _check_pass(w4, records, cfg, monkeypatch, "after the non-finite pass")
 
 
 def test_chain_graph_replays(w4, gpu, monkeypatch):
