@@ -1,18 +1,23 @@
 """Benchmark of the W4A16 decode linear on one MI355X.
 
-Headline (the JSON line's `value`): achieved algorithmic HBM bandwidth of
-w4_linear at M = 1 on the 2560x9216 / 9216x2560 FFN pair with 0.5% outliers
-(workload ffn_pair_outliers).  One step is one decode-style pass: every one of
-the 2 x C weight copies is multiplied once at M = 1 (C copies, > 2x the 256 MB
-Infinity Cache, so every step streams from HBM).  Steps are replayed from one
-HIP graph; the timed region is bracketed by synchronisations and measured with
-events on the replay stream.  Also reported in the same line: the same pass at
-M = 8 (verifying 7 drafted tokens + 1), quantization throughput, 4B-, 27B- and
-70B-class layer stacks in several launch modes (one launch per matrix, per
-shared-input stage, per layer, and the whole pass as one chained launch) with
-the equivalent decode tokens/s of the fastest mode that keeps a layer's
-dependencies, the roofline of the dominant kernel, and the CPU oracle timed on
-a bounded sample.
+Headline (the JSON line's `value`): achieved algorithmic HBM bandwidth of one
+decode step's linear layers on the 70B-class stack (hidden 8192, FFN 28672,
+80 layers: q/k/v, o, gate/up and down of every layer, 36.4 GB of 4-bit codes
+and fp32 scales per pass) at M = 1, run as ONE chained launch that keeps the
+layer's dependencies (w4_chain_run: q|k|v read the previous layer's down
+output, o reads q, gate|up read o, down reads gate).  Every pass reads every
+weight once, so it streams from HBM.  One step = one pass; exactly --steps
+passes are timed after --warmup passes (and at least 150 ms of warmup), replayed
+from a HIP graph, with events on the replay stream bracketed by
+synchronisations.
+
+Reported beside it in the same line: the same stack at M = 8 (verifying 7
+drafted tokens + 1) in the fastest launch mode that keeps the dependencies;
+the roofline of the chained kernel; the CPU oracle timed on this host's cores
+(a sequential phase after the GPU work); and, as extra keys, the 4B- and
+27B-class stacks in every launch mode, the 2560x9216 / 9216x2560 pair one
+launch per linear and batched, quantization throughput, 16-bit scales, and the
+channel-scaling (AWQ) and GPTQ quantizers.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stacks 4b,27b,70b|none] [--no-cpu]
 """
@@ -32,11 +37,13 @@ if ROOT not in sys.path:
 METRIC = "w4_linear achieved HBM GB/s (% of peak) at M=1 and M=8; equiv decode tok/s"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E nameplate
 PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
-HEADLINE = "ffn_pair_outliers"
-KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_gemv_ffn_pair_outliers_m1_batched_counters.json")
-HEADLINE_KERNEL = "linear_gemv_kernel<1, 2, 2, false>"  # dot2 kernel, x in LDS, fp32 scales: the batched M = 1 step
-HEADLINE_GRID = 32 * (80 + 288) * 128            # threads of one 64-linear launch (R = 2 row blocks, 2 waves)
+HEADLINE = "stack_70b"    # the largest configuration: the 70B-class layer stack
+PAIR = "ffn_pair_outliers"
+KERNEL_SOURCES = ["bit_group_quantized_w4_amd/csrc/linear.hip", "bit_group_quantized_w4_amd/csrc/w4_device.h",
+                  "bit_group_quantized_w4_amd/csrc/w4_launch.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "linear_chain_stack_70b_m1_counters.json")
+HEADLINE_KERNEL = "linear_chain_kernel"  # the persistent chained pass (one dispatch per pass)
+BENCH_SUPPORT = os.path.join(ROOT, "bench_support")
 
 
 def log(msg):
@@ -111,14 +118,16 @@ def time_graph(torch, g, replays, warmup):
 # ----------------------------------------------------------------------------
 
 def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms=None, quantize=True):
+    """The 2560x9216 / 9216x2560 pair: each of `copies` weight copies of both
+    matrices multiplied once per step, one launch per linear and batched."""
     dev = torch.device("cuda:0")
-    wl = workloads.WORKLOADS[HEADLINE]
+    wl = workloads.WORKLOADS[PAIR]
     scale_dtype = scale_dtype or torch.float32
     sb = 2 if scale_dtype == torch.bfloat16 else 4
     tag = "" if sb == 4 else " (16-bit scales)"
     mats = []
     for m in wl.matrices:
-        W = torch.from_numpy(workloads.weight(HEADLINE, 0, m.name, "cpu")).to(dev)
+        W = torch.from_numpy(workloads.weight(PAIR, 0, m.name, "cpu")).to(dev)
         q0, d0 = w4.quantize_rtn(W, scale_dtype=scale_dtype)
         qs = [q0] + [q0.clone() for _ in range(copies - 1)]
         ds = [d0] + [d0.clone() for _ in range(copies - 1)]
@@ -126,7 +135,7 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms
     torch.cuda.synchronize()
     out = {}
     for M in (ms or wl.ms):
-        xs = [workloads.activations(HEADLINE, 0, m.name, M, dev) for (m, _, _, _) in mats]
+        xs = [workloads.activations(PAIR, 0, m.name, M, dev) for (m, _, _, _) in mats]
         ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
         # batched mode: every linear of a step writes its own output
         ysb = [[torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
@@ -160,7 +169,7 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms
                 "ms_per_step": round(t / steps * 1e3, 4),
                 "launches_per_step": launches // steps,
             }
-            log(f"[bench] {HEADLINE}{tag} M={M} {mode}: {gbs:.0f} GB/s, "
+            log(f"[bench] {PAIR}{tag} M={M} {mode}: {gbs:.0f} GB/s, "
                 f"{t / (steps * copies * len(mats)) * 1e6:.2f} us per linear")
             del g
         res["bytes_per_call"] = {m.name: workloads.algorithmic_bytes(M, m.N, m.K, sb) for (m, _, _, _) in mats}
@@ -218,7 +227,8 @@ def _shared_input_groups(wl):
     return [by_tag[t] for t in order]
 
 
-def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_modes=None, scale_dtype=None):
+def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_modes=None, scale_dtype=None,
+                chain_steps=None, chain_warmup=None):
     dev = torch.device("cuda:0")
     wl = workloads.WORKLOADS[name]
     scale_dtype = scale_dtype or torch.float32
@@ -275,7 +285,8 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
                 f"{1 / per:.1f} passes/s")
             del g
         if M == 1 and (not only_modes or "chained" in only_modes):
-            res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, sb)
+            res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, chain_steps or steps,
+                                            chain_warmup or warmup, name, sb)
         res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M, sb)
     del layers
     torch.cuda.empty_cache()
@@ -328,6 +339,8 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale
     g = capture(torch, plan.run)
     t = time_graph(torch, g, steps, warmup)
     err = plan.error()
+    if err:
+        raise RuntimeError(f"{name} chained pass: a wait timed out (error flag {err}); the timing is invalid")
     per = t / steps
     nbytes = workloads.stack_bytes(name, 1, scale_bytes)
     gbs = nbytes / per / 1e9
@@ -336,7 +349,7 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale
            "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(1 / per, 1), "launches_per_pass": 1,
            "stages_per_pass": len(stages), "useful_tflops": round(flops / per / 1e12, 2),
            "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3),
-           "plan": plan.info, "wait_timeouts": err}
+           "plan": plan.info, "wait_timeouts": err, "timed_passes": steps}
     log(f"[bench] stack {name}{'' if scale_bytes == 4 else ' (16-bit scales)'} M=1 chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
         f"(plan {plan.info}, timeouts {err})")
     del g, plan
@@ -512,62 +525,103 @@ def bench_gptq(torch, w4, workloads, T=16384, T_eval=1024):
 # CPU oracle baseline (bounded sample, rank 0, after the GPU phase)
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(workloads, budget_s=12.0):
+def host_cores():
+    """Cores this process may run on; on hosts that give a GPU a share of the CPU
+    (OMP_NUM_THREADS set), that share."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
+
+
+def cpu_baseline(workloads, budget_s=20.0):
+    """The CPU oracle as it stands (oracle.w4_linear_ref: fp64 dequantization, then a
+    BLAS product), timed after the GPU phase on this host's cores:
+
+    * the headline workload's M = 1 pass, estimated from each distinct matrix shape
+      of a 70B-class layer timed once and summed over its multiplicity and the 80
+      layers (all cores: BLAS threads pinned to the core count; NumPy's elementwise
+      steps run on one thread);
+    * the 2560 x 9216 matrix at M = 1 on one core, and the quantizer on it
+      (oracle.rtn_quantize_ref; the weights are drawn before the clock starts).
+
+    Codes and scales are drawn at random for the timing (the oracle's cost does not
+    depend on their values)."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_limits
 
     import oracle
 
+    cores = host_cores()
     wl = workloads.WORKLOADS[HEADLINE]
-    data = []
+    rng = np.random.default_rng(0)
+    shapes = {}
     for m in wl.matrices:
-        W = workloads.weight(HEADLINE, 0, m.name, "cpu")
-        q, d = oracle.rtn_quantize_ref(W)
-        x = workloads.activations(HEADLINE, 0, m.name, 1, "cpu")
-        xb = x.view(torch.int16).numpy().view(np.uint16)
-        data.append((m, q, d, xb))
-    passes = 0
-    nbytes = 0
+        shapes.setdefault((m.N, m.K), []).append(m.name)
+    per_shape = {}
+    t_layer = 0.0
+    with threadpool_limits(limits=cores):
+        for (N, K), names in shapes.items():
+            q = rng.integers(-7, 8, (N, K), dtype=np.int8)
+            d = rng.uniform(1e-3, 1e-2, (N, K // 128)).astype(np.float32)
+            x = (rng.standard_normal((1, K), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            oracle.w4_linear_ref(x[:, :128], q[:16, :128], d[:16, :1])  # warm the BLAS threads
+            t0 = time.perf_counter()
+            oracle.w4_linear_ref(x, q, d)
+            t = time.perf_counter() - t0
+            per_shape[f"{N}x{K}"] = {"seconds": round(t, 3), "matrices_per_layer": len(names)}
+            t_layer += t * len(names)
+            del q, d
+    t_pass = t_layer * wl.layers
+    nbytes = workloads.stack_bytes(HEADLINE, 1)
+    # one core, the 2560 x 9216 matrix: the linear and the quantizer
+    N, K = 2560, 9216
+    W = workloads.weight("ffn_2560x9216", 0, "ffn", "cpu")
+    x1 = workloads.activations("ffn_2560x9216", 0, "ffn", 1, "cpu").view(-1).view(__import__("torch").int16).numpy()
+    x1 = x1.view(np.uint16).reshape(1, K)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while True:
-            for (m, q, d, xb) in data:
-                oracle.w4_linear_ref(xb, q, d)
-                nbytes += workloads.algorithmic_bytes(1, m.N, m.K)
-            passes += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        t = time.perf_counter() - t0
-        # the quantizer on the same matrices, a few seconds' worth
-        qpasses, qbytes = 0, 0
-        t1 = time.perf_counter()
-        while True:
-            for m in wl.matrices:
-                oracle.rtn_quantize_ref(workloads.weight(HEADLINE, 0, m.name, "cpu"))
-                qbytes += workloads.quantize_bytes(m.N, m.K)
-            qpasses += 1
-            if time.perf_counter() - t1 >= budget_s / 3:
-                break
-        tq = time.perf_counter() - t1
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full M=1 passes over both {HEADLINE} matrices "
-                      f"(2560x9216 and 9216x2560, fp64 oracle.w4_linear_ref), {t:.1f} s, "
-                      "one BLAS/NumPy thread",
-            "seconds": round(t, 2),
-            "quantize": {"GBps": round(qbytes / tq / 1e9, 4), "seconds": round(tq, 2),
-                         "sample": f"{qpasses} passes of oracle.rtn_quantize_ref over both matrices "
-                                   "(weights drawn again each pass, draw time included)"}}
+        q1, d1 = oracle.rtn_quantize_ref(W)
+        tq = time.perf_counter() - t0
+        n1, t0 = 0, time.perf_counter()
+        while n1 < 3 or time.perf_counter() - t0 < budget_s / 4:
+            oracle.w4_linear_ref(x1, q1, d1)
+            n1 += 1
+        t1 = (time.perf_counter() - t0) / n1
+    b1 = workloads.algorithmic_bytes(1, N, K)
+    return {"value": round(nbytes / t_pass / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"70B-class stack at M = 1: each distinct matrix shape of a layer timed once with "
+                      f"oracle.w4_linear_ref ({', '.join(per_shape)}), summed over its matrices and the "
+                      f"{wl.layers} layers; BLAS on {cores} threads, NumPy's elementwise steps on one",
+            "seconds_per_pass_estimated": round(t_pass, 2), "equiv_decode_tokens_per_s": round(1 / t_pass, 5),
+            "per_shape": per_shape,
+            "one_core_2560x9216_m1": {"GBps": round(b1 / t1 / 1e9, 4), "ms_per_call": round(t1 * 1e3, 1),
+                                      "calls": n1, "cores": 1},
+            "one_core_quantize_2560x9216": {"GBps": round(workloads.quantize_bytes(N, K) / tq / 1e9, 4),
+                                            "seconds": round(tq, 2), "cores": 1}}
 
 
 # ----------------------------------------------------------------------------
+
+def bench_lib():
+    """bench_support/libw4_bench.so (measurement-only kernels), built if missing."""
+    import ctypes
+    import importlib.util
+
+    path = os.path.join(BENCH_SUPPORT, "libw4_bench.so")
+    if not os.path.exists(path):
+        spec = importlib.util.spec_from_file_location("w4_bench_build", os.path.join(BENCH_SUPPORT, "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build(verbose=False)
+    return ctypes.CDLL(path)
+
 
 def measure_read_peak(torch, w4, gib=4, reps=5):
     """Bandwidth of a plain streaming read (grid-stride, non-temporal 16-byte loads) over
     `gib` GiB on this GPU: the practical ceiling for a kernel that only reads."""
     import ctypes
 
-    lib = ctypes.CDLL(os.path.join(os.path.dirname(w4.__file__), "libw4_bench.so"))
+    lib = bench_lib()
     nb = gib << 30
     buf = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
     grid = 2048
@@ -589,22 +643,28 @@ def measure_read_peak(torch, w4, gib=4, reps=5):
             "bytes": nb}
 
 
-def roofline(pair_m1, bytes_per_call, copies, read_peak=None):
-    """Dominant kernel: the M = 1 dot2 linear on the headline pair, one launch per step."""
-    achieved = pair_m1["GBps"]
+def roofline(chained, bytes_per_pass, read_peak=None):
+    """Dominant kernel: the chained pass over the 70B-class stack at M = 1 (one
+    dispatch of the persistent kernel per pass, after a small fill launch).
+    achieved = algorithmic bytes per pass / the pass time measured with events
+    on the replay stream over the timed passes (the fill launch, ~5 us, is
+    inside that time)."""
+    achieved = round(bytes_per_pass / (chained["ms_per_pass"] * 1e-3) / 1e9, 1)
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
         if c.get("kernel_source_hash") == kernel_source_hash():
             traffic = c.get("hbm_bytes_per_launch")
+    p = chained.get("plan", {})
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": f"{HEADLINE_KERNEL} (dot2, x in LDS, fp32 scales), 64 linears per launch",
+            "kernel": f"{HEADLINE_KERNEL}<{p.get('rows_per_item', 32) // 16}, {p.get('waves_per_block')}, false> "
+                      f"(persistent dot2 pass, {p.get('blocks')} blocks), one dispatch per pass",
+            "algorithmic_bytes_per_launch": bytes_per_pass,
+            "avg_launch_us": round(chained["ms_per_pass"] * 1e3, 1),
             "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4) if read_peak else None,
-            "algorithmic_bytes_per_launch": copies * sum(bytes_per_call.values()),
-            "avg_launch_us": pair_m1["us_per_launch"],
-            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this launch, copy-kernel calibrated"
+            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel, copy-kernel calibrated"
                               if traffic else None}
 
 
@@ -615,18 +675,18 @@ def roofline(pair_m1, bytes_per_call, copies, read_peak=None):
 def summarize_trace(path, last=0):
     """Per (kernel, grid, block) duration statistics from a rocprofv3 kernel_trace.csv.
     With `last`, also the mean duration of the last `last` dispatches of the
-    headline launch (the timed steps of the M = 1 batched pass)."""
+    headline kernel (the timed passes of a run that times only the 70B-class
+    chained pass, e.g. --stacks 70b --stack-ms 1 --stack-modes chained)."""
     import csv
     import statistics
 
     rows = list(csv.DictReader(open(path)))
     if last:
-        head = sorted((r for r in rows if HEADLINE_KERNEL.replace(" ", "") in r["Kernel_Name"].replace(" ", "")
-                       and int(r["Grid_Size_X"]) == HEADLINE_GRID), key=lambda r: int(r["Start_Timestamp"]))
+        head = sorted((r for r in rows if HEADLINE_KERNEL in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in head]
         tail = d[-last:]
-        print(f"headline {HEADLINE_KERNEL}, grid {HEADLINE_GRID} threads: {len(d)} dispatches; "
-              f"last {len(tail)} (the timed steps): mean {statistics.mean(tail):.2f} us, "
+        print(f"headline {HEADLINE_KERNEL}: {len(d)} dispatches; "
+              f"last {len(tail)} (the timed passes): mean {statistics.mean(tail):.2f} us, "
               f"median {statistics.median(tail):.2f} us, min {min(tail):.2f} us, max {max(tail):.2f} us\n")
     groups = {}
     for r in rows:
@@ -702,9 +762,9 @@ def summarize_counters(path):
 
 def write_counters(fetch_csv, write_csv, copy_mb, out_path):
     """Traffic of the headline kernel from two rocprofv3 --pmc runs of
-    `bench.py --calibrate-copy-mb copy_mb` (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch), each scaled by what the same counter reads for the plain copy
-    kernel of known size."""
+    `bench.py --calibrate-copy-mb copy_mb` that time only the 70B-class chained
+    pass (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the plain copy kernel of known size."""
     import csv
     import statistics
 
@@ -714,29 +774,26 @@ def write_counters(fetch_csv, write_csv, copy_mb, out_path):
         out = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                out.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return out
 
     copy_bytes = copy_mb << 20
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         d = per_dispatch(path, counter)
-        copy = [v for (k, g), v in d.items() if "copy_kernel" in k]
+        copy = [v for k, v in d.items() if "copy_kernel" in k]
         factor = statistics.mean(copy[0]) * 1024 / copy_bytes  # counter bytes per real byte
-        # the headline launch: 64 linears (32 copies of 2560x9216 and of 9216x2560) at M = 1
-        grid = HEADLINE_GRID
-        vals = [v for (k, g), v in d.items() if HEADLINE_KERNEL.replace(" ", "") in k.replace(" ", "") and g == grid]
+        vals = [v for k, v in d.items() if HEADLINE_KERNEL in k]
         if not vals:
-            raise SystemExit(f"no {HEADLINE_KERNEL} dispatch with grid {grid} in {path}")
-        kib = statistics.mean(vals[0])
-        res[counter] = {"kib_per_dispatch": kib, "copy_calibration_factor": round(factor, 4),
-                        "bytes_per_dispatch": round(kib * 1024 / factor)}
+            raise SystemExit(f"no {HEADLINE_KERNEL} dispatch in {path}")
+        kib = statistics.median(vals[0])
+        res[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals[0]),
+                        "copy_calibration_factor": round(factor, 4), "bytes_per_dispatch": round(kib * 1024 / factor)}
     traffic = res["FETCH_SIZE"]["bytes_per_dispatch"] + res["WRITE_SIZE"]["bytes_per_dispatch"]
-    out = {"kernel": HEADLINE_KERNEL, "launch": "64 linears: 32 x (2560x9216 + 9216x2560), M = 1",
+    out = {"kernel": HEADLINE_KERNEL, "launch": "one chained pass over the 70B-class stack at M = 1 (80 layers)",
            "kernel_source_hash": kernel_source_hash(), "counters": res,
            "hbm_bytes_per_launch": traffic,
-           "algorithmic_bytes_per_launch": 32 * (workloads.algorithmic_bytes(1, 2560, 9216)
-                                                 + workloads.algorithmic_bytes(1, 9216, 2560))}
+           "algorithmic_bytes_per_launch": workloads.stack_bytes(HEADLINE, 1)}
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -748,8 +805,11 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--copies", type=int, default=32)
-    ap.add_argument("--stacks", default="4b,27b,70b")
+    ap.add_argument("--stacks", default="4b,27b,70b",
+                    help="stacks measured besides the headline 70B-class stack (always measured)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-pair", action="store_true",
+                    help="skip the 2560x9216 / 9216x2560 pair, its quantization and the read peak (profiling runs)")
     ap.add_argument("--no-awq", action="store_true", help="skip the channel-scaling (AWQ) search and decode timing")
     ap.add_argument("--no-s16", action="store_true", help="skip the 16-bit-scale measurements")
     ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQ quantizer measurement")
@@ -805,32 +865,39 @@ def main():
         print(json.dumps({"path_compare": path_compare(torch, w4, workloads)}), flush=True)
         return
 
-    pair, quant = bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies)
+    only_ms = [int(m) for m in args.stack_ms.split(",") if m] or None
+    only_modes = [m for m in args.stack_modes.split(",") if m] or None
 
-    stacks = {}
-    for s in [s for s in args.stacks.split(",") if s and s != "none"]:
+    # The headline: the 70B-class stack, its chained M = 1 pass timed over exactly
+    # --steps passes (the other launch modes and M over a fifth of that).
+    stacks = {HEADLINE: bench_stack(torch, w4, workloads, HEADLINE, max(5, args.steps // 5), max(2, args.warmup),
+                                    only_ms, only_modes, chain_steps=args.steps, chain_warmup=args.warmup)}
+    for s in [s for s in args.stacks.split(",") if s and s != "none" and "stack_" + s != HEADLINE]:
         stacks["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
-                                           max(2, args.warmup),
-                                           [int(m) for m in args.stack_ms.split(",") if m] or None,
-                                           [m for m in args.stack_modes.split(",") if m] or None)
+                                           max(2, args.warmup), only_ms, only_modes)
 
-    # 16-bit scales: the headline pair at M = 1 and the stacks at M = 1 in the two launch modes that keep
+    pair = quant = None
+    if not args.no_pair:
+        pair, quant = bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies)
+
+    # 16-bit scales: the pair at M = 1 and the stacks at M = 1 in the two launch modes that keep
     # a layer's dependencies (one launch per stage, chained)
-    s16 = None if args.no_s16 else {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
-                                                       scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
-    for s in [s for s in args.stacks.split(",") if s and s != "none" and not args.no_s16]:
-        s16["stack_" + s] = bench_stack(torch, w4, workloads, "stack_" + s, max(5, args.steps // 5),
-                                        max(2, args.warmup), [1], ["fused_shared_input", "chained"],
-                                        scale_dtype=torch.bfloat16)
+    s16 = None
+    if not args.no_s16:
+        s16 = {} if args.no_pair else {"pair": bench_pair(torch, w4, workloads, args.steps, args.warmup, args.copies,
+                                                          scale_dtype=torch.bfloat16, ms=[1], quantize=False)[0]}
+        for name in stacks:
+            s16[name] = bench_stack(torch, w4, workloads, name, max(5, args.steps // 5), max(2, args.warmup), [1],
+                                    ["fused_shared_input", "chained"], scale_dtype=torch.bfloat16)
 
     awq_res = None if args.no_awq else bench_awq(torch, w4, workloads, args.steps, args.warmup)
     gptq_res = None if args.no_gptq else bench_gptq(torch, w4, workloads)
-    read_peak = measure_read_peak(torch, w4)
+    read_peak = None if args.no_pair else measure_read_peak(torch, w4)
 
     if args.calibrate_copy_mb:
         import ctypes
 
-        lib = ctypes.CDLL(os.path.join(os.path.dirname(w4.__file__), "libw4_bench.so"))
+        lib = bench_lib()
         nb = args.calibrate_copy_mb << 20
         a = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
         b = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
@@ -842,37 +909,52 @@ def main():
         log(f"[bench] copy kernel: 3 x {args.calibrate_copy_mb} MiB")
 
     torch.cuda.synchronize()
+    # CPU phase: after every GPU measurement, never overlapped with one
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
-    m1 = pair[1]["batched"]
+    wl = workloads.WORKLOADS[HEADLINE]
+    head_res = stacks[HEADLINE].get(1, {})
+    head = head_res.get("chained")
+    if head is None:
+        print(json.dumps({"stacks": stacks}), flush=True)  # a profiling run without the chained pass
+        return
+    nbytes = workloads.stack_bytes(HEADLINE, 1)
+    dec = decode_summary(stacks)
+    m8 = stacks[HEADLINE].get(8, {})
+    m8_dep = {k: v for k, v in m8.items() if k in DEPENDENT_MODES}
+    m8_best = min(m8_dep.items(), key=lambda kv: kv[1]["ms_per_pass"]) if m8_dep else None
     line = {
         "metric": METRIC,
-        "value": m1["GBps"],
+        "value": head["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": m1["ms_per_step"],
+        "ms_per_step": head["ms_per_pass"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": HEADLINE, "matrices": ["2560x9216", "9216x2560"], "M": 1,
-                   "weight_copies": args.copies, "linears_per_step": 2 * args.copies,
-                   "launch": "w4_linear_batched, 64 independent linears per launch",
+        "config": {"workload": HEADLINE, "layers": wl.layers,
+                   "matrices_per_layer": {m.name: f"{m.N}x{m.K}" for m in wl.matrices},
+                   "M": 1, "linears_per_pass": wl.layers * len(wl.matrices), "stages_per_pass": head["stages_per_pass"],
+                   "launch": "w4_chain_run: the whole dependent pass as one persistent launch (after a fill launch)",
                    "group": 128, "weights": "int4 codes + fp32 scales", "x": "bf16",
-                   "timing": "hip graph replay, events on the replay stream",
+                   "bytes_per_pass": nbytes,
+                   "timing": "hip graph replay of one pass per step, events on the replay stream",
                    "min_warmup_ms": int(MIN_WARMUP_S * 1000)},
-        "pct_of_peak": m1["pct_of_peak"],
-        "us_per_linear": m1["us_per_linear"],
-        "per_call_m1": pair[1]["per_call"],
-        "pair": pair,
-        "quantize": quant,
-        "stacks": stacks,
-        "equiv_decode_tokens_per_s": decode_summary(stacks),
-        "roofline": roofline(m1, pair[1]["bytes_per_call"], args.copies, read_peak),
+        "pct_of_peak": head["pct_of_peak"],
+        "equiv_decode_tokens_per_s": round(1e3 / head["ms_per_pass"], 1),
+        "m8": ({"mode": m8_best[0], **m8_best[1],
+                "bytes_per_pass": m8.get("bytes_per_pass")} if m8_best else None),
+        "decode_summary": dec,
+        "roofline": roofline(head, nbytes, read_peak),
         "hbm_read_peak_measured": read_peak,
+        "stacks": stacks,
+        "pair": pair,
+        "per_call_m1": pair[1]["per_call"] if pair else None,
+        "quantize": quant,
         "scales_16bit": s16,
         "awq": awq_res,
         "gptq": gptq_res,
