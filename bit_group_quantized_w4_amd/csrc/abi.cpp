@@ -10,8 +10,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <utility>
-#include <vector>
 
 namespace {
 
@@ -417,29 +415,37 @@ w4_status w4_gptq_block_s16(const float* W, int64_t N, int64_t K, int64_t b0, co
 // ---------------------------------------------------------------------------
 // chained decode pass
 // ---------------------------------------------------------------------------
-size_t w4_chain_workspace_bytes(int64_t count) {
-  if (count < 1 || count > W4_CHAIN_MAX) return 0;
-  return w4::chain_workspace_bytes(count);
-}
-
 extern "C++" {
 namespace {
-// Does [a, a + na) lie within the union of the byte ranges r?
-bool covered(uintptr_t a, size_t na, std::vector<std::pair<uintptr_t, uintptr_t>>& r) {
-  std::sort(r.begin(), r.end());
+uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+
+// Is [a, a + na) covered by the outputs of the linears of stages before `stage`?
+// (No allocation: the covered prefix grows by any output that reaches past it.)
+template <typename Desc>
+bool covered_by_earlier(const Desc* l, int64_t count, int64_t stage, uintptr_t a, size_t na) {
   uintptr_t at = a;
   const uintptr_t end = a + na;
-  for (const auto& iv : r) {
-    if (iv.first > at) break;
-    if (iv.second > at) at = iv.second;
-    if (at >= end) return true;
+  for (bool grew = true; at < end && grew;) {
+    grew = false;
+    for (int64_t i = 0; i < count && l[i].stage < stage; ++i) {
+      const uintptr_t y0 = addr(l[i].y), y1 = y0 + 2 * (size_t)l[i].N;
+      if (y0 <= at && y1 > at) {
+        at = y1;
+        grew = true;
+      }
+    }
   }
   return at >= end;
 }
 
+// The chain's checks and its plan (see include/w4.h).  Allocates nothing, on
+// the device or the host: flags are recomputed per linear, the table is built
+// in a small buffer and uploaded in pieces, and the stream is synchronised
+// before returning.  A workspace smaller than the plan needs returns
+// `too_small`.
 template <typename Desc>
 w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, size_t workspace_bytes,
-                        w4_chain_plan* plan, bool s16, hipStream_t stream) {
+                        w4_chain_plan* plan, bool s16, w4_status too_small, hipStream_t stream) {
   if (count < 1 || count > W4_CHAIN_MAX) return W4_ERR_ARG;
   if (!linears || !workspace || !plan) return W4_ERR_NULL;
   if (!aligned(workspace, 16)) return W4_ERR_ALIGN;
@@ -465,13 +471,12 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   // as x by a later stage is the intended use; such an x must then be
   // written entirely by earlier stages (it is read once no value of it is
   // unwritten).
-  std::vector<int> wait_x(count, 0), fill(count, 0);
   for (int64_t i = 0; i < count; ++i) {
     const Desc& a = linears[i];
     const size_t yb = 2 * (size_t)a.N;
-    const uintptr_t y0 = reinterpret_cast<uintptr_t>(a.y) & ~(uintptr_t)127;
+    const uintptr_t y0 = addr(a.y) & ~(uintptr_t)127;
     const void* ylines = reinterpret_cast<const void*>(y0);
-    const size_t ylb = ((reinterpret_cast<uintptr_t>(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
+    const size_t ylb = ((addr(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
     for (int64_t j = 0; j < count; ++j) {
       const Desc& b = linears[j];
       if (overlaps(ylines, ylb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
@@ -481,23 +486,38 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
       if (!overlaps(ylines, ylb, b.x, 2 * (size_t)b.K)) continue;
       // b reads a line that a writes: only as a later stage reading a's output
       if (b.stage <= a.stage || !overlaps(a.y, yb, b.x, 2 * (size_t)b.K)) return W4_ERR_ARG;
-      fill[i] = 1;
-      wait_x[j] = 1;
     }
   }
-  for (int64_t j = 0; j < count; ++j) {
-    if (!wait_x[j]) continue;
-    std::vector<std::pair<uintptr_t, uintptr_t>> r;
+  // an x that reads outputs of earlier stages must lie entirely within them
+  auto reads_earlier = [&](int64_t j) {
     for (int64_t i = 0; i < count; ++i)
-      if (linears[i].stage < linears[j].stage) {
-        const uintptr_t y = reinterpret_cast<uintptr_t>(linears[i].y);
-        r.emplace_back(y, y + 2 * (size_t)linears[i].N);
-      }
-    if (!covered(reinterpret_cast<uintptr_t>(linears[j].x), 2 * (size_t)linears[j].K, r)) return W4_ERR_ARG;
-  }
+      if (linears[i].stage < linears[j].stage && overlaps(linears[i].y, 2 * (size_t)linears[i].N, linears[j].x,
+                                                          2 * (size_t)linears[j].K))
+        return true;
+    return false;
+  };
+  auto read_later = [&](int64_t i) {
+    for (int64_t j = 0; j < count; ++j)
+      if (linears[j].stage > linears[i].stage && overlaps(linears[i].y, 2 * (size_t)linears[i].N, linears[j].x,
+                                                          2 * (size_t)linears[j].K))
+        return true;
+    return false;
+  };
+  for (int64_t j = 0; j < count; ++j)
+    if (reads_earlier(j) && !covered_by_earlier(linears, count, linears[j].stage, addr(linears[j].x),
+                                                2 * (size_t)linears[j].K))
+      return W4_ERR_ARG;
   const int stages = (int)linears[count - 1].stage + 1;
   const size_t need = w4::chain_workspace_bytes(count);
-  if (workspace_bytes < need) return W4_ERR_ARG;
+  if (workspace_bytes < need) return too_small;
+  // the workspace overlaps no buffer of the chain
+  for (int64_t i = 0; i < count; ++i) {
+    const Desc& l = linears[i];
+    if (overlaps(workspace, need, l.x, 2 * (size_t)l.K) || overlaps(workspace, need, l.y, 2 * (size_t)l.N) ||
+        overlaps(workspace, need, l.q_packed, w4_packed_bytes(l.N, l.K)) ||
+        overlaps(workspace, need, l.d_packed, (s16 ? 2 : 4) * w4_scale_count(l.N, l.K)))
+      return W4_ERR_ARG;
+  }
 
   double code_bytes = 0;
   for (int64_t i = 0; i < count; ++i) code_bytes += (double)w4_packed_bytes(linears[i].N, linears[i].K);
@@ -508,42 +528,66 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   const size_t lds = (size_t)w4::gemv_lds_bytes(1, kmax);
 
   // Table: the linears of each stage laid out longest K first (stable), as a
-  // batched launch does, each followed by its panels of R row blocks.
-  std::vector<uint8_t> host(need, 0);
-  auto* tab = reinterpret_cast<w4::ChainLinear*>(host.data() + sizeof(w4::ChainHeader));
-  std::vector<int64_t> order;
-  order.reserve(count);
+  // batched launch does, each followed by its panels of R row blocks.  The
+  // entries are built kChunk at a time and uploaded.
+  constexpr int kChunk = 32;
+  w4::ChainLinear buf[kChunk];
+  uint8_t* const ws = static_cast<uint8_t*>(workspace);
+  int nbuf = 0;
+  int64_t emitted = 0;  // table entries built so far
+  auto flush = [&]() -> hipError_t {
+    if (nbuf == 0) return hipSuccess;
+    uint8_t* dst = ws + sizeof(w4::ChainHeader) + (size_t)(emitted - nbuf) * sizeof(w4::ChainLinear);
+    hipError_t err = hipMemcpyAsync(dst, buf, nbuf * sizeof(w4::ChainLinear), hipMemcpyHostToDevice, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);  // buf is reused
+    nbuf = 0;
+    return err;
+  };
   int64_t items = 0;
   for (int64_t i = 0; i < count;) {
     int64_t e = i;
     while (e < count && linears[e].stage == linears[i].stage) ++e;
-    const size_t first = order.size();
-    for (int64_t j = i; j < e; ++j) {
-      size_t at = order.size();
-      order.push_back(j);
-      while (at > first && linears[order[at - 1]].K < linears[j].K) {
-        order[at] = order[at - 1];
-        --at;
+    // distinct K values of the stage, longest first; linears of equal K in order
+    for (int64_t kcur = INT64_MAX;;) {
+      int64_t knext = 0;
+      for (int64_t j = i; j < e; ++j)
+        if (linears[j].K < kcur) knext = std::max(knext, (int64_t)linears[j].K);
+      if (knext == 0) break;
+      kcur = knext;
+      for (int64_t src = i; src < e; ++src) {
+        const Desc& l = linears[src];
+        if (l.K != kcur) continue;
+        w4::ChainLinear& c = buf[nbuf++];
+        memset(&c, 0, sizeof(c));
+        c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, 1, (int)l.K, (int)l.N, 0};
+        c.item0 = (int)items;
+        c.stage = (int)l.stage;
+        c.wait_x = reads_earlier(src);
+        c.fill = read_later(src);
+        const int64_t nb = (l.N + 15) / 16;
+        items += (nb + R - 1) / R;
+        if (items > 0x7FFFFFFF) return W4_ERR_SHAPE;
+        ++emitted;
+        if (nbuf == kChunk)
+          if (hipError_t err = flush()) return hip_status(err);
       }
-      order[at] = j;
-    }
-    for (size_t t = first; t < order.size(); ++t) {
-      const int64_t src = order[t];
-      const Desc& l = linears[src];
-      w4::ChainLinear& c = tab[t];
-      c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, 1, (int)l.K, (int)l.N, 0};
-      c.item0 = (int)items;
-      c.stage = (int)l.stage;
-      c.wait_x = wait_x[src];
-      c.fill = fill[src];
-      const int64_t nb = (l.N + 15) / 16;
-      items += (nb + R - 1) / R;
-      if (items > 0x7FFFFFFF) return W4_ERR_SHAPE;
     }
     i = e;
   }
-  tab[count].item0 = (int)items;
-  tab[count].stage = stages;
+  {
+    // the sentinel entry (the first item past the last linear), then the
+    // header: the error flag starts clear
+    w4::ChainLinear& c = buf[nbuf++];
+    memset(&c, 0, sizeof(c));
+    c.item0 = (int)items;
+    c.stage = stages;
+    ++emitted;
+    if (hipError_t err = flush()) return hip_status(err);
+    w4::ChainHeader h;
+    memset(&h, 0, sizeof(h));
+    if (hipError_t err = hipMemcpyAsync(ws, &h, sizeof(h), hipMemcpyHostToDevice, stream)) return hip_status(err);
+    if (hipError_t err = hipStreamSynchronize(stream)) return hip_status(err);
+  }
 
   // Grid: every block resident at once (waits look only at earlier items).
   // Two blocks per CU measured fastest; W4_CHAIN_BLOCKS may ask for another
@@ -561,9 +605,6 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   }
   if (blocks > items) blocks = items;
 
-  if (hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, stream)) return hip_status(e);
-  if (hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
-
   plan->workspace = workspace;
   plan->linears = (int32_t)count;
   plan->stages = stages;
@@ -580,14 +621,19 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
 }  // namespace
 }  // extern "C++"
 
+size_t w4_chain_workspace_bytes(int64_t count) {
+  if (count < 1 || count > W4_CHAIN_MAX) return 0;
+  return w4::chain_workspace_bytes(count);
+}
+
 w4_status w4_chain_prepare(const w4_chain_linear* linears, int64_t count, void* workspace, size_t workspace_bytes,
                            w4_chain_plan* plan, hipStream_t stream) {
-  return chain_prepare(linears, count, workspace, workspace_bytes, plan, false, stream);
+  return chain_prepare(linears, count, workspace, workspace_bytes, plan, false, W4_ERR_ARG, stream);
 }
 
 w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count, void* workspace,
                                size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream) {
-  return chain_prepare(linears, count, workspace, workspace_bytes, plan, true, stream);
+  return chain_prepare(linears, count, workspace, workspace_bytes, plan, true, W4_ERR_ARG, stream);
 }
 
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream) {

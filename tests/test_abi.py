@@ -193,8 +193,9 @@ def test_chain_validation(w4):
     # a later stage reading x from the line of an earlier output without reading
     # that output (stage 0 writes 64 bytes at 0x30000; stage 1 reads from 0x30040)
     assert prep([lin(0, 0), lin(1, 1, x=FAKE + 0x30040, K=128)]) == ERR_ARG
-    # workspace too small
+    # workspace too small, or overlapping a buffer of the chain
     assert prep([lin(0, 0), lin(1, 1)], nbytes=64) == ERR_ARG
+    assert prep([lin(0, 0), lin(1, 1)], workspace=FAKE + 0x100000 + 0x30000 - 0x40) == ERR_ARG  # reaches y of linear 1
     # the 16-bit-scale variant checks the same (its descriptors have the same layout)
     arr = (C * 2)(lin(0, 0), lin(1, 2))
     assert lib.w4_chain_prepare_s16(arr, 2, ws, n, ctypes.byref(plan), None) == ERR_ARG
