@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4.so")
 
-W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_HIP, W4_ERR_ARG = range(6)
+W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_HIP, W4_ERR_ARG, W4_ERR_SCRATCH = range(7)
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 GROUP = 128
 
@@ -82,6 +82,7 @@ SIGNATURES = {
     "w4_chain_workspace_bytes": (_SZ, [_I64]),
     "w4_chain_prepare": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_prepare_s16": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
+    "w4_chain_prepare_noalloc": (_INT, [ctypes.POINTER(ChainLinear), _I64, ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_run": (_INT, [ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_error": (_INT, [ctypes.POINTER(ChainPlanC), ctypes.POINTER(ctypes.c_uint32), _VP]),
     # GPTQ steps
@@ -251,23 +252,27 @@ def linear_batched(items, path="auto"):
 
 
 class ChainPlan:
-    """A prepared chain (w4_chain_prepare): its device workspace, the plan, and
+    """A prepared chain (w4_chain_prepare): its device workspace (None when the
+    library's static scratch holds it: w4_chain_prepare_noalloc), the plan, and
     references to every tensor it names, which must stay alive while it is used."""
 
-    def __init__(self, workspace, plan, tensors):
+    def __init__(self, workspace, plan, tensors, device):
         self.workspace = workspace
         self.plan = plan
+        self.device = device
         self._tensors = tensors
+
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
 
     def run(self):
         """Enqueue one pass on the current stream (w4_chain_run)."""
-        _check(_lib.w4_chain_run(ctypes.byref(self.plan), _stream(self.workspace)), "w4_chain_run")
+        _check(_lib.w4_chain_run(ctypes.byref(self.plan), self._stream()), "w4_chain_run")
 
     def error(self):
         """The workspace's error flag (synchronises the current stream; w4_chain_error)."""
         flag = ctypes.c_uint32(0)
-        _check(_lib.w4_chain_error(ctypes.byref(self.plan), ctypes.byref(flag), _stream(self.workspace)),
-               "w4_chain_error")
+        _check(_lib.w4_chain_error(ctypes.byref(self.plan), ctypes.byref(flag), self._stream()), "w4_chain_error")
         return int(flag.value)
 
     @property
@@ -278,14 +283,16 @@ class ChainPlan:
                 "lds_bytes": p.lds_bytes, "scale_bytes": p.scale_bytes}
 
 
-def chain_prepare(stages):
+def chain_prepare(stages, noalloc=False):
     """Prepare a chained decode pass (w4_chain_prepare).
 
     stages: sequence of stages, each a sequence of (x [1, K] bf16, q, d, N,
     y [1, N] bf16), with d fp32 scales throughout or bf16 (16-bit) scales
     throughout.  A linear whose x lies in outputs of earlier stages reads it
     once all of it is written.  Returns a ChainPlan; plan.run() enqueues one
-    pass.
+    pass.  With noalloc (fp32 scales only), the workspace is the library's
+    static scratch (w4_chain_prepare_noalloc): nothing is allocated, and only
+    the most recent such plan of a GPU may be run.
     """
     flat = [(s, it) for s, stage in enumerate(stages) for it in stage]
     if not flat:
@@ -305,15 +312,21 @@ def chain_prepare(stages):
                                _dev(d, sd, "d").value, N, _dev(y, torch.bfloat16, "y").value, s)
         tensors += [x, q, d, y]
         dev = dev or x.device
+    plan = ChainPlanC()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if noalloc:
+        if sd != torch.float32:
+            raise TypeError("w4_chain_prepare_noalloc takes fp32 scales")
+        _check(_lib.w4_chain_prepare_noalloc(descs, len(flat), ctypes.byref(plan), stream), "w4_chain_prepare_noalloc")
+        return ChainPlan(None, plan, tensors, dev)
     nbytes = int(_lib.w4_chain_workspace_bytes(len(flat)))
     if nbytes == 0:
         _check(W4_ERR_ARG, "w4_chain_workspace_bytes")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    plan = ChainPlanC()
     fn, name = ((_lib.w4_chain_prepare_s16, "w4_chain_prepare_s16") if sd == torch.bfloat16
                 else (_lib.w4_chain_prepare, "w4_chain_prepare"))
-    _check(fn(descs, len(flat), ctypes.c_void_p(ws.data_ptr()), nbytes, ctypes.byref(plan), _stream(ws)), name)
-    return ChainPlan(ws, plan, tensors)
+    _check(fn(descs, len(flat), ctypes.c_void_p(ws.data_ptr()), nbytes, ctypes.byref(plan), stream), name)
+    return ChainPlan(ws, plan, tensors, dev)
 
 
 def pack(q_canon, d_canon, out=None):

@@ -4,12 +4,15 @@
 #include "w4.h"
 #include "w4_launch.h"
 
+#include <hip/hip_runtime.h>
+
 #include <float.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace {
 
@@ -191,6 +194,8 @@ const char* w4_status_str(int status) {
     case W4_ERR_ALIGN: return "W4_ERR_ALIGN: a pointer is not aligned as required";
     case W4_ERR_HIP: return "W4_ERR_HIP: a HIP runtime call or kernel launch failed";
     case W4_ERR_ARG: return "W4_ERR_ARG: invalid argument";
+    case W4_ERR_SCRATCH:
+      return "W4_ERR_SCRATCH: the chain's workspace exceeds the library's static scratch (W4_CHAIN_SCRATCH_BYTES)";
     default: return "unknown w4 status";
   }
 }
@@ -620,6 +625,53 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
 }
 }  // namespace
 }  // extern "C++"
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// chained pass set up in the library's own device memory
+// ---------------------------------------------------------------------------
+// The workspace of w4_chain_prepare_noalloc.  Each GPU the library runs on
+// holds its own copy from the module's load until the process ends.  In host
+// code `scratch` names a host-side stand-in, not a device address: the device
+// address of a GPU's copy comes from hipGetSymbolAddress, looked up once per
+// device (with that device current) and kept in g_scratch_addr.
+static __device__ __align__(256) uint8_t scratch[W4_CHAIN_SCRATCH_BYTES];
+static_assert(W4_CHAIN_SCRATCH_BYTES >= 32 + 2 * 64, "room for a chain of one linear");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on first use).
+w4_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return W4_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return hip_status(e);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return W4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+w4_status w4_chain_prepare_noalloc(const w4_chain_linear* linears, int64_t count, w4_chain_plan* plan,
+                                   hipStream_t stream) {
+  if (count < 1 || count > W4_CHAIN_MAX) return W4_ERR_ARG;
+  if (!linears || !plan) return W4_ERR_NULL;
+  if (w4::chain_workspace_bytes(count) > W4_CHAIN_SCRATCH_BYTES) return W4_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (w4_status st = scratch_address(&ws)) return st;
+  return chain_prepare(linears, count, ws, W4_CHAIN_SCRATCH_BYTES, plan, false, W4_ERR_SCRATCH, stream);
+}
 
 size_t w4_chain_workspace_bytes(int64_t count) {
   if (count < 1 || count > W4_CHAIN_MAX) return 0;

@@ -91,7 +91,8 @@ typedef enum {
   W4_ERR_SHAPE = 2,  /* N, M < 0; K not a positive multiple of 128; too large */
   W4_ERR_ALIGN = 3,  /* a pointer is not aligned as documented                */
   W4_ERR_HIP = 4,    /* a HIP runtime call or launch failed                   */
-  W4_ERR_ARG = 5     /* another invalid argument (unknown path, aliasing ...) */
+  W4_ERR_ARG = 5,    /* another invalid argument (unknown path, aliasing ...) */
+  W4_ERR_SCRATCH = 6 /* w4_chain_prepare_noalloc: the chain does not fit the static scratch */
 } w4_status;
 
 /* Which linear kernel w4_linear_ex / w4_linear_batched run. */
@@ -331,6 +332,28 @@ w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count
                                size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream);
+
+/*
+ * w4_chain_prepare_noalloc -- w4_chain_prepare for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc): the same checks, plan and
+ * status codes, with the workspace taken from a static device array of
+ * W4_CHAIN_SCRATCH_BYTES bytes that the library holds on each GPU it runs on
+ * until the process ends (its device address is looked up once per device,
+ * on the first call there).  No hipMalloc, hipFree or other allocation, on
+ * the device or the host.  A chain whose workspace
+ * (w4_chain_workspace_bytes(count): up to 1022 linears) does not fit is
+ * refused with W4_ERR_SCRATCH before anything is written.  The plan is used
+ * with w4_chain_run / w4_chain_error as any other.
+ * Every plan prepared this way on one GPU shares that GPU's array, which
+ * keeps the last call's contents: preparing a plan overwrites the table of
+ * the previous one, so only the most recently prepared plan of a GPU may be
+ * run, and prepares or passes of such plans that overlap in time (other
+ * streams, other threads) race.
+ */
+#define W4_CHAIN_SCRATCH_BYTES 65536
+w4_status w4_chain_prepare_noalloc(const w4_chain_linear* linears, int64_t count, w4_chain_plan* plan,
+                                   hipStream_t stream);
 
 /*
  * 16-bit scales.  The study's checkpoint sizes imply about two bytes per

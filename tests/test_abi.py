@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(w4):
 
 def test_status_strings(w4):
     lib = w4.library()
-    for s in range(6):
+    for s in range(7):
         assert lib.w4_status_str(s).decode().startswith("W4_")
     assert b"unknown" in lib.w4_status_str(99)
     assert lib.w4_last_hip_error() == 0
