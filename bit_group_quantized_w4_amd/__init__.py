@@ -87,6 +87,11 @@ SIGNATURES = {
     "w4_chain_error": (_INT, [ctypes.POINTER(ChainPlanC), ctypes.POINTER(ctypes.c_uint32), _VP]),
     # GPTQ steps
     "w4_gptq_damp": (_INT, [_VP, _I64, ctypes.c_double, _VP]),
+    "w4_gptq_hessian": (_INT, [_VP, _I64, _I64, _VP, _VP]),
+    "w4_gptq_factor_workspace_bytes": (_SZ, [_I64]),
+    "w4_gptq_inverse_factor": (_INT, [_VP, _I64, _VP, _SZ, _VP, _VP]),
+    "w4_gptq_update": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP]),
+    "w4_dense_linear_f32": (_INT, [_VP, _I64, _I64, _VP, _I64, _VP, _VP]),
     "w4_gptq_block": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "w4_gptq_block_s16": (_INT, [_VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
 }
@@ -436,6 +441,52 @@ def gptq_block(W, U, b0, q_canon, d_canon, err):
     _check(fn(_dev(W, torch.float32, "W"), N, K, int(b0), _dev(U, torch.float32, "U"),
               _dev(q_canon, torch.int8, "q_canon"), _dev(d_canon, sd, "d_canon"),
               _dev(err, torch.float32, "err"), _stream(W)), "w4_gptq_block")
+
+
+def gptq_hessian(x, out=None):
+    """H = (2/T) x^T x, fp64 [K, K], from bf16 calibration rows x [T, K] (w4_gptq_hessian)."""
+    T, K = x.shape
+    H = out if out is not None else torch.empty((K, K), dtype=torch.float64, device=x.device)
+    _check(_lib.w4_gptq_hessian(_dev(x, torch.bfloat16, "x"), T, K, _dev(H, torch.float64, "H"), _stream(x)),
+           "w4_gptq_hessian")
+    return H
+
+
+def gptq_inverse_factor(H, out=None):
+    """U (fp32 [K, K], upper triangular) with H^-1 = U^T U for a damped fp64 Hessian
+    (w4_gptq_inverse_factor; H is not modified)."""
+    K = H.shape[0]
+    if H.dim() != 2 or H.shape[1] != K:
+        raise ValueError("H must be square")
+    nb = int(_lib.w4_gptq_factor_workspace_bytes(K))
+    if nb == 0:
+        _check(W4_ERR_SHAPE, "w4_gptq_factor_workspace_bytes")
+    work = torch.empty(nb, dtype=torch.uint8, device=H.device)
+    U = out if out is not None else torch.empty((K, K), dtype=torch.float32, device=H.device)
+    _check(_lib.w4_gptq_inverse_factor(_dev(H, torch.float64, "H"), K, ctypes.c_void_p(work.data_ptr()), nb,
+                                       _dev(U, torch.float32, "U"), _stream(H)), "w4_gptq_inverse_factor")
+    return U
+
+
+def gptq_update(W, U, b0, err):
+    """In place: W[:, b0+128:] -= err^T U[b0:b0+128, b0+128:] (w4_gptq_update); err fp32 [128, N]."""
+    N, K = W.shape
+    if U.shape != (K, K) or err.shape != (128, N):
+        raise ValueError("shape mismatch")
+    _check(_lib.w4_gptq_update(_dev(W, torch.float32, "W"), N, K, int(b0), _dev(U, torch.float32, "U"),
+                               _dev(err, torch.float32, "err"), _stream(W)), "w4_gptq_update")
+
+
+def dense_linear_f32(x, W, out=None):
+    """y = x W^T in fp32 (x bf16 [T, K], W fp32 [N, K]; w4_dense_linear_f32)."""
+    T, K = x.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    y = out if out is not None else torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _check(_lib.w4_dense_linear_f32(_dev(x, torch.bfloat16, "x"), T, K, _dev(W, torch.float32, "W"), N,
+                                    _dev(y, torch.float32, "y"), _stream(x)), "w4_dense_linear_f32")
+    return y
 
 
 class W4Linear:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 LIB = os.path.join(PKG, "libw4.so")
 
-LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip", "gptq.hip"]
+LIB_SOURCES = ["abi.cpp", "quantize.hip", "linear.hip", "awq.hip", "gptq.hip", "dense.hip"]
 
 ARCH = "gfx950"
 

@@ -2,14 +2,14 @@
 Qwen3.5-4B quantization study, section 2: candidate scales from input
 statistics only, s_j proportional to (mean |x_j|)^alpha for alpha = k/19,
 k = 0..19, compared by the output error on calibration inputs; no clipping
-search).  Every step runs in the library's kernels; the reference output
-W x of the unquantized layer is one plain library GEMM (fp32).  The host only
-picks the smallest of the 20 errors (ties to the smaller exponent).
+search).  Every step runs in the library's kernels, the reference output
+W x of the unquantized layer included (w4_dense_linear_f32, fp32).  The host
+only picks the smallest of the 20 errors (ties to the smaller exponent).
 """
 
 import torch
 
-from . import awq_scales, channel_absmean, linear, quantize_rtn_scaled, scale_activations, sq_error
+from . import awq_scales, channel_absmean, dense_linear_f32, linear, quantize_rtn_scaled, scale_activations, sq_error
 
 ALPHAS = tuple(k / 19 for k in range(20))
 
@@ -25,7 +25,7 @@ def search(W, x_cal, scale_dtype=torch.float32):
     N, K = W.shape
     T = x_cal.shape[0]
     m = channel_absmean(x_cal)
-    y_ref = torch.matmul(x_cal.float(), W.t())  # W x of the unquantized layer, fp32
+    y_ref = dense_linear_f32(x_cal, W)  # W x of the unquantized layer, fp32
     errs = torch.empty(len(ALPHAS), dtype=torch.float64, device=W.device)
     x_s = torch.empty_like(x_cal)
     y = torch.empty((T, N), dtype=torch.bfloat16, device=W.device)

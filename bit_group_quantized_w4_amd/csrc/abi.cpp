@@ -417,6 +417,61 @@ w4_status w4_gptq_block_s16(const float* W, int64_t N, int64_t K, int64_t b0, co
   return gptq_block(W, N, K, b0, U, q_canon, d_canon, true, err, stream);
 }
 
+namespace {
+constexpr int64_t kMaxGptqK = 32768;  // keeps K^2 doubles of work addressable and each grid in range
+
+bool gptq_k_ok(int64_t K) { return K >= kGroup && K % kGroup == 0 && K <= kMaxGptqK; }
+}  // namespace
+
+w4_status w4_gptq_hessian(const uint16_t* x, int64_t T, int64_t K, double* H, hipStream_t stream) {
+  if (T < 1 || T > ((int64_t)1 << 31) / 2 || !gptq_k_ok(K) || T * K > ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (!x || !H) return W4_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(H, 8)) return W4_ERR_ALIGN;
+  if (overlaps(H, 8 * (size_t)K * K, x, 2 * (size_t)T * K)) return W4_ERR_ARG;
+  return hip_status(w4::launch_gptq_hessian(x, T, K, H, stream));
+}
+
+size_t w4_gptq_factor_workspace_bytes(int64_t K) {
+  if (!gptq_k_ok(K)) return 0;
+  return 8 * w4::gptq_factor_work_doubles(K);
+}
+
+w4_status w4_gptq_inverse_factor(const double* H, int64_t K, void* workspace, size_t workspace_bytes, float* U,
+                                 hipStream_t stream) {
+  if (!gptq_k_ok(K)) return W4_ERR_SHAPE;
+  if (!H || !workspace || !U) return W4_ERR_NULL;
+  if (!aligned(H, 8) || !aligned(workspace, 8) || !aligned(U, 4)) return W4_ERR_ALIGN;
+  const size_t wb = w4_gptq_factor_workspace_bytes(K), hb = 8 * (size_t)K * K, ub = 4 * (size_t)K * K;
+  if (workspace_bytes < wb) return W4_ERR_ARG;
+  if (overlaps(workspace, wb, H, hb) || overlaps(workspace, wb, U, ub) || overlaps(U, ub, H, hb)) return W4_ERR_ARG;
+  return hip_status(w4::launch_gptq_inverse_factor(H, K, static_cast<double*>(workspace), U, stream));
+}
+
+w4_status w4_gptq_update(float* W, int64_t N, int64_t K, int64_t b0, const float* U, const float* err,
+                         hipStream_t stream) {
+  if (!n_ok(N) || !gptq_k_ok(K) || N > ((int64_t)1 << 31) - 1 || b0 < 0 || b0 >= K || b0 % kGroup)
+    return W4_ERR_SHAPE;
+  if (N == 0) return W4_OK;
+  if (!W || !U || !err) return W4_ERR_NULL;
+  if (!aligned(W, 4) || !aligned(U, 4) || !aligned(err, 4)) return W4_ERR_ALIGN;
+  const size_t wb = 4 * (size_t)N * K;
+  if (overlaps(W, wb, U, 4 * (size_t)K * K) || overlaps(W, wb, err, 4 * (size_t)kGroup * N)) return W4_ERR_ARG;
+  return hip_status(w4::launch_gptq_update(W, N, K, b0, U, err, stream));
+}
+
+w4_status w4_dense_linear_f32(const uint16_t* x, int64_t T, int64_t K, const float* W, int64_t N, float* y,
+                              hipStream_t stream) {
+  if (T < 0 || N < 0 || K < 1 || T > ((int64_t)1 << 31) - 1 || N > ((int64_t)1 << 31) - 1 ||
+      K > ((int64_t)1 << 31) - 1)
+    return W4_ERR_SHAPE;
+  if (T == 0 || N == 0) return W4_OK;
+  if (!x || !W || !y) return W4_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(W, 4) || !aligned(y, 4)) return W4_ERR_ALIGN;
+  const size_t yb = 4 * (size_t)T * N;
+  if (overlaps(y, yb, x, 2 * (size_t)T * K) || overlaps(y, yb, W, 4 * (size_t)N * K)) return W4_ERR_ARG;
+  return hip_status(w4::launch_dense_linear_f32(x, T, K, W, N, y, stream));
+}
+
 // ---------------------------------------------------------------------------
 // chained decode pass
 // ---------------------------------------------------------------------------

@@ -119,4 +119,19 @@ hipError_t launch_gptq_block(const float* W, int64_t N, int64_t K, int64_t b0, c
                              void* d_canon, bool s16, float* errT, hipStream_t stream);
 hipError_t launch_gptq_damp(double* H, int64_t K, double damp, hipStream_t stream);
 
+// Dense linear algebra of the offline quantizers (dense.hip).
+// H = (2/T) x^T x, fp64 [K][K] (both triangles), from bf16 x [T][K].
+hipError_t launch_gptq_hessian(const uint16_t* x, int64_t T, int64_t K, double* H, hipStream_t stream);
+// Doubles of work launch_gptq_inverse_factor needs for a K x K Hessian.
+size_t gptq_factor_work_doubles(int64_t K);
+// U (fp32 [K][K], upper triangular) with H^-1 = U^T U for the damped H (fp64
+// [K][K], lower triangle read, not modified); K a multiple of 64.
+hipError_t launch_gptq_inverse_factor(const double* H, int64_t K, double* work, float* U, hipStream_t stream);
+// W[:, b0+128:] -= err^T U[b0:b0+128, b0+128:], fp32 (err [128][N]).
+hipError_t launch_gptq_update(float* W, int64_t N, int64_t K, int64_t b0, const float* U, const float* err,
+                              hipStream_t stream);
+// y[t][n] = sum_k x[t][k] W[n][k], fp32 (x bf16 [T][K], W fp32 [N][K], y [T][N]).
+hipError_t launch_dense_linear_f32(const uint16_t* x, int64_t T, int64_t K, const float* W, int64_t N, float* y,
+                                   hipStream_t stream);
+
 }  // namespace w4

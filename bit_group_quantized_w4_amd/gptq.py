@@ -2,20 +2,19 @@
 its settings -- damping 0.01 of the mean Hessian diagonal, 128-column blocks,
 no reordering, RTN's storage; update rule of the published GPTQ algorithm).
 
-The method-specific steps run in the library's kernels: damping the Hessian
-(w4_gptq_damp), the column loop of every block with its code decisions and
-in-block corrections (w4_gptq_block) and the packing into the native layout
-(w4_pack).  Three plain dense linear-algebra steps use the GPU libraries
-PyTorch links: the Hessian product X^T X and the factorization of the damped
-Hessian's inverse (one Cholesky factorization and one triangular inverse),
-both in fp64 -- a strongly anisotropic Hessian (outlier input channels) loses
-too much in an fp32 factorization -- and, in fp32, the product that corrects
-the columns after each block.
+Every step runs in the library's kernels: the Hessian X^T X in fp64
+(w4_gptq_hessian), its damping (w4_gptq_damp), the factor U of the damped
+Hessian's inverse, H^-1 = U^T U, by a blocked fp64 Cholesky factorization and
+triangular inverse (w4_gptq_inverse_factor), the column loop of every block
+with its code decisions and in-block corrections (w4_gptq_block), the product
+correcting the columns after each block (w4_gptq_update), and the packing
+into the native layout (w4_pack).  PyTorch only provides the buffers and the
+stream.
 """
 
 import torch
 
-from . import gptq_block, gptq_damp, pack
+from . import gptq_block, gptq_damp, gptq_hessian, gptq_inverse_factor, gptq_update, pack
 
 DAMP = 0.01
 BLOCK = 128
@@ -23,18 +22,12 @@ BLOCK = 128
 
 def hessian(x_cal):
     """H = (2/T) X^T X, fp64 [K, K], from bf16 calibration rows [T, K]."""
-    X = x_cal.double()
-    return (X.t() @ X).mul_(2.0 / X.shape[0])
+    return gptq_hessian(x_cal)
 
 
 def inverse_factor(H):
-    """U upper triangular with H^-1 = U^T U.
-
-    With J the index reversal, J H J = L L^T (L lower) gives H = V V^T for the
-    upper triangular V = J L J, so H^-1 = (V^-1)^T V^-1 and U = V^-1 = J L^-1 J."""
-    L = torch.linalg.cholesky(torch.flip(H, [0, 1]))
-    eye = torch.eye(H.shape[0], dtype=H.dtype, device=H.device)
-    return torch.flip(torch.linalg.solve_triangular(L, eye, upper=False), [0, 1]).contiguous()
+    """U upper triangular (fp32) with H^-1 = U^T U (H damped; not modified)."""
+    return gptq_inverse_factor(H)
 
 
 def quantize(W, x_cal, damp=DAMP, timings=None, scale_dtype=torch.float32):
@@ -56,6 +49,8 @@ def quantize(W, x_cal, damp=DAMP, timings=None, scale_dtype=torch.float32):
         raise ValueError("x_cal must have at least one row of K inputs")
     if not (damp >= 0.0 and damp < float("inf")):
         raise ValueError("damp must be finite and >= 0")
+    if scale_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("scale_dtype must be torch.float32 or torch.bfloat16")
     marks = []
 
     def mark():
@@ -68,20 +63,16 @@ def quantize(W, x_cal, damp=DAMP, timings=None, scale_dtype=torch.float32):
     H = hessian(x_cal)
     gptq_damp(H, damp)
     mark()
-    U = inverse_factor(H).float()
+    U = inverse_factor(H)
     del H
     mark()
     Wk = W.clone()
     q_canon = torch.empty((N, K), dtype=torch.int8, device=W.device)
-    if scale_dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("scale_dtype must be torch.float32 or torch.bfloat16")
     d_canon = torch.empty((N, K // BLOCK), dtype=scale_dtype, device=W.device)
     err = torch.empty((BLOCK, N), dtype=torch.float32, device=W.device)
     for b0 in range(0, K, BLOCK):
         gptq_block(Wk, U, b0, q_canon, d_canon, err)
-        b1 = b0 + BLOCK
-        if b1 < K:
-            Wk[:, b1:].addmm_(err.t(), U[b0:b1, b1:], alpha=-1.0)
+        gptq_update(Wk, U, b0, err)
     mark()
     q, d = pack(q_canon, d_canon)
     mark()

@@ -451,15 +451,54 @@ w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, doub
  * no reordering).  The update rule is the published GPTQ algorithm.  The
  * quantizer runs, per matrix W [N][K] (fp32, finite) and calibration rows
  * x [T][K]:
- *   H = (2/T) x^T x                          (fp64 [K][K], a plain product)
+ *   w4_gptq_hessian(x) -> H = (2/T) x^T x           (fp64 [K][K])
  *   w4_gptq_damp(H, 0.01)
- *   U = upper triangular with H^-1 = U^T U   (a plain fp64 factorization,
- *                                             then rounded to fp32)
+ *   w4_gptq_inverse_factor(H) -> U                  (upper triangular, fp32,
+ *                                                    H^-1 = U^T U)
  *   for b0 = 0, 128, ...:
  *     w4_gptq_block(W, b0, U) -> codes and scales of columns b0..b0+127, err
- *     W[:, b0+128:] -= err^T U[b0:b0+128, b0+128:]   (a plain product)
+ *     w4_gptq_update(W, b0, U, err): W[:, b0+128:] -= err^T U[b0:b0+128, b0+128:]
  *   w4_pack(codes, scales) -> the native layout w4_linear reads.
+ * The products run in the library's LDS-tiled fp64 / fp32 kernels, each
+ * element summed in a fixed order (bitwise reproducible).
  */
+
+/* H = (2/T) x^T x, fp64 [K][K] row-major, both triangles (H[i][j] is
+ * computed for i >= j and mirrored); each entry sums the exact products of
+ * the bf16 inputs in fp64 over t in order.  x bf16 [T][K] (2-byte aligned),
+ * H 8-byte aligned, disjoint.  T >= 1, T*K <= 2^31; K a multiple of 128 up
+ * to 32768 (else W4_ERR_SHAPE). */
+w4_status w4_gptq_hessian(const uint16_t* x, int64_t T, int64_t K, double* H, hipStream_t stream);
+
+/* Bytes of device workspace w4_gptq_inverse_factor needs: (2 K^2 + 64 K) * 8
+ * (0 for a K it does not take). */
+size_t w4_gptq_factor_workspace_bytes(int64_t K);
+
+/* U (fp32 [K][K] row-major, upper triangular, zeros below the diagonal) with
+ * H^-1 = U^T U, for a damped Hessian H (fp64 [K][K]; only its lower triangle
+ * is read; not modified): with J the index reversal, J H J = L L^T (blocked
+ * Cholesky, fp64), and U = J L^-1 J (blocked triangular inverse, fp64),
+ * rounded to fp32.  A matrix that is not positive definite gives NaN in U.
+ * workspace: device, 8-byte aligned, >= w4_gptq_factor_workspace_bytes(K)
+ * (else W4_ERR_ARG); H, U and the workspace disjoint.  K as for
+ * w4_gptq_hessian. */
+w4_status w4_gptq_inverse_factor(const double* H, int64_t K, void* workspace, size_t workspace_bytes, float* U,
+                                 hipStream_t stream);
+
+/* The correction of the columns after block b0 (a multiple of 128):
+ * W[n][k] -= sum_{j<128} err[j][n] U[b0 + j][k] for k >= b0 + 128, fp32 (each
+ * element summed over j in order).  W fp32 [N][K], U fp32 [K][K], err fp32
+ * [128][N] (as w4_gptq_block writes it), all 4-byte aligned; W disjoint from
+ * U and err.  Nothing is done for the last block. */
+w4_status w4_gptq_update(float* W, int64_t N, int64_t K, int64_t b0, const float* U, const float* err,
+                         hipStream_t stream);
+
+/* The unquantized layer's output, y[t][n] = sum_k x[t][k] W[n][k] in fp32
+ * (each element summed over k in order): the reference the channel-scaling
+ * search compares quantized outputs with.  x bf16 [T][K] (2-byte aligned), W
+ * fp32 [N][K], y fp32 [T][N] (4-byte aligned, disjoint from x and W). */
+w4_status w4_dense_linear_f32(const uint16_t* x, int64_t T, int64_t K, const float* W, int64_t N, float* y,
+                              hipStream_t stream);
 
 /* H [K][K] fp64 row-major, in place: a zero diagonal entry becomes 1, then
  * damp * mean(diag) is added to every diagonal entry (fixed summation
