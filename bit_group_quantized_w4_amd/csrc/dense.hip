@@ -53,8 +53,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, Acc alph
   constexpr int BT = 16 * TM;  // tile edge
   const int m0 = blockIdx.y * BT, n0 = blockIdx.x * BT;
   if (MODE != kFull && n0 > m0 + BT - 1) return;  // entirely above the diagonal
-  __shared__ Acc as[kKC][BT + 1];
-  __shared__ Acc bs[kKC][BT + 1];
+  // rows padded by 16 bytes: 16-byte aligned for wide LDS reads, rows on shifted banks
+  constexpr int kPad = 16 / sizeof(Acc);
+  __shared__ Acc as[kKC][BT + kPad];
+  __shared__ Acc bs[kKC][BT + kPad];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   Acc acc[TM][TM];
 #pragma unroll
@@ -126,37 +128,33 @@ constexpr int kNB = 64;
 
 // In place: the lower triangle of the 64 x 64 block at A (leading dimension
 // lda) becomes its Cholesky factor L (A = L L^T), by the right-looking
-// algorithm in LDS.  A pivot that is not positive gives NaN (or infinity),
-// which spreads through everything computed from it.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* A, int64_t lda) {
+// algorithm in LDS with one wavefront, lane r owning row r.  A pivot that is
+// not positive gives NaN (or infinity), which spreads through everything
+// computed from it.
+__global__ __launch_bounds__(kNB) void potrf_diag_kernel(double* A, int64_t lda) {
   __shared__ double a[kNB][kNB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int r = e / kNB, c = e % kNB;
-    a[r][c] = c <= r ? A[(int64_t)r * lda + c] : 0.0;
-  }
+  const int r = threadIdx.x;
+  for (int c = 0; c <= r; ++c) a[r][c] = A[(int64_t)r * lda + c];
   __syncthreads();
   for (int c = 0; c < kNB; ++c) {
-    if (tid == 0) a[c][c] = sqrt(a[c][c]);
+    if (r == c) a[c][c] = sqrt(a[c][c]);
     __syncthreads();
-    if (tid > c && tid < kNB) a[tid][c] /= a[c][c];
-    __syncthreads();
-    for (int e = tid; e < kNB * kNB; e += 256) {
-      const int r = e / kNB, k = e % kNB;
-      if (k > c && k <= r) a[r][k] = fma(-a[r][c], a[k][c], a[r][k]);
+    if (r > c) {
+      const double l = a[r][c] / a[c][c];
+      a[r][c] = l;
+      for (int k = c + 1; k <= r; ++k) a[r][k] = fma(-l, a[k][c], a[r][k]);
     }
     __syncthreads();
   }
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int r = e / kNB, c = e % kNB;
-    if (c <= r) A[(int64_t)r * lda + c] = a[r][c];
-  }
+  for (int c = 0; c <= r; ++c) A[(int64_t)r * lda + c] = a[r][c];
 }
 
 // X = L^-1 for the lower triangular 64 x 64 blocks L at A + i (64 lda + 64)
 // (block i = blockIdx.x), written to X at the same position (leading
 // dimension ldx; its upper triangle becomes 0).  Column j of X by forward
-// substitution in one thread: X[i][j] = -(sum_{k=j}^{i-1} L[i][k] X[k][j]) / L[i][i].
+// substitution, X[i][j] = -(sum_{k=j}^{i-1} L[i][k] X[k][j]) / L[i][i], with
+// the sum over k split among four lanes (k = j + 4t + u, lane u) and their
+// partial sums added in a fixed order.
 __global__ __launch_bounds__(256) void trtri_diag_kernel(const double* A, int64_t lda, double* X, int64_t ldx) {
   __shared__ double l[kNB][kNB + 1];
   __shared__ double x[kNB][kNB + 1];
@@ -167,23 +165,20 @@ __global__ __launch_bounds__(256) void trtri_diag_kernel(const double* A, int64_
   for (int e = tid; e < kNB * kNB; e += 256) {
     const int r = e / kNB, c = e % kNB;
     l[r][c] = c <= r ? Ab[(int64_t)r * lda + c] : 0.0;
+    x[r][c] = 0.0;
   }
   __syncthreads();
-  if (tid < kNB) {
-    const int j = tid;
-    for (int i = 0; i < kNB; ++i) {
-      if (i < j) {
-        x[i][j] = 0.0;
-      } else if (i == j) {
-        x[i][j] = 1.0 / l[j][j];
-      } else {
-        double s = 0.0;
-        for (int k = j; k < i; ++k) s = fma(l[i][k], x[k][j], s);
-        x[i][j] = -s / l[i][i];
-      }
-    }
-  }
+  const int j = tid >> 2, u = tid & 3;  // column, and this lane's share of the sum
+  if (u == 0) x[j][j] = 1.0 / l[j][j];
   __syncthreads();
+  for (int i = 1; i < kNB; ++i) {
+    double s = 0.0;
+    for (int k = j + u; k < i; k += 4) s = fma(l[i][k], x[k][j], s);
+    // lanes 4j .. 4j+3 are adjacent: add the four shares in lane order
+    const double s1 = __shfl_down(s, 1, 4), s2 = __shfl_down(s, 2, 4), s3 = __shfl_down(s, 3, 4);
+    if (u == 0 && i > j) x[i][j] = -(((s + s1) + s2) + s3) / l[i][i];
+    __syncthreads();
+  }
   for (int e = tid; e < kNB * kNB; e += 256) {
     const int r = e / kNB, c = e % kNB;
     Xb[(int64_t)r * ldx + c] = x[r][c];
@@ -214,13 +209,13 @@ unsigned grid_x(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256,
 
 }  // namespace
 
-size_t gptq_factor_work_doubles(int64_t K) { return (size_t)K * K * 2 + (size_t)kNB * K; }
+size_t gptq_factor_work_doubles(int64_t K) { return (size_t)K * K * 2 + (size_t)kNB * kNB; }
 
 // H (fp64 [K][K], damped, lower triangle read) -> U upper triangular fp32
 // [K][K] with H^-1 = U^T U.  With J the index reversal, J H J = L L^T (L
 // lower) gives H = V V^T for the upper triangular V = J L J, hence
 // H^-1 = (V^-1)^T V^-1 and U = V^-1 = J L^-1 J.  work: gptq_factor_work_doubles(K)
-// doubles: L (the factorization in place of J H J), X = L^-1, and a 64 x K panel.
+// doubles: L (the factorization in place of J H J), X = L^-1, and a 64 x 64 block.
 hipError_t launch_gptq_inverse_factor(const double* H, int64_t K, double* work, float* U, hipStream_t s) {
   const int64_t nb = K / kNB;
   double* L = work;
@@ -232,7 +227,7 @@ hipError_t launch_gptq_inverse_factor(const double* H, int64_t K, double* work, 
   for (int64_t jb = 0; jb < nb; ++jb) {
     const int64_t j0 = jb * kNB, rest = K - j0 - kNB;
     double* Ljj = L + j0 * K + j0;
-    potrf_diag_kernel<<<1, 256, 0, s>>>(Ljj, K);
+    potrf_diag_kernel<<<1, kNB, 0, s>>>(Ljj, K);
     if (hipError_t e = hipGetLastError()) return e;
     if (rest == 0) break;
     // panel P = L[j0+64:, j0:j0+64] <- P Ljj^-T (Ljj^-1 into the 64 x 64 corner of T)
@@ -252,19 +247,33 @@ hipError_t launch_gptq_inverse_factor(const double* H, int64_t K, double* work, 
                                                                                     1.0, Ct, K, s))
       return e;
   }
-  // X = L^-1: the diagonal blocks, then block row by block row
-  // X[i0:i0+64, 0:i0] = -X_ii (L[i0:i0+64, 0:i0] X[0:i0, 0:i0])
+  // X = L^-1, block row by block row.  Below the finished rows, X holds the
+  // running sums S[i][j] = sum over finished block rows k of L[i][k] X[k][j];
+  // block row i is then X[i][j] = -X[i][i] S[i][j] (j < i), X[i][i] = L[i][i]^-1,
+  // and its rows are added into S of every later block row:
+  // S[i+1:, 0:i+1] += L[i+1:, i] X[i, 0:i+1] (a product with 64-wide inner dimension).
   zero_f64_kernel<<<1024, 256, 0, s>>>(X, (int64_t)K * K);
   if (hipError_t e = hipGetLastError()) return e;
   trtri_diag_kernel<<<(unsigned)nb, 256, 0, s>>>(L, K, X, K);
   if (hipError_t e = hipGetLastError()) return e;
-  for (int64_t ib = 1; ib < nb; ++ib) {
+  for (int64_t ib = 0; ib < nb; ++ib) {
     const int64_t i0 = ib * kNB;
-    if (hipError_t e = gemm<double, double, double, false, false, 4, kFull>(kNB, i0, i0, 1.0, L + i0 * K, K, X, K,
-                                                                             0.0, T, K, s))
-      return e;
-    if (hipError_t e = gemm<double, double, double, false, false, 4, kFull>(kNB, i0, kNB, -1.0, X + i0 * K + i0, K,
-                                                                             T, K, 0.0, X + i0 * K, K, s))
+    if (ib > 0) {
+      // in place: each block reads only the 64-wide column tile of S it writes
+      if (hipError_t e = gemm<double, double, double, false, false, 4, kFull>(kNB, i0, kNB, -1.0, X + i0 * K + i0, K,
+                                                                               X + i0 * K, K, 0.0, X + i0 * K, K, s))
+        return e;
+    }
+    const int64_t rest = K - i0 - kNB;
+    if (rest == 0) break;
+    double* Srest = X + (i0 + kNB) * K;
+    if (hipError_t e = rest >= 1024 && i0 + kNB >= 1024
+                           ? gemm<double, double, double, false, false, 8, kFull>(rest, i0 + kNB, kNB, 1.0,
+                                                                                    L + (i0 + kNB) * K + i0, K,
+                                                                                    X + i0 * K, K, 1.0, Srest, K, s)
+                           : gemm<double, double, double, false, false, 4, kFull>(rest, i0 + kNB, kNB, 1.0,
+                                                                                    L + (i0 + kNB) * K + i0, K,
+                                                                                    X + i0 * K, K, 1.0, Srest, K, s))
       return e;
   }
   flip_to_upper_f32_kernel<<<dim3(grid_x(K), (unsigned)K), 256, 0, s>>>(X, U, K);

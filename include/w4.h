@@ -470,7 +470,7 @@ w4_status w4_sq_error(const uint16_t* y, const float* y_ref, int64_t count, doub
  * to 32768 (else W4_ERR_SHAPE). */
 w4_status w4_gptq_hessian(const uint16_t* x, int64_t T, int64_t K, double* H, hipStream_t stream);
 
-/* Bytes of device workspace w4_gptq_inverse_factor needs: (2 K^2 + 64 K) * 8
+/* Bytes of device workspace w4_gptq_inverse_factor needs: (2 K^2 + 4096) * 8
  * (0 for a K it does not take). */
 size_t w4_gptq_factor_workspace_bytes(int64_t K);
 
