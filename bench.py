@@ -140,17 +140,18 @@ def bench_pair(torch, w4, workloads, steps, warmup, copies, scale_dtype=None, ms
         # batched mode: every linear of a step writes its own output
         ysb = [[torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for (m, _, _, _) in mats]
                for _ in range(copies)]
+        ws = w4.SplitWorkspace(dev) if M > 1 else None
 
         def step():
             for c in range(copies):
                 for i, (m, _, qs, ds) in enumerate(mats):
-                    w4.linear(xs[i], qs[c], ds[c], m.N, out=ys[i])
+                    w4.linear(xs[i], qs[c], ds[c], m.N, out=ys[i], workspace=ws)
 
         def step_batched():
             items = [(xs[i], qs[c], ds[c], m.N, ysb[c][i])
                      for c in range(copies) for i, (m, _, qs, ds) in enumerate(mats)]
             for b in range(0, len(items), w4.MAX_BATCH):
-                w4.linear_batched(items[b:b + w4.MAX_BATCH])
+                w4.linear_batched(items[b:b + w4.MAX_BATCH], workspace=ws)
 
         step_bytes = copies * sum(workloads.algorithmic_bytes(M, m.N, m.K, sb) for (m, _, _, _) in mats)
         res = {}
@@ -257,6 +258,8 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
             continue
         xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
         ys = [torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices]
+        # verification widths: the MFMA kernel may split a launch's K across blocks
+        ws = w4.SplitWorkspace(dev) if M > 1 else None
         res[M] = {}
         for mode, grp in groups.items():
             def step():
@@ -264,10 +267,10 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
                     for gi in grp:
                         if len(gi) == 1:
                             m, q, d = mats[gi[0]]
-                            w4.linear(xs[m.K], q, d, m.N, out=ys[gi[0]])
+                            w4.linear(xs[m.K], q, d, m.N, out=ys[gi[0]], workspace=ws)
                         else:
                             w4.linear_batched([(xs[mats[i][0].K], mats[i][1], mats[i][2], mats[i][0].N, ys[i])
-                                               for i in gi])
+                                               for i in gi], workspace=ws)
 
             g = capture(torch, step)
             t = time_graph(torch, g, steps, warmup)

@@ -78,6 +78,13 @@ SIGNATURES = {
     "w4_scale_activations": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP]),
     "w4_linear_awq": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _VP, _VP, _VP]),
     "w4_sq_error": (_INT, [_VP, _VP, _I64, _VP, _VP]),
+    # split launches (draft verification widths)
+    "w4_split_workspace_bytes": (_SZ, []),
+    "w4_split_workspace_init": (_INT, [_VP, _SZ, _VP]),
+    "w4_split_workspace_error": (_INT, [_VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "w4_linear_batched_split": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP, _SZ, _VP]),
+    "w4_linear_batched_split_s16": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP, _SZ, _VP]),
+    "w4_linear_batched_split_f32": (_INT, [ctypes.POINTER(LinearDesc), _INT, _INT, _VP, _SZ, _VP]),
     # chained decode pass
     "w4_chain_workspace_bytes": (_SZ, [_I64]),
     "w4_chain_prepare": (_INT, [ctypes.POINTER(ChainLinear), _I64, _VP, _SZ, ctypes.POINTER(ChainPlanC), _VP]),
@@ -194,11 +201,40 @@ def quantize_rtn(W, out=None, scale_dtype=torch.float32):
 OUT_DTYPES = (torch.bfloat16, torch.float32)
 
 
-def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16):
+class SplitWorkspace:
+    """Device workspace of the split launches (w4_split_workspace_init): pass it
+    as `workspace=` to linear / linear_batched.  Calls that use one workspace
+    must be ordered (one stream)."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.nbytes = int(_lib.w4_split_workspace_bytes())
+        self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+        self.init()
+
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def init(self):
+        """(Re-)initialise on the current stream."""
+        _check(_lib.w4_split_workspace_init(ctypes.c_void_p(self.buffer.data_ptr()), self.nbytes, self._stream()),
+               "w4_split_workspace_init")
+
+    def error(self):
+        """The workspace's error flag (synchronises the current stream)."""
+        flag = ctypes.c_uint32(0)
+        _check(_lib.w4_split_workspace_error(ctypes.c_void_p(self.buffer.data_ptr()), ctypes.byref(flag),
+                                             self._stream()), "w4_split_workspace_error")
+        return int(flag.value)
+
+
+def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16, workspace=None):
     """y [M, N] = x [M, K] bf16 times the dequantized weight (native q, d).
 
     y is bf16 by default; with out_dtype=torch.float32 (or an fp32 `out`) it is the
-    fp32 value the kernel accumulated, before rounding (the *_f32 entry points)."""
+    fp32 value the kernel accumulated, before rounding (the *_f32 entry points).
+    With a SplitWorkspace the MFMA kernel may split K across blocks
+    (w4_linear_batched_split*)."""
     M, K = x.shape
     if out is not None:
         out_dtype = out.dtype
@@ -209,6 +245,8 @@ def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16):
         raise ValueError("out must be [M, N]")
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
+    if workspace is not None:
+        return linear_batched([(x, q, d, N, y)], path=path, workspace=workspace)[0]
     sd = _scale_dtype(d)
     if out_dtype == torch.float32:
         fn, name = ((_lib.w4_linear_f32_s16, "w4_linear_f32_s16") if sd == torch.bfloat16
@@ -221,12 +259,13 @@ def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16):
     return y
 
 
-def linear_batched(items, path="auto"):
+def linear_batched(items, path="auto", workspace=None):
     """Several independent linears in one launch.
 
     items: sequence of (x [M, K] bf16, q, d, N, y [M, N]) with every y
     preallocated; at most MAX_BATCH items.  y is bf16 throughout, or fp32
-    throughout (fp32 scales only: w4_linear_batched_f32).  Returns the list of y.
+    throughout (fp32 scales only: w4_linear_batched_f32).  With a
+    SplitWorkspace, the split entry points.  Returns the list of y.
     """
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
@@ -248,11 +287,15 @@ def linear_batched(items, path="auto"):
         stream = stream or _stream(x)
     # the descriptor structs of every variant have the same layout (pointers and int64s)
     if od == torch.float32:
-        fn, name = _lib.w4_linear_batched_f32, "w4_linear_batched_f32"
+        name = "w4_linear_batched_f32"
     else:
-        fn, name = ((_lib.w4_linear_batched_s16, "w4_linear_batched_s16") if sd == torch.bfloat16
-                    else (_lib.w4_linear_batched, "w4_linear_batched"))
-    _check(fn(descs, len(items), PATHS[path], stream), name)
+        name = "w4_linear_batched_s16" if sd == torch.bfloat16 else "w4_linear_batched"
+    if workspace is not None:
+        name = name.replace("batched", "batched_split")
+        _check(getattr(_lib, name)(descs, len(items), PATHS[path], ctypes.c_void_p(workspace.buffer.data_ptr()),
+                                   workspace.nbytes, stream), name)
+    else:
+        _check(getattr(_lib, name)(descs, len(items), PATHS[path], stream), name)
     return [it[4] for it in items]
 
 
@@ -506,7 +549,7 @@ class W4Linear:
 
 __all__ = [
     "GROUP", "LIB_PATH", "MAX_BATCH", "OUT_DTYPES", "PATHS", "SCALE_DTYPES", "SIGNATURES", "LinearDesc", "W4Error",
-    "W4Linear",
+    "W4Linear", "SplitWorkspace",
     "awq_scales", "channel_absmean", "library", "linear", "linear_awq", "linear_batched",
     "quantize_rtn_scaled", "scale_activations", "sq_error",
     "pack", "packed_bytes", "quantize_rtn", "scale_count", "unpack",

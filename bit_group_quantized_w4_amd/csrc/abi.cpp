@@ -102,18 +102,37 @@ w4_status check_aliasing(const LinearArgs* l, int count, size_t scale_elem) {
   return W4_OK;
 }
 
-w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, bool s16, hipStream_t stream) {
+w4_status run_batch(w4::BatchArgs& a, int path, int64_t max_m, int64_t max_k, bool s16, hipStream_t stream,
+                    void* split_ws = nullptr, size_t split_ws_bytes = 0) {
   if (a.count == 0) return W4_OK;
   if (path == W4_PATH_AUTO) path = auto_path(max_m, max_k);
   if (path == W4_PATH_GEMV) {
     if (w4::gemv_lds_bytes(1, max_k) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
     return hip_status(w4::launch_linear_gemv(a, w4::gemv_rows_per_slab(max_m, max_k), s16, stream));
   }
-  return hip_status(w4::launch_linear_mfma(a, s16, stream));
+  return hip_status(w4::launch_linear_mfma(a, s16, stream, split_ws, split_ws_bytes));
+}
+
+bool split_workspace_ok(const void* ws, size_t bytes) {
+  return ws && aligned(ws, 256) && bytes >= W4_SPLIT_WORKSPACE_BYTES;
+}
+
+// The split workspace may share no byte with any operand of the call.
+bool split_workspace_disjoint(const void* ws, size_t bytes, const LinearArgs* l, int count, size_t scale_elem) {
+  for (int i = 0; i < count; ++i) {
+    if (l[i].M <= 0 || l[i].N <= 0) continue;
+    if (overlaps(ws, bytes, l[i].x, 2 * (size_t)l[i].M * l[i].K) ||
+        overlaps(ws, bytes, l[i].q, w4_packed_bytes(l[i].N, l[i].K)) ||
+        overlaps(ws, bytes, l[i].d, scale_elem * w4_scale_count(l[i].N, l[i].K)) ||
+        overlaps(ws, bytes, l[i].y, l[i].ybytes * (size_t)l[i].M * l[i].N))
+      return false;
+  }
+  return true;
 }
 
 template <typename Desc>
-w4_status linear_batched(const Desc* linears, int count, int path, bool s16, hipStream_t stream) {
+w4_status linear_batched(const Desc* linears, int count, int path, bool s16, hipStream_t stream,
+                         void* split_ws = nullptr, size_t split_ws_bytes = 0) {
   if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_MFMA) return W4_ERR_ARG;
   if (count < 0 || count > W4_MAX_BATCH) return W4_ERR_ARG;
   if (count == 0) return W4_OK;
@@ -133,7 +152,16 @@ w4_status linear_batched(const Desc* linears, int count, int path, bool s16, hip
   }
   const w4_status al = check_aliasing(args, count, s16 ? 2 : 4);
   if (al != W4_OK) return al;
-  return run_batch(a, path, max_m, max_k, s16, stream);
+  if (split_ws && !split_workspace_disjoint(split_ws, split_ws_bytes, args, count, s16 ? 2 : 4)) return W4_ERR_ARG;
+  return run_batch(a, path, max_m, max_k, s16, stream, split_ws, split_ws_bytes);
+}
+
+template <typename Desc>
+w4_status linear_batched_split(const Desc* linears, int count, int path, bool s16, void* ws, size_t bytes,
+                               hipStream_t stream) {
+  if (!ws) return W4_ERR_NULL;
+  if (!split_workspace_ok(ws, bytes)) return !aligned(ws, 256) ? W4_ERR_ALIGN : W4_ERR_ARG;
+  return linear_batched(linears, count, path, s16, stream, ws, bytes);
 }
 
 w4_status quantize(const float* W, int64_t N, int64_t K, uint8_t* q_packed, void* d_packed, bool s16,
@@ -270,6 +298,39 @@ w4_status w4_linear_f32_s16(const uint16_t* x, int64_t M, int64_t K, const uint8
     float* y;
   } l = {x, M, K, q_packed, d_packed, N, y};
   return linear_batched(&l, 1, path, true, stream);
+}
+
+size_t w4_split_workspace_bytes(void) { return W4_SPLIT_WORKSPACE_BYTES; }
+
+w4_status w4_split_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return W4_ERR_NULL;
+  if (!aligned(workspace, 256)) return W4_ERR_ALIGN;
+  if (workspace_bytes < W4_SPLIT_WORKSPACE_BYTES) return W4_ERR_ARG;
+  return hip_status(w4::launch_split_init(workspace, workspace_bytes, stream));
+}
+
+w4_status w4_split_workspace_error(const void* workspace, uint32_t* flag, hipStream_t stream) {
+  if (!workspace || !flag) return W4_ERR_NULL;
+  uint32_t v = 0;
+  if (hipError_t e = hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, stream)) return hip_status(e);
+  if (hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
+  *flag = v;
+  return W4_OK;
+}
+
+w4_status w4_linear_batched_split(const w4_linear_desc* linears, int count, int path, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return linear_batched_split(linears, count, path, false, workspace, workspace_bytes, stream);
+}
+
+w4_status w4_linear_batched_split_s16(const w4_linear_desc_s16* linears, int count, int path, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return linear_batched_split(linears, count, path, true, workspace, workspace_bytes, stream);
+}
+
+w4_status w4_linear_batched_split_f32(const w4_linear_desc_f32* linears, int count, int path, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return linear_batched_split(linears, count, path, false, workspace, workspace_bytes, stream);
 }
 
 w4_status w4_pack(const int8_t* q_canon, const float* d_canon, int64_t N, int64_t K,
@@ -587,6 +648,20 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   w4::chain_cfg(ci, &R, &NW);
   const size_t lds = (size_t)w4::gemv_lds_bytes(1, kmax);
 
+  // Grid: every block resident at once (waits look only at earlier items).
+  // Two blocks per CU measured fastest; W4_CHAIN_BLOCKS may ask for another
+  // count, up to what is resident.
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_status(e);
+  if (hipError_t e = w4::chain_blocks_per_cu(ci, s16, lds, &per_cu)) return hip_status(e);
+  if (per_cu < 1 || cus < 1) return hip_status(hipErrorInvalidConfiguration);
+  const int64_t resident = (int64_t)per_cu * cus;
+  int64_t blocks = resident < 2 * (int64_t)cus ? resident : 2 * (int64_t)cus;
+  if (const char* e = getenv("W4_CHAIN_BLOCKS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) blocks = v < resident ? v : resident;
+  }
   // Table: the linears of each stage laid out longest K first (stable), as a
   // batched launch does, each followed by its panels of R row blocks.  The
   // entries are built kChunk at a time and uploaded.
@@ -649,20 +724,6 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
     if (hipError_t err = hipStreamSynchronize(stream)) return hip_status(err);
   }
 
-  // Grid: every block resident at once (waits look only at earlier items).
-  // Two blocks per CU measured fastest; W4_CHAIN_BLOCKS may ask for another
-  // count, up to what is resident.
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
-  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_status(e);
-  if (hipError_t e = w4::chain_blocks_per_cu(ci, s16, lds, &per_cu)) return hip_status(e);
-  if (per_cu < 1 || cus < 1) return hip_status(hipErrorInvalidConfiguration);
-  const int64_t resident = (int64_t)per_cu * cus;
-  int64_t blocks = resident < 2 * (int64_t)cus ? resident : 2 * (int64_t)cus;
-  if (const char* e = getenv("W4_CHAIN_BLOCKS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v > 0) blocks = v < resident ? v : resident;
-  }
   if (blocks > items) blocks = items;
 
   plan->workspace = workspace;

@@ -95,29 +95,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // Which linear of the batch, and which (row panel, x slab) of it, a block runs.
 struct Work {
   int di, rb0, m0;
+  int ks = 0, nks = 1;  // K slice of the block and slices per (row panel, x slab) (split launches)
 };
 
-__device__ __forceinline__ Work locate(const BatchArgs& a, int R, int MT) {
+__device__ __forceinline__ Work locate(const BatchArgs& a, int R, int MT, int S = 1) {
   const int b = blockIdx.x;
   int di = 0;
+  if (a.count <= 4) {  // the projections of a layer that share an input: a short scan
 #pragma unroll
-  for (int i = 1; i < kMaxBatch; ++i)
-    if (i < a.count && b >= a.block0[i]) di = i;
+    for (int i = 1; i < 4; ++i)
+      if (i < a.count && b >= a.block0[i]) di = i;
+  } else {
+#pragma unroll
+    for (int i = 1; i < kMaxBatch; ++i)
+      if (i < a.count && b >= a.block0[i]) di = i;
+  }
   const LinearDesc& d = a.desc[di];
   const int nb = (d.N + kTileRows - 1) / kTileRows;
   const int panels = (nb + R - 1) / R;
-  const int local = b - a.block0[di];
+  const int all = b - a.block0[di];
+  const int local = S == 1 ? all : (int)((uint32_t)all / (uint32_t)S);  // no division when unsplit
   const int slab = local / panels;
-  return Work{di, (local - slab * panels) * R, slab * MT};
+  return Work{di, (local - slab * panels) * R, slab * MT, all - local * S, S};
 }
 
 // The same for a launch of one linear.
-__device__ __forceinline__ Work locate_one(int N, int R, int MT) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ Work locate_one(int N, int R, int MT, int S = 1) {
+  const int all = blockIdx.x;
+  const int b = S == 1 ? all : (int)((uint32_t)all / (uint32_t)S);
   const int nb = (N + kTileRows - 1) / kTileRows;
   const int panels = (nb + R - 1) / R;
   const int slab = b / panels;
-  return Work{0, (b - slab * panels) * R, slab * MT};
+  return Work{0, (b - slab * panels) * R, slab * MT, all - b * S, S};
 }
 
 // Geometry of one linear and the weight-side buffers of one wavefront
@@ -135,8 +144,17 @@ struct Weights {
     GP = 4 * Q;
     nb = (D.N + kTileRows - 1) / kTileRows;
     rvalid = min(R, nb - wk.rb0);
-    j0 = (int)(((int64_t)Q * wave) / nw);
-    j1 = (int)(((int64_t)Q * (wave + 1)) / nw);
+    // the wavefront's range of scale quads: part `wave` of nw of the block's
+    // K slice (Q * parts < 2^22: 32-bit arithmetic; nw is a compile-time
+    // constant, so the unsplit case needs no division instruction sequence)
+    if (wk.nks == 1) {
+      j0 = (int)(((uint32_t)Q * (uint32_t)wave) / (uint32_t)nw);
+      j1 = (int)(((uint32_t)Q * (uint32_t)(wave + 1)) / (uint32_t)nw);
+    } else {
+      const uint32_t part = (uint32_t)(wk.ks * nw + wave), parts = (uint32_t)(wk.nks * nw);
+      j0 = (int)(((uint32_t)Q * part) / parts);
+      j1 = (int)(((uint32_t)Q * (part + 1)) / parts);
+    }
     rq = make_rsrc(D.q, (uint32_t)nb * GP * 1024u);
     rd = make_rsrc(D.d, (uint32_t)nb * GP * 4u * kScaleBytes);
 #pragma unroll
@@ -155,26 +173,137 @@ struct Weights {
 };
 
 // ---------------------------------------------------------------------------
+// Split launches (MFMA kernel, one slab of at most 16 x rows): the K range of
+// a row panel is divided among S consecutive blocks.  Slices 0 .. S-2 write
+// their fp32 partial sums to the workspace; the last slice waits for them,
+// adds them in slice order and then its own, and stores the output, so the
+// result does not depend on which block finishes first.  Completion is the
+// data itself: a slot holds kPartUnwritten until its partial is written (a
+// NaN pattern partial sums never take: it is replaced on the way out), is
+// read with coherent loads, and is reset to kPartUnwritten by the last slice
+// once read, so each call leaves the workspace as it found it.  The last
+// slice of a panel is its highest-numbered block, and blocks are dispatched
+// in order, so every block it waits for has been dispatched before it and
+// waits for nothing: each wait ends.  It is bounded all the same (a timeout
+// sets the workspace's error word and the output becomes NaN).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPartUnwritten = 0xFFFFFFFFu;
+constexpr uint32_t kPartNanForUnwritten = 0xFFC00000u;
+constexpr uint32_t kSplitSpinLimit = 1u << 17;  // polls (each at least one memory round trip)
+constexpr int kMaxSplit = 8;
+
+// Slot of row block r of the panel of block b: 64 lanes x 16 bytes.
+__device__ __forceinline__ uint32_t* split_slot(uint8_t* ws, int R, int b, int r) {
+  return reinterpret_cast<uint32_t*>(ws + kSplitHeaderBytes + ((size_t)b * R + r) * 1024u) +
+         4 * (threadIdx.x & 63);
+}
+
+__device__ __forceinline__ void split_publish(uint32_t* slot, const f32x4& v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t b = __float_as_uint(v[e]);
+    __hip_atomic_store(slot + e, b == kPartUnwritten ? kPartNanForUnwritten : b, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waits for the partial in `slot`, returns it and marks the slot unwritten again.
+__device__ __forceinline__ f32x4 split_take(uint32_t* slot, uint32_t* error) {
+  uint32_t v[4];
+  for (uint32_t t = 0;; ++t) {
+    bool u = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      u |= v[e] == kPartUnwritten;
+    }
+    if (!__any(u)) break;
+    if (t >= kSplitSpinLimit) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;  // the unwritten pattern is a NaN: the output shows the failure
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) __hip_atomic_store(slot + e, kPartUnwritten, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
+
+// One output tile (16 rows x 16 x rows, this lane's four values) of a block
+// whose sum covers its K slice only.  Unsplit: v is final.  Slices before the
+// last publish v and return false; the last slice turns v into
+// ((p_0 + p_1) + ... + p_{S-2}) + v and returns true.  `slots` per block,
+// `slot` this tile's index among them.
+__device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int slots, int slot, f32x4& v) {
+  if (wk.nks == 1) return true;
+  if (wk.ks + 1 < wk.nks) {
+    split_publish(split_slot(ws, slots, blockIdx.x, slot), v);
+    return false;
+  }
+  uint32_t* error = reinterpret_cast<uint32_t*>(ws);
+  const int b0 = blockIdx.x - (wk.nks - 1);
+  f32x4 t = split_take(split_slot(ws, slots, b0, slot), error);
+  for (int k = 1; k + 1 < wk.nks; ++k) {
+    const f32x4 p = split_take(split_slot(ws, slots, b0 + k, slot), error);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = t[e] + v[e];
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // MFMA kernel.  One v_mfma_f32_16x16x32_bf16 per 32-input step: A = 16 rows
 // of x, B = the tile's 16 rows of W^T.  Lane l holds A[l%16][8(l/16)..+7],
 // B[8(l/16)..+7][l%16] and D[4(l/16)+j][l%16], j = 0..3.  Rows of A at or
 // beyond M read zeros (their outputs are discarded).  The -1.5*sum(x) start
 // value is itself one MFMA chain with B = -1.5.  One quad is in flight: the x
-// operands of a quad alone take 64 VGPRs.
+// loads of a quad alone take 64 VGPRs.
+//
+// Two routes for x (XL):
+//   * registers (M <= 8): each lane loads its A operand directly, 16 rows x
+//     64 bytes per instruction; rows at or past M are out of range, so at
+//     M <= 8 half the lanes load nothing;
+//   * a slot of LDS private to the wavefront (M > 8): the group's 16 x
+//     256-byte tile is loaded four rows per instruction, 16 lanes reading one
+//     row's 256 contiguous bytes (two whole cache lines per row), written to
+//     the slot and read back in the A layout one group ahead, so the LDS
+//     round trip overlaps the previous group's MFMA chains.  With every row
+//     of the tile carrying data, the direct loads touch sixteen half lines
+//     per instruction whose lookups (rows a large power-of-two stride apart)
+//     stall the vector L1 on tag conflicts: that was the limit of the split-K
+//     launches at M = 16 (counters: the L1's address unit stalled by the
+//     cache two thirds of its busy time).  At M <= 8 the direct loads are
+//     cheaper than the extra LDS traffic.  The slot needs no barrier: a
+//     wavefront's LDS accesses execute in program order, so the next group's
+//     writes follow this group's reads.
 // ---------------------------------------------------------------------------
-template <int R, int NW, bool S16>
-__device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int R, int NW, bool S16, bool XL>
+__device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, uint8_t* ws = nullptr) {
+  // (the wavefront index as a uniform value costs the register route ~20 VGPRs)
+  const int lane = threadIdx.x & 63;
+  const int wave = XL ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int nl = lane & 15, kb = lane >> 4;
   const int M = D.M, K = D.K, N = D.N;
   const Weights<R, S16> w(D, wk, lane, wave, NW);
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)M * K * 2u);
-  const int xrow = wk.m0 + nl;
-  const uint32_t xo = xrow < M ? ((uint32_t)xrow * K + 8u * kb) * 2u : kOobX;
+  // this lane's x loads, at byte offsets xo[t] + (group base) + xi[t]:
+  //   XL: rows xr + 4t of the slab, 16-byte chunk xc of the group;
+  //   registers: row nl of the slab, the 16 bytes of step t for quarter kb.
+  const int xr = lane >> 4, xc = lane & 15;
+  uint32_t xo[4], xi[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = wk.m0 + (XL ? xr + 4 * t : nl);
+    xo[t] = row < M ? ((uint32_t)row * K + 8u * (XL ? xc : kb)) * 2u : kOobX;
+    xi[t] = XL ? 0u : 64u * t;
+  }
   const int j1 = w.j1;
   auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
 
+  __shared__ uint4 xs[XL ? NW : 1][XL ? kTileRows : 1][17];  // XL: a slot per wavefront, rows padded
   uint4 bx[4][4];
   uint4 bw[4][R];
   ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
@@ -183,7 +312,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
     const int g = 4 * j + s;
     const uint32_t xb = xbase(j, g), qb = w.qbase(j, g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bx[s][i] = bload<0>(rx, xo + xb + 64u * i);
+    for (int t = 0; t < 4; ++t) bx[s][t] = bload<0>(rx, xo[t] + xb + xi[t]);
 #pragma unroll
     for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
@@ -203,20 +332,28 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 
   // Group s of the current quad: the MFMA chains (which read the group's x
   // and code registers at issue), then the scaled accumulation (which waits
-  // for the chains' results).
-  auto products = [&](int s, f32x4 (&c)[R]) {
-    bf16x8 a[4];
+  // for the chains' results).  XL: A operands of the group being multiplied
+  // and of the next one (a[2][4]); registers: the loads are the operands.
+  bf16x8 a[2][4];
+  auto stage_x = [&](int s, bf16x8 (&dst)[4]) {
+    if constexpr (XL) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = bitcast<bf16x8>(bx[s][i]);
+      for (int t = 0; t < 4; ++t) xs[wave][xr + 4 * t][xc] = bx[s][t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = bitcast<bf16x8>(xs[wave][nl][4 * i + kb]);
+    }
+  };
+
+  auto products = [&](int s, const bf16x8 (&ax)[4], f32x4 (&c)[R]) {
     f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) off = mfma16x16x32(a[i], kneg, off);
+    for (int i = 0; i < 4; ++i) off = mfma16x16x32(ax[i], kneg, off);
 #pragma unroll
     for (int r = 0; r < R; ++r) c[r] = off;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < R; ++r) c[r] = mfma16x16x32(a[i], unpack_step(word(bw[s][r], i), uc), c[r]);
+      for (int r = 0; r < R; ++r) c[r] = mfma16x16x32(ax[i], unpack_step(word(bw[s][r], i), uc), c[r]);
   };
   auto accumulate = [&](int s, const f32x4 (&c)[R]) {
 #pragma unroll
@@ -236,12 +373,23 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
     issue_group(s, w.j0);
     __builtin_amdgcn_sched_barrier(0);
   }
+  stage_x(0, a[0]);
   for (int j = w.j0; j < j1; ++j) {
     issue_scales(sn, j + 1);  // past the range: zeros, no memory access
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       f32x4 c[R];
-      products(s, c);
+      if constexpr (XL) {
+        // the next group's x: group s + 1 of this quad, or group 0 of the
+        // next quad (refilled three groups ago; zeros past the range)
+        stage_x((s + 1) & 3, a[(s + 1) & 1]);
+        products(s, a[s & 1], c);
+      } else {
+        bf16x8 ax[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ax[i] = bitcast<bf16x8>(bx[s][i]);
+        products(s, ax, c);
+      }
       // refill as soon as the chains have read the registers, not after their
       // results are in (nor sunk to the loop end)
       issue_group(s, j + 1);
@@ -252,7 +400,10 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
     for (int r = 0; r < R; ++r) sc[r] = sn[r];
   }
 
-  auto store = [&](int r, const f32x4& v) {
+  // Row block r's sum over the block's K slice: stored, or (split launches)
+  // published for the panel's last slice, which adds the slices in order.
+  auto store = [&](int r, f32x4 v) {
+    if (!split_combine(ws, wk, R, r, v)) return;
     const int n = (wk.rb0 + r) * kTileRows + nl;
     if (n >= N) return;
 #pragma unroll
@@ -298,15 +449,15 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk) {
 // kernel with all of K (NW = 1), so the two give identical bits.
 // ---------------------------------------------------------------------------
 template <int R, int NWN, bool S16>
-__device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work& wkb) {
+__device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work& wkb, uint8_t* ws = nullptr) {
   static_assert(16 % NWN == 0, "x rows split evenly over the wavefronts");
   constexpr int kRowsPerWave = 16 / NWN;
   constexpr int XL = kRowsPerWave >= 4 ? kRowsPerWave / 4 : 1;  // x loads per lane and group
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
   const int M = D.M, K = D.K, N = D.N;
-  const Work wk{wkb.di, wkb.rb0 + wave * R, wkb.m0};
-  const Weights<R, S16> w(D, wk, lane, 0, 1);  // all of K
+  const Work wk{wkb.di, wkb.rb0 + wave * R, wkb.m0, wkb.ks, wkb.nks};
+  const Weights<R, S16> w(D, wk, lane, 0, 1);  // all of the block's K slice
 
   // This wavefront's slice of the x tile: rows xr[t] of the slab, 16-byte
   // chunk xc of the group's 256 bytes per row.  With fewer than four rows per
@@ -407,45 +558,48 @@ __device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r >= w.rvalid) continue;  // row blocks past the end (a partial panel)
+    f32x4 v = acc[r];
+    if (!split_combine(ws, wk, R * NWN, wave * R + r, v)) continue;
     const int n = (wk.rb0 + r) * kTileRows + nl;
     if (n >= N) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = wk.m0 + 4 * kb + e;
-      if (m < M) store_out(D, (int64_t)m * N + n, 16.0f * acc[r][e]);
+      if (m < M) store_out(D, (int64_t)m * N + n, 16.0f * v[e]);
     }
   }
 }
 
 template <int R, int NWN, bool S16>
 __global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_kernel(const BatchArgs args) {
-  const Work wk = locate(args, R * NWN, 16);
-  mfma_shared_body<R, NWN, S16>(args.desc[wk.di], wk);
+  const Work wk = locate(args, R * NWN, 16, args.ksplit);
+  mfma_shared_body<R, NWN, S16>(args.desc[wk.di], wk, static_cast<uint8_t*>(args.ws));
 }
 
 template <int R, int NWN, bool S16>
 __global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_one(const uint16_t* x, const uint8_t* q,
                                                                    const void* d, void* y, int M, int K, int N,
-                                                                   int flags) {
+                                                                   int flags, uint8_t* ws, int S) {
   const LinearDesc D{x, q, d, y, M, K, N, flags};
-  mfma_shared_body<R, NWN, S16>(D, locate_one(N, R * NWN, 16));
+  mfma_shared_body<R, NWN, S16>(D, locate_one(N, R * NWN, 16, S), ws);
 }
 
 // Batched launch: the block finds its linear in the kernel arguments.
-template <int R, int NW, bool S16>
+template <int R, int NW, bool S16, bool XL>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
-  const Work wk = locate(args, R, 16);
-  mfma_body<R, NW, S16>(args.desc[wk.di], wk);
+  const Work wk = locate(args, R, 16, args.ksplit);
+  mfma_body<R, NW, S16, XL>(args.desc[wk.di], wk, static_cast<uint8_t*>(args.ws));
 }
 
 // Launch of one linear.  Its arguments are plain scalars that the hardware
 // preloads into SGPRs at wave launch, so the kernel does not wait for a
 // kernel-argument fetch before it can issue its first loads.
-template <int R, int NW, bool S16>
+template <int R, int NW, bool S16, bool XL>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const void* d,
-                                                           void* y, int M, int K, int N, int flags) {
+                                                           void* y, int M, int K, int N, int flags, uint8_t* ws,
+                                                           int S) {
   const LinearDesc D{x, q, d, y, M, K, N, flags};
-  mfma_body<R, NW, S16>(D, locate_one(N, R, 16));
+  mfma_body<R, NW, S16, XL>(D, locate_one(N, R, 16, S), ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -933,14 +1087,19 @@ LaunchShape launch_shape(const BatchArgs& a) {
 //     while a block of four holds its slots until the last of the four ends
 //     and a new block needs four free slots on one CU.  Short K (few scale
 //     quads per wavefront) makes the second effect stronger.
-int choose_cfg_mfma(const BatchArgs& a) {
+int choose_cfg_mfma(const BatchArgs& a, bool can_split) {
   // More row blocks per wavefront also reuse each x operand across more
   // weights (x is read through L1 once per row panel).
   const LaunchShape l = launch_shape(a);
   if (l.rows < 256) return find_cfg(1, 4);
-  // with more than 8 rows of x every lane of the x operand carries data, and
-  // fewer, longer wavefronts pay off sooner
-  if (l.rows < 600) return l.mmax > 8 ? find_cfg(2, 2) : find_cfg(2, 4);
+  if (l.rows < 600) {
+    // Few row panels of long rows, more than 8 rows of x (every row of the
+    // x tile carries data): four row blocks per wavefront halve the x loads
+    // per weight byte, and splitting K across blocks (a workspace is given)
+    // wins back the wavefronts that the larger panels lose.
+    if (can_split && l.mmax > 8 && l.kmin >= 16384) return find_cfg(4, 4);
+    return find_cfg(2, 4);
+  }
   if (l.rows < 2048) {
     if (l.kmin >= 4096) return find_cfg(4, 4);
     // short K: few quads per wavefront; with more than 8 rows of x and every
@@ -977,13 +1136,51 @@ int choose_cfg_gemv(const BatchArgs& a) {
   return find_cfg(1, 4);
 }
 
+// K slices per row panel of a split launch (1: no split), or -1 for a
+// W4_MFMA_SPLIT value that is not a slice count (1..kMaxSplit; any
+// configuration may be split that way for measurement).  The count never
+// needs more slots than the workspace holds.
+int choose_split(const BatchArgs& a, const Cfg& c, size_t ws_bytes) {
+  const LaunchShape l = launch_shape(a);
+  const int pr = c.shared ? c.R * c.NW : c.R;  // row blocks per panel (and slots per block)
+  const int kparts = c.shared ? 1 : c.NW;      // parts of the block's K slice
+  int64_t panels = 0;
+  for (int i = 0; i < a.count; ++i) {
+    const int64_t nb = (a.desc[i].N + kTileRows - 1) / kTileRows;
+    panels += (nb + pr - 1) / pr * ((a.desc[i].M + 15) / 16);
+  }
+  if (panels == 0) return 1;
+  int S = 0;
+  if (const char* e = getenv("W4_MFMA_SPLIT")) {
+    S = atoi(e);
+    if (S < 1 || S > kMaxSplit) return -1;
+  } else if (!c.shared && c.R >= 4 && l.rows < 600 && l.mmax > 8) {
+    // Splitting pays only where it wins back the wavefronts that four-row-
+    // block panels lose on a launch of few row panels with every row of the
+    // x tile carrying data (measured: splitting panels of one or two row
+    // blocks, shared-x blocks, or launches at M <= 8 gained nothing on any
+    // projection shape); it aims at about one wavefront per SIMD and at two
+    // scale quads or more each.
+    const int64_t waves = panels * c.NW;
+    const int qmin = (l.kmin / kGroup + 3) / 4;
+    S = (int)((1024 + waves - 1) / waves);
+    S = S < qmin / (2 * kparts) ? S : qmin / (2 * kparts);
+    S = S < kMaxSplit ? S : kMaxSplit;
+    S = S > 1 ? S : 1;
+  } else {
+    S = 1;
+  }
+  while (S > 1 && kSplitHeaderBytes + (size_t)(panels * S * pr) * 1024u > ws_bytes) --S;
+  return S;
+}
+
 // Block ranges of the batch's linears.  Blocks are dispatched roughly in index
 // order, so the linears are laid out longest K first (stable for equal K):
 // the blocks that run longest start first and the grid ends on short ones,
 // which shortens the tail of a launch that mixes long and short rows.  Each
 // linear's blocks compute the same thing wherever they sit, so the order
 // changes no result.
-int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
+int64_t fill_blocks(BatchArgs& a, int R, int slab_rows, int S = 1) {
   for (int i = 1; i < a.count; ++i) {
     const LinearDesc t = a.desc[i];
     int j = i;
@@ -996,7 +1193,7 @@ int64_t fill_blocks(BatchArgs& a, int R, int slab_rows) {
     const int nb = (a.desc[i].N + kTileRows - 1) / kTileRows;
     const int panels = (nb + R - 1) / R;
     const int slabs = (a.desc[i].M + slab_rows - 1) / slab_rows;
-    total += (int64_t)panels * slabs;
+    total += (int64_t)panels * slabs * S;
   }
   return total;
 }
@@ -1032,14 +1229,27 @@ void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
   if constexpr (c.shared) {
     if (a.count == 1)
       linear_mfma_shared_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N,
-                                                                            l.flags);
+                                                                            l.flags, static_cast<uint8_t*>(a.ws),
+                                                                            a.ksplit);
     else
       linear_mfma_shared_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   } else {
-    if (a.count == 1)
-      linear_mfma_one<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags);
-    else
-      linear_mfma_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
+    // x through LDS once every row of the 16-row x tile may carry data
+    int mmax = 0;
+    for (int i = 0; i < a.count; ++i) mmax = a.desc[i].M > mmax ? a.desc[i].M : mmax;
+    if (a.count == 1) {
+      if (mmax > 8)
+        linear_mfma_one<c.R, c.NW, S16, true><<<blocks, c.NW * 64, 0, st>>>(
+            l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags, static_cast<uint8_t*>(a.ws), a.ksplit);
+      else
+        linear_mfma_one<c.R, c.NW, S16, false><<<blocks, c.NW * 64, 0, st>>>(
+            l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags, static_cast<uint8_t*>(a.ws), a.ksplit);
+    } else {
+      if (mmax > 8)
+        linear_mfma_kernel<c.R, c.NW, S16, true><<<blocks, c.NW * 64, 0, st>>>(a);
+      else
+        linear_mfma_kernel<c.R, c.NW, S16, false><<<blocks, c.NW * 64, 0, st>>>(a);
+    }
   }
 }
 
@@ -1057,12 +1267,22 @@ void launch_mfma_cfg(int ci, unsigned blocks, hipStream_t st, const BatchArgs& a
 
 }  // namespace
 
-hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream) {
+hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream, void* split_ws, size_t split_ws_bytes) {
   const int env = cfg_from_env("W4_MFMA_CFG", true);
   if (env == -2) return hipErrorInvalidValue;
-  const int ci = env >= 0 ? env : choose_cfg_mfma(a);
+  const int ci = env >= 0 ? env : choose_cfg_mfma(a, split_ws != nullptr);
   const Cfg c = kCfgs[ci];
-  const int64_t blocks = fill_blocks(a, c.shared ? c.R * c.NW : c.R, 16);
+  a.ksplit = 1;
+  a.ws = nullptr;
+  if (split_ws) {
+    const int S = choose_split(a, c, split_ws_bytes);
+    if (S < 0) return hipErrorInvalidValue;
+    if (S > 1) {
+      a.ksplit = S;
+      a.ws = split_ws;
+    }
+  }
+  const int64_t blocks = fill_blocks(a, c.shared ? c.R * c.NW : c.R, 16, a.ksplit);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (s16) launch_mfma_cfg<true>(ci, (unsigned)blocks, stream, a);
@@ -1186,6 +1406,22 @@ int chain_choose_cfg(int kmax, double stage_bytes) {
 hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int* blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, s16 ? chain_kernel<true>(ci) : chain_kernel<false>(ci),
                                                       kChainCfgs[ci][1] * 64, lds);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void split_init_kernel(uint32_t* ws, size_t words) {
+  const size_t hdr = kSplitHeaderBytes / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
+    ws[i] = i < hdr ? 0u : kPartUnwritten;
+}
+}  // namespace
+
+hipError_t launch_split_init(void* ws, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  const unsigned blocks = (unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
+  if (blocks == 0) return hipSuccess;
+  split_init_kernel<<<blocks, 256, 0, stream>>>(static_cast<uint32_t*>(ws), words);
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds,

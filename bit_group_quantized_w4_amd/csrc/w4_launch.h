@@ -32,11 +32,20 @@ struct LinearDesc {
 };
 
 // Kernel argument block: block0[i] is the first workgroup of linear i.
+// Split launches (MFMA kernel): ksplit blocks share each row panel's K range
+// and exchange partial sums through the workspace `ws` (see linear.hip).
 struct BatchArgs {
   int count;
+  int ksplit = 1;
+  void* ws = nullptr;
   int block0[kMaxBatch];
   LinearDesc desc[kMaxBatch];
 };
+
+// Split workspace: a header (error word, then padding) and one 1 KiB slot per
+// (block, row block of its panel).  Slots hold kPartUnwritten (all one bits)
+// between calls.
+constexpr size_t kSplitHeaderBytes = 256;
 
 // ---------------------------------------------------------------------------
 // Chained launch: a dependent sequence of M = 1 linears in stages (a decode
@@ -96,7 +105,10 @@ hipError_t launch_unpack(const uint8_t* q_packed, const void* d_packed, int64_t 
                          int8_t* q_canon, void* d_canon, bool s16, hipStream_t stream);
 
 // MFMA streaming kernel over a batch (16-row slabs of x).
-hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream);
+hipError_t launch_linear_mfma(BatchArgs& a, bool s16, hipStream_t stream, void* split_ws = nullptr,
+                              size_t split_ws_bytes = 0);
+// Marks a split workspace ready: error word zero, every slot unwritten.
+hipError_t launch_split_init(void* ws, size_t bytes, hipStream_t stream);
 // dot2 streaming kernel over a batch (MT-row slabs of x staged in LDS; every
 // K must satisfy gemv_lds_bytes(MT, K) <= kGemvLdsBytes).
 hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream);

@@ -227,6 +227,44 @@ w4_status w4_linear_batched_f32(const w4_linear_desc_f32* linears, int count, in
                                 hipStream_t stream);
 
 /*
+ * Split launches -- the same linears (study, section 1: y = W x) for the
+ * draft-verification widths (M = K + 1 rows for K drafted tokens, 27B
+ * quantization-and-drafter ladder, stage 2), where a launch of few, long row
+ * panels leaves most compute units idle: the MFMA kernel may divide each
+ * panel's inputs among up to 8 blocks that hand their fp32 partial sums to
+ * the panel's last block through a caller-owned workspace.  The last block
+ * adds them in a fixed order, so results are reproducible run to run (they
+ * depend on the shapes, the kernel configuration and the chosen number of
+ * slices, not on timing), and they obey the accuracy convention above; they
+ * may differ in the last bits from the unsplit entry points.  The dot2 path
+ * (W4_PATH_GEMV, and W4_PATH_AUTO at M = 1) never splits.
+ *   workspace       [in/out] device memory of at least
+ *                   W4_SPLIT_WORKSPACE_BYTES bytes (w4_split_workspace_bytes()),
+ *                   256-byte aligned (W4_ERR_ALIGN), sharing no byte with any
+ *                   operand of the call (W4_ERR_ARG); too small: W4_ERR_ARG.
+ *                   Owned by the caller.  Initialise it once with
+ *                   w4_split_workspace_init before its first use; every call
+ *                   leaves it initialised again.  Calls that use one
+ *                   workspace must not overlap in time (one stream, or
+ *                   ordered by the caller): concurrent calls race on it.
+ *   other arguments as w4_linear_batched / _s16 / _f32.
+ * The last block's wait for the others is bounded: should it ever time out
+ * (only an uninitialised or concurrently used workspace can cause that), the
+ * affected outputs are NaN and w4_split_workspace_error reports a nonzero
+ * flag (it synchronises `stream`); re-initialise the workspace then.
+ */
+#define W4_SPLIT_WORKSPACE_BYTES ((size_t)4 << 20)
+size_t w4_split_workspace_bytes(void);
+w4_status w4_split_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+w4_status w4_split_workspace_error(const void* workspace, uint32_t* flag, hipStream_t stream);
+w4_status w4_linear_batched_split(const w4_linear_desc* linears, int count, int path,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+w4_status w4_linear_batched_split_s16(const w4_linear_desc_s16* linears, int count, int path,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+w4_status w4_linear_batched_split_f32(const w4_linear_desc_f32* linears, int count, int path,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * w4_pack -- canonical codes and scales -> native layout (for codes computed
  * elsewhere).  q_canon int8 [N][K] (values must lie in [-8, 7]; others are
  * reduced modulo 16), d_canon fp32 [N][K/128].  Outputs as w4_quantize_rtn.

@@ -137,6 +137,35 @@ def test_batched_validation(w4):
     assert lib.w4_linear_batched(big, 1, 1, None) == ERR_SHAPE
 
 
+def test_split_validation(w4):
+    """The split entry points refuse a bad workspace before anything is launched."""
+    lib = w4.library()
+    D = w4.LinearDesc
+    MiB = 1 << 20
+    assert lib.w4_split_workspace_bytes() == 4 * MiB
+    good = dict(x=FAKE, M=8, K=128, q_packed=FAKE + 0x100000, d_packed=FAKE + 0x200000, N=16,
+                y=FAKE + 0x300000)
+    a = (D * 1)(D(**good))
+    ws = FAKE + 0x1000000
+    for fn in (lib.w4_linear_batched_split, lib.w4_linear_batched_split_s16):
+        assert fn(a, 1, 2, None, 4 * MiB, None) == ERR_NULL
+        assert fn(a, 1, 2, ws + 16, 4 * MiB, None) == ERR_ALIGN
+        assert fn(a, 1, 2, ws, 4 * MiB - 256, None) == ERR_ARG  # smaller than W4_SPLIT_WORKSPACE_BYTES
+        assert fn(a, 1, 2, FAKE + 0x280000, 4 * MiB, None) == ERR_ARG  # covers the codes, scales and y
+        assert fn(a, 1, 2, FAKE - 4 * MiB + 256, 4 * MiB, None) == ERR_ARG  # its last bytes are x
+        bad = (D * 1)(D(**dict(good, K=100)))
+        assert fn(bad, 1, 2, ws, 4 * MiB, None) == ERR_SHAPE
+        assert fn(a, 1, 9, ws, 4 * MiB, None) == ERR_ARG  # unknown path
+    f = (D * 1)(D(**dict(good, y=FAKE + 0x300002)))
+    assert lib.w4_linear_batched_split_f32(f, 1, 2, ws, 4 * MiB, None) == ERR_ALIGN  # fp32 y needs 4 bytes
+    assert lib.w4_split_workspace_init(None, 4 * MiB, None) == ERR_NULL
+    assert lib.w4_split_workspace_init(ws + 64, 4 * MiB, None) == ERR_ALIGN
+    assert lib.w4_split_workspace_init(ws, MiB, None) == ERR_ARG
+    flag = ctypes.c_uint32(7)
+    assert lib.w4_split_workspace_error(None, ctypes.byref(flag), None) == ERR_NULL
+    assert lib.w4_split_workspace_error(ws, None, None) == ERR_NULL
+
+
 def test_chain_validation(w4):
     """w4_chain_prepare refuses bad chains on the host, before any HIP call."""
     lib = w4.library()
