@@ -1026,8 +1026,10 @@ struct Cfg {
   bool shared;
 };
 
-// Every configuration compiled for each kernel and scale format (the first
-// kNumSplitCfgs for both kernels, the shared-x ones for the MFMA kernel).
+// Every configuration compiled for each kernel and scale format: the first
+// kNumSplitCfgs (split-K) for both kernels, the shared-x forms for the MFMA
+// kernel only.  (Split-K MFMA forms of eight wavefronts with two or four row
+// blocks each measured slower on every projection group at M = 8 and 16.)
 // W4_MFMA_CFG / W4_GEMV_CFG ("R,NW", or "R,NWs" for shared x) may pick one of
 // them for measurement; a value naming no configuration compiled for that
 // kernel makes the launch fail (hipErrorInvalidValue).
@@ -1038,10 +1040,11 @@ constexpr int kNumSplitCfgs = 8;
 static_assert(kNumCfgs == 10, "the launch switches below list 10 configurations");
 static_assert(!kCfgs[0].shared && !kCfgs[1].shared && !kCfgs[2].shared && !kCfgs[3].shared && !kCfgs[4].shared &&
                   !kCfgs[5].shared && !kCfgs[6].shared && !kCfgs[7].shared && kCfgs[8].shared && kCfgs[9].shared,
-              "split-K configurations first: the dot2 launch compiles only those");
+              "configurations of both kernels first: the dot2 launch compiles only those");
 
-// -1: not set; -2: set to something that is not compiled for this kernel.
-int cfg_from_env(const char* name, bool allow_shared) {
+// -1: not set; -2: set to something that is not compiled for this kernel
+// (mfma: the MFMA kernel, which has every configuration).
+int cfg_from_env(const char* name, bool mfma) {
   const char* s = getenv(name);
   if (!s) return -1;
   int R = 0, NW = 0;
@@ -1052,7 +1055,7 @@ int cfg_from_env(const char* name, bool allow_shared) {
   if (got == 3 && !shared) return -2;
   for (int i = 0; i < kNumCfgs; ++i)
     if (kCfgs[i].R == R && kCfgs[i].NW == NW && kCfgs[i].shared == shared)
-      return shared && !allow_shared ? -2 : i;
+      return i >= kNumSplitCfgs && !mfma ? -2 : i;
   return -2;
 }
 

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads
-from tests.test_gpu_parity import CONFIGS, _bits, _say, check_y
+from tests.test_gpu_parity import CONFIGS, MFMA_ONLY, _bits, _say, check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +106,8 @@ def test_same_sign_batched(w4, gpu, path):
 def test_fp32_outputs_every_config(w4, gpu, cfg, path, scale_dtype, monkeypatch):
     """fp32 outputs of every compiled configuration meet the bound itself, and the
     bf16 outputs of the same configuration are their nearest-even rounding."""
-    if cfg.endswith("s") and path == "gemv":
-        pytest.skip("shared-x configurations exist for the MFMA kernel only")
+    if cfg in MFMA_ONLY and path == "gemv":
+        pytest.skip("configuration compiled for the MFMA kernel only")
     monkeypatch.setenv("W4_MFMA_CFG" if path == "mfma" else "W4_GEMV_CFG", cfg)
     sd = torch.bfloat16 if scale_dtype == "bf16" else torch.float32
     for i, (N, K) in enumerate([(700, 1408), (37, 384), (260, 2560)]):
