@@ -321,6 +321,36 @@ def decode_summary(stacks):
     return out
 
 
+# Mean tokens accepted per verification pass of seven drafted tokens (M = 8), as the
+# 27B quantization-and-drafter ladder page reports them for its drafter (stage 2): 2.2-2.5
+# on prose, 5.3-5.6 on code.  Used only for the illustrative rates of verify_summary.
+ACCEPTANCE_M8 = {"prose": (2.2, 2.5), "code": (5.3, 5.6)}
+
+
+def verify_summary(stacks):
+    """Per stack at each M > 1: the fastest launch mode that keeps the layer's
+    dependencies, as passes/s and the ceiling M / T_pass (every drafted token
+    accepted); at M = 8 also the illustrative tokens/s tau / T_pass at the
+    acceptance lengths above (linear layers only, drafter cost not included)."""
+    out = {}
+    for name, res in stacks.items():
+        for M, modes in res.items():
+            if not isinstance(modes, dict) or int(M) <= 1:
+                continue
+            dep = {k: v for k, v in modes.items() if k in DEPENDENT_MODES and isinstance(v, dict)}
+            if not dep:
+                continue
+            mode, best = min(dep.items(), key=lambda kv: kv[1]["ms_per_pass"])
+            passes = 1e3 / best["ms_per_pass"]
+            entry = {"mode": mode, "ms_per_pass": best["ms_per_pass"], "pct_of_peak": best["pct_of_peak"],
+                     "passes_per_s": round(passes, 1), "ceiling_tokens_per_s": round(int(M) * passes, 1)}
+            if int(M) == 8:
+                entry["tokens_per_s_at_acceptance"] = {k: [round(t * passes, 1) for t in v]
+                                                       for k, v in ACCEPTANCE_M8.items()}
+            out.setdefault(name, {})[int(M)] = entry
+    return out
+
+
 def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4):
     """One decode pass of the whole stack as one chained launch (w4_chain_run):
     the shared-input groups of every layer become stages, and each stage reads
@@ -952,6 +982,7 @@ def main():
         "m8": ({"mode": m8_best[0], **m8_best[1],
                 "bytes_per_pass": m8.get("bytes_per_pass")} if m8_best else None),
         "decode_summary": dec,
+        "verify_summary": verify_summary(stacks),
         "roofline": roofline(head, nbytes, read_peak),
         "hbm_read_peak_measured": read_peak,
         "stacks": stacks,

@@ -145,3 +145,18 @@ def test_decode_summary_takes_the_fastest_dependent_mode(bench):
     assert s["stack_x"]["mode"] == "chained" and s["stack_x"]["tokens_per_s"] == 400.0
     assert s["stack_x"]["upper_bound_independent_launches"]["tokens_per_s"] == 500.0
     assert s["stack_y"]["mode"] == "fused_shared_input" and "upper_bound_independent_launches" not in s["stack_y"]
+
+
+def test_verify_summary_rates(bench):
+    """At M > 1 the fastest dependency-keeping mode gives passes/s and the ceiling
+    M / T; at M = 8 also tau / T for the acceptance lengths the drafter page reports."""
+    m = lambda ms: {"ms_per_pass": ms, "GBps": 1.0, "pct_of_peak": 50.0}
+    stacks = {"stack_x": {1: {"chained": m(1.0)},
+                          8: {"per_call": m(4.0), "fused_shared_input": m(2.0), "layer_batched": m(1.0)},
+                          16: {"fused_shared_input": m(2.5)}}}
+    s = bench.verify_summary(stacks)["stack_x"]
+    assert 1 not in s
+    assert s[8]["mode"] == "fused_shared_input" and s[8]["passes_per_s"] == 500.0
+    assert s[8]["ceiling_tokens_per_s"] == 4000.0
+    assert s[8]["tokens_per_s_at_acceptance"] == {"prose": [1100.0, 1250.0], "code": [2650.0, 2800.0]}
+    assert s[16]["ceiling_tokens_per_s"] == 6400.0 and "tokens_per_s_at_acceptance" not in s[16]
