@@ -185,9 +185,12 @@ struct Weights {
 // slice of a panel is its highest-numbered block, and blocks are dispatched
 // in order, so every block it waits for has been dispatched before it and
 // waits for nothing: each wait ends.  It is bounded all the same (a timeout
-// sets the workspace's error word and the output becomes NaN).
+// sets the workspace's error word and the output becomes NaN).  A
+// workspace that was never initialised (no magic word in its header) is not
+// waited on at all: the last slice sets bit 1 of the error word and stores NaN.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kPartUnwritten = 0xFFFFFFFFu;
+constexpr uint32_t kSplitMagic = 0x57345350u;  // header word 1 of an initialised workspace
 constexpr uint32_t kPartNanForUnwritten = 0xFFC00000u;
 constexpr uint32_t kSplitSpinLimit = 1u << 17;  // polls (each at least one memory round trip)
 constexpr int kMaxSplit = 8;
@@ -241,6 +244,13 @@ __device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int s
     return false;
   }
   uint32_t* error = reinterpret_cast<uint32_t*>(ws);
+  if (__hip_atomic_load(error + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kSplitMagic) {
+    // never initialised: its slots cannot be trusted, so nothing is waited for
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = f32x4{__uint_as_float(kNanBits), __uint_as_float(kNanBits), __uint_as_float(kNanBits),
+              __uint_as_float(kNanBits)};
+    return true;
+  }
   const int b0 = blockIdx.x - (wk.nks - 1);
   f32x4 t = split_take(split_slot(ws, slots, b0, slot), error);
   for (int k = 1; k + 1 < wk.nks; ++k) {
@@ -261,12 +271,13 @@ __device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int s
 // value is itself one MFMA chain with B = -1.5.  One quad is in flight: the x
 // loads of a quad alone take 64 VGPRs.
 //
-// Two routes for x (XL):
-//   * registers (M <= 8): each lane loads its A operand directly, 16 rows x
-//     64 bytes per instruction; rows at or past M are out of range, so at
-//     M <= 8 half the lanes load nothing;
-//   * a slot of LDS private to the wavefront (M > 8): the group's 16 x
-//     256-byte tile is loaded four rows per instruction, 16 lanes reading one
+// Two routes for x (XR = rows of x staged through LDS: 0, 8 or 16):
+//   * registers (XR = 0; one-wavefront blocks at M <= 8): each lane loads its
+//     A operand directly, 16 rows x 64 bytes per instruction; rows at or past
+//     M are out of range, so at M <= 8 half the lanes load nothing;
+//   * a slot of LDS private to the wavefront (XR = 16 at M > 8, XR = 8 at
+//     M <= 8 with rows 8..15 of the slot zero): the group's XR x 256-byte
+//     tile is loaded four rows per instruction, 16 lanes reading one
 //     row's 256 contiguous bytes (two whole cache lines per row), written to
 //     the slot and read back in the A layout one group ahead, so the LDS
 //     round trip overlaps the previous group's MFMA chains.  With every row
@@ -274,13 +285,17 @@ __device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int s
 //     per instruction whose lookups (rows a large power-of-two stride apart)
 //     stall the vector L1 on tag conflicts: that was the limit of the split-K
 //     launches at M = 16 (counters: the L1's address unit stalled by the
-//     cache two thirds of its busy time).  At M <= 8 the direct loads are
-//     cheaper than the extra LDS traffic.  The slot needs no barrier: a
-//     wavefront's LDS accesses execute in program order, so the next group's
-//     writes follow this group's reads.
+//     cache two thirds of its busy time).  At M <= 8 the slot also wins in
+//     blocks of two or more wavefronts (half the load instructions of the
+//     direct route); a block of one wavefront has nothing to hide the LDS
+//     round trip behind and keeps the direct loads.  The slot needs no
+//     barrier: a wavefront's LDS accesses execute in program order, so the
+//     next group's writes follow this group's reads.
 // ---------------------------------------------------------------------------
-template <int R, int NW, bool S16, bool XL>
+template <int R, int NW, bool S16, int XR>
 __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, uint8_t* ws = nullptr) {
+  constexpr bool XL = XR > 0;          // x through the LDS slot
+  constexpr int NT = XL ? XR / 4 : 4;  // x load instructions per group
   // (the wavefront index as a uniform value costs the register route ~20 VGPRs)
   const int lane = threadIdx.x & 63;
   const int wave = XL ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
@@ -295,7 +310,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   const int xr = lane >> 4, xc = lane & 15;
   uint32_t xo[4], xi[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 4; ++t) {  // (the route through LDS uses the first NT)
     const int row = wk.m0 + (XL ? xr + 4 * t : nl);
     xo[t] = row < M ? ((uint32_t)row * K + 8u * (XL ? xc : kb)) * 2u : kOobX;
     xi[t] = XL ? 0u : 64u * t;
@@ -304,7 +319,11 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
 
   __shared__ uint4 xs[XL ? NW : 1][XL ? kTileRows : 1][17];  // XL: a slot per wavefront, rows padded
-  uint4 bx[4][4];
+  uint4 bx[4][NT];
+  if constexpr (XL && XR < kTileRows) {
+    // rows XR..15 of the slot hold zeros for the whole launch (x rows never loaded)
+    for (int e = lane; e < (kTileRows - XR) * 16; e += 64) xs[wave][XR + e / 16][e % 16] = make_uint4(0, 0, 0, 0);
+  }
   uint4 bw[4][R];
   ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
 
@@ -312,7 +331,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
     const int g = 4 * j + s;
     const uint32_t xb = xbase(j, g), qb = w.qbase(j, g);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bx[s][t] = bload<0>(rx, xo[t] + xb + xi[t]);
+    for (int t = 0; t < NT; ++t) bx[s][t] = bload<0>(rx, xo[t] + xb + xi[t]);
 #pragma unroll
     for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
@@ -338,7 +357,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   auto stage_x = [&](int s, bf16x8 (&dst)[4]) {
     if constexpr (XL) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xs[wave][xr + 4 * t][xc] = bx[s][t];
+      for (int t = 0; t < NT; ++t) xs[wave][xr + 4 * t][xc] = bx[s][t];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[i] = bitcast<bf16x8>(xs[wave][nl][4 * i + kb]);
     }
@@ -585,21 +604,21 @@ __global__ __launch_bounds__(NWN * 64) void linear_mfma_shared_one(const uint16_
 }
 
 // Batched launch: the block finds its linear in the kernel arguments.
-template <int R, int NW, bool S16, bool XL>
+template <int R, int NW, bool S16, int XR>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_kernel(const BatchArgs args) {
   const Work wk = locate(args, R, 16, args.ksplit);
-  mfma_body<R, NW, S16, XL>(args.desc[wk.di], wk, static_cast<uint8_t*>(args.ws));
+  mfma_body<R, NW, S16, XR>(args.desc[wk.di], wk, static_cast<uint8_t*>(args.ws));
 }
 
 // Launch of one linear.  Its arguments are plain scalars that the hardware
 // preloads into SGPRs at wave launch, so the kernel does not wait for a
 // kernel-argument fetch before it can issue its first loads.
-template <int R, int NW, bool S16, bool XL>
+template <int R, int NW, bool S16, int XR>
 __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, const uint8_t* q, const void* d,
                                                            void* y, int M, int K, int N, int flags, uint8_t* ws,
                                                            int S) {
   const LinearDesc D{x, q, d, y, M, K, N, flags};
-  mfma_body<R, NW, S16, XL>(D, locate_one(N, R, 16, S), ws);
+  mfma_body<R, NW, S16, XR>(D, locate_one(N, R, 16, S), ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -1117,7 +1136,10 @@ int choose_cfg_mfma(const BatchArgs& a, bool can_split) {
   // block.
   const int qmax = (l.kmax / kGroup + 3) / 4;
   if (qmax > 20) return find_cfg(4, 4);
-  return l.mmax > 8 || l.rows >= 8192 ? find_cfg(2, 8, true) : find_cfg(4, 1);
+  if (l.mmax > 8 || l.rows >= 8192) return find_cfg(2, 8, true);
+  // at M <= 8, four wavefronts splitting rows of 8192 inputs or more (four
+  // quads each or more) with x through LDS beat one-wavefront blocks
+  return l.kmin >= 8192 ? find_cfg(2, 4) : find_cfg(4, 1);
 }
 
 int choose_cfg_gemv(const BatchArgs& a) {
@@ -1237,21 +1259,25 @@ void launch_mfma_at(unsigned blocks, hipStream_t st, const BatchArgs& a) {
     else
       linear_mfma_shared_kernel<c.R, c.NW, S16><<<blocks, c.NW * 64, 0, st>>>(a);
   } else {
-    // x through LDS once every row of the 16-row x tile may carry data
+    // x route: all 16 rows through LDS when M > 8; at M <= 8 the 8 rows that
+    // carry data through LDS in blocks of two or more wavefronts, registers in
+    // one-wavefront blocks (whose LDS round trip nothing would hide)
+    constexpr int kXrSmall = c.NW >= 2 ? 8 : 0;
     int mmax = 0;
     for (int i = 0; i < a.count; ++i) mmax = a.desc[i].M > mmax ? a.desc[i].M : mmax;
+    uint8_t* wsp = static_cast<uint8_t*>(a.ws);
     if (a.count == 1) {
       if (mmax > 8)
-        linear_mfma_one<c.R, c.NW, S16, true><<<blocks, c.NW * 64, 0, st>>>(
-            l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags, static_cast<uint8_t*>(a.ws), a.ksplit);
+        linear_mfma_one<c.R, c.NW, S16, 16><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K, l.N,
+                                                                          l.flags, wsp, a.ksplit);
       else
-        linear_mfma_one<c.R, c.NW, S16, false><<<blocks, c.NW * 64, 0, st>>>(
-            l.x, l.q, l.d, l.y, l.M, l.K, l.N, l.flags, static_cast<uint8_t*>(a.ws), a.ksplit);
+        linear_mfma_one<c.R, c.NW, S16, kXrSmall><<<blocks, c.NW * 64, 0, st>>>(l.x, l.q, l.d, l.y, l.M, l.K,
+                                                                                l.N, l.flags, wsp, a.ksplit);
     } else {
       if (mmax > 8)
-        linear_mfma_kernel<c.R, c.NW, S16, true><<<blocks, c.NW * 64, 0, st>>>(a);
+        linear_mfma_kernel<c.R, c.NW, S16, 16><<<blocks, c.NW * 64, 0, st>>>(a);
       else
-        linear_mfma_kernel<c.R, c.NW, S16, false><<<blocks, c.NW * 64, 0, st>>>(a);
+        linear_mfma_kernel<c.R, c.NW, S16, kXrSmall><<<blocks, c.NW * 64, 0, st>>>(a);
     }
   }
 }
@@ -1415,7 +1441,7 @@ namespace {
 __global__ __launch_bounds__(256) void split_init_kernel(uint32_t* ws, size_t words) {
   const size_t hdr = kSplitHeaderBytes / 4;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
-    ws[i] = i < hdr ? 0u : kPartUnwritten;
+    ws[i] = i >= hdr ? kPartUnwritten : i == 1 ? kSplitMagic : 0u;
 }
 }  // namespace
 

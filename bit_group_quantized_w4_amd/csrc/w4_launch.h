@@ -42,9 +42,9 @@ struct BatchArgs {
   LinearDesc desc[kMaxBatch];
 };
 
-// Split workspace: a header (error word, then padding) and one 1 KiB slot per
-// (block, row block of its panel).  Slots hold kPartUnwritten (all one bits)
-// between calls.
+// Split workspace: a header (error word, a magic word written by the
+// initialisation, then padding) and one 1 KiB slot per (block, row block of
+// its panel).  Slots hold kPartUnwritten (all one bits) between calls.
 constexpr size_t kSplitHeaderBytes = 256;
 
 // ---------------------------------------------------------------------------

@@ -249,9 +249,12 @@ w4_status w4_linear_batched_f32(const w4_linear_desc_f32* linears, int count, in
  *                   ordered by the caller): concurrent calls race on it.
  *   other arguments as w4_linear_batched / _s16 / _f32.
  * The last block's wait for the others is bounded: should it ever time out
- * (only an uninitialised or concurrently used workspace can cause that), the
- * affected outputs are NaN and w4_split_workspace_error reports a nonzero
- * flag (it synchronises `stream`); re-initialise the workspace then.
+ * (only a concurrently used workspace can cause that), the affected outputs
+ * are NaN and w4_split_workspace_error reports bit 0 of its flag (it
+ * synchronises `stream`).  A workspace that was never initialised is
+ * detected (the initialisation writes a magic word): the split outputs are
+ * NaN, nothing waits, and the flag has bit 1 set.  Re-initialise the
+ * workspace after either.
  */
 #define W4_SPLIT_WORKSPACE_BYTES ((size_t)4 << 20)
 size_t w4_split_workspace_bytes(void);

@@ -14,7 +14,9 @@ them in slice order.  Checked here:
 * the workspace is left initialised (error word zero, every slot unwritten),
   and its error word stays zero;
 * non-finite activations still poison exactly their rows, including the bf16
-  pattern 0xFFFF, whose widening is the unwritten-slot pattern's upper half.
+  pattern 0xFFFF, whose widening is the unwritten-slot pattern's upper half;
+* a workspace that was never initialised is detected on the device: the split
+  outputs are NaN, nothing waits, and the error word has bit 1 set.
 """
 
 import numpy as np
@@ -155,3 +157,23 @@ def test_split_workspace_reuse_after_smaller_call(w4, gpu, ws, monkeypatch):
         check_y(y, y_ref, absdot, "reuse")
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
     check_workspace_clean(ws)
+
+
+def test_split_uninitialised_workspace(w4, gpu, monkeypatch):
+    monkeypatch.setenv("W4_MFMA_CFG", "2,4")
+    monkeypatch.setenv("W4_MFMA_SPLIT", "3")
+    N, K, M = 300, 4096, 8
+    q, d, q_ref, d_ref = _quantized(w4, gpu, N, K, seed=21)
+    x = workloads.random_activations(M, K, seed=22, device=gpu)
+    fresh = w4.SplitWorkspace(gpu)
+    fresh.buffer.zero_()  # as if allocated and never initialised
+    _say("split with an uninitialised workspace")
+    y = w4.linear(x, q, d, N, path="mfma", workspace=fresh)
+    assert torch.isnan(y.float()).all(), "outputs of an uninitialised workspace must be NaN"
+    assert fresh.error() == 2
+    fresh.init()
+    y = w4.linear(x, q, d, N, path="mfma", workspace=fresh)
+    y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+    check_y(y, y_ref, absdot, "after initialisation")
+    assert fresh.error() == 0
+    check_workspace_clean(fresh)
