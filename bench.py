@@ -287,9 +287,9 @@ def bench_stack(torch, w4, workloads, name, steps, warmup, only_ms=None, only_mo
             log(f"[bench] stack {name}{'' if sb == 4 else ' (16-bit scales)'} M={M} {mode}: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, "
                 f"{1 / per:.1f} passes/s")
             del g
-        if M == 1 and (not only_modes or "chained" in only_modes):
+        if not only_modes or "chained" in only_modes:
             res[M]["chained"] = bench_chain(torch, w4, workloads, wl, layers, xs, chain_steps or steps,
-                                            chain_warmup or warmup, name, sb)
+                                            chain_warmup or warmup, name, sb, M)
         res[M]["bytes_per_pass"] = workloads.stack_bytes(name, M, sb)
     del layers
     torch.cuda.empty_cache()
@@ -351,18 +351,18 @@ def verify_summary(stacks):
     return out
 
 
-def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4):
-    """One decode pass of the whole stack as one chained launch (w4_chain_run):
-    the shared-input groups of every layer become stages, and each stage reads
-    the output of the previous one (q|k|v <- previous down, o <- q, gate|up <- o,
-    down <- gate), so every stage waits for the whole previous stage, as in a
-    real decode step."""
+def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4, M=1):
+    """One pass of the whole stack at M rows of x (a decode step at M = 1, the
+    verification of M - 1 drafted tokens above) as one chained launch
+    (w4_chain_run): the shared-input groups of every layer become stages, and
+    each stage reads the output of the previous one (q|k|v <- previous down,
+    o <- q, gate|up <- o, down <- gate), as in a real pass."""
     dev = torch.device("cuda:0")
     groups = _shared_input_groups(wl)
     stages, prev = [], []  # prev: (N, y) of the previous stage's linears
     for mats in layers:
         # outputs of every layer in buffers of their own: a chain writes each line once
-        ys = {m.name: torch.empty((1, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+        ys = {m.name: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
         for gi in groups:
             K = mats[gi[0]][0].K
             x = next((y for n, y in prev if n == K), xs[K])
@@ -375,15 +375,15 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale
     if err:
         raise RuntimeError(f"{name} chained pass: a wait timed out (error flag {err}); the timing is invalid")
     per = t / steps
-    nbytes = workloads.stack_bytes(name, 1, scale_bytes)
+    nbytes = workloads.stack_bytes(name, M, scale_bytes)
     gbs = nbytes / per / 1e9
-    flops = 2.0 * workloads.stack_weights(name)
+    flops = 2.0 * M * workloads.stack_weights(name)
     out = {"ms_per_pass": round(per * 1e3, 4), "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-           "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(1 / per, 1), "launches_per_pass": 1,
+           "passes_per_s": round(1 / per, 2), "tokens_per_s_ceiling": round(M / per, 1), "launches_per_pass": 1,
            "stages_per_pass": len(stages), "useful_tflops": round(flops / per / 1e12, 2),
            "pct_of_bf16_mfma_peak": round(100 * flops / per / PEAK_BF16_FLOPS, 3),
            "plan": plan.info, "wait_timeouts": err, "timed_passes": steps}
-    log(f"[bench] stack {name}{'' if scale_bytes == 4 else ' (16-bit scales)'} M=1 chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
+    log(f"[bench] stack {name}{'' if scale_bytes == 4 else ' (16-bit scales)'} M={M} chained: {per * 1e3:.3f} ms/pass, {gbs:.0f} GB/s, {1 / per:.1f} passes/s "
         f"(plan {plan.info}, timeouts {err})")
     del g, plan
     return out

@@ -44,7 +44,7 @@ class ChainPlanC(ctypes.Structure):
     _I32 = ctypes.c_int32
     _fields_ = [("workspace", _VP), ("linears", _I32), ("stages", _I32), ("items", _I32), ("blocks", _I32),
                 ("config", _I32), ("lds_bytes", _I32), ("rows_per_item", _I32), ("waves_per_block", _I32),
-                ("scale_bytes", _I32), ("reserved", _I32)]
+                ("scale_bytes", _I32), ("rows", _I32)]
 
 
 # (name, restype, argtypes) of every symbol include/w4.h declares
@@ -328,7 +328,7 @@ class ChainPlan:
         p = self.plan
         return {"linears": p.linears, "stages": p.stages, "items": p.items, "blocks": p.blocks,
                 "rows_per_item": p.rows_per_item * 16, "waves_per_block": p.waves_per_block,
-                "lds_bytes": p.lds_bytes, "scale_bytes": p.scale_bytes}
+                "lds_bytes": p.lds_bytes, "scale_bytes": p.scale_bytes, "x_rows": p.rows}
 
 
 def chain_prepare(stages, noalloc=False):

@@ -540,16 +540,17 @@ extern "C++" {
 namespace {
 uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Is [a, a + na) covered by the outputs of the linears of stages before `stage`?
-// (No allocation: the covered prefix grows by any output that reaches past it.)
+// Is [a, a + na) covered by the outputs (M rows each) of the linears of
+// stages before `stage`?  (No allocation: the covered prefix grows by any
+// output that reaches past it.)
 template <typename Desc>
-bool covered_by_earlier(const Desc* l, int64_t count, int64_t stage, uintptr_t a, size_t na) {
+bool covered_by_earlier(const Desc* l, int64_t count, int64_t stage, uintptr_t a, size_t na, int64_t M) {
   uintptr_t at = a;
   const uintptr_t end = a + na;
   for (bool grew = true; at < end && grew;) {
     grew = false;
     for (int64_t i = 0; i < count && l[i].stage < stage; ++i) {
-      const uintptr_t y0 = addr(l[i].y), y1 = y0 + 2 * (size_t)l[i].N;
+      const uintptr_t y0 = addr(l[i].y), y1 = y0 + 2 * (size_t)M * l[i].N;
       if (y0 <= at && y1 > at) {
         at = y1;
         grew = true;
@@ -570,13 +571,17 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   if (count < 1 || count > W4_CHAIN_MAX) return W4_ERR_ARG;
   if (!linears || !workspace || !plan) return W4_ERR_NULL;
   if (!aligned(workspace, 16)) return W4_ERR_ALIGN;
-  // shapes, pointers and stage numbering
+  // shapes, pointers and stage numbering: one M for the whole chain, 1 (dot2
+  // items, x staged whole in LDS) or 2..16 (MFMA items, one slab of x rows)
+  const int64_t M = linears[0].M;
+  if (M < 1 || M > 16) return W4_ERR_SHAPE;
   int64_t kmax = 0;
   for (int64_t i = 0; i < count; ++i) {
     const Desc& l = linears[i];
-    if (l.M != 1 || l.N < 1 || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
-    if (w4::gemv_lds_bytes(1, l.K) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
-    if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31) return W4_ERR_SHAPE;
+    if (l.M != M || l.N < 1 || !n_ok(l.N) || !k_ok(l.K)) return W4_ERR_SHAPE;
+    if (M == 1 && w4::gemv_lds_bytes(1, l.K) > w4::kGemvLdsBytes) return W4_ERR_SHAPE;
+    if (w4_packed_bytes(l.N, l.K) >= (size_t)1 << 31 || 2 * (size_t)M * l.K > (size_t)1 << 30)
+      return W4_ERR_SHAPE;
     if (!l.x || !l.q_packed || !l.d_packed || !l.y) return W4_ERR_NULL;
     if (!aligned(l.x, 16) || !aligned(l.q_packed, 16) || !aligned(l.d_packed, 16) || !aligned(l.y, 2))
       return W4_ERR_ALIGN;
@@ -592,9 +597,10 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   // as x by a later stage is the intended use; such an x must then be
   // written entirely by earlier stages (it is read once no value of it is
   // unwritten).
+  const size_t mrows = (size_t)M;  // bytes of a y: 2 * M * N; of an x: 2 * M * K
   for (int64_t i = 0; i < count; ++i) {
     const Desc& a = linears[i];
-    const size_t yb = 2 * (size_t)a.N;
+    const size_t yb = 2 * mrows * a.N;
     const uintptr_t y0 = addr(a.y) & ~(uintptr_t)127;
     const void* ylines = reinterpret_cast<const void*>(y0);
     const size_t ylb = ((addr(a.y) + yb + 127) & ~(uintptr_t)127) - y0;
@@ -603,30 +609,30 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
       if (overlaps(ylines, ylb, b.q_packed, w4_packed_bytes(b.N, b.K)) ||
           overlaps(ylines, ylb, b.d_packed, (s16 ? 2 : 4) * w4_scale_count(b.N, b.K)))
         return W4_ERR_ARG;
-      if (j != i && overlaps(a.y, yb, b.y, 2 * (size_t)b.N)) return W4_ERR_ARG;
-      if (!overlaps(ylines, ylb, b.x, 2 * (size_t)b.K)) continue;
+      if (j != i && overlaps(a.y, yb, b.y, 2 * mrows * b.N)) return W4_ERR_ARG;
+      if (!overlaps(ylines, ylb, b.x, 2 * mrows * b.K)) continue;
       // b reads a line that a writes: only as a later stage reading a's output
-      if (b.stage <= a.stage || !overlaps(a.y, yb, b.x, 2 * (size_t)b.K)) return W4_ERR_ARG;
+      if (b.stage <= a.stage || !overlaps(a.y, yb, b.x, 2 * mrows * b.K)) return W4_ERR_ARG;
     }
   }
   // an x that reads outputs of earlier stages must lie entirely within them
   auto reads_earlier = [&](int64_t j) {
     for (int64_t i = 0; i < count; ++i)
-      if (linears[i].stage < linears[j].stage && overlaps(linears[i].y, 2 * (size_t)linears[i].N, linears[j].x,
-                                                          2 * (size_t)linears[j].K))
+      if (linears[i].stage < linears[j].stage && overlaps(linears[i].y, 2 * mrows * linears[i].N, linears[j].x,
+                                                          2 * mrows * linears[j].K))
         return true;
     return false;
   };
   auto read_later = [&](int64_t i) {
     for (int64_t j = 0; j < count; ++j)
-      if (linears[j].stage > linears[i].stage && overlaps(linears[i].y, 2 * (size_t)linears[i].N, linears[j].x,
-                                                          2 * (size_t)linears[j].K))
+      if (linears[j].stage > linears[i].stage && overlaps(linears[i].y, 2 * mrows * linears[i].N, linears[j].x,
+                                                          2 * mrows * linears[j].K))
         return true;
     return false;
   };
   for (int64_t j = 0; j < count; ++j)
     if (reads_earlier(j) && !covered_by_earlier(linears, count, linears[j].stage, addr(linears[j].x),
-                                                2 * (size_t)linears[j].K))
+                                                2 * mrows * linears[j].K, M))
       return W4_ERR_ARG;
   const int stages = (int)linears[count - 1].stage + 1;
   const size_t need = w4::chain_workspace_bytes(count);
@@ -634,7 +640,7 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   // the workspace overlaps no buffer of the chain
   for (int64_t i = 0; i < count; ++i) {
     const Desc& l = linears[i];
-    if (overlaps(workspace, need, l.x, 2 * (size_t)l.K) || overlaps(workspace, need, l.y, 2 * (size_t)l.N) ||
+    if (overlaps(workspace, need, l.x, 2 * mrows * l.K) || overlaps(workspace, need, l.y, 2 * mrows * l.N) ||
         overlaps(workspace, need, l.q_packed, w4_packed_bytes(l.N, l.K)) ||
         overlaps(workspace, need, l.d_packed, (s16 ? 2 : 4) * w4_scale_count(l.N, l.K)))
       return W4_ERR_ARG;
@@ -642,11 +648,11 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
 
   double code_bytes = 0;
   for (int64_t i = 0; i < count; ++i) code_bytes += (double)w4_packed_bytes(linears[i].N, linears[i].K);
-  const int ci = w4::chain_choose_cfg((int)kmax, code_bytes / stages);
+  const int ci = w4::chain_choose_cfg((int)kmax, code_bytes / stages, (int)M);
   if (ci < 0) return W4_ERR_ARG;
   int R = 0, NW = 0;
   w4::chain_cfg(ci, &R, &NW);
-  const size_t lds = (size_t)w4::gemv_lds_bytes(1, kmax);
+  const size_t lds = M == 1 ? (size_t)w4::gemv_lds_bytes(1, kmax) : 0;  // the MFMA items' LDS is static
 
   // Grid: every block resident at once (waits look only at earlier items).
   // Two blocks per CU measured fastest; W4_CHAIN_BLOCKS may ask for another
@@ -654,7 +660,7 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   int dev = 0, cus = 0, per_cu = 0;
   if (hipError_t e = hipGetDevice(&dev)) return hip_status(e);
   if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_status(e);
-  if (hipError_t e = w4::chain_blocks_per_cu(ci, s16, lds, &per_cu)) return hip_status(e);
+  if (hipError_t e = w4::chain_blocks_per_cu(ci, s16, lds, (int)M, &per_cu)) return hip_status(e);
   if (per_cu < 1 || cus < 1) return hip_status(hipErrorInvalidConfiguration);
   const int64_t resident = (int64_t)per_cu * cus;
   int64_t blocks = resident < 2 * (int64_t)cus ? resident : 2 * (int64_t)cus;
@@ -694,7 +700,7 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
         if (l.K != kcur) continue;
         w4::ChainLinear& c = buf[nbuf++];
         memset(&c, 0, sizeof(c));
-        c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, 1, (int)l.K, (int)l.N, 0};
+        c.desc = w4::LinearDesc{l.x, l.q_packed, l.d_packed, l.y, (int)M, (int)l.K, (int)l.N, 0};
         c.item0 = (int)items;
         c.stage = (int)l.stage;
         c.wait_x = reads_earlier(src);
@@ -736,7 +742,7 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   plan->rows_per_item = R;
   plan->waves_per_block = NW;
   plan->scale_bytes = s16 ? 2 : 4;
-  plan->reserved = 0;
+  plan->rows = (int32_t)M;
   return W4_OK;
 }
 }  // namespace
@@ -808,9 +814,11 @@ w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream) {
   if (!plan || !plan->workspace) return W4_ERR_NULL;
   if (plan->config < 0 || plan->config >= w4::chain_num_cfgs() || plan->blocks < 0) return W4_ERR_ARG;
   if (plan->scale_bytes != 2 && plan->scale_bytes != 4) return W4_ERR_ARG;
+  if (plan->rows < 1 || plan->rows > 16 || w4::chain_cfg_mfma(plan->config) != (plan->rows > 1)) return W4_ERR_ARG;
   if (plan->blocks == 0) return W4_OK;
   return hip_status(w4::launch_linear_chain(plan->workspace, plan->linears, plan->items, plan->config,
-                                            plan->scale_bytes == 2, plan->blocks, (size_t)plan->lds_bytes, stream));
+                                            plan->scale_bytes == 2, plan->blocks, (size_t)plan->lds_bytes,
+                                            plan->rows, stream));
 }
 
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream) {

@@ -264,6 +264,90 @@ __device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int s
 }
 
 // ---------------------------------------------------------------------------
+// Chained launches (protocol below the kernels' bodies): values that later
+// stages read start as kUnwritten and are written once, through to memory;
+// a reader loads them coherently and waits, boundedly, while any is unwritten.
+// ---------------------------------------------------------------------------
+constexpr uint16_t kUnwritten = 0xFFFF;     // a NaN pattern the chain never writes
+constexpr uint16_t kNanForUnwritten = 0xFFC0;
+// Polls before a wait gives up (each poll is a round trip to memory of at
+// least ~0.5 us, so this is tens of milliseconds: far longer than any stage,
+// far shorter than a hang).
+constexpr uint32_t kChainSpinLimit = 1u << 17;
+constexpr int kChainPollSleep = 4;  // s_sleep units (64 clocks) between polls
+
+// No dependency to wait for: x is read as soon as the block starts.
+struct NoGate {
+  static constexpr bool kActive = false;
+  static constexpr int parity = 0;
+};
+
+struct ChainGate {
+  static constexpr bool kActive = true;
+  static constexpr int kCoherent = 16;  // buffer-load cache policy: agent-scope coherent (sc1)
+  bool wait_x;                          // x is written by earlier stages of this pass
+  bool reuse;                           // LDS already holds this x, staged by the block's previous item
+  bool same_stage;                      // the block's previous item was in this stage
+  int parity;                           // the block's item count mod 2 (reduction buffer)
+  uint32_t* error;
+
+  __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
+    __hip_atomic_store(p, v == kUnwritten ? kNanForUnwritten : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ static bool unwritten(const uint32_t w) {
+    return (~w & 0xFFFFu) == 0u || (~w & 0xFFFF0000u) == 0u;
+  }
+  __device__ __forceinline__ static bool unwritten(const uint4& v) {
+    return unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
+  }
+  __device__ __forceinline__ static bool unwritten(const uint4 (&v)[4]) {
+    bool u = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u |= unwritten(v[i].x) | unwritten(v[i].y) | unwritten(v[i].z) | unwritten(v[i].w);
+    return u;
+  }
+  // true (and the launch's error flag set) once waiting has gone on too long,
+  // or when a wait anywhere has timed out (this launch or an earlier one)
+  __device__ __forceinline__ bool give_up(uint32_t t) const {
+    if (t < kChainSpinLimit && ((t & 31) != 31 || __hip_atomic_load(error, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT) == 0u)) {
+      __builtin_amdgcn_s_sleep(kChainPollSleep);
+      return false;
+    }
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  // Lane 0 of the calling wavefront polls the 16 bytes of x at byte offset
+  // `off` until they are written; false once waiting has gone on too long.
+  __device__ __forceinline__ bool poll(__amdgpu_buffer_rsrc_t rx, uint32_t off) const {
+    const uint32_t o = (threadIdx.x & 63) == 0 ? off : kOobX;
+    for (uint32_t t = 0;; ++t) {
+      if (!__any(unwritten(bload<kCoherent>(rx, o)))) return true;
+      if (give_up(t)) return false;
+    }
+  }
+  // The calling wavefront polls the last 16-byte chunk of bytes [b0, b1) of
+  // x (a block's four wavefronts poll 64 bytes in all: polls compete with
+  // the producers' last reads, so they are kept small) until it is written.
+  // An empty range, or one past the end of x, reads zeros.
+  __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, uint32_t b0, uint32_t b1) const {
+    const int lane = threadIdx.x & 63;
+    const uint32_t off = (lane == 0 && b1 > b0) ? b1 - 16u : kOobX;
+    for (uint32_t t = 0;; ++t) {
+      const uint4 v = bload<kCoherent>(rx, off);
+      const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
+      if (!__any(u)) break;
+      if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+        if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(kChainPollSleep);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // MFMA kernel.  One v_mfma_f32_16x16x32_bf16 per 32-input step: A = 16 rows
 // of x, B = the tile's 16 rows of W^T.  Lane l holds A[l%16][8(l/16)..+7],
 // B[8(l/16)..+7][l%16] and D[4(l/16)+j][l%16], j = 0..3.  Rows of A at or
@@ -291,11 +375,21 @@ __device__ __forceinline__ bool split_combine(uint8_t* ws, const Work& wk, int s
 //     round trip behind and keeps the direct loads.  The slot needs no
 //     barrier: a wavefront's LDS accesses execute in program order, so the
 //     next group's writes follow this group's reads.
+//
+// Gate (kActive: an item of a chained launch, x through the LDS slot): x is
+// loaded coherently, and when x is written by earlier stages each group's
+// loads are checked before they are staged.  If a value is still unwritten,
+// lane 0 polls one unwritten chunk until it is written, then the x of all four
+// groups in flight is loaded again (each may predate the write) and the
+// group is checked anew.  Outputs are written through (bf16 only).
 // ---------------------------------------------------------------------------
-template <int R, int NW, bool S16, int XR>
-__device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, uint8_t* ws = nullptr) {
+template <int R, int NW, bool S16, int XR, class Gate = NoGate>
+__device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, uint8_t* ws = nullptr,
+                                          const Gate& gate = Gate()) {
   constexpr bool XL = XR > 0;          // x through the LDS slot
   constexpr int NT = XL ? XR / 4 : 4;  // x load instructions per group
+  static_assert(XL || !Gate::kActive, "a chained item reads x through the LDS slot");
+  constexpr int kXPolicy = Gate::kActive ? ChainGate::kCoherent : 0;
   // (the wavefront index as a uniform value costs the register route ~20 VGPRs)
   const int lane = threadIdx.x & 63;
   const int wave = XL ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
@@ -315,8 +409,11 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
     xo[t] = row < M ? ((uint32_t)row * K + 8u * (XL ? xc : kb)) * 2u : kOobX;
     xi[t] = XL ? 0u : 64u * t;
   }
-  const int j1 = w.j1;
-  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
+  const int j1 = w.j1, G = w.G;
+  // Groups past K (the padding of a partial last quad) read zeros, not the
+  // start of the next row of x: their codes and scales are zero, but an
+  // infinity or NaN there would still make the product NaN.
+  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 && g < G ? (uint32_t)g * 256u : kOobX; };
 
   __shared__ uint4 xs[XL ? NW : 1][XL ? kTileRows : 1][17];  // XL: a slot per wavefront, rows padded
   uint4 bx[4][NT];
@@ -326,12 +423,14 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   }
   uint4 bw[4][R];
   ScaleQuad<S16> sc[R], sn[R];  // scale quads: current and next
+  uint32_t xbs[4];              // (Gate) group base of each slot's x loads
 
   auto issue_group = [&](int s, int j) {
     const int g = 4 * j + s;
     const uint32_t xb = xbase(j, g), qb = w.qbase(j, g);
+    if constexpr (Gate::kActive) xbs[s] = xb;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bx[s][t] = bload<0>(rx, xo[t] + xb + xi[t]);
+    for (int t = 0; t < NT; ++t) bx[s][t] = bload<kXPolicy>(rx, xo[t] + xb + xi[t]);
 #pragma unroll
     for (int r = 0; r < R; ++r) bw[s][r] = bload<kNonTemporal>(w.rq, w.qo[r] + qb);
   };
@@ -354,8 +453,34 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   // for the chains' results).  XL: A operands of the group being multiplied
   // and of the next one (a[2][4]); registers: the loads are the operands.
   bf16x8 a[2][4];
+  // (Gate) wait until slot s holds no unwritten value (see above)
+  auto await_x = [&](int s) {
+    if constexpr (Gate::kActive) {
+      for (uint32_t it = 0;; ++it) {
+        uint32_t mine = kOobX;  // this lane's first unwritten chunk, if any
+#pragma unroll
+        for (int t = NT - 1; t >= 0; --t)
+          if (ChainGate::unwritten(bx[s][t])) mine = xo[t] + xbs[s] + xi[t];
+        const uint64_t lanes = __ballot(mine != kOobX);
+        if (lanes == 0) return;
+        const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)mine, __builtin_ctzll(lanes));
+        // timed out (also after too many rounds): the error flag is set, the outputs are NaN
+        if (!gate.poll(rx, off) || it >= kChainSpinLimit) {
+          if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(gate.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) bx[s2][t] = bload<kXPolicy>(rx, xo[t] + xbs[s2] + xi[t]);
+      }
+    }
+  };
   auto stage_x = [&](int s, bf16x8 (&dst)[4]) {
     if constexpr (XL) {
+      if constexpr (Gate::kActive) {
+        if (gate.wait_x) await_x(s);
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) xs[wave][xr + 4 * t][xc] = bx[s][t];
 #pragma unroll
@@ -428,7 +553,12 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = wk.m0 + 4 * kb + e;
-      if (m < M) store_out(D, (int64_t)m * N + n, 16.0f * v[e]);
+      if (m < M) {
+        if constexpr (Gate::kActive)
+          Gate::store(static_cast<uint16_t*>(D.y) + (int64_t)m * N + n, f32_to_bf16_rne(16.0f * v[e]));
+        else
+          store_out(D, (int64_t)m * N + n, 16.0f * v[e]);
+      }
     }
   };
 
@@ -437,15 +567,17 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
     for (int r = 0; r < R; ++r)
       if (r < w.rvalid) store(r, acc[r]);
   } else {
-    __shared__ f32x4 red[NW][R][64];
+    // (Gate: two copies by item parity, as in the dot2 kernel's reduction)
+    __shared__ f32x4 red[Gate::kActive ? 2 : 1][NW][R][64];
+    const int rp = Gate::kActive ? gate.parity : 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r];
+    for (int r = 0; r < R; ++r) red[rp][wave][r][lane] = acc[r];
     __syncthreads();
     for (int r = wave; r < w.rvalid; r += NW) {
-      f32x4 v = red[0][r][lane];
+      f32x4 v = red[rp][0][r][lane];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) {
-        const f32x4 o = red[ww][r][lane];
+        const f32x4 o = red[rp][ww][r][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += o[e];
       }
@@ -491,8 +623,11 @@ __device__ __forceinline__ void mfma_shared_body(const LinearDesc& D, const Work
     xr[t] = wave * kRowsPerWave + (lane >> 4) % kRowsPerWave + 4 * t;
     xo[t] = (xlane && wk.m0 + xr[t] < M) ? ((uint32_t)(wk.m0 + xr[t]) * K + 8u * xc) * 2u : kOobX;
   }
-  const int j1 = w.j1;
-  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 ? (uint32_t)g * 256u : kOobX; };
+  const int j1 = w.j1, G = w.G;
+  // Groups past K (the padding of a partial last quad) read zeros, not the
+  // start of the next row of x: their codes and scales are zero, but an
+  // infinity or NaN there would still make the product NaN.
+  auto xbase = [&](int j, int g) -> uint32_t { return j < j1 && g < G ? (uint32_t)g * 256u : kOobX; };
 
   __shared__ uint4 xs[2][kTileRows][17];  // rows padded to 272 bytes: conflict-free A reads
 
@@ -634,12 +769,6 @@ __global__ __launch_bounds__(NW * 64) void linear_mfma_one(const uint16_t* x, co
 // kXScale: x is divided by channel scales while it is staged,
 // x'[k] = bf16(fl32(x[k] * inv_s[k])) (channel scaling before RTN, the
 // study's section 2 AWQ row; inv_s holds the fp32 reciprocals of the scales).
-// No dependency to wait for: x is read as soon as the block starts.
-struct NoGate {
-  static constexpr bool kActive = false;
-  static constexpr int parity = 0;
-};
-
 // Gate (kActive, chained launches): the block's weight prologue is issued
 // first, then x is staged once it is completely written (see ChainGate).
 template <int MT, int R, int NW, bool S16, bool kXScale = false, class Gate = NoGate>
@@ -936,67 +1065,6 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
 // stale copy.  A chain writes each byte at most once and never writes a
 // cache line that the pass reads earlier (the C ABI refuses such chains).
 // ---------------------------------------------------------------------------
-constexpr uint16_t kUnwritten = 0xFFFF;     // a NaN pattern the chain never writes
-constexpr uint16_t kNanForUnwritten = 0xFFC0;
-// Polls before a wait gives up (each poll is a round trip to memory of at
-// least ~0.5 us, so this is tens of milliseconds: far longer than any stage,
-// far shorter than a hang).
-constexpr uint32_t kChainSpinLimit = 1u << 17;
-constexpr int kChainPollSleep = 4;  // s_sleep units (64 clocks) between polls
-
-struct ChainGate {
-  static constexpr bool kActive = true;
-  static constexpr int kCoherent = 16;  // buffer-load cache policy: agent-scope coherent (sc1)
-  bool wait_x;                          // x is written by earlier stages of this pass
-  bool reuse;                           // LDS already holds this x, staged by the block's previous item
-  bool same_stage;                      // the block's previous item was in this stage
-  int parity;                           // the block's item count mod 2 (reduction buffer)
-  uint32_t* error;
-
-  __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
-    __hip_atomic_store(p, v == kUnwritten ? kNanForUnwritten : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __device__ __forceinline__ static bool unwritten(const uint32_t w) {
-    return (~w & 0xFFFFu) == 0u || (~w & 0xFFFF0000u) == 0u;
-  }
-  __device__ __forceinline__ static bool unwritten(const uint4 (&v)[4]) {
-    bool u = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u |= unwritten(v[i].x) | unwritten(v[i].y) | unwritten(v[i].z) | unwritten(v[i].w);
-    return u;
-  }
-  // true (and the launch's error flag set) once waiting has gone on too long,
-  // or when a wait anywhere has timed out (this launch or an earlier one)
-  __device__ __forceinline__ bool give_up(uint32_t t) const {
-    if (t < kChainSpinLimit && ((t & 31) != 31 || __hip_atomic_load(error, __ATOMIC_RELAXED,
-                                                                    __HIP_MEMORY_SCOPE_AGENT) == 0u)) {
-      __builtin_amdgcn_s_sleep(kChainPollSleep);
-      return false;
-    }
-    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-  }
-  // The calling wavefront polls the last 16-byte chunk of bytes [b0, b1) of
-  // x (a block's four wavefronts poll 64 bytes in all: polls compete with
-  // the producers' last reads, so they are kept small) until it is written.
-  // An empty range, or one past the end of x, reads zeros.
-  __device__ __forceinline__ void wait_sample(__amdgpu_buffer_rsrc_t rx, uint32_t b0, uint32_t b1) const {
-    const int lane = threadIdx.x & 63;
-    const uint32_t off = (lane == 0 && b1 > b0) ? b1 - 16u : kOobX;
-    for (uint32_t t = 0;; ++t) {
-      const uint4 v = bload<kCoherent>(rx, off);
-      const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
-      if (!__any(u)) break;
-      if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
-                                                                       __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-        if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(kChainPollSleep);
-    }
-  }
-};
-
 // lin: the table (linears + 1 entries, the last a sentinel); hdr: the
 // workspace header's error word.
 template <int R, int NW, bool S16>
@@ -1025,11 +1093,36 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
   }
 }
 
-// Marks the outputs that later linears read as unwritten (one block per linear).
+// The same walk for a chain of linears with 2..16 rows of x (verification
+// widths), each item run by the MFMA body (split-K form, x through the LDS
+// slot) with the gate: the item's weight and x loads are issued at once, and
+// a group's x is checked for unwritten values just before it is staged.  Per
+// item the arithmetic is exactly the MFMA kernel's with the same (R, NW),
+// unsplit, so results are identical bits (NaN outputs aside, as above).
+template <int R, int NW, bool S16, int XR>
+__global__ __launch_bounds__(NW * 64) void linear_chain_mfma_kernel(const ChainLinear* __restrict__ lin,
+                                                                    uint32_t* hdr, int items) {
+  const int P = gridDim.x;
+  int i = blockIdx.x;
+  int li = 0;
+  int li_end = lin[1].item0;
+  while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
+  int parity = 0;
+  while (i < items) {
+    const ChainGate gate{lin[li].wait_x != 0, false, false, parity, hdr};
+    parity ^= 1;
+    mfma_body<R, NW, S16, XR, ChainGate>(lin[li].desc, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
+    i += P;
+    while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
+  }
+}
+
+// Marks the outputs that later linears read as unwritten (block (i, m): row
+// m of linear i's output).
 __global__ __launch_bounds__(256) void chain_fill_kernel(const ChainLinear* __restrict__ lin) {
   const ChainLinear& l = lin[blockIdx.x];
-  if (!l.fill) return;
-  uint16_t* y = static_cast<uint16_t*>(l.desc.y);
+  if (!l.fill || (int)blockIdx.y >= l.desc.M) return;
+  uint16_t* y = static_cast<uint16_t*>(l.desc.y) + (int64_t)blockIdx.y * l.desc.N;
   for (int n = threadIdx.x; n < l.desc.N; n += 256) y[n] = kUnwritten;
 }
 
@@ -1375,12 +1468,22 @@ hipError_t launch_linear_gemv(BatchArgs& a, int MT, bool s16, hipStream_t stream
 // chained launch
 // ---------------------------------------------------------------------------
 namespace {
+// dot2 items (M = 1), then MFMA items (M = 2..16: split-K forms, x through the
+// LDS slot); a configuration index counts through both lists.
 constexpr int kChainCfgs[][2] = {{1, 4}, {1, 8}, {2, 4}, {2, 2}, {1, 2}, {4, 4}};
 constexpr int kNumChainCfgs = sizeof(kChainCfgs) / sizeof(kChainCfgs[0]);
+constexpr int kChainMfmaCfgs[][2] = {{2, 4}, {4, 4}, {1, 4}, {2, 2}, {4, 2}};
+constexpr int kNumChainMfmaCfgs = sizeof(kChainMfmaCfgs) / sizeof(kChainMfmaCfgs[0]);
+static_assert(kNumChainCfgs == 6 && kNumChainMfmaCfgs == 5, "the switches below list these configurations");
 
 template <int I, bool S16>
 const void* chain_kernel_ptr() {
   return reinterpret_cast<const void*>(&linear_chain_kernel<kChainCfgs[I][0], kChainCfgs[I][1], S16>);
+}
+template <int I, bool S16, int XR>
+const void* chain_mfma_kernel_ptr() {
+  return reinterpret_cast<const void*>(
+      &linear_chain_mfma_kernel<kChainMfmaCfgs[I][0], kChainMfmaCfgs[I][1], S16, XR>);
 }
 template <bool S16>
 const void* chain_kernel(int ci) {
@@ -1391,6 +1494,16 @@ const void* chain_kernel(int ci) {
     case 3: return chain_kernel_ptr<3, S16>();
     case 4: return chain_kernel_ptr<4, S16>();
     default: return chain_kernel_ptr<5, S16>();
+  }
+}
+template <bool S16, int XR>
+const void* chain_mfma_kernel(int mi) {
+  switch (mi) {
+    case 0: return chain_mfma_kernel_ptr<0, S16, XR>();
+    case 1: return chain_mfma_kernel_ptr<1, S16, XR>();
+    case 2: return chain_mfma_kernel_ptr<2, S16, XR>();
+    case 3: return chain_mfma_kernel_ptr<3, S16, XR>();
+    default: return chain_mfma_kernel_ptr<4, S16, XR>();
   }
 }
 template <bool S16>
@@ -1406,35 +1519,66 @@ void launch_chain_cfg(int ci, int blocks, size_t lds, hipStream_t stream, const 
 #undef W4_CHAIN
   }
 }
+// x rows staged per group: the 8 of a slab at M <= 8, all 16 above
+template <bool S16, int XR>
+void launch_chain_mfma_cfg(int mi, int blocks, hipStream_t stream, const ChainLinear* lin, uint32_t* hdr,
+                           int items) {
+  switch (mi) {
+#define W4_CHAIN(i)                                                                          \
+  case i:                                                                                    \
+    linear_chain_mfma_kernel<kChainMfmaCfgs[i][0], kChainMfmaCfgs[i][1], S16, XR>            \
+        <<<blocks, kChainMfmaCfgs[i][1] * 64, 0, stream>>>(lin, hdr, items);                 \
+    break;
+    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4)
+#undef W4_CHAIN
+  }
+}
 }  // namespace
 
-int chain_num_cfgs() { return kNumChainCfgs; }
+int chain_num_cfgs() { return kNumChainCfgs + kNumChainMfmaCfgs; }
+
+bool chain_cfg_mfma(int ci) { return ci >= kNumChainCfgs; }
 
 void chain_cfg(int ci, int* R, int* NW) {
-  *R = kChainCfgs[ci][0];
-  *NW = kChainCfgs[ci][1];
+  const int(&c)[2] = ci < kNumChainCfgs ? kChainCfgs[ci] : kChainMfmaCfgs[ci - kNumChainCfgs];
+  *R = c[0];
+  *NW = c[1];
 }
 
-int chain_choose_cfg(int kmax, double stage_bytes) {
+int chain_choose_cfg(int kmax, double stage_bytes, int M) {
+  const bool mfma = M > 1;
   if (const char* e = getenv("W4_CHAIN_CFG")) {
     int R = 0, NW = 0;
     if (sscanf(e, "%d,%d", &R, &NW) != 2) return -1;
-    for (int i = 0; i < kNumChainCfgs; ++i)
-      if (kChainCfgs[i][0] == R && kChainCfgs[i][1] == NW) return i;
+    for (int i = 0; i < chain_num_cfgs(); ++i) {
+      int r = 0, nw = 0;
+      chain_cfg(i, &r, &nw);
+      if (chain_cfg_mfma(i) == mfma && r == R && nw == NW) return i;
+    }
     return -1;
   }
+  (void)kmax;
+  if (mfma) return kNumChainCfgs;  // two row blocks per item, four wavefronts
   // Measured on MI355X (two blocks per CU; the grid size is chosen by the C
   // ABI): with stages of tens of MB or more (27B- and 70B-class stacks, 45
   // and 110 MB of codes per stage on average) two row blocks per item and
   // four wavefronts per block; with small stages (4B-class, 12 MB) one row
   // block and eight wavefronts, so that every stage has more, shorter items.
-  (void)kmax;
   return stage_bytes < 24e6 ? 1 : 2;
 }
 
-hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, s16 ? chain_kernel<true>(ci) : chain_kernel<false>(ci),
-                                                      kChainCfgs[ci][1] * 64, lds);
+hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int M, int* blocks) {
+  if (ci < 0 || ci >= chain_num_cfgs()) return hipErrorInvalidValue;
+  int R = 0, NW = 0;
+  chain_cfg(ci, &R, &NW);
+  const void* k = nullptr;
+  if (!chain_cfg_mfma(ci))
+    k = s16 ? chain_kernel<true>(ci) : chain_kernel<false>(ci);
+  else if (M > 8)
+    k = s16 ? chain_mfma_kernel<true, 16>(ci - kNumChainCfgs) : chain_mfma_kernel<false, 16>(ci - kNumChainCfgs);
+  else
+    k = s16 ? chain_mfma_kernel<true, 8>(ci - kNumChainCfgs) : chain_mfma_kernel<false, 8>(ci - kNumChainCfgs);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, NW * 64, chain_cfg_mfma(ci) ? 0 : lds);
 }
 
 namespace {
@@ -1453,15 +1597,27 @@ hipError_t launch_split_init(void* ws, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds,
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds, int M,
                                hipStream_t stream) {
-  if (ci < 0 || ci >= kNumChainCfgs) return hipErrorInvalidValue;
+  if (ci < 0 || ci >= chain_num_cfgs() || M < 1 || M > 16 || chain_cfg_mfma(ci) != (M > 1))
+    return hipErrorInvalidValue;
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
   const ChainLinear* lin = reinterpret_cast<const ChainLinear*>(w + sizeof(ChainHeader));
-  chain_fill_kernel<<<linears, 256, 0, stream>>>(lin);
-  if (s16) launch_chain_cfg<true>(ci, blocks, lds, stream, lin, hdr, items);
-  else launch_chain_cfg<false>(ci, blocks, lds, stream, lin, hdr, items);
+  chain_fill_kernel<<<dim3(linears, M), 256, 0, stream>>>(lin);
+  if (!chain_cfg_mfma(ci)) {
+    if (s16) launch_chain_cfg<true>(ci, blocks, lds, stream, lin, hdr, items);
+    else launch_chain_cfg<false>(ci, blocks, lds, stream, lin, hdr, items);
+  } else {
+    const int mi = ci - kNumChainCfgs;
+    if (M > 8) {
+      if (s16) launch_chain_mfma_cfg<true, 16>(mi, blocks, stream, lin, hdr, items);
+      else launch_chain_mfma_cfg<false, 16>(mi, blocks, stream, lin, hdr, items);
+    } else {
+      if (s16) launch_chain_mfma_cfg<true, 8>(mi, blocks, stream, lin, hdr, items);
+      else launch_chain_mfma_cfg<false, 8>(mi, blocks, stream, lin, hdr, items);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -48,17 +48,20 @@ struct BatchArgs {
 constexpr size_t kSplitHeaderBytes = 256;
 
 // ---------------------------------------------------------------------------
-// Chained launch: a dependent sequence of M = 1 linears in stages (a decode
-// layer's q|k|v, then o, then gate|up, then down, layer after layer).  A
-// linear whose x is written by earlier stages reads it only once all of it is
-// written.  One persistent grid of co-resident blocks walks the items
-// (R-row-block panels) of every stage in order; block b takes items b, b+P,
-// b+2P, ...  Before the pass a fill launch marks every output that a later
-// linear reads with an unwritten-value pattern; a block about to stage such
-// an x first issues its item's weight loads, then each of its wavefronts
-// waits until no value of its own range of x is unwritten.  Waits only ever look at outputs of earlier items, which
-// co-resident blocks hold, so every wait ends; it is also bounded (a timeout
-// sets `error` and lets the launch drain).
+// Chained launch: a dependent sequence of linears with the same M (1 for a
+// decode step, up to 16 for draft verification) in stages (a layer's q|k|v,
+// then o, then gate|up, then down, layer after layer).  A linear whose x is
+// written by earlier stages uses no value of it that is not yet written.
+// One persistent grid of co-resident blocks walks the items (R-row-block
+// panels) of every stage in order; block b takes items b, b+P, b+2P, ...
+// Before the pass a fill launch marks every output that a later linear reads
+// with an unwritten-value pattern.  A block's item issues its weight loads
+// first; then (M = 1) each wavefront waits until no value of its own range of
+// x is unwritten and stages that range, or (M > 1) each group's x is checked
+// as it is staged and waited for while any value is unwritten.  Waits only
+// ever look at outputs of earlier items, which co-resident blocks hold, so
+// every wait ends; it is also bounded (a timeout sets `error` and lets the
+// launch drain).
 // ---------------------------------------------------------------------------
 // Workspace layout (device): ChainHeader | ChainLinear[linears + 1] (the last
 // is a sentinel with item0 = items).
@@ -79,18 +82,21 @@ inline size_t chain_workspace_bytes(int64_t linears) {
   return sizeof(ChainHeader) + (size_t)(linears + 1) * sizeof(ChainLinear);
 }
 
-// Chain configurations: (R row blocks per item, NW wavefronts per block).
+// Chain configurations: (R row blocks per item, NW wavefronts per block) of
+// the dot2 items (chains of M = 1 linears), then of the MFMA items (chains of
+// M = 2..16 linears); chain_cfg_mfma tells which list an index is in.
 int chain_num_cfgs();
+bool chain_cfg_mfma(int ci);
 void chain_cfg(int ci, int* R, int* NW);
-// Configuration for a chain whose longest K is kmax and whose stages hold
-// stage_bytes of codes on average (W4_CHAIN_CFG "R,NW" overrides; -1 if it
-// names no compiled configuration).
-int chain_choose_cfg(int kmax, double stage_bytes);
-// Co-resident blocks per CU of configuration ci (s16: bf16 scales) with
-// `lds` bytes of dynamic LDS.
-hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int* blocks);
+// Configuration for a chain of M-row linears whose longest K is kmax and
+// whose stages hold stage_bytes of codes on average (W4_CHAIN_CFG "R,NW"
+// overrides; -1 if it names no configuration compiled for that M).
+int chain_choose_cfg(int kmax, double stage_bytes, int M);
+// Co-resident blocks per CU of configuration ci (s16: bf16 scales) for
+// M-row linears, with `lds` bytes of dynamic LDS (dot2 items only).
+hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int M, int* blocks);
 // The fill launch, then the chain launch.
-hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds,
+hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds, int M,
                                hipStream_t stream);
 
 // s16: scales are bf16 bit patterns (uint16_t) instead of fp32.

@@ -362,7 +362,7 @@ typedef struct w4_chain_plan {
   void* workspace;
   int32_t linears, stages, items, blocks;
   int32_t config, lds_bytes, rows_per_item, waves_per_block;
-  int32_t scale_bytes, reserved;
+  int32_t scale_bytes, rows;
 } w4_chain_plan;
 
 size_t w4_chain_workspace_bytes(int64_t count);

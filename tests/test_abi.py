@@ -193,9 +193,11 @@ def test_chain_validation(w4):
     assert lib.w4_chain_prepare(None, 1, ws, n, ctypes.byref(plan), None) == ERR_NULL
     assert prep([lin(0, 0)], workspace=None) == ERR_NULL
     assert prep([lin(0, 0)], workspace=ws + 4) == ERR_ALIGN
-    assert prep([lin(0, 0, M=2)]) == ERR_SHAPE                      # decode only: M = 1
+    assert prep([lin(0, 0, M=0)]) == ERR_SHAPE                      # M from 1 to 16
+    assert prep([lin(0, 0, M=17)]) == ERR_SHAPE
+    assert prep([lin(0, 0, M=2), lin(1, 1, M=1)]) == ERR_SHAPE      # one M for the whole chain
     assert prep([lin(0, 0, K=100)]) == ERR_SHAPE
-    assert prep([lin(0, 0, K=30720 + 512)]) == ERR_SHAPE            # x must fit the LDS stage
+    assert prep([lin(0, 0, K=30720 + 512)]) == ERR_SHAPE            # at M = 1 x must fit the LDS stage
     assert prep([lin(0, 0, N=0)]) == ERR_SHAPE
     assert prep([lin(0, 0, q_packed=None)]) == ERR_NULL
     assert prep([lin(0, 0, x=FAKE + 2)]) == ERR_ALIGN
@@ -222,13 +224,18 @@ def test_chain_validation(w4):
     # a later stage reading x from the line of an earlier output without reading
     # that output (stage 0 writes 64 bytes at 0x30000; stage 1 reads from 0x30040)
     assert prep([lin(0, 0), lin(1, 1, x=FAKE + 0x30040, K=128)]) == ERR_ARG
+    # at M > 1 every x and y spans M rows: outputs of 2 x 32 values (128 bytes)
+    # overlap where one row would not, and an input of 2 x 256 values is not
+    # covered by an earlier output of 2 x 128
+    assert prep([lin(0, 0, M=2), lin(1, 1, M=2, y=FAKE + 0x30040)]) == ERR_ARG
+    assert prep([lin(0, 0, M=2, N=128), lin(1, 1, M=2, x=FAKE + 0x30000, K=256)]) == ERR_ARG
     # workspace too small, or overlapping a buffer of the chain
     assert prep([lin(0, 0), lin(1, 1)], nbytes=64) == ERR_ARG
     assert prep([lin(0, 0), lin(1, 1)], workspace=FAKE + 0x100000 + 0x30000 - 0x40) == ERR_ARG  # reaches y of linear 1
     # the 16-bit-scale variant checks the same (its descriptors have the same layout)
     arr = (C * 2)(lin(0, 0), lin(1, 2))
     assert lib.w4_chain_prepare_s16(arr, 2, ws, n, ctypes.byref(plan), None) == ERR_ARG
-    arr = (C * 1)(lin(0, 0, M=2))
+    arr = (C * 1)(lin(0, 0, M=17))
     assert lib.w4_chain_prepare_s16(arr, 1, ws, n, ctypes.byref(plan), None) == ERR_SHAPE
     # an output over 16-bit scales (32 x 256: 128 native scale slots of 2 bytes)
     arr = (C * 2)(lin(0, 0), lin(1, 1, y=FAKE + 0x20000 + 64))

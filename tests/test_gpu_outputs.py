@@ -8,7 +8,8 @@ of the range -- through the C ABI on an MI355X, against the CPU oracle.
   of such a value (oracle.admissible) and equal, bit for bit, the bf16
   rounding of the fp32 outputs.
 * Non-finite activations: a NaN or infinity in row m of x makes every output
-  of row m NaN, and leaves the other rows untouched.
+  of row m NaN, and leaves the other rows untouched (also where K is not a
+  multiple of 512 and the last scale quad is padded).
 * Large activations: inside the range where no fp32 intermediate overflows
   (|x| <= 2^64, |w| <= 2^38) the bound holds; past it an output may be
   non-finite where the exact value is finite, but never a wrong finite value.
@@ -138,20 +139,25 @@ def _poison(x, rows):
 def test_nonfinite_activations_poison_their_rows(w4, gpu, path, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("W4_MFMA_CFG" if path == "mfma" else "W4_GEMV_CFG", cfg)
-    N, K = 300, 2560
-    W = workloads.random_weight(N, K, seed=81)
-    q, d = w4.quantize_rtn(torch.from_numpy(W).to(gpu))
-    q_ref, d_ref = oracle.rtn_quantize_ref(W)
-    for M, rows in ((1, [0]), (4, [1, 2]), (8, [2, 3, 7]), (16, [0, 5, 9, 10, 15])):
-        if path == "gemv" and M > 4:
-            continue
-        _say(f"non-finite activations M={M} rows={rows} path={path} cfg={cfg}")
-        x = _poison(workloads.random_activations(M, K, seed=M, device=gpu), rows)
-        yb, yf = run_both(w4, x, q, d, N, path)
-        y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
-        assert np.isnan(y_ref[rows]).all()
-        check_y(yb, y_ref, absdot, f"bf16 M={M}")
-        check_y(yf, y_ref, absdot, f"fp32 M={M}")
+    # K = 2688: 21 groups, the last scale quad padded with three groups, whose
+    # x must read as zeros (not as the start of the next row of x); a poisoned
+    # value at column 37 or 74 then sits where the padding of the row before
+    # would have read it
+    for K in (2560, 2688):
+        N = 300
+        W = workloads.random_weight(N, K, seed=81)
+        q, d = w4.quantize_rtn(torch.from_numpy(W).to(gpu))
+        q_ref, d_ref = oracle.rtn_quantize_ref(W)
+        for M, rows in ((1, [0]), (4, [1, 2]), (8, [2, 3, 7]), (16, [0, 5, 9, 10, 15])):
+            if path == "gemv" and M > 4:
+                continue
+            _say(f"non-finite activations K={K} M={M} rows={rows} path={path} cfg={cfg}")
+            x = _poison(workloads.random_activations(M, K, seed=M, device=gpu), rows)
+            yb, yf = run_both(w4, x, q, d, N, path)
+            y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
+            assert np.isnan(y_ref[rows]).all()
+            check_y(yb, y_ref, absdot, f"bf16 K={K} M={M}")
+            check_y(yf, y_ref, absdot, f"fp32 K={K} M={M}")
 
 
 @pytest.mark.parametrize("path", ["gemv", "mfma"])

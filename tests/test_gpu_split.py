@@ -119,17 +119,20 @@ def test_split_full_size_down_projection(w4, gpu, ws):
     check_workspace_clean(ws)
 
 
-def test_split_nonfinite_rows(w4, gpu, ws, monkeypatch):
+@pytest.mark.parametrize("K", [4096, 2688])
+def test_split_nonfinite_rows(w4, gpu, ws, K, monkeypatch):
+    """(K = 2688: the last scale quad is padded; the NaN in row 1 at column 5
+    must not reach row 0 through the padding's x.)"""
     monkeypatch.setenv("W4_MFMA_CFG", "2,4")
     monkeypatch.setenv("W4_MFMA_SPLIT", "4")
-    N, K, M = 300, 4096, 16
+    N, M = 300, 16
     q, d, q_ref, d_ref = _quantized(w4, gpu, N, K, seed=77)
     x = workloads.random_activations(M, K, seed=9, device=gpu)
     xb = x.view(torch.int16)
     xb[1, 5] = -1            # bf16 0xFFFF: a NaN with every payload bit set
     xb[4, K - 1] = 0x7F80    # +inf
     xb[9, 2000] = -128       # 0xFF80: -inf
-    _say("split non-finite rows")
+    _say(f"split non-finite rows K={K}")
     y_ref, absdot = oracle.w4_linear_ref(_bits(x), q_ref, d_ref)
     assert np.isnan(y_ref[[1, 4, 9]]).all()
     for od in (torch.bfloat16, torch.float32):
