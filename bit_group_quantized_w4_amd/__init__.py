@@ -332,12 +332,13 @@ class ChainPlan:
 
 
 def chain_prepare(stages, noalloc=False):
-    """Prepare a chained decode pass (w4_chain_prepare).
+    """Prepare a chained pass (w4_chain_prepare): a decode step (M = 1) or a
+    verification pass (M = 2..16).
 
-    stages: sequence of stages, each a sequence of (x [1, K] bf16, q, d, N,
-    y [1, N] bf16), with d fp32 scales throughout or bf16 (16-bit) scales
-    throughout.  A linear whose x lies in outputs of earlier stages reads it
-    once all of it is written.  Returns a ChainPlan; plan.run() enqueues one
+    stages: sequence of stages, each a sequence of (x [M, K] bf16, q, d, N,
+    y [M, N] bf16), one M throughout, with d fp32 scales throughout or bf16
+    (16-bit) scales throughout.  A linear whose x lies in outputs of earlier
+    stages uses no value of it before that value is written.  Returns a ChainPlan; plan.run() enqueues one
     pass.  With noalloc (fp32 scales only), the workspace is the library's
     static scratch (w4_chain_prepare_noalloc): nothing is allocated, and only
     the most recent such plan of a GPU may be run.

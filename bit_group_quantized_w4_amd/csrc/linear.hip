@@ -379,9 +379,13 @@ struct ChainGate {
 // Gate (kActive: an item of a chained launch, x through the LDS slot): x is
 // loaded coherently, and when x is written by earlier stages each group's
 // loads are checked before they are staged.  If a value is still unwritten,
-// lane 0 polls one unwritten chunk until it is written, then the x of all four
-// groups in flight is loaded again (each may predate the write) and the
-// group is checked anew.  Outputs are written through (bf16 only).
+// lane 0 polls one chunk until it is written -- the first time in an item the
+// last chunk of the wavefront's range of x (its producer, the stage's
+// highest-numbered item over that range, tends to finish last; waiting for
+// the chunk found unwritten instead trails the producers one round trip each),
+// later the unwritten chunk found -- then the x of all four groups in flight
+// is loaded again (each may predate the write) and the group is checked anew.
+// Outputs are written through (bf16 only).
 // ---------------------------------------------------------------------------
 template <int R, int NW, bool S16, int XR, class Gate = NoGate>
 __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, uint8_t* ws = nullptr,
@@ -454,6 +458,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
   // and of the next one (a[2][4]); registers: the loads are the operands.
   bf16x8 a[2][4];
   // (Gate) wait until slot s holds no unwritten value (see above)
+  bool polled_end = false;
   auto await_x = [&](int s) {
     if constexpr (Gate::kActive) {
       for (uint32_t it = 0;; ++it) {
@@ -463,7 +468,11 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
           if (ChainGate::unwritten(bx[s][t])) mine = xo[t] + xbs[s] + xi[t];
         const uint64_t lanes = __ballot(mine != kOobX);
         if (lanes == 0) return;
-        const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)mine, __builtin_ctzll(lanes));
+        uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)mine, __builtin_ctzll(lanes));
+        if (!polled_end) {  // the last 16 bytes of the range in the last row of x
+          polled_end = true;
+          off = ((uint32_t)(wk.m0 + min(M - wk.m0, kTileRows) - 1) * K + min(K, 512 * j1) - 8) * 2u;
+        }
         // timed out (also after too many rounds): the error flag is set, the outputs are NaN
         if (!gate.poll(rx, off) || it >= kChainSpinLimit) {
           if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(gate.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1472,9 +1481,10 @@ namespace {
 // LDS slot); a configuration index counts through both lists.
 constexpr int kChainCfgs[][2] = {{1, 4}, {1, 8}, {2, 4}, {2, 2}, {1, 2}, {4, 4}};
 constexpr int kNumChainCfgs = sizeof(kChainCfgs) / sizeof(kChainCfgs[0]);
-constexpr int kChainMfmaCfgs[][2] = {{2, 4}, {4, 4}, {1, 4}, {2, 2}, {4, 2}};
+// (each also an MFMA configuration of the batched launch, whose bits it gives)
+constexpr int kChainMfmaCfgs[][2] = {{2, 4}, {4, 4}, {1, 4}, {2, 2}};
 constexpr int kNumChainMfmaCfgs = sizeof(kChainMfmaCfgs) / sizeof(kChainMfmaCfgs[0]);
-static_assert(kNumChainCfgs == 6 && kNumChainMfmaCfgs == 5, "the switches below list these configurations");
+static_assert(kNumChainCfgs == 6 && kNumChainMfmaCfgs == 4, "the switches below list these configurations");
 
 template <int I, bool S16>
 const void* chain_kernel_ptr() {
@@ -1502,8 +1512,7 @@ const void* chain_mfma_kernel(int mi) {
     case 0: return chain_mfma_kernel_ptr<0, S16, XR>();
     case 1: return chain_mfma_kernel_ptr<1, S16, XR>();
     case 2: return chain_mfma_kernel_ptr<2, S16, XR>();
-    case 3: return chain_mfma_kernel_ptr<3, S16, XR>();
-    default: return chain_mfma_kernel_ptr<4, S16, XR>();
+    default: return chain_mfma_kernel_ptr<3, S16, XR>();
   }
 }
 template <bool S16>
@@ -1529,7 +1538,7 @@ void launch_chain_mfma_cfg(int mi, int blocks, hipStream_t stream, const ChainLi
     linear_chain_mfma_kernel<kChainMfmaCfgs[i][0], kChainMfmaCfgs[i][1], S16, XR>            \
         <<<blocks, kChainMfmaCfgs[i][1] * 64, 0, stream>>>(lin, hdr, items);                 \
     break;
-    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4)
+    W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3)
 #undef W4_CHAIN
   }
 }
@@ -1558,7 +1567,11 @@ int chain_choose_cfg(int kmax, double stage_bytes, int M) {
     return -1;
   }
   (void)kmax;
-  if (mfma) return kNumChainCfgs;  // two row blocks per item, four wavefronts
+  // MFMA items (70B- and 27B-class stacks at M = 8 and 16, up to two blocks
+  // per CU): two row blocks and four wavefronts were fastest of (2,4), (4,4),
+  // (1,4), (2,2), (4,2) and of eight-wavefront forms (2,8) and (1,8), except
+  // (2,8) by 3% on the 70B-class stack at M = 8.
+  if (mfma) return kNumChainCfgs;
   // Measured on MI355X (two blocks per CU; the grid size is chosen by the C
   // ABI): with stages of tens of MB or more (27B- and 70B-class stacks, 45
   // and 110 MB of codes per stage on average) two row blocks per item and

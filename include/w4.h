@@ -284,23 +284,27 @@ w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, i
                     int8_t* q_canon, float* d_canon, hipStream_t stream);
 
 /*
- * Chained decode pass -- a dependent sequence of M = 1 linears run as one
- * pass of two launches.  Every generated token runs each linear of every
- * layer once, one after the other (27B quantization-and-drafter ladder,
- * stage 1: decode reads all weights per token); within a layer q|k|v read
+ * Chained pass -- a dependent sequence of linears with one M run as one pass
+ * of two launches.  Every generated token runs each linear of every layer
+ * once, one after the other (27B quantization-and-drafter ladder, stage 1:
+ * decode reads all weights per token), at M = 1; verifying K drafted tokens
+ * runs the same sequence at M = K + 1 (stage 2).  Within a layer q|k|v read
  * the layer input, o reads what they lead to, gate|up read o's result and
  * down reads theirs.  The linears are given in stages; a linear whose x lies
- * in outputs of earlier stages reads it only once all of it is written.  Each
- * linear computes exactly what w4_linear computes (study, section 1: y = W x
- * with the group-quantization equation): its bits equal those of one
- * w4_linear_batched call per stage run with the dot2 kernel in the chain's
- * (R, NW) configuration, except that a NaN output with bits 0xFFFF is
- * written as 0xFFC0 (0xFFFF marks unwritten values inside the pass).
+ * in outputs of earlier stages uses no value of it before that value is
+ * written.  Each linear computes exactly what w4_linear computes (study,
+ * section 1: y = W x with the group-quantization equation): its bits equal
+ * those of one w4_linear_batched call per stage run in the chain's (R, NW)
+ * configuration -- with the dot2 kernel at M = 1, with the MFMA kernel and no
+ * split workspace at M = 2..16 -- except that a NaN output with bits 0xFFFF
+ * is written as 0xFFC0 (0xFFFF marks unwritten values inside the pass).
  *
  * Unlike one launch per stage, the pass does not drain between stages: a
- * persistent grid walks the stages' row panels in order, issues the weight
- * loads of its next panel before that panel's input is ready, and stages the
- * input once no value of it is unwritten.  A first, small launch marks every
+ * persistent grid walks the stages' row panels in order and issues the
+ * weight loads of its next panel before that panel's input is ready; at
+ * M = 1 each wavefront stages its range of the input once no value of it is
+ * unwritten, at M > 1 each group of the input is checked as it is read and
+ * waited for while any value is unwritten.  A first, small launch marks every
  * output that a later stage reads as unwritten.
  *
  *   w4_chain_workspace_bytes(count) -- bytes of device workspace for `count`
@@ -312,9 +316,11 @@ w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, i
  *       fills `*plan` (host), and SYNCHRONISES `stream` once (a set-up call,
  *       not part of the pass).  `linears` is host memory, read before the
  *       call returns.  Requirements (W4_ERR_SHAPE / _NULL / _ALIGN / _ARG as
- *       for w4_linear): 1 <= count <= W4_CHAIN_MAX; every M == 1; every K a
- *       multiple of 128 up to 30720; N >= 1; stage[0] == 0 and each stage
- *       equal to the previous one or one more.  Each byte is written at most
+ *       for w4_linear): 1 <= count <= W4_CHAIN_MAX; one M for every linear,
+ *       from 1 to 16 (x is [M][K] and y [M][N], rows contiguous); every K a
+ *       multiple of 128 (up to 30720 at M = 1, as w4_linear otherwise);
+ *       N >= 1; stage[0] == 0 and each stage equal to the previous one or one
+ *       more.  Each byte is written at most
  *       once per pass and never after the pass has read it: no y overlaps any
  *       q or d, any other y, or the 128-byte cache lines of any x of its own
  *       or an earlier stage.  An x that overlaps outputs of earlier stages
@@ -334,26 +340,26 @@ w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, i
 #define W4_CHAIN_MAX 8192
 
 typedef struct w4_chain_linear {
-  const uint16_t* x;       /* bf16 [1][K]                                  */
-  int64_t M;               /* must be 1                                    */
+  const uint16_t* x;       /* bf16 [M][K]                                  */
+  int64_t M;               /* 1..16, the same for every linear of a chain  */
   int64_t K;
   const uint8_t* q_packed; /* native codes of the N x K W                  */
   const float* d_packed;   /* native fp32 scales                           */
   int64_t N;
-  uint16_t* y;             /* bf16 [1][N]                                  */
+  uint16_t* y;             /* bf16 [M][N]                                  */
   int64_t stage;           /* 0, 1, 2 ... non-decreasing, steps of 0 or 1  */
 } w4_chain_linear;
 
 /* The same with 16-bit scales (bf16 bit patterns, as the *_s16 entry points
  * store them), for w4_chain_prepare_s16. */
 typedef struct w4_chain_linear_s16 {
-  const uint16_t* x;        /* bf16 [1][K]                                  */
-  int64_t M;                /* must be 1                                    */
+  const uint16_t* x;        /* bf16 [M][K]                                  */
+  int64_t M;                /* 1..16, the same for every linear of a chain  */
   int64_t K;
   const uint8_t* q_packed;  /* native codes of the N x K W                  */
   const uint16_t* d_packed; /* native bf16 scales                           */
   int64_t N;
-  uint16_t* y;              /* bf16 [1][N]                                  */
+  uint16_t* y;              /* bf16 [M][N]                                  */
   int64_t stage;
 } w4_chain_linear_s16;
 
