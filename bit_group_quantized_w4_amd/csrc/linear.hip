@@ -1108,8 +1108,11 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
 // a group's x is checked for unwritten values just before it is staged.  Per
 // item the arithmetic is exactly the MFMA kernel's with the same (R, NW),
 // unsplit, so results are identical bits (NaN outputs aside, as above).
+// At M <= 8 with up to two row blocks the item fits in 168 VGPRs without
+// spilling: three wavefronts per SIMD (the batched kernel's occupancy there)
+// keep more bytes in flight per CU than two.
 template <int R, int NW, bool S16, int XR>
-__global__ __launch_bounds__(NW * 64) void linear_chain_mfma_kernel(const ChainLinear* __restrict__ lin,
+__global__ __launch_bounds__(NW * 64, (XR == 8 && R <= 2) ? 3 : 1) void linear_chain_mfma_kernel(const ChainLinear* __restrict__ lin,
                                                                     uint32_t* hdr, int items) {
   const int P = gridDim.x;
   int i = blockIdx.x;
