@@ -453,3 +453,17 @@ def test_chain_verify_error_flag_is_sticky_until_prepare(w4, gpu, monkeypatch):
     assert plan.error() == 0
     cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
     _check_pass(w4, records, cfg, monkeypatch, "M=8 after prepare")
+
+
+def test_chain_verify_noalloc(w4, gpu, monkeypatch):
+    """M = 8 set up in the library's static scratch (w4_chain_prepare_noalloc):
+    the same pass as with a caller-owned workspace, bit for bit."""
+    _say("chain M=8 prepared in the static scratch (noalloc): 2 layers")
+    stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=512, nq=768, nkv=256, ffn=1408, seed=27,
+                                       side=False, M=8)
+    plan = w4.chain_prepare(stages, noalloc=True)
+    assert plan.info["x_rows"] == 8
+    plan.run()
+    assert plan.error() == 0
+    cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
+    _check_pass(w4, records, cfg, monkeypatch, "M=8 noalloc")
