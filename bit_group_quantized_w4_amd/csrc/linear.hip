@@ -297,14 +297,15 @@ struct ChainGate {
   __device__ __forceinline__ static bool unwritten(const uint32_t w) {
     return (~w & 0xFFFFu) == 0u || (~w & 0xFFFF0000u) == 0u;
   }
+  // (the checks of a chunk are or-ed without branches)
   __device__ __forceinline__ static bool unwritten(const uint4& v) {
-    return unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
+    return ((int)unwritten(v.x) | (int)unwritten(v.y) | (int)unwritten(v.z) | (int)unwritten(v.w)) != 0;
   }
   __device__ __forceinline__ static bool unwritten(const uint4 (&v)[4]) {
-    bool u = false;
+    int u = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u |= unwritten(v[i].x) | unwritten(v[i].y) | unwritten(v[i].z) | unwritten(v[i].w);
-    return u;
+    for (int i = 0; i < 4; ++i) u |= (int)unwritten(v[i]);
+    return u != 0;
   }
   // true (and the launch's error flag set) once waiting has gone on too long,
   // or when a wait anywhere has timed out (this launch or an earlier one)
@@ -335,8 +336,7 @@ struct ChainGate {
     const uint32_t off = (lane == 0 && b1 > b0) ? b1 - 16u : kOobX;
     for (uint32_t t = 0;; ++t) {
       const uint4 v = bload<kCoherent>(rx, off);
-      const bool u = unwritten(v.x) | unwritten(v.y) | unwritten(v.z) | unwritten(v.w);
-      if (!__any(u)) break;
+      if (!__any(unwritten(v))) break;
       if (t >= kChainSpinLimit || ((t & 31) == 31 && __hip_atomic_load(error, __ATOMIC_RELAXED,
                                                                        __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
         if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
