@@ -389,6 +389,89 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale
     return out
 
 
+def chain_stage_times(torch, w4, workloads, name, M, passes=3):
+    """Where a chained pass spends its time, stage by stage (w4_chain_trace).
+
+    The stack's chain at M (as bench_chain builds it) runs `passes` eager
+    passes; the last one is traced.  Per kind of stage (q|k|v, o, gate|up,
+    down), averaged over the layers: its items, the stage's span (from the end
+    of the previous stage's last item to the end of its own last item), when
+    its first item had its input relative to the previous stage's end, the
+    items' mean and longest duration from input to end, and the share of the
+    grid's blocks that held one of its items.  Times in microseconds.
+    """
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[name]
+    layers = []
+    for layer in range(wl.layers):
+        mats = []
+        for m in wl.matrices:
+            W = workloads.weight(name, layer, m.name, dev)
+            q, d = w4.quantize_rtn(W)
+            del W
+            mats.append((m, q, d))
+        layers.append(mats)
+    xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
+    groups = _shared_input_groups(wl)
+    stages, kinds, prev = [], [], []
+    for mats in layers:
+        ys = {m.name: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+        for gi in groups:
+            K = mats[gi[0]][0].K
+            x = next((y for n, y in prev if n == K), xs[K])
+            stages.append([(x, mats[i][1], mats[i][2], mats[i][0].N, ys[mats[i][0].name]) for i in gi])
+            kinds.append("|".join(mats[i][0].name for i in gi))
+            prev = [(mats[i][0].N, ys[mats[i][0].name]) for i in gi]
+    plan = w4.chain_prepare(stages)
+    items = plan.plan.items
+    stamps = torch.zeros(3 * items, dtype=torch.int64, device=dev)
+    for p in range(passes):
+        if p == passes - 1:
+            plan.trace(stamps)
+        plan.run()
+    if plan.error():
+        raise RuntimeError(f"{name} chained pass: a wait timed out")
+    plan.trace(None)
+    t = stamps.cpu().numpy().reshape(items, 3).astype(np.int64)
+    # item ranges of the stages, from the chain's table (item0 and stage of each linear)
+    n = plan.plan.linears
+    tab = plan.workspace[32:32 + 64 * n].cpu().numpy().view(np.int32).reshape(n, 16)
+    first = {}
+    for item0, st in zip(tab[:, 12], tab[:, 13]):
+        first[int(st)] = min(first.get(int(st), items), int(item0))
+    bounds = [first[s] for s in range(len(stages))] + [items]
+    T0 = t[:, 0].min()
+    prev_end = T0
+    acc = {}
+    for s, kind in enumerate(kinds):
+        a, b = bounds[s], bounds[s + 1]
+        st = t[a:b]
+        end = st[:, 2].max()
+        ready = st[:, 1][st[:, 1] > 0]
+        first_ready = ready.min() if len(ready) else st[:, 0].min()
+        dur = st[:, 2] - np.maximum(st[:, 0], st[:, 1])
+        r = acc.setdefault(kind, {"items": b - a, "span": [], "ready": [], "mean": [], "max": []})
+        r["span"].append((end - prev_end) * 0.01)
+        r["ready"].append((first_ready - prev_end) * 0.01)
+        r["mean"].append(dur.mean() * 0.01)
+        r["max"].append(dur.max() * 0.01)
+        prev_end = end
+    total = (t[:, 2].max() - T0) * 0.01
+    out = {"workload": name, "M": M, "items": items, "blocks": plan.plan.blocks, "rows_per_item": plan.plan.rows_per_item * 16,
+           "waves_per_block": plan.plan.waves_per_block, "traced_pass_us": round(float(total), 1), "stages": {}}
+    for kind, r in acc.items():
+        out["stages"][kind] = {"items": r["items"], "span_us": round(float(np.mean(r["span"])), 2),
+                               "first_input_after_prev_end_us": round(float(np.mean(r["ready"])), 2),
+                               "item_mean_us": round(float(np.mean(r["mean"])), 2),
+                               "item_max_us": round(float(np.mean(r["max"])), 2),
+                               "grid_share": round(min(1.0, r["items"] / plan.plan.blocks), 3)}
+    del plan, layers
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------
 # channel scaling before RTN (AWQ): the exponent search and the fused decode linear
 # ----------------------------------------------------------------------------
@@ -859,6 +942,8 @@ def main():
                     help="with --trace-summary: mean of the last N headline dispatches (the timed steps)")
     ap.add_argument("--path-compare-summary", metavar="KERNEL_TRACE_CSV",
                     help="per-case kernel durations of a --path-compare run")
+    ap.add_argument("--chain-stage-times", metavar="STACK:M",
+                    help="per-stage times of one traced chained pass (e.g. stack_27b:1) as a JSON line, and exit")
     ap.add_argument("--counter-summary", metavar="COUNTER_COLLECTION_CSV",
                     help="print a summary of a rocprofv3 counter collection and exit")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -896,6 +981,10 @@ def main():
 
     if args.path_compare:
         print(json.dumps({"path_compare": path_compare(torch, w4, workloads)}), flush=True)
+        return
+    if args.chain_stage_times:
+        name, M = args.chain_stage_times.split(":")
+        print(json.dumps({"chain_stage_times": chain_stage_times(torch, w4, workloads, name, int(M))}), flush=True)
         return
 
     only_ms = [int(m) for m in args.stack_ms.split(",") if m] or None

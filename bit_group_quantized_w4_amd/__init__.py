@@ -92,6 +92,7 @@ SIGNATURES = {
     "w4_chain_prepare_noalloc": (_INT, [ctypes.POINTER(ChainLinear), _I64, ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_run": (_INT, [ctypes.POINTER(ChainPlanC), _VP]),
     "w4_chain_error": (_INT, [ctypes.POINTER(ChainPlanC), ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "w4_chain_trace": (_INT, [ctypes.POINTER(ChainPlanC), _VP, _SZ, _VP]),
     # GPTQ steps
     "w4_gptq_damp": (_INT, [_VP, _I64, ctypes.c_double, _VP]),
     "w4_gptq_hessian": (_INT, [_VP, _I64, _I64, _VP, _VP]),
@@ -316,6 +317,19 @@ class ChainPlan:
     def run(self):
         """Enqueue one pass on the current stream (w4_chain_run)."""
         _check(_lib.w4_chain_run(ctypes.byref(self.plan), self._stream()), "w4_chain_run")
+
+    def trace(self, stamps):
+        """Per-item timestamps of later passes into `stamps` (int64 device tensor of
+        at least 3 * items values), or None to stop (w4_chain_trace)."""
+        if stamps is None:
+            _check(_lib.w4_chain_trace(ctypes.byref(self.plan), None, 0, self._stream()), "w4_chain_trace")
+            self._stamps = None
+            return
+        if not isinstance(stamps, torch.Tensor) or stamps.dtype != torch.int64 or not stamps.is_contiguous():
+            raise TypeError("stamps must be a contiguous int64 torch.Tensor")
+        _check(_lib.w4_chain_trace(ctypes.byref(self.plan), ctypes.c_void_p(stamps.data_ptr()), stamps.numel(),
+                                   self._stream()), "w4_chain_trace")
+        self._stamps = stamps  # kept alive while the chain may write it
 
     def error(self):
         """The workspace's error flag (synchronises the current stream; w4_chain_error)."""

@@ -276,6 +276,14 @@ constexpr uint16_t kNanForUnwritten = 0xFFC0;
 constexpr uint32_t kChainSpinLimit = 1u << 17;
 constexpr int kChainPollSleep = 4;  // s_sleep units (64 clocks) between polls
 
+// Chained launches with per-item timestamps (w4_chain_trace): the GPU's
+// 100 MHz real-time counter when the block's first wavefront had its input
+// in hand (after staging it, or after its last wait for it), per item.
+__device__ __forceinline__ uint64_t& chain_ready_stamp() {
+  __shared__ uint64_t t;
+  return t;
+}
+
 // No dependency to wait for: x is read as soon as the block starts.
 struct NoGate {
   static constexpr bool kActive = false;
@@ -290,6 +298,7 @@ struct ChainGate {
   bool same_stage;                      // the block's previous item was in this stage
   int parity;                           // the block's item count mod 2 (reduction buffer)
   uint32_t* error;
+  bool trace = false;                   // per-item timestamps are taken (chain_ready_stamp)
 
   __device__ __forceinline__ static void store(uint16_t* p, uint16_t v) {
     __hip_atomic_store(p, v == kUnwritten ? kNanForUnwritten : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -467,7 +476,10 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
         for (int t = NT - 1; t >= 0; --t)
           if (ChainGate::unwritten(bx[s][t])) mine = xo[t] + xbs[s] + xi[t];
         const uint64_t lanes = __ballot(mine != kOobX);
-        if (lanes == 0) return;
+        if (lanes == 0) {
+          if (gate.trace && it > 0 && threadIdx.x == 0) chain_ready_stamp() = __builtin_amdgcn_s_memrealtime();
+          return;
+        }
         uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)mine, __builtin_ctzll(lanes));
         if (!polled_end) {  // the last 16 bytes of the range in the last row of x
           polled_end = true;
@@ -909,6 +921,7 @@ __device__ __forceinline__ void gemv_body(const LinearDesc& D, const Work& wk, c
           gate.wait_sample(rx, 1024u * w.j0, xb1);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's LDS writes land before its reads
+        if (gate.trace && threadIdx.x == 0) chain_ready_stamp() = __builtin_amdgcn_s_memrealtime();
       }
     } else {
       // Consume x here, before the branches, so the loads are not sunk into
@@ -1074,8 +1087,28 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
 // stale copy.  A chain writes each byte at most once and never writes a
 // cache line that the pass reads earlier (the C ABI refuses such chains).
 // ---------------------------------------------------------------------------
+// Per-item timestamps (w4_chain_trace): the header's words 2-3 hold the
+// buffer (null: none).  Thread 0 writes, per item i, stamps[3i] = start,
+// [3i + 1] = when the block's first wavefront had its input (0 if it had
+// nothing to stage or wait for), [3i + 2] = end (after the outputs' stores
+// were issued).
+__device__ __forceinline__ uint64_t* chain_stamps(const uint32_t* hdr) {
+  return *reinterpret_cast<uint64_t* const*>(hdr + 2);
+}
+__device__ __forceinline__ uint64_t chain_item_start() {
+  if (threadIdx.x == 0) chain_ready_stamp() = 0;
+  return __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void chain_item_end(uint64_t* stamps, int i, uint64_t t0) {
+  if (threadIdx.x == 0) {
+    stamps[3 * (size_t)i] = t0;
+    stamps[3 * (size_t)i + 1] = chain_ready_stamp();
+    stamps[3 * (size_t)i + 2] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
 // lin: the table (linears + 1 entries, the last a sentinel); hdr: the
-// workspace header's error word.
+// workspace header (error word, then the timestamp buffer).
 template <int R, int NW, bool S16>
 __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear* __restrict__ lin, uint32_t* hdr,
                                                                int items) {
@@ -1088,13 +1121,16 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
   int staged_k = 0;
   int prev_stage = -1;
   int parity = 0;
+  uint64_t* const stamps = chain_stamps(hdr);
   while (i < items) {
     const LinearDesc& D = lin[li].desc;
     const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage,
-                         parity, hdr};
+                         parity, hdr, stamps != nullptr};
     prev_stage = lin[li].stage;
     parity ^= 1;
+    const uint64_t t0 = stamps ? chain_item_start() : 0;
     gemv_body<1, R, NW, S16, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
+    if (stamps) chain_item_end(stamps, i, t0);
     staged = D.x;
     staged_k = D.K;
     i += P;
@@ -1120,10 +1156,13 @@ __global__ __launch_bounds__(NW * 64, (XR == 8 && R <= 2) ? 3 : 1) void linear_c
   int li_end = lin[1].item0;
   while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
   int parity = 0;
+  uint64_t* const stamps = chain_stamps(hdr);
   while (i < items) {
-    const ChainGate gate{lin[li].wait_x != 0, false, false, parity, hdr};
+    const ChainGate gate{lin[li].wait_x != 0, false, false, parity, hdr, stamps != nullptr};
     parity ^= 1;
+    const uint64_t t0 = stamps ? chain_item_start() : 0;
     mfma_body<R, NW, S16, XR, ChainGate>(lin[li].desc, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
+    if (stamps) chain_item_end(stamps, i, t0);
     i += P;
     while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
   }

@@ -66,8 +66,10 @@ constexpr size_t kSplitHeaderBytes = 256;
 // Workspace layout (device): ChainHeader | ChainLinear[linears + 1] (the last
 // is a sentinel with item0 = items).
 struct ChainHeader {
-  uint32_t error;  // sticky: nonzero once a wait has timed out
-  uint32_t pad[7];
+  uint32_t error;      // sticky: nonzero once a wait has timed out
+  uint32_t pad;
+  uint64_t* stamps;    // per-item timestamps of later passes (w4_chain_trace), or null
+  uint32_t pad2[4];
 };
 struct ChainLinear {
   LinearDesc desc;

@@ -329,6 +329,17 @@ w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, i
  *   w4_chain_run(plan, stream) -- enqueues one pass (asynchronous, no
  *       allocation, capturable in a HIP graph).  Passes on one workspace must
  *       not overlap in time (one stream, or ordered streams).
+ *   w4_chain_trace(plan, stamps, count, stream) -- a measuring aid: from the
+ *       next pass on, thread 0 of each block writes three values of the
+ *       GPU's 100 MHz real-time counter per item (the chain's panels in the
+ *       order it runs them: stage by stage, within a stage longest K first,
+ *       each linear's panels of rows_per_item rows in order) to the device
+ *       buffer `stamps` (count >= 3 * plan->items uint64 values, 8-byte
+ *       aligned, owned by the caller): [3i] the item's start, [3i + 1] when
+ *       its block's first wavefront had its input (0 if it staged or waited
+ *       for nothing), [3i + 2] its end.  stamps == NULL stops it.  The
+ *       outputs do not change.  Synchronises `stream`; w4_chain_prepare
+ *       clears it.
  *   w4_chain_error(plan, &flag, stream) -- synchronises `stream` and reads
  *       the workspace's error flag: nonzero if a wait of some pass ran out of
  *       time (it is bounded at tens of milliseconds; it can only run out if
@@ -379,6 +390,7 @@ w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count
                                size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream);
+w4_status w4_chain_trace(const w4_chain_plan* plan, uint64_t* stamps, size_t count, hipStream_t stream);
 
 /*
  * w4_chain_prepare_noalloc -- w4_chain_prepare for callers that cannot

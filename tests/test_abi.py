@@ -171,6 +171,14 @@ def test_chain_validation(w4):
     lib = w4.library()
     C = w4.ChainLinear
     plan = w4.ChainPlanC()
+    # the timestamp aid checks its arguments before touching the workspace
+    assert lib.w4_chain_trace(None, None, 0, None) == ERR_NULL
+    assert lib.w4_chain_trace(ctypes.byref(plan), None, 0, None) == ERR_NULL  # no workspace
+    plan.workspace = FAKE
+    plan.items = 10
+    assert lib.w4_chain_trace(ctypes.byref(plan), FAKE + 4, 30, None) == ERR_ALIGN
+    assert lib.w4_chain_trace(ctypes.byref(plan), FAKE, 29, None) == ERR_ARG  # 3 values per item
+    plan = w4.ChainPlanC()
     assert lib.w4_chain_workspace_bytes(0) == 0
     assert lib.w4_chain_workspace_bytes(8193) == 0
     n = lib.w4_chain_workspace_bytes(4)

@@ -467,3 +467,38 @@ def test_chain_verify_noalloc(w4, gpu, monkeypatch):
     assert plan.error() == 0
     cfg = f"{plan.plan.rows_per_item},{plan.plan.waves_per_block}"
     _check_pass(w4, records, cfg, monkeypatch, "M=8 noalloc")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_chain_trace_timestamps(w4, gpu, M, monkeypatch):
+    """w4_chain_trace: every item gets a start, an input-ready and an end stamp
+    in order (ready 0 only for items that waited for nothing), the outputs are
+    those of an untraced pass bit for bit, and clearing it stops the writes."""
+    # (K of 2048 and more: every wavefront of an item has a scale quad of its own)
+    _say(f"chain timestamps M={M}: 2 layers (hidden 2048)")
+    stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=2048, nq=2048, nkv=512, ffn=2816, seed=28,
+                                       side=False, M=M)
+    plan = w4.chain_prepare(stages)
+    plan.run()
+    torch.cuda.synchronize()
+    ref = [r[7].clone() for r in records]
+    items = plan.plan.items
+    stamps = torch.zeros(3 * items + 3, dtype=torch.int64, device=gpu)
+    plan.trace(stamps)
+    plan.run()
+    assert plan.error() == 0
+    for r, y in zip(records, ref):
+        assert torch.equal(r[7].view(torch.int16), y.view(torch.int16)), f"{r[0]}: traced pass differs"
+    t = stamps.cpu().numpy()
+    assert t[-3:].tolist() == [0, 0, 0], "wrote past the items"
+    t = t[:-3].reshape(items, 3)
+    start, ready, end = t[:, 0], t[:, 1], t[:, 2]
+    assert (start > 0).all() and (end >= start).all()
+    waited = ready > 0
+    assert ((ready[waited] >= start[waited]) & (ready[waited] <= end[waited])).all()
+    assert waited.any()
+    plan.trace(None)
+    stamps.zero_()
+    plan.run()
+    assert plan.error() == 0
+    assert int(stamps.abs().sum()) == 0
