@@ -44,7 +44,7 @@ class ChainPlanC(ctypes.Structure):
     _I32 = ctypes.c_int32
     _fields_ = [("workspace", _VP), ("linears", _I32), ("stages", _I32), ("items", _I32), ("blocks", _I32),
                 ("config", _I32), ("lds_bytes", _I32), ("rows_per_item", _I32), ("waves_per_block", _I32),
-                ("scale_bytes", _I32), ("rows", _I32)]
+                ("scale_bytes", _I32), ("rows", _I32), ("trace", _I32), ("reserved", _I32)]
 
 
 # (name, restype, argtypes) of every symbol include/w4.h declares

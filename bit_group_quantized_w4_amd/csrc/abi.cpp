@@ -745,6 +745,8 @@ w4_status chain_prepare(const Desc* linears, int64_t count, void* workspace, siz
   plan->waves_per_block = NW;
   plan->scale_bytes = s16 ? 2 : 4;
   plan->rows = (int32_t)M;
+  plan->trace = 0;
+  plan->reserved = 0;
   return W4_OK;
 }
 }  // namespace
@@ -820,17 +822,19 @@ w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream) {
   if (plan->blocks == 0) return W4_OK;
   return hip_status(w4::launch_linear_chain(plan->workspace, plan->linears, plan->items, plan->config,
                                             plan->scale_bytes == 2, plan->blocks, (size_t)plan->lds_bytes,
-                                            plan->rows, stream));
+                                            plan->rows, plan->trace != 0, stream));
 }
 
-w4_status w4_chain_trace(const w4_chain_plan* plan, uint64_t* stamps, size_t count, hipStream_t stream) {
+w4_status w4_chain_trace(w4_chain_plan* plan, uint64_t* stamps, size_t count, hipStream_t stream) {
   if (!plan || !plan->workspace) return W4_ERR_NULL;
   if (plan->items < 0) return W4_ERR_ARG;
   if (stamps && !aligned(stamps, 8)) return W4_ERR_ALIGN;
   if (stamps && count < 3 * (size_t)plan->items) return W4_ERR_ARG;
   uint8_t* field = static_cast<uint8_t*>(plan->workspace) + offsetof(w4::ChainHeader, stamps);
   if (hipError_t e = hipMemcpyAsync(field, &stamps, sizeof(stamps), hipMemcpyHostToDevice, stream)) return hip_status(e);
-  return hip_status(hipStreamSynchronize(stream));
+  if (hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
+  plan->trace = stamps != nullptr;
+  return W4_OK;
 }
 
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream) {

@@ -277,9 +277,14 @@ constexpr uint32_t kChainSpinLimit = 1u << 17;
 constexpr int kChainPollSleep = 4;  // s_sleep units (64 clocks) between polls
 
 // Chained launches with per-item timestamps (w4_chain_trace): the GPU's
-// 100 MHz real-time counter when the block's first wavefront had its input
-// in hand (after staging it, or after its last wait for it), per item.
+// 100 MHz real-time counter when the block's first wavefront had staged its
+// input (dot2 items; MFMA items read their input group by group and record
+// no such time: a stamp inside their wait spilled registers of the loop).
 __device__ __forceinline__ uint64_t& chain_ready_stamp() {
+  __shared__ uint64_t t;
+  return t;
+}
+__device__ __forceinline__ uint64_t& chain_start_stamp() {
   __shared__ uint64_t t;
   return t;
 }
@@ -476,10 +481,7 @@ __device__ __forceinline__ void mfma_body(const LinearDesc& D, const Work& wk, u
         for (int t = NT - 1; t >= 0; --t)
           if (ChainGate::unwritten(bx[s][t])) mine = xo[t] + xbs[s] + xi[t];
         const uint64_t lanes = __ballot(mine != kOobX);
-        if (lanes == 0) {
-          if (gate.trace && it > 0 && threadIdx.x == 0) chain_ready_stamp() = __builtin_amdgcn_s_memrealtime();
-          return;
-        }
+        if (lanes == 0) return;
         uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)mine, __builtin_ctzll(lanes));
         if (!polled_end) {  // the last 16 bytes of the range in the last row of x
           polled_end = true;
@@ -1089,27 +1091,31 @@ __global__ __launch_bounds__(NW * 64) void linear_gemv_xscaled(const uint16_t* x
 // ---------------------------------------------------------------------------
 // Per-item timestamps (w4_chain_trace): the header's words 2-3 hold the
 // buffer (null: none).  Thread 0 writes, per item i, stamps[3i] = start,
-// [3i + 1] = when the block's first wavefront had its input (0 if it had
-// nothing to stage or wait for), [3i + 2] = end (after the outputs' stores
-// were issued).
+// [3i + 1] = when the block's first wavefront had staged its input (dot2
+// items that staged one; 0 otherwise), [3i + 2] = end (after the outputs'
+// stores were issued).
 __device__ __forceinline__ uint64_t* chain_stamps(const uint32_t* hdr) {
   return *reinterpret_cast<uint64_t* const*>(hdr + 2);
 }
-__device__ __forceinline__ uint64_t chain_item_start() {
-  if (threadIdx.x == 0) chain_ready_stamp() = 0;
-  return __builtin_amdgcn_s_memrealtime();
-}
-__device__ __forceinline__ void chain_item_end(uint64_t* stamps, int i, uint64_t t0) {
+// (the start is kept in LDS, not in a register live across the item's body)
+__device__ __forceinline__ void chain_item_start() {
   if (threadIdx.x == 0) {
-    stamps[3 * (size_t)i] = t0;
+    chain_ready_stamp() = 0;
+    chain_start_stamp() = __builtin_amdgcn_s_memrealtime();
+  }
+}
+__device__ __forceinline__ void chain_item_end(uint64_t* stamps, int i) {
+  if (threadIdx.x == 0) {
+    stamps[3 * (size_t)i] = chain_start_stamp();
     stamps[3 * (size_t)i + 1] = chain_ready_stamp();
     stamps[3 * (size_t)i + 2] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
 // lin: the table (linears + 1 entries, the last a sentinel); hdr: the
-// workspace header (error word, then the timestamp buffer).
-template <int R, int NW, bool S16>
+// workspace header (error word, then the timestamp buffer).  kTrace: the
+// variant that takes per-item timestamps (the other has none of that code).
+template <int R, int NW, bool S16, bool kTrace = false>
 __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear* __restrict__ lin, uint32_t* hdr,
                                                                int items) {
   const int P = gridDim.x;
@@ -1121,16 +1127,20 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
   int staged_k = 0;
   int prev_stage = -1;
   int parity = 0;
-  uint64_t* const stamps = chain_stamps(hdr);
+  uint64_t* const stamps = kTrace ? chain_stamps(hdr) : nullptr;
   while (i < items) {
     const LinearDesc& D = lin[li].desc;
     const ChainGate gate{lin[li].wait_x != 0, D.x == staged && D.K == staged_k, lin[li].stage == prev_stage,
-                         parity, hdr, stamps != nullptr};
+                         parity, hdr, kTrace && stamps != nullptr};
     prev_stage = lin[li].stage;
     parity ^= 1;
-    const uint64_t t0 = stamps ? chain_item_start() : 0;
+    if constexpr (kTrace) {
+      if (stamps) chain_item_start();
+    }
     gemv_body<1, R, NW, S16, false, ChainGate>(D, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
-    if (stamps) chain_item_end(stamps, i, t0);
+    if constexpr (kTrace) {
+      if (stamps) chain_item_end(stamps, i);
+    }
     staged = D.x;
     staged_k = D.K;
     i += P;
@@ -1147,22 +1157,26 @@ __global__ __launch_bounds__(NW * 64) void linear_chain_kernel(const ChainLinear
 // At M <= 8 with up to two row blocks the item fits in 168 VGPRs without
 // spilling: three wavefronts per SIMD (the batched kernel's occupancy there)
 // keep more bytes in flight per CU than two.
-template <int R, int NW, bool S16, int XR>
-__global__ __launch_bounds__(NW * 64, (XR == 8 && R <= 2) ? 3 : 1) void linear_chain_mfma_kernel(const ChainLinear* __restrict__ lin,
-                                                                    uint32_t* hdr, int items) {
+template <int R, int NW, bool S16, int XR, bool kTrace = false>
+__global__ __launch_bounds__(NW * 64, (XR == 8 && R <= 2) ? 3 : 1) void linear_chain_mfma_kernel(
+    const ChainLinear* __restrict__ lin, uint32_t* hdr, int items) {
   const int P = gridDim.x;
   int i = blockIdx.x;
   int li = 0;
   int li_end = lin[1].item0;
   while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
   int parity = 0;
-  uint64_t* const stamps = chain_stamps(hdr);
+  uint64_t* const stamps = kTrace ? chain_stamps(hdr) : nullptr;
   while (i < items) {
-    const ChainGate gate{lin[li].wait_x != 0, false, false, parity, hdr, stamps != nullptr};
+    const ChainGate gate{lin[li].wait_x != 0, false, false, parity, hdr, kTrace && stamps != nullptr};
     parity ^= 1;
-    const uint64_t t0 = stamps ? chain_item_start() : 0;
+    if constexpr (kTrace) {
+      if (stamps) chain_item_start();
+    }
     mfma_body<R, NW, S16, XR, ChainGate>(lin[li].desc, Work{0, (i - lin[li].item0) * R, 0}, nullptr, gate);
-    if (stamps) chain_item_end(stamps, i, t0);
+    if constexpr (kTrace) {
+      if (stamps) chain_item_end(stamps, i);
+    }
     i += P;
     while (i < items && i >= li_end) li_end = lin[++li + 1].item0;
   }
@@ -1557,13 +1571,13 @@ const void* chain_mfma_kernel(int mi) {
     default: return chain_mfma_kernel_ptr<3, S16, XR>();
   }
 }
-template <bool S16>
+template <bool S16, bool kTrace>
 void launch_chain_cfg(int ci, int blocks, size_t lds, hipStream_t stream, const ChainLinear* lin, uint32_t* hdr,
                       int items) {
   switch (ci) {
 #define W4_CHAIN(i)                                                                      \
   case i:                                                                                \
-    linear_chain_kernel<kChainCfgs[i][0], kChainCfgs[i][1], S16>                         \
+    linear_chain_kernel<kChainCfgs[i][0], kChainCfgs[i][1], S16, kTrace>                 \
         <<<blocks, kChainCfgs[i][1] * 64, lds, stream>>>(lin, hdr, items);               \
     break;
     W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3) W4_CHAIN(4) W4_CHAIN(5)
@@ -1571,13 +1585,13 @@ void launch_chain_cfg(int ci, int blocks, size_t lds, hipStream_t stream, const 
   }
 }
 // x rows staged per group: the 8 of a slab at M <= 8, all 16 above
-template <bool S16, int XR>
+template <bool S16, int XR, bool kTrace>
 void launch_chain_mfma_cfg(int mi, int blocks, hipStream_t stream, const ChainLinear* lin, uint32_t* hdr,
                            int items) {
   switch (mi) {
 #define W4_CHAIN(i)                                                                          \
   case i:                                                                                    \
-    linear_chain_mfma_kernel<kChainMfmaCfgs[i][0], kChainMfmaCfgs[i][1], S16, XR>            \
+    linear_chain_mfma_kernel<kChainMfmaCfgs[i][0], kChainMfmaCfgs[i][1], S16, XR, kTrace>    \
         <<<blocks, kChainMfmaCfgs[i][1] * 64, 0, stream>>>(lin, hdr, items);                 \
     break;
     W4_CHAIN(0) W4_CHAIN(1) W4_CHAIN(2) W4_CHAIN(3)
@@ -1652,27 +1666,36 @@ hipError_t launch_split_init(void* ws, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+template <bool kTrace>
+void launch_chain_kernels(int ci, bool s16, int blocks, size_t lds, int M, hipStream_t stream,
+                          const ChainLinear* lin, uint32_t* hdr, int items) {
+  if (!chain_cfg_mfma(ci)) {
+    if (s16) launch_chain_cfg<true, kTrace>(ci, blocks, lds, stream, lin, hdr, items);
+    else launch_chain_cfg<false, kTrace>(ci, blocks, lds, stream, lin, hdr, items);
+  } else {
+    const int mi = ci - kNumChainCfgs;
+    if (M > 8) {
+      if (s16) launch_chain_mfma_cfg<true, 16, kTrace>(mi, blocks, stream, lin, hdr, items);
+      else launch_chain_mfma_cfg<false, 16, kTrace>(mi, blocks, stream, lin, hdr, items);
+    } else {
+      if (s16) launch_chain_mfma_cfg<true, 8, kTrace>(mi, blocks, stream, lin, hdr, items);
+      else launch_chain_mfma_cfg<false, 8, kTrace>(mi, blocks, stream, lin, hdr, items);
+    }
+  }
+}
+}  // namespace
+
 hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds, int M,
-                               hipStream_t stream) {
+                               bool trace, hipStream_t stream) {
   if (ci < 0 || ci >= chain_num_cfgs() || M < 1 || M > 16 || chain_cfg_mfma(ci) != (M > 1))
     return hipErrorInvalidValue;
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
   const ChainLinear* lin = reinterpret_cast<const ChainLinear*>(w + sizeof(ChainHeader));
   chain_fill_kernel<<<dim3(linears, M), 256, 0, stream>>>(lin);
-  if (!chain_cfg_mfma(ci)) {
-    if (s16) launch_chain_cfg<true>(ci, blocks, lds, stream, lin, hdr, items);
-    else launch_chain_cfg<false>(ci, blocks, lds, stream, lin, hdr, items);
-  } else {
-    const int mi = ci - kNumChainCfgs;
-    if (M > 8) {
-      if (s16) launch_chain_mfma_cfg<true, 16>(mi, blocks, stream, lin, hdr, items);
-      else launch_chain_mfma_cfg<false, 16>(mi, blocks, stream, lin, hdr, items);
-    } else {
-      if (s16) launch_chain_mfma_cfg<true, 8>(mi, blocks, stream, lin, hdr, items);
-      else launch_chain_mfma_cfg<false, 8>(mi, blocks, stream, lin, hdr, items);
-    }
-  }
+  if (trace) launch_chain_kernels<true>(ci, s16, blocks, lds, M, stream, lin, hdr, items);
+  else launch_chain_kernels<false>(ci, s16, blocks, lds, M, stream, lin, hdr, items);
   return hipGetLastError();
 }
 

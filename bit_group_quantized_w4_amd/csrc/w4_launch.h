@@ -97,9 +97,10 @@ int chain_choose_cfg(int kmax, double stage_bytes, int M);
 // Co-resident blocks per CU of configuration ci (s16: bf16 scales) for
 // M-row linears, with `lds` bytes of dynamic LDS (dot2 items only).
 hipError_t chain_blocks_per_cu(int ci, bool s16, size_t lds, int M, int* blocks);
-// The fill launch, then the chain launch.
+// The fill launch, then the chain launch (trace: the variant that writes
+// per-item timestamps to the buffer named in the workspace header).
 hipError_t launch_linear_chain(void* ws, int linears, int items, int ci, bool s16, int blocks, size_t lds, int M,
-                               hipStream_t stream);
+                               bool trace, hipStream_t stream);
 
 // s16: scales are bf16 bit patterns (uint16_t) instead of fp32.
 hipError_t launch_quantize_rtn(const float* W, int64_t N, int64_t K, uint8_t* q_packed,

@@ -335,11 +335,14 @@ w4_status w4_unpack(const uint8_t* q_packed, const float* d_packed, int64_t N, i
  *       order it runs them: stage by stage, within a stage longest K first,
  *       each linear's panels of rows_per_item rows in order) to the device
  *       buffer `stamps` (count >= 3 * plan->items uint64 values, 8-byte
- *       aligned, owned by the caller): [3i] the item's start, [3i + 1] when
- *       its block's first wavefront had its input (0 if it staged or waited
- *       for nothing), [3i + 2] its end.  stamps == NULL stops it.  The
- *       outputs do not change.  Synchronises `stream`; w4_chain_prepare
- *       clears it.
+ *       aligned, owned by the caller): [3i] the item's start, [3i + 1] at
+ *       M = 1 when its block's first wavefront had staged its input (0 if it
+ *       reused the previous item's, and always 0 at M > 1), [3i + 2] its end.
+ *       stamps == NULL stops it.  `plan` is updated (its `trace` field).  The
+ *       outputs do not change; passes run a variant of the chained kernel
+ *       that takes the stamps only while it is set (the plan's `trace`), so
+ *       untraced passes carry none of its cost.  Synchronises `stream`;
+ *       w4_chain_prepare clears it.
  *   w4_chain_error(plan, &flag, stream) -- synchronises `stream` and reads
  *       the workspace's error flag: nonzero if a wait of some pass ran out of
  *       time (it is bounded at tens of milliseconds; it can only run out if
@@ -380,6 +383,7 @@ typedef struct w4_chain_plan {
   int32_t linears, stages, items, blocks;
   int32_t config, lds_bytes, rows_per_item, waves_per_block;
   int32_t scale_bytes, rows;
+  int32_t trace, reserved;  /* trace: set by w4_chain_trace */
 } w4_chain_plan;
 
 size_t w4_chain_workspace_bytes(int64_t count);
@@ -390,7 +394,7 @@ w4_status w4_chain_prepare_s16(const w4_chain_linear_s16* linears, int64_t count
                                size_t workspace_bytes, w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_run(const w4_chain_plan* plan, hipStream_t stream);
 w4_status w4_chain_error(const w4_chain_plan* plan, uint32_t* flag, hipStream_t stream);
-w4_status w4_chain_trace(const w4_chain_plan* plan, uint64_t* stamps, size_t count, hipStream_t stream);
+w4_status w4_chain_trace(w4_chain_plan* plan, uint64_t* stamps, size_t count, hipStream_t stream);
 
 /*
  * w4_chain_prepare_noalloc -- w4_chain_prepare for callers that cannot

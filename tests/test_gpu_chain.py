@@ -471,9 +471,10 @@ def test_chain_verify_noalloc(w4, gpu, monkeypatch):
 
 @pytest.mark.parametrize("M", [1, 8])
 def test_chain_trace_timestamps(w4, gpu, M, monkeypatch):
-    """w4_chain_trace: every item gets a start, an input-ready and an end stamp
-    in order (ready 0 only for items that waited for nothing), the outputs are
-    those of an untraced pass bit for bit, and clearing it stops the writes."""
+    """w4_chain_trace: every item gets a start and an end stamp in order, and at
+    M = 1 an input-staged stamp between them (0 for items that reused the
+    previous item's input; always 0 at M > 1); the outputs are those of an
+    untraced pass bit for bit, and clearing it stops the writes."""
     # (K of 2048 and more: every wavefront of an item has a scale quad of its own)
     _say(f"chain timestamps M={M}: 2 layers (hidden 2048)")
     stages, records, x0 = _build_chain(w4, gpu, layers=2, hidden=2048, nq=2048, nkv=512, ffn=2816, seed=28,
@@ -496,8 +497,10 @@ def test_chain_trace_timestamps(w4, gpu, M, monkeypatch):
     assert (start > 0).all() and (end >= start).all()
     waited = ready > 0
     assert ((ready[waited] >= start[waited]) & (ready[waited] <= end[waited])).all()
-    assert waited.any()
+    assert waited.any() if M == 1 else not waited.any()
+    assert plan.plan.trace == 1
     plan.trace(None)
+    assert plan.plan.trace == 0
     stamps.zero_()
     plan.run()
     assert plan.error() == 0
