@@ -398,7 +398,10 @@ def chain_stage_times(torch, w4, workloads, name, M, passes=3):
     of the previous stage's last item to the end of its own last item), when
     its first item had its input relative to the previous stage's end, the
     items' mean and longest duration from input to end, and the share of the
-    grid's blocks that held one of its items.  Times in microseconds.
+    grid's blocks that held one of its items.  Times in microseconds.  Only
+    the M = 1 kernel stamps when an item had its input; at M > 1
+    ("timed_from": "start") both figures count from the item's start, so an
+    item's duration includes its wait for the input.
     """
     import numpy as np
 
@@ -460,7 +463,8 @@ def chain_stage_times(torch, w4, workloads, name, M, passes=3):
         prev_end = end
     total = (t[:, 2].max() - T0) * 0.01
     out = {"workload": name, "M": M, "items": items, "blocks": plan.plan.blocks, "rows_per_item": plan.plan.rows_per_item * 16,
-           "waves_per_block": plan.plan.waves_per_block, "traced_pass_us": round(float(total), 1), "stages": {}}
+           "waves_per_block": plan.plan.waves_per_block, "traced_pass_us": round(float(total), 1),
+           "timed_from": "input" if (t[:, 1] > 0).any() else "start", "stages": {}}
     for kind, r in acc.items():
         out["stages"][kind] = {"items": r["items"], "span_us": round(float(np.mean(r["span"])), 2),
                                "first_input_after_prev_end_us": round(float(np.mean(r["ready"])), 2),
