@@ -351,15 +351,15 @@ def verify_summary(stacks):
     return out
 
 
-def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4, M=1):
-    """One pass of the whole stack at M rows of x (a decode step at M = 1, the
-    verification of M - 1 drafted tokens above) as one chained launch
-    (w4_chain_run): the shared-input groups of every layer become stages, and
-    each stage reads the output of the previous one (q|k|v <- previous down,
-    o <- q, gate|up <- o, down <- gate), as in a real pass."""
+def chain_stages(torch, wl, layers, xs, M):
+    """The stages of a chained pass over a stack: the shared-input groups of
+    every layer, each stage reading the output of the previous one (q|k|v <-
+    previous down, o <- q, gate|up <- o, down <- gate); the first stage reads
+    xs[K].  layers: per layer, (matrix, q, d) in the stack's matrix order.
+    Returns (stages for w4.chain_prepare, the kind of each stage)."""
     dev = torch.device("cuda:0")
     groups = _shared_input_groups(wl)
-    stages, prev = [], []  # prev: (N, y) of the previous stage's linears
+    stages, kinds, prev = [], [], []  # prev: (N, y) of the previous stage's linears
     for mats in layers:
         # outputs of every layer in buffers of their own: a chain writes each line once
         ys = {m.name: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
@@ -367,7 +367,16 @@ def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale
             K = mats[gi[0]][0].K
             x = next((y for n, y in prev if n == K), xs[K])
             stages.append([(x, mats[i][1], mats[i][2], mats[i][0].N, ys[mats[i][0].name]) for i in gi])
+            kinds.append("|".join(mats[i][0].name for i in gi))
             prev = [(mats[i][0].N, ys[mats[i][0].name]) for i in gi]
+    return stages, kinds
+
+
+def bench_chain(torch, w4, workloads, wl, layers, xs, steps, warmup, name, scale_bytes=4, M=1):
+    """One pass of the whole stack at M rows of x (a decode step at M = 1, the
+    verification of M - 1 drafted tokens above) as one chained launch
+    (w4_chain_run) over the stages of chain_stages, as in a real pass."""
+    stages, _ = chain_stages(torch, wl, layers, xs, M)
     plan = w4.chain_prepare(stages)
     g = capture(torch, plan.run)
     t = time_graph(torch, g, steps, warmup)
@@ -417,16 +426,7 @@ def chain_stage_times(torch, w4, workloads, name, M, passes=3):
             mats.append((m, q, d))
         layers.append(mats)
     xs = {m.K: workloads.activations(name, 0, m.name, M, dev) for m in wl.matrices}
-    groups = _shared_input_groups(wl)
-    stages, kinds, prev = [], [], []
-    for mats in layers:
-        ys = {m.name: torch.empty((M, m.N), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
-        for gi in groups:
-            K = mats[gi[0]][0].K
-            x = next((y for n, y in prev if n == K), xs[K])
-            stages.append([(x, mats[i][1], mats[i][2], mats[i][0].N, ys[mats[i][0].name]) for i in gi])
-            kinds.append("|".join(mats[i][0].name for i in gi))
-            prev = [(mats[i][0].N, ys[mats[i][0].name]) for i in gi]
+    stages, kinds = chain_stages(torch, wl, layers, xs, M)
     plan = w4.chain_prepare(stages)
     items = plan.plan.items
     stamps = torch.zeros(3 * items, dtype=torch.int64, device=dev)
