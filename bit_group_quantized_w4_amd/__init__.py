@@ -325,10 +325,10 @@ class ChainPlan:
             _check(_lib.w4_chain_trace(ctypes.byref(self.plan), None, 0, self._stream()), "w4_chain_trace")
             self._stamps = None
             return
-        if not isinstance(stamps, torch.Tensor) or stamps.dtype != torch.int64 or not stamps.is_contiguous():
-            raise TypeError("stamps must be a contiguous int64 torch.Tensor")
-        _check(_lib.w4_chain_trace(ctypes.byref(self.plan), ctypes.c_void_p(stamps.data_ptr()), stamps.numel(),
-                                   self._stream()), "w4_chain_trace")
+        ptr = _dev(stamps, torch.int64, "stamps")
+        if stamps.device != torch.device(self.device):
+            raise ValueError(f"stamps must be on the chain's device {self.device} (got {stamps.device})")
+        _check(_lib.w4_chain_trace(ctypes.byref(self.plan), ptr, stamps.numel(), self._stream()), "w4_chain_trace")
         self._stamps = stamps  # kept alive while the chain may write it
 
     def error(self):

@@ -178,6 +178,14 @@ def test_chain_validation(w4):
     plan.items = 10
     assert lib.w4_chain_trace(ctypes.byref(plan), FAKE + 4, 30, None) == ERR_ALIGN
     assert lib.w4_chain_trace(ctypes.byref(plan), FAKE, 29, None) == ERR_ARG  # 3 values per item
+    # the binding passes only a GPU int64 tensor on the chain's device (a host
+    # address would become a write target of the kernel)
+    import torch
+    cp = w4.ChainPlan(None, plan, [], torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        cp.trace(torch.zeros(30, dtype=torch.int64))
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        cp.trace([0] * 30)
     plan = w4.ChainPlanC()
     assert lib.w4_chain_workspace_bytes(0) == 0
     assert lib.w4_chain_workspace_bytes(8193) == 0
