@@ -156,6 +156,15 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _one_device(tensors, what):
+    """The single device of `tensors`: every buffer of one call must live on the
+    GPU whose stream runs it."""
+    devs = {t.device for t in tensors if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError(f"{what}: tensors on several devices ({sorted(str(d) for d in devs)})")
+    return devs.pop() if devs else None
+
+
 def packed_bytes(N, K):
     return int(_lib.w4_packed_bytes(N, K))
 
@@ -248,6 +257,7 @@ def linear(x, q, d, N, path="auto", out=None, out_dtype=torch.bfloat16, workspac
         raise ValueError(f"path must be one of {sorted(PATHS)}")
     if workspace is not None:
         return linear_batched([(x, q, d, N, y)], path=path, workspace=workspace)[0]
+    _one_device([x, q, d, y], "linear")
     sd = _scale_dtype(d)
     if out_dtype == torch.float32:
         fn, name = ((_lib.w4_linear_f32_s16, "w4_linear_f32_s16") if sd == torch.bfloat16
@@ -286,6 +296,9 @@ def linear_batched(items, path="auto", workspace=None):
         descs[i] = LinearDesc(_dev(x, torch.bfloat16, "x").value, M, K, _dev(q, torch.uint8, "q").value,
                               _dev(d, sd, "d").value, N, _dev(y, od, "y").value)
         stream = stream or _stream(x)
+    dev = _one_device([t for it in items for t in (it[0], it[1], it[2], it[4])], "linear_batched")
+    if workspace is not None and dev is not None and workspace.buffer.device != dev:
+        raise ValueError(f"linear_batched: the workspace is on {workspace.buffer.device}, the linears on {dev}")
     # the descriptor structs of every variant have the same layout (pointers and int64s)
     if od == torch.float32:
         name = "w4_linear_batched_f32"
@@ -375,6 +388,7 @@ def chain_prepare(stages, noalloc=False):
                                _dev(d, sd, "d").value, N, _dev(y, torch.bfloat16, "y").value, s)
         tensors += [x, q, d, y]
         dev = dev or x.device
+    _one_device(tensors, "chain_prepare")
     plan = ChainPlanC()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     if noalloc:

@@ -186,6 +186,10 @@ def test_chain_validation(w4):
         cp.trace(torch.zeros(30, dtype=torch.int64))
     with pytest.raises(TypeError, match="torch.Tensor"):
         cp.trace([0] * 30)
+    # every buffer of one call on one device
+    assert w4._one_device([torch.zeros(2), torch.zeros(3)], "t") == torch.device("cpu")
+    with pytest.raises(ValueError, match="several devices"):
+        w4._one_device([torch.zeros(2), torch.empty(2, device="meta")], "t")
     plan = w4.ChainPlanC()
     assert lib.w4_chain_workspace_bytes(0) == 0
     assert lib.w4_chain_workspace_bytes(8193) == 0
