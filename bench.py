@@ -351,13 +351,14 @@ def verify_summary(stacks):
     return out
 
 
-def chain_stages(torch, wl, layers, xs, M):
+def chain_stages(torch, wl, layers, xs, M, dev=None):
     """The stages of a chained pass over a stack: the shared-input groups of
     every layer, each stage reading the output of the previous one (q|k|v <-
     previous down, o <- q, gate|up <- o, down <- gate); the first stage reads
     xs[K].  layers: per layer, (matrix, q, d) in the stack's matrix order.
+    Outputs are allocated on `dev` (default cuda:0).
     Returns (stages for w4.chain_prepare, the kind of each stage)."""
-    dev = torch.device("cuda:0")
+    dev = dev if dev is not None else torch.device("cuda:0")
     groups = _shared_input_groups(wl)
     stages, kinds, prev = [], [], []  # prev: (N, y) of the previous stage's linears
     for mats in layers:

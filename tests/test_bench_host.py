@@ -160,3 +160,38 @@ def test_verify_summary_rates(bench):
     assert s[8]["ceiling_tokens_per_s"] == 4000.0
     assert s[8]["tokens_per_s_at_acceptance"] == {"prose": [1100.0, 1250.0], "code": [2650.0, 2800.0]}
     assert s[16]["ceiling_tokens_per_s"] == 6400.0 and "tokens_per_s_at_acceptance" not in s[16]
+
+
+@pytest.mark.parametrize("name", ["stack_4b", "stack_27b", "stack_70b"])
+def test_chain_stages_wire_each_stage_to_the_previous_output(bench, name):
+    """The chained pass bench.py times: per layer the stages q|k|v, o, gate|up,
+    down; the first reads the external input, every later one the output of
+    the previous stage with matching width (q|k|v <- the previous layer's
+    down, o <- q, gate|up <- o, down <- gate)."""
+    import torch
+
+    import workloads
+
+    wl = workloads.WORKLOADS[name]
+    layers = [[(m, None, None) for m in wl.matrices] for _ in range(3)]
+    dev = torch.device("meta")
+    xs = {m.K: torch.empty((1, m.K), dtype=torch.bfloat16, device=dev) for m in wl.matrices}
+    stages, kinds = bench.chain_stages(torch, wl, layers, xs, 1, dev=dev)
+    assert kinds == ["q|k|v", "o", "gate|up", "down"] * 3
+    mats = {m.name: m for m in wl.matrices}
+    out = {}  # (stage, matrix name) -> y
+    for s, (st, kind) in enumerate(zip(stages, kinds)):
+        names = kind.split("|")
+        assert [N for _, _, _, N, _ in st] == [mats[n].N for n in names]
+        for n, (x, _, _, N, y) in zip(names, st):
+            assert x.shape == (1, mats[n].K) and y.shape == (1, N)
+            out[(s, n)] = y
+        x = st[0][0]
+        assert all(item[0] is x for item in st), "a stage's linears share one input"
+        if s == 0:
+            assert x is xs[mats["q"].K]
+        else:
+            feeder = {"q|k|v": "down", "o": "q", "gate|up": "o", "down": "gate"}[kind]
+            assert x is out[(s - 1, feeder)], f"stage {s} ({kind}) must read {feeder} of stage {s - 1}"
+    ys = [y for st in stages for *_, y in st]
+    assert len({id(y) for y in ys}) == len(ys), "every linear writes a buffer of its own"
