@@ -442,6 +442,16 @@ def chain_stage_times(torch, w4, workloads, name, M, passes=3):
     # item ranges of the stages, from the chain's table (item0 and stage of each linear)
     n = plan.plan.linears
     tab = plan.workspace[32:32 + 64 * n].cpu().numpy().view(np.int32).reshape(n, 16)
+    # the table's entries (w4_launch.h ChainLinear: a 48-byte LinearDesc whose
+    # int32 words 8-11 are M, K, N, flags, then item0 and stage) must be the
+    # chain's linears, stage by stage, their items in order
+    if not (tab[0, 12] == 0 and np.all(np.diff(tab[:, 12]) >= 0) and np.all(np.diff(tab[:, 13]) >= 0)
+            and tab[-1, 13] == len(stages) - 1):
+        raise RuntimeError("chain table layout: item and stage columns are not where expected")
+    for si, st in enumerate(stages):
+        got = sorted((int(k), int(nn)) for k, nn, s_ in zip(tab[:, 9], tab[:, 10], tab[:, 13]) if s_ == si)
+        if got != sorted((int(x.shape[1]), int(N)) for x, _, _, N, _ in st):
+            raise RuntimeError(f"chain table layout: stage {si} does not hold the stage's linears")
     first = {}
     for item0, st in zip(tab[:, 12], tab[:, 13]):
         first[int(st)] = min(first.get(int(st), items), int(item0))
